@@ -1,0 +1,169 @@
+"""CPU oracle of the rollout hot path: numpy wrappers over the plain C in ``oracle.c``.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the tests, the smoke check and the bench's CPU-baseline leg
+import this package. It shares no code with the HIP path and never imports it.
+
+``build()`` compiles ``oracle.c`` with gcc (-O2, no floating-point contraction) into ``liboracle.so``
+next to it; the wrappers build it on first use when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+NF = 16            # canonical state fields per env
+STACK = 4
+FRAME_DIMS = 15
+OBS_TILES = 31 * 43 + STACK * FRAME_DIMS + 4   # 1397
+PIX = 84
+STATE_FIELDS = ("x", "y", "vx", "vy", "facing", "freeze_ticks", "hook_ticks", "hook_held", "jump_held",
+                "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action")
+
+
+def build() -> str:
+    """Compile the oracle into liboracle.so (always recompiles)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("num_envs", "env_offset", "num_maps", "map_h", "map_w", "num_ckpts", "frame_skip",
+                 "time_limit")]
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    p = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    cfgp = ctypes.POINTER(_Cfg)
+    lib.oracle_env_reset.argtypes = [cfgp, p, p, p, p]
+    lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p]
+    lib.oracle_env_obs_tiles.argtypes = [cfgp, p, p, p, p, p, i64]
+    lib.oracle_env_obs_pixels.argtypes = [cfgp, p, p, p, p]
+    lib.oracle_gae.argtypes = [p, p, p, p, i32, i32, f64, f64, p, p]
+    lib.oracle_normalize.argtypes = [p, i64, f64, p, p, p]
+    lib.oracle_ppo_loss.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p]
+    for fn in (lib.oracle_env_reset, lib.oracle_env_step, lib.oracle_env_obs_tiles,
+               lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss):
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleEnv:
+    """A batch of envs held in numpy arrays: canonical state int32[N][16] and the frame stack
+    f32[N][4][15] (newest first)."""
+
+    def __init__(self, maps, ckpts, spawns, num_envs, frame_skip=3, time_limit=2000, sprites=None,
+                 env_offset=0):
+        self.maps = _c(maps, np.uint8)
+        self.ckpts = _c(ckpts, np.int32).reshape(self.maps.shape[0], -1, 2)
+        self.spawns = _c(spawns, np.int32).reshape(self.maps.shape[0], 2)
+        self.sprites = None if sprites is None else _c(sprites, np.uint8)
+        m, h, w = self.maps.shape
+        self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit)
+        self.n = num_envs
+        self.state = np.zeros((num_envs, NF), np.int32)
+        self.stack = np.zeros((num_envs, STACK, FRAME_DIMS), np.float32)
+        self._lib = _load()
+
+    def reset(self, mask=None):
+        mask = None if mask is None else _c(mask, np.uint8)
+        self._lib.oracle_env_reset(ctypes.byref(self.cfg), _ptr(self.spawns), _ptr(mask),
+                                   _ptr(self.state), _ptr(self.stack))
+
+    def step(self, actions):
+        """Advance every env one decision; returns (rewards f32[N], dones f32[N])."""
+        actions = _c(actions, np.int32)
+        assert actions.shape == (self.n,)
+        rew = np.empty(self.n, np.float32)
+        done = np.empty(self.n, np.float32)
+        self._lib.oracle_env_step(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.ckpts),
+                                  _ptr(self.spawns), _ptr(actions), _ptr(self.state), _ptr(self.stack),
+                                  _ptr(rew), _ptr(done))
+        return rew, done
+
+    def obs_tiles(self, out=None):
+        if out is None:
+            out = np.empty((self.n, OBS_TILES), np.float32)
+        assert out.dtype == np.float32 and out.flags.c_contiguous and out.shape[0] == self.n
+        self._lib.oracle_env_obs_tiles(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.ckpts),
+                                       _ptr(self.state), _ptr(self.stack), _ptr(out), out.shape[1])
+        return out
+
+    def obs_pixels(self, out=None):
+        assert self.sprites is not None
+        if out is None:
+            out = np.empty((self.n, STACK, PIX, PIX), np.uint8)
+        assert out.dtype == np.uint8 and out.flags.c_contiguous and out.shape[0] == self.n
+        self._lib.oracle_env_obs_pixels(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.sprites),
+                                        _ptr(self.stack), _ptr(out))
+        return out
+
+
+def gae(rewards, values, dones, last_values, gamma, lam):
+    """GAE by its definition sum, float64. Returns (adv, ret) float64[T][N]."""
+    r, v, d = (_c(a, np.float32) for a in (rewards, values, dones))
+    vl = _c(last_values, np.float32)
+    t, n = r.shape
+    adv = np.empty((t, n), np.float64)
+    ret = np.empty((t, n), np.float64)
+    _load().oracle_gae(_ptr(r), _ptr(v), _ptr(d), _ptr(vl), t, n, float(gamma), float(lam),
+                       _ptr(adv), _ptr(ret))
+    return adv, ret
+
+
+def normalize(adv, eps=1e-8):
+    """Whole-batch advantage normalisation, float64. Returns (normalised, mean, std)."""
+    a = _c(adv, np.float64)
+    out = np.empty_like(a)
+    mean = ctypes.c_double()
+    std = ctypes.c_double()
+    _load().oracle_normalize(_ptr(a), a.size, float(eps), _ptr(out), ctypes.byref(mean), ctypes.byref(std))
+    return out, mean.value, std.value
+
+
+def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2,
+             vf_coef=0.5, ent_coef=0.01):
+    """Per-minibatch PPO loss scalars, float64. Returns (out[num_mb][4], scale[num_mb][4]) with columns
+    (pg, value, entropy, total)."""
+    lg = _c(logits, np.float32)
+    b, a = lg.shape
+    act = _c(actions, np.int32).reshape(b)
+    olp = _c(old_logp, np.float32).reshape(b)
+    ad = _c(adv, np.float64).reshape(b)
+    rt = _c(ret, np.float64).reshape(b)
+    nv = _c(new_values, np.float32).reshape(b)
+    pm = None if perm is None else _c(perm, np.int32).reshape(b)
+    assert b % minibatch == 0
+    nmb = b // minibatch
+    out = np.empty((nmb, 4), np.float64)
+    scale = np.empty((nmb, 4), np.float64)
+    _load().oracle_ppo_loss(_ptr(lg), _ptr(act), _ptr(olp), _ptr(ad), _ptr(rt), _ptr(nv), _ptr(pm), b, a,
+                            minibatch, float(clip_eps), float(vf_coef), float(ent_coef), _ptr(out), _ptr(scale))
+    return out, scale

@@ -1,0 +1,490 @@
+/*
+ * CPU oracle of the GPU-resident PPO rollout hot path.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only the tests, the smoke check and the bench's CPU-baseline
+ * leg may load this library. It shares no source with the HIP path: every constant, table and step
+ * below is written out here on its own, from the pages that define the method.
+ *
+ * Plain, slow, single-threaded C. The environment is all integer arithmetic, so its outputs are exact;
+ * GAE, advantage normalisation and the PPO loss are computed in float64 from float32 inputs.
+ *
+ * Sources (page, then section):
+ *   [MARIO]    "Teaching Mario to speedrun" (bigmah.com): s.4 Reward (the return G_t), s.5 (the reverse
+ *              return loop), s.6 PPO (GAE, the clipped loss, the collect/judge/learn loop), s.7
+ *              PufferLib (the four shared arrays, the vecenv step, the platformer step function).
+ *   [DDNET]    boesch.dev DDNet RL post: "How it works each tick" (frame-skip 3, rewards accumulate
+ *              between decisions, contiguous [actions|observations|rewards|dones]), "What the agent
+ *              sees and does" (43x31 tile grid, 15-dim player state stacked 4 frames, 4 checkpoint
+ *              dims; direction/jump/hook), "Reward Engineering" Version 1 (+10 per checkpoint in
+ *              order, high-water-mark progress, time penalty) and Version 2 (+100 finish).
+ *   [PLAYTRAIN] "PlayTrain: An Efficient RL Framework for LLM-Generated Adaptable JavaScript Games":
+ *              Table 4 (terminated / truncated at 2000), Table 8 (clip 0.2, value 0.5, entropy 0.01),
+ *              App. B (frame stack, grayscale observation knobs).
+ *
+ * The pages never fix the environment's mechanics; every constant and step of the tick below is a
+ * reading, stated where it is used.
+ *
+ * Parity pins: GAE, normalisation and the loss are pinned by closed forms and hand-worked cases; the
+ * environment is pinned by hand-worked episodes and invariants only, since no page gives its outputs
+ * (its exhaustive-enumeration checks are "parity unpinned" beyond those invariants).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------------------------------- */
+/* Environment constants (readings; units: 1 tile = 256 sub-units, 1 pixel = 32 sub-units).         */
+/* ---------------------------------------------------------------------------------------------- */
+enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
+
+#define TILE 256            /* sub-units per tile */
+#define BOX 192             /* player box side, sub-units */
+#define GRAVITY 12          /* sub/tick^2 */
+#define MAX_FALL 160        /* sub/tick */
+#define JUMP_V 120          /* sub/tick */
+#define MAX_VX 48           /* sub/tick */
+#define ACC_GROUND 8
+#define ACC_AIR 4
+#define FREEZE_TICKS 30
+#define UNITS_CHECKPOINT 10240   /* +10 reward   (1 reward = 1024 units) */
+#define UNITS_FINISH 102400      /* +100 reward */
+#define WIN_W 43            /* tile window: 43 columns ... */
+#define WIN_H 31            /* ... by 31 rows */
+#define WIN_CX 21           /* the player's tile sits at window column 21, row 15 */
+#define WIN_CY 15
+#define STACK 4
+#define FRAME_DIMS 15
+#define OBS_TILES (WIN_W * WIN_H + STACK * FRAME_DIMS + 4) /* 1397 */
+#define PIX 84              /* pixel frame side */
+
+/* Canonical state layout: int32[N][NF] in this field order. */
+enum {
+    F_X, F_Y, F_VX, F_VY, F_FACING, F_FREEZE, F_HOOK_TICKS, F_HOOK_HELD, F_JUMP_HELD, F_GROUNDED,
+    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, NF
+};
+
+typedef struct {
+    int32_t num_envs;    /* envs in the arrays passed to this call */
+    int32_t env_offset;  /* global index of the first of them (env n plays map n mod num_maps) */
+    int32_t num_maps, map_h, map_w, num_ckpts;
+    int32_t frame_skip, time_limit;
+} oracle_cfg;
+
+typedef struct {
+    int32_t x, y, vx, vy, facing, freeze, hook_ticks, hook_held, jump_held, grounded;
+    int32_t wall_l, wall_r, tick, next, best_x, last_action;
+} env_t;
+
+static void load_env(const int32_t *s, env_t *e)
+{
+    e->x = s[F_X]; e->y = s[F_Y]; e->vx = s[F_VX]; e->vy = s[F_VY];
+    e->facing = s[F_FACING]; e->freeze = s[F_FREEZE]; e->hook_ticks = s[F_HOOK_TICKS];
+    e->hook_held = s[F_HOOK_HELD]; e->jump_held = s[F_JUMP_HELD]; e->grounded = s[F_GROUNDED];
+    e->wall_l = s[F_WALL_L]; e->wall_r = s[F_WALL_R]; e->tick = s[F_TICK]; e->next = s[F_NEXT];
+    e->best_x = s[F_BEST_X]; e->last_action = s[F_LAST_ACTION];
+}
+
+static void store_env(const env_t *e, int32_t *s)
+{
+    s[F_X] = e->x; s[F_Y] = e->y; s[F_VX] = e->vx; s[F_VY] = e->vy;
+    s[F_FACING] = e->facing; s[F_FREEZE] = e->freeze; s[F_HOOK_TICKS] = e->hook_ticks;
+    s[F_HOOK_HELD] = e->hook_held; s[F_JUMP_HELD] = e->jump_held; s[F_GROUNDED] = e->grounded;
+    s[F_WALL_L] = e->wall_l; s[F_WALL_R] = e->wall_r; s[F_TICK] = e->tick; s[F_NEXT] = e->next;
+    s[F_BEST_X] = e->best_x; s[F_LAST_ACTION] = e->last_action;
+}
+
+/* Mathematical floor of a / b for b > 0 (C's '/' truncates toward zero). */
+static int32_t floordiv(int32_t a, int32_t b)
+{
+    int32_t q = a / b;
+    if ((a % b) != 0 && a < 0) q -= 1;
+    return q;
+}
+
+/* Tile at (row, col) of map m; anything outside the map reads as SOLID (a reading). */
+static int tile_at(const oracle_cfg *c, const uint8_t *maps, int m, int32_t row, int32_t col)
+{
+    if (row < 0 || row >= c->map_h || col < 0 || col >= c->map_w) return SOLID;
+    return maps[((size_t)m * c->map_h + row) * c->map_w + col];
+}
+
+static int blocks(int t) { return t == SOLID || t == PLATFORM; }
+
+/* Is any blocking tile in column `col` over rows r0..r1? */
+static int solid_in_col(const oracle_cfg *c, const uint8_t *maps, int m, int32_t col, int32_t r0, int32_t r1)
+{
+    for (int32_t r = r0; r <= r1; ++r)
+        if (blocks(tile_at(c, maps, m, r, col))) return 1;
+    return 0;
+}
+
+/* Is any blocking tile in row `row` over columns c0..c1? */
+static int solid_in_row(const oracle_cfg *c, const uint8_t *maps, int m, int32_t row, int32_t c0, int32_t c1)
+{
+    for (int32_t col = c0; col <= c1; ++col)
+        if (blocks(tile_at(c, maps, m, row, col))) return 1;
+    return 0;
+}
+
+static int map_of(const oracle_cfg *c, int n) { return (c->env_offset + n) % c->num_maps; }
+
+/* Spawn state of an env on map m: standing at the map's spawn point, facing right, everything zero. */
+static void spawn_env(const int32_t *spawns, int m, env_t *e)
+{
+    memset(e, 0, sizeof *e);
+    e->x = spawns[2 * m + 0];
+    e->y = spawns[2 * m + 1];
+    e->facing = 1;
+    e->grounded = 1;
+    e->best_x = e->x;
+}
+
+/* The 15-dim frame of a state ("What the agent sees and does": position, velocity, hook state,
+ * freeze status). Sub-unit quantities are scaled by 2^-8 (tile units), the tick by 2^-11. */
+static void make_frame(const env_t *e, float *f)
+{
+    f[0] = (float)e->x * 0x1p-8f;
+    f[1] = (float)e->y * 0x1p-8f;
+    f[2] = (float)e->vx * 0x1p-8f;
+    f[3] = (float)e->vy * 0x1p-8f;
+    f[4] = (float)e->grounded;
+    f[5] = (float)e->facing;
+    f[6] = e->freeze > 0 ? 1.0f : 0.0f;
+    f[7] = (float)e->freeze;
+    f[8] = (float)e->hook_held;
+    f[9] = (float)e->hook_ticks;
+    f[10] = (float)e->jump_held;
+    f[11] = (float)e->wall_l;
+    f[12] = (float)e->wall_r;
+    f[13] = (float)e->tick * 0x1p-11f;
+    f[14] = (float)e->last_action;
+}
+
+/* Move v toward target by at most acc. */
+static int32_t approach(int32_t v, int32_t target, int32_t acc)
+{
+    if (v < target) return (v + acc > target) ? target : v + acc;
+    if (v > target) return (v - acc < target) ? target : v - acc;
+    return v;
+}
+
+/* One physics tick (all integer). Adds the tick's reward units to *units; returns 1 on the finish. */
+static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts, int m,
+                        env_t *e, int dir, int jump, int hook, int32_t *units)
+{
+    /* 1. a frozen player's input is ignored */
+    if (e->freeze > 0) { dir = 0; jump = 0; hook = 0; }
+
+    /* 2. horizontal velocity toward dir * MAX_VX; facing follows the pushed direction */
+    int32_t sign = dir == 1 ? -1 : (dir == 2 ? 1 : 0);
+    e->vx = approach(e->vx, sign * MAX_VX, e->grounded ? ACC_GROUND : ACC_AIR);
+    if (sign != 0) e->facing = sign;
+
+    /* 3-4. jump from the ground, then gravity with a terminal fall speed */
+    if (jump && e->grounded) e->vy = -JUMP_V;
+    e->vy = e->vy + GRAVITY;
+    if (e->vy > MAX_FALL) e->vy = MAX_FALL;
+
+    /* 5. move along x against the rows the box covers before the y move */
+    {
+        int32_t nx = e->x + e->vx;
+        int32_t r0 = floordiv(e->y, TILE), r1 = floordiv(e->y + BOX - 1, TILE);
+        if (e->vx > 0) {
+            int32_t col = floordiv(nx + BOX - 1, TILE);
+            if (solid_in_col(c, maps, m, col, r0, r1)) { nx = col * TILE - BOX; e->vx = 0; }
+        } else if (e->vx < 0) {
+            int32_t col = floordiv(nx, TILE);
+            if (solid_in_col(c, maps, m, col, r0, r1)) { nx = (col + 1) * TILE; e->vx = 0; }
+        }
+        e->x = nx;
+    }
+
+    /* 6. move along y against the columns the box covers after the x move */
+    {
+        int32_t ny = e->y + e->vy;
+        int32_t c0 = floordiv(e->x, TILE), c1 = floordiv(e->x + BOX - 1, TILE);
+        if (e->vy > 0) {
+            int32_t row = floordiv(ny + BOX - 1, TILE);
+            if (solid_in_row(c, maps, m, row, c0, c1)) { ny = row * TILE - BOX; e->vy = 0; }
+        } else if (e->vy < 0) {
+            int32_t row = floordiv(ny, TILE);
+            if (solid_in_row(c, maps, m, row, c0, c1)) { ny = (row + 1) * TILE; e->vy = 0; }
+        }
+        e->y = ny;
+    }
+
+    /* 7. contacts of the final box */
+    {
+        int32_t c0 = floordiv(e->x, TILE), c1 = floordiv(e->x + BOX - 1, TILE);
+        int32_t r0 = floordiv(e->y, TILE), r1 = floordiv(e->y + BOX - 1, TILE);
+        e->grounded = solid_in_row(c, maps, m, floordiv(e->y + BOX, TILE), c0, c1);
+        e->wall_l = solid_in_col(c, maps, m, floordiv(e->x - 1, TILE), r0, r1);
+        e->wall_r = solid_in_col(c, maps, m, floordiv(e->x + BOX, TILE), r0, r1);
+
+        /* 8. freeze: touching a freeze tile (re)arms the counter, otherwise it counts down */
+        int touching = 0;
+        for (int32_t r = r0; r <= r1; ++r)
+            for (int32_t col = c0; col <= c1; ++col)
+                if (tile_at(c, maps, m, r, col) == FREEZE) touching = 1;
+        if (touching) e->freeze = FREEZE_TICKS;
+        else if (e->freeze > 0) e->freeze -= 1;
+    }
+
+    /* 9. hook and jump state */
+    e->hook_ticks = hook ? (e->hook_ticks + 1 > 255 ? 255 : e->hook_ticks + 1) : 0;
+    e->hook_held = hook;
+    e->jump_held = jump;
+
+    /* 10. progress reward: one unit per sub-unit past the high-water mark, no backtrack penalty */
+    if (e->x > e->best_x) { *units += e->x - e->best_x; e->best_x = e->x; }
+
+    /* 11. checkpoints in order; passing the last one is the finish */
+    int finished = 0;
+    if (e->next < c->num_ckpts) {
+        const int32_t *ck = ckpts + ((size_t)m * c->num_ckpts + e->next) * 2;
+        if (floordiv(e->x + BOX / 2, TILE) >= ck[0]) {
+            *units += UNITS_CHECKPOINT;
+            e->next += 1;
+            if (e->next == c->num_ckpts) { *units += UNITS_FINISH; finished = 1; }
+        }
+    }
+
+    /* 12. time: one unit per tick */
+    e->tick += 1;
+    *units -= 1;
+    return finished;
+}
+
+/* Reset the envs whose mask byte is non-zero (all when mask is NULL): spawn state, and all STACK
+ * frames of the stack set to the spawn frame. */
+int oracle_env_reset(const oracle_cfg *c, const int32_t *spawns, const uint8_t *mask,
+                     int32_t *state, float *stack)
+{
+    for (int n = 0; n < c->num_envs; ++n) {
+        if (mask && !mask[n]) continue;
+        env_t e;
+        spawn_env(spawns, map_of(c, n), &e);
+        store_env(&e, state + (size_t)n * NF);
+        float f[FRAME_DIMS];
+        make_frame(&e, f);
+        for (int k = 0; k < STACK; ++k)
+            memcpy(stack + ((size_t)n * STACK + k) * FRAME_DIMS, f, sizeof f);
+    }
+    return 0;
+}
+
+/* One decision of every env ([MARIO] s.7 platformer step; [DDNET] frame-skip 3 with the rewards of
+ * the skipped ticks summed): up to frame_skip ticks, stopping after a terminal tick. The reward is
+ * the summed units times 2^-10; done = terminated or truncated. A done env is reset in place, so the
+ * reward and done describe the episode that ended while the state and stack are the new episode's.
+ * Otherwise the new frame is pushed onto the stack (newest first). */
+int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts,
+                    const int32_t *spawns, const int32_t *actions, int32_t *state, float *stack,
+                    float *rewards, float *dones)
+{
+    for (int n = 0; n < c->num_envs; ++n) {
+        int m = map_of(c, n);
+        env_t e;
+        load_env(state + (size_t)n * NF, &e);
+        int32_t a = actions[n];
+        if (a < 0 || a >= 12) a = 0;                   /* out-of-range actions act as no-op */
+        int dir = a / 4, jump = (a >> 1) & 1, hook = a & 1;
+
+        int32_t units = 0;
+        int terminated = 0, truncated = 0;
+        for (int i = 0; i < c->frame_skip && !terminated && !truncated; ++i) {
+            terminated = physics_tick(c, maps, ckpts, m, &e, dir, jump, hook, &units);
+            if (e.tick >= c->time_limit) truncated = 1;
+        }
+        e.last_action = a;
+        rewards[n] = (float)units * 0x1p-10f;
+        dones[n] = (terminated || truncated) ? 1.0f : 0.0f;
+
+        float *st = stack + (size_t)n * STACK * FRAME_DIMS;
+        if (terminated || truncated) {
+            spawn_env(spawns, m, &e);
+            float f[FRAME_DIMS];
+            make_frame(&e, f);
+            for (int k = 0; k < STACK; ++k) memcpy(st + k * FRAME_DIMS, f, sizeof f);
+        } else {
+            memmove(st + FRAME_DIMS, st, (STACK - 1) * FRAME_DIMS * sizeof(float));
+            make_frame(&e, st);
+        }
+        store_env(&e, state + (size_t)n * NF);
+    }
+    return 0;
+}
+
+/* Tile-mode observation of every env, f32[N][obs_stride] (first 1397 elements written):
+ *   [0, 1333)     the 31-row x 43-column tile window around the player's tile, row-major, value =
+ *                 tile code, outside the map = SOLID;
+ *   [1333, 1393)  the 4 most recent frames of 15 dims, newest first;
+ *   [1393, 1397)  next checkpoint dx, dy (tile units, from the box centre to the checkpoint tile's
+ *                 centre), checkpoints passed, best x (tile units). */
+int oracle_env_obs_tiles(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts,
+                         const int32_t *state, const float *stack, float *obs, int64_t obs_stride)
+{
+    for (int n = 0; n < c->num_envs; ++n) {
+        int m = map_of(c, n);
+        env_t e;
+        load_env(state + (size_t)n * NF, &e);
+        float *o = obs + (size_t)n * obs_stride;
+        int32_t pcol = floordiv(e.x + BOX / 2, TILE), prow = floordiv(e.y + BOX / 2, TILE);
+        for (int r = 0; r < WIN_H; ++r)
+            for (int col = 0; col < WIN_W; ++col)
+                o[r * WIN_W + col] = (float)tile_at(c, maps, m, prow - WIN_CY + r, pcol - WIN_CX + col);
+        memcpy(o + WIN_W * WIN_H, stack + (size_t)n * STACK * FRAME_DIMS,
+               STACK * FRAME_DIMS * sizeof(float));
+        float *ck = o + WIN_W * WIN_H + STACK * FRAME_DIMS;
+        if (e.next < c->num_ckpts) {
+            const int32_t *p = ckpts + ((size_t)m * c->num_ckpts + e.next) * 2;
+            ck[0] = (float)(p[0] * TILE + TILE / 2 - (e.x + BOX / 2)) * 0x1p-8f;
+            ck[1] = (float)(p[1] * TILE + TILE / 2 - (e.y + BOX / 2)) * 0x1p-8f;
+        } else {
+            ck[0] = 0.0f;
+            ck[1] = 0.0f;
+        }
+        ck[2] = (float)e.next;
+        ck[3] = (float)e.best_x * 0x1p-8f;
+    }
+    return 0;
+}
+
+/* Pixel-mode observation of every env, u8[N][4][84][84], newest frame first. Each frame is the 84x84
+ * grayscale camera view centred on the player's box at that frame's position, drawn from 8x8 sprites
+ * (pattern = tile code & 15, outside the map = SOLID), with the player's box drawn as 255. The
+ * positions of the older frames are the ones kept in the frame stack. */
+int oracle_env_obs_pixels(const oracle_cfg *c, const uint8_t *maps, const uint8_t *sprites,
+                          const float *stack, uint8_t *obs)
+{
+    for (int n = 0; n < c->num_envs; ++n) {
+        int m = map_of(c, n);
+        for (int k = 0; k < STACK; ++k) {
+            const float *f = stack + ((size_t)n * STACK + k) * FRAME_DIMS;
+            int32_t x = (int32_t)(f[0] * 256.0f), y = (int32_t)(f[1] * 256.0f);  /* exact */
+            int32_t cam_x = floordiv(x + BOX / 2, 32) - PIX / 2;
+            int32_t cam_y = floordiv(y + BOX / 2, 32) - PIX / 2;
+            int32_t bx0 = floordiv(x, 32), bx1 = floordiv(x + BOX - 1, 32);
+            int32_t by0 = floordiv(y, 32), by1 = floordiv(y + BOX - 1, 32);
+            uint8_t *o = obs + ((size_t)n * STACK + k) * PIX * PIX;
+            for (int py = 0; py < PIX; ++py) {
+                for (int px = 0; px < PIX; ++px) {
+                    int32_t wx = cam_x + px, wy = cam_y + py;
+                    uint8_t v;
+                    if (wx >= bx0 && wx <= bx1 && wy >= by0 && wy <= by1) {
+                        v = 255;
+                    } else {
+                        int t = tile_at(c, maps, m, floordiv(wy, 8), floordiv(wx, 8));
+                        int sy = wy - 8 * floordiv(wy, 8), sx = wx - 8 * floordiv(wx, 8);
+                        v = sprites[((t & 15) * 8 + sy) * 8 + sx];
+                    }
+                    o[py * PIX + px] = v;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------- */
+/* GAE ([MARIO] s.6 "Better advantages"), written as its definition:                               */
+/*   delta_t = r_t + gamma * V_{t+1} * (1 - d_t) - V_t,  V_T = last_values                          */
+/*   A_t     = sum_{k>=0} (gamma*lambda)^k * prod_{j<k} (1 - d_{t+j}) * delta_{t+k}                 */
+/*   R_t     = A_t + V_t                                                                            */
+/* d_t = 1 means the episode ended during step t (dones[t] is what step(actions[t]) returned), so it  */
+/* cuts both the bootstrap of delta_t and every later term. O(T^2) per env, float64.                */
+/* ---------------------------------------------------------------------------------------------- */
+int oracle_gae(const float *rewards, const float *values, const float *dones, const float *last_values,
+               int32_t T, int32_t N, double gamma, double lambda, double *adv, double *ret)
+{
+    for (int32_t n = 0; n < N; ++n) {
+        for (int32_t t = 0; t < T; ++t) {
+            double a = 0.0, w = 1.0;
+            for (int32_t k = t; k < T; ++k) {
+                double v_next = (k + 1 < T) ? (double)values[(size_t)(k + 1) * N + n] : (double)last_values[n];
+                double d = (double)dones[(size_t)k * N + n];
+                double delta = (double)rewards[(size_t)k * N + n] + gamma * v_next * (1.0 - d)
+                             - (double)values[(size_t)k * N + n];
+                a += w * delta;
+                w *= gamma * lambda * (1.0 - d);
+            }
+            adv[(size_t)t * N + n] = a;
+            ret[(size_t)t * N + n] = a + (double)values[(size_t)t * N + n];
+        }
+    }
+    return 0;
+}
+
+/* Advantage normalisation over the whole batch: mean and population standard deviation, then
+ * (A - mean) / (std + eps). Two passes, float64. */
+int oracle_normalize(const double *adv, int64_t n, double eps, double *out, double *mean_out, double *std_out)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += adv[i];
+    double mean = s / (double)n;
+    double q = 0.0;
+    for (int64_t i = 0; i < n; ++i) q += (adv[i] - mean) * (adv[i] - mean);
+    double std = sqrt(q / (double)n);
+    if (out)
+        for (int64_t i = 0; i < n; ++i) out[i] = (adv[i] - mean) / (std + eps);
+    if (mean_out) *mean_out = mean;
+    if (std_out) *std_out = std;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------- */
+/* PPO loss forward ([MARIO] s.6 "Don't move too far at once"), per minibatch m over the samples      */
+/* i = perm[m*mb + k] (k < mb; i = m*mb + k when perm is NULL):                                     */
+/*   logp_i  = z_{i,a_i} - logsumexp(z_i)                                                           */
+/*   ratio_i = exp(logp_i - old_logp_i)          (new probability over old probability)             */
+/*   pg_i    = -min(ratio_i * A_i, clip(ratio_i, 1 - eps, 1 + eps) * A_i)                           */
+/*   v_i     = (V_i - R_i)^2                                                                         */
+/*   H_i     = entropy of softmax(z_i)                                                               */
+/* out[m] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}; scale[m] holds */
+/* the mean absolute summand of each (the tolerance floor).                                          */
+/* ---------------------------------------------------------------------------------------------- */
+int oracle_ppo_loss(const float *logits, const int32_t *actions, const float *old_logp, const double *adv,
+                    const double *ret, const float *new_values, const int32_t *perm, int64_t B, int32_t A,
+                    int32_t mb, double clip_eps, double vf_coef, double ent_coef, double *out, double *scale)
+{
+    int64_t num_mb = B / mb;
+    for (int64_t m = 0; m < num_mb; ++m) {
+        double s_pg = 0, s_v = 0, s_h = 0, a_pg = 0, a_h = 0;
+        for (int64_t k = 0; k < mb; ++k) {
+            int64_t i = perm ? (int64_t)perm[m * mb + k] : m * mb + k;
+            const float *z = logits + (size_t)i * A;
+            double zmax = z[0];
+            for (int j = 1; j < A; ++j) if ((double)z[j] > zmax) zmax = z[j];
+            double sum = 0.0;
+            for (int j = 0; j < A; ++j) sum += exp((double)z[j] - zmax);
+            double lse = zmax + log(sum);
+            double ent = 0.0;  /* -sum p_j log p_j */
+            for (int j = 0; j < A; ++j) {
+                double lp = (double)z[j] - lse;
+                ent -= exp(lp) * lp;
+            }
+            double logp = (double)z[actions[i]] - lse;
+            double ratio = exp(logp - (double)old_logp[i]);
+            double clipped = ratio < 1.0 - clip_eps ? 1.0 - clip_eps : (ratio > 1.0 + clip_eps ? 1.0 + clip_eps : ratio);
+            double s1 = ratio * adv[i], s2 = clipped * adv[i];
+            double pg = -(s1 < s2 ? s1 : s2);
+            double dv = (double)new_values[i] - ret[i];
+            double v = dv * dv;
+            s_pg += pg; s_v += v; s_h += ent;
+            a_pg += fabs(pg); a_h += fabs(ent);
+        }
+        double pg = s_pg / mb, v = s_v / mb, h = s_h / mb;
+        out[m * 4 + 0] = pg;
+        out[m * 4 + 1] = v;
+        out[m * 4 + 2] = h;
+        out[m * 4 + 3] = pg + vf_coef * v - ent_coef * h;
+        if (scale) {
+            scale[m * 4 + 0] = a_pg / mb;
+            scale[m * 4 + 1] = v;
+            scale[m * 4 + 2] = a_h / mb;
+            scale[m * 4 + 3] = a_pg / mb + vf_coef * v + ent_coef * a_h / mb;
+        }
+    }
+    return 0;
+}
