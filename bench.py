@@ -1,0 +1,230 @@
+"""Throughput of the GPU-resident PPO rollout hot path on one MI355X.
+
+One timed step is one whole rollout of the full-rollout workload: 65536 envs on 64 seeded 256x1024 tile
+maps step 128 times (env_step + obs_gather writing 31x43 tile windows, 4x15 frame stacks and checkpoint
+dims into a resident [actions | obs | rewards | dones] rollout buffer), then GAE (gamma 0.99, lambda 0.95)
+with whole-batch advantage normalisation, then the PPO clipped-surrogate / value / entropy loss over 16
+shuffled minibatches of 524288 samples. Policy outputs (actions sampled from seeded old logits, new
+logits, values) are seeded N(0,1) stand-ins, generated before timing and resident in HBM.
+
+Prints one JSON line: env-steps/s of the whole job, the roofline of the env step (the dominant kernels),
+GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N_ENVS, HORIZON, N_MAPS, MAP_H, MAP_W, MINIBATCHES = 65536, 128, 64, 256, 1024, 16
+GAMMA, LAMBDA = 0.99, 0.95
+
+# Algorithmic HBM bytes per unit (state layout of the env kernels: 5 ring words + 2 extra words per env).
+ENV_STEP_BYTES = 4 + 20 + 8 + 20 + 8 + 4 + 4          # action, slot read, extras r/w, slot write, reward, done
+OBS_TILE_BYTES = 1397 * 4 + 4 * 20 + 8                # observation write + 4 ring slots + extras read
+ENV_BYTES_PER_ENV_STEP = ENV_STEP_BYTES + OBS_TILE_BYTES
+GAE_BYTES_PER_ELEM = 5 * 4 + 2 * 4                    # r, v, d in; adv, ret out; normalise: adv in + out
+LOSS_BYTES_PER_SAMPLE = 12 * 4 + 6 * 4                # logits row; action, old logp, adv, ret, value, perm
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10, help="timed rollouts")
+    p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-envs", type=int, default=8192, help="envs in the oracle's bounded sample")
+    return p.parse_args()
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when the kernel source has
+    changed since they were taken (or none were taken)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or source_sha(src) != rec["source_sha"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
+    """The oracle as it stands, single-threaded, on the first n_sample envs of the same workload: 128
+    steps with tile observations, GAE by its definition with normalisation, and the loss over the
+    sample's batch in minibatches of the same share. Returns env-steps/s of the whole path."""
+    import oracle
+    n = n_sample
+    t0 = time.perf_counter()
+    env = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n)
+    env.reset()
+    obs = np.empty((n, 1397), np.float32)
+    rew = np.empty((HORIZON, n), np.float32)
+    dn = np.empty((HORIZON, n), np.float32)
+    for t in range(HORIZON):
+        rew[t], dn[t] = env.step(policy_actions[t, :n])
+        env.obs_tiles(obs)
+    adv, ret = oracle.gae(rew, values[:, :n], dn, last_values[:n], float(np.float32(GAMMA)),
+                          float(np.float32(LAMBDA)))
+    na, _, _ = oracle.normalize(adv)
+    b = HORIZON * n
+    sel = np.arange(HORIZON)[:, None] * N_ENVS + np.arange(n)[None, :]
+    sel = sel.reshape(-1)
+    perm = np.random.default_rng(5).permutation(b).astype(np.int32)
+    oracle.ppo_loss(pi.new_logits[sel], policy_actions[:, :n].reshape(-1), pi.old_logp[sel], na.reshape(-1),
+                    ret.reshape(-1), pi.new_values[sel], perm, b // MINIBATCHES)
+    dt = time.perf_counter() - t0
+    return b / dt, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from resident_rl_rollout_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+
+    # ---- seeded inputs, made resident before timing ----
+    ms = inputs.make_mapset(range(100, 100 + N_MAPS), MAP_H, MAP_W)
+    b = HORIZON * N_ENVS
+    pi = inputs.make_policy_inputs(20, b)
+    values, last_values = inputs.make_values(21, HORIZON, N_ENVS)
+    policy_actions = pi.actions.reshape(HORIZON, N_ENVS)
+
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev)
+    # rollout buffer: one allocation of [actions T*N | obs T*N*1397 | rewards T*N | dones T*N]
+    a_bytes = HORIZON * N_ENVS * 4
+    o_bytes = HORIZON * N_ENVS * 1397 * 4
+    offs = [0, a_bytes, a_bytes + o_bytes, a_bytes + o_bytes + a_bytes]
+    buf = torch.empty(offs[3] + a_bytes, dtype=torch.uint8, device=dev)
+    actions = buf[offs[0]:offs[1]].view(torch.int32).view(HORIZON, N_ENVS)
+    obs = buf[offs[1]:offs[2]].view(torch.float32).view(HORIZON, N_ENVS, 1397)
+    rewards = buf[offs[2]:offs[3]].view(torch.float32).view(HORIZON, N_ENVS)
+    dones = buf[offs[3]:].view(torch.float32).view(HORIZON, N_ENVS)
+    actions.copy_(torch.from_numpy(policy_actions))
+    t_ = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    logits, old_logp, new_v, perm = t_(pi.new_logits), t_(pi.old_logp), t_(pi.new_values), t_(pi.perm)
+    values_d, last_d = t_(values), t_(last_values)
+    adv = torch.empty((HORIZON, N_ENVS), dtype=torch.float32, device=dev)
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    loss_out = torch.empty((MINIBATCHES, 4), dtype=torch.float32, device=dev)
+    mb = b // MINIBATCHES
+    env.reset(obs[0])
+    torch.cuda.synchronize()
+
+    def rollout(ev=None):
+        for t in range(HORIZON):
+            if ev is not None:
+                ev["env"][t][0].record()
+            env.step(actions[t], obs[t], rewards[t], dones[t])
+            if ev is not None:
+                ev["env"][t][1].record()
+        if ev is not None:
+            ev["gae"][0].record()
+        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=1, adv=adv, ret=ret, adv_stats=stats)
+        if ev is not None:
+            ev["gae"][1].record()
+            ev["loss"][0].record()
+        binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, perm, mb,
+                         out=loss_out)
+        if ev is not None:
+            ev["loss"][1].record()
+
+    for _ in range(args.warmup):
+        rollout()
+    torch.cuda.synchronize()
+
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    events = [{"env": [mk() for _ in range(HORIZON)], "gae": mk(), "loss": mk()} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        rollout(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    env_ms = np.array([[s.elapsed_time(e) for s, e in ev["env"]] for ev in events])   # [K][T]
+    gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
+    loss_ms = np.array([ev["loss"][0].elapsed_time(ev["loss"][1]) for ev in events])
+    env_steps = args.steps * HORIZON * N_ENVS
+    value = env_steps / wall
+
+    env_launch_bytes = N_ENVS * ENV_BYTES_PER_ENV_STEP
+    env_avg_s = float(env_ms.mean()) * 1e-3
+    achieved = env_launch_bytes / env_avg_s / 1e9
+    gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
+    loss_bytes = b * LOSS_BYTES_PER_SAMPLE
+    gae_gbs = gae_bytes / (float(gae_ms.mean()) * 1e-3) / 1e9
+    loss_gbs = loss_bytes / (float(loss_ms.mean()) * 1e-3) / 1e9
+    gl_gbs = (gae_bytes + loss_bytes) / (float((gae_ms + loss_ms).mean()) * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_s = min(args.cpu_envs, N_ENVS)
+        rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
+        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} of the 65536 envs x 128 steps (env step + tile obs), GAE + normalisation "
+                         f"over [128][{n_s}], loss over the sample's {HORIZON * n_s} samples in 16 minibatches; "
+                         f"{dt:.1f} s single-threaded"}
+
+    out = {
+        "metric": "env-steps/s incl. obs write at 65536 envs; GAE+loss GB/s vs HBM peak",
+        "value": value,
+        "unit": "env-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i32+f32",
+        "data": "synthetic",
+        "config": {"workload": "full rollout: 65536 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
+                               "tile obs (31x43 + 4x15 + 4) into a resident rollout buffer, GAE + whole-batch "
+                               "normalisation, PPO loss over 16 shuffled minibatches of 524288",
+                   "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES},
+        "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("env_step+obs_gather"),
+                     "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
+        "env_step_us": float(env_ms.mean()) * 1e3,
+        "gae": {"us": float(gae_ms.mean()) * 1e3, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS},
+        "loss": {"us": float(loss_ms.mean()) * 1e3, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS},
+        "gae_loss_GB/s": gl_gbs,
+        "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
+        "loss_check": loss_out[0].tolist(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * rl.h -- C ABI of the GPU-resident PPO rollout hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Three stages, all on one GPU, all data resident in HBM:
+ *   1. batched platformer stepping with frame-skip and auto-reset, writing observations, rewards and
+ *      dones into caller-owned device buffers (rl_env_*);
+ *   2. the GAE reverse scan over a [T][N] rollout with optional whole-batch advantage normalisation
+ *      (rl_gae);
+ *   3. the PPO clipped-surrogate, value and entropy loss reductions per minibatch (rl_ppo_loss).
+ *
+ * Sources (page, then section):
+ *   "Teaching Mario to speedrun" (bigmah.com): s.4 the return; s.6 GAE, the clipped loss and the
+ *     collect / judge / learn loop; s.7 the four flat arrays shared by trainer and envs (observations
+ *     [num_agents][obs_size], actions, rewards, terminals) and the env functions init / reset / step /
+ *     close, with a platformer step that runs `frameskip` physics ticks and stops on a terminal tick.
+ *   boesch.dev DDNet RL post: "How it works each tick" (frame-skip 3, rewards summed between decisions,
+ *     one contiguous [actions | observations | rewards | dones] region), "What the agent sees and does"
+ *     (43x31 tile grid, 15-dim player state stacked over 4 frames, 4 checkpoint dims; direction x jump x
+ *     hook actions), "Reward Engineering" (+10 per checkpoint in order, high-water-mark progress, time
+ *     penalty; +100 finish).
+ *   NeSLE article on kongchang.com ("observations never leave VRAM"): observations written by the
+ *     kernels into preallocated device buffers that the trainer uses in place, buffers reused across
+ *     iterations.
+ *   PlayTrain (arXiv 2609.09059): Table 4 (terminated / truncated at a 2000-step limit), Table 8 (clip
+ *     0.2, value coefficient 0.5, entropy coefficient 0.01, GAE lambda 0.95), App. B (frame stack,
+ *     grayscale observation).
+ *
+ * Conventions for every function:
+ *   - Returns RL_OK (0) or a negative RL_E* code; rl_last_error() then holds a message (thread-local).
+ *   - Arguments are validated before any HIP call; a rejected call enqueues nothing.
+ *   - Pointers named as device pointers must be device memory the caller owns (for instance torch
+ *     tensors); the library never allocates, frees or synchronises device memory, and never copies
+ *     between host and device except where stated.
+ *   - `stream` is a hipStream_t (NULL = the default stream); all work is enqueued on it in order.
+ *     Kernel faults surface at the caller's next synchronisation.
+ *   - An env handle may be used from one stream at a time. No C++ exception crosses this ABI.
+ */
+#ifndef RL_H
+#define RL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    RL_OK = 0,
+    RL_EINVAL = -1,     /* null pointer, size or enum out of range */
+    RL_EALIGN = -2,     /* a pointer or stride breaks the stated alignment */
+    RL_ESIZE = -3,      /* a caller buffer (state, workspace) is smaller than required */
+    RL_EHIP = -4        /* a HIP launch or API call failed; the HIP message is in rl_last_error() */
+};
+
+enum { RL_OBS_TILES = 0, RL_OBS_PIXELS = 1 };
+
+#define RL_STATE_FIELDS 16      /* canonical state fields per env, see rl_env_read_state */
+#define RL_OBS_TILES_SIZE 1397  /* f32 elements: 31*43 window + 4*15 frames + 4 checkpoint dims */
+#define RL_OBS_PIXELS_SIZE 28224 /* u8 elements: 4 frames of 84*84 */
+#define RL_MAX_FRAME_SKIP 5
+
+/* Environment configuration. Positions are in sub-units: one tile = 256, the player box is 192 wide
+ * and tall. Tile codes: 0 air, 1 solid, 2 platform (solid), 3 freeze (passable; touching it ignores the
+ * player's input for 30 ticks). */
+typedef struct rl_env_config {
+    int32_t num_envs;    /* N >= 1; env n plays map n mod num_maps for its whole life */
+    int32_t num_maps;    /* M >= 1 */
+    int32_t map_h;       /* rows per map, 1 .. 4096 */
+    int32_t map_w;       /* columns per map, 1 .. 65536 */
+    int32_t num_ckpts;   /* K >= 0 checkpoints per map; passing the K-th is the finish */
+    int32_t frame_skip;  /* physics ticks per decision, 1 .. RL_MAX_FRAME_SKIP (3 on the pages) */
+    int32_t time_limit;  /* ticks per episode before truncation, >= 1 (2000) */
+    int32_t obs_mode;    /* RL_OBS_TILES (f32 observations) or RL_OBS_PIXELS (u8 observations) */
+    int64_t obs_stride;  /* elements from one env's observation to the next, >= the observation size;
+                            tiles: a multiple of 1 f32, pixels: a multiple of 4 u8 */
+} rl_env_config;
+
+typedef struct rl_env rl_env;   /* opaque host handle */
+
+/* Bytes of device memory the caller must provide as the env state buffer (256-byte aligned). It holds
+ * the per-env state in structure-of-arrays form, a ring of the last 4 frames, a padded copy of the maps
+ * and the checkpoint, spawn and sprite tables. */
+int rl_env_state_bytes(const rl_env_config* cfg, size_t* bytes);
+
+/* Elements in one env's observation (1397 for tiles, 28224 for pixels) and the element size in bytes
+ * (4 for f32 tiles, 1 for u8 pixels). */
+int rl_env_obs_size(const rl_env_config* cfg, size_t* elems, size_t* elem_bytes);
+
+/* Layout of one contiguous step block [actions int32[N] | observations [N][obs_stride] | rewards f32[N]
+ * | dones f32[N]] (the four flat arrays of the pages, each sub-array 256-byte aligned): writes the four
+ * byte offsets and the block size. */
+int rl_step_layout(const rl_env_config* cfg, size_t offsets[4], size_t* block_bytes);
+
+/* Create an env batch over the caller's state buffer. Copies maps, checkpoints, spawns and sprites into
+ * the state buffer with kernels on `stream` (the inputs may be freed once the stream has passed this
+ * call) and resets every env.
+ *   maps     device u8[M][H][W], row 0 at the top; cells outside the map read as solid.
+ *   ckpts    device int32[M][K][2] (column, row) of each map's checkpoints, in the order they must be
+ *            passed; may be NULL when K = 0.
+ *   spawns   device int32[M][2] (x, y) spawn position of each map in sub-units.
+ *   sprites  device u8[16][8][8] grayscale patterns (pattern = tile code & 15); required for pixel mode,
+ *            ignored (may be NULL) for tiles.
+ *   state    device buffer of rl_env_state_bytes() bytes, 256-byte aligned, owned by the caller for the
+ *            handle's lifetime; its contents are the whole env state (copying it snapshots the envs).
+ * On success *out receives a handle to free with rl_env_destroy. */
+int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* ckpts,
+                  const int32_t* spawns, const uint8_t* sprites, void* state, size_t state_bytes,
+                  void* stream, rl_env** out);
+
+/* Reset the envs whose mask byte is non-zero (mask = device u8[N], or NULL for all) to their spawn
+ * state with all 4 stacked frames equal to the spawn frame, then, when obs is not NULL, write every
+ * env's observation to obs (device, [N][obs_stride] of the mode's element type). */
+int rl_env_reset(rl_env* env, const uint8_t* mask, void* obs, void* stream);
+
+/* One decision of every env (the pages' step: read actions, advance, write observations / rewards /
+ * terminals). For env n: decode actions[n] in [0, 12) as direction = a / 4 (none, left, right),
+ * jump = bit 1, hook = bit 0 (other values act as 0); run up to frame_skip ticks, stopping after a
+ * terminal tick; rewards[n] = the summed reward units times 2^-10 (progress past the best x, +10 per
+ * checkpoint in order, +100 at the finish, -2^-10 per tick); dones[n] = 1 if the episode finished or hit
+ * the time limit, else 0. A done env is reset in place: its reward and done describe the episode that
+ * ended, its observation is the new episode's first. Observations (tiles: the 31x43 window around the
+ * player's tile, the last 4 frames newest first, next checkpoint dx / dy, checkpoints passed, best x;
+ * pixels: 4 frames of 84x84, newest first) go to obs.
+ *   actions  device int32[N]; obs device [N][obs_stride]; rewards, dones device f32[N]. */
+int rl_env_step(rl_env* env, const int32_t* actions, void* obs, float* rewards, float* dones,
+                void* stream);
+
+/* Decode the state of every env into device int32[N][RL_STATE_FIELDS] with fields in the order
+ * x, y, vx, vy, facing (+1/-1), freeze_ticks, hook_ticks, hook_held, jump_held, grounded, wall_left,
+ * wall_right, tick, next_ckpt, best_x, last_action. */
+int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
+
+/* The decision counter, whose value mod 4 selects the frame ring's newest slot. Saving the state
+ * buffer together with this counter and restoring both resumes the envs exactly. */
+int rl_env_get_step_counter(const rl_env* env, int64_t* counter);
+int rl_env_set_step_counter(rl_env* env, int64_t counter);
+
+/* Free the host handle (the state buffer stays the caller's). NULL is ignored. */
+void rl_env_destroy(rl_env* env);
+
+/* Workspace bytes rl_gae needs for T x N. */
+int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes);
+
+/* GAE over a [T][N] rollout ("Teaching Mario to speedrun", s.6 Better advantages), float32:
+ *   delta_t = r_t + gamma * V_{t+1} * (1 - d_t) - V_t  (V_T = last_values)
+ *   A_t = delta_t + gamma * lambda * (1 - d_t) * A_{t+1},  A_T = 0;   ret_t = A_t + V_t
+ * where dones[t][n] = 1 means env n's episode ended during step t.
+ *   rewards, values, dones  device f32[T][N];  last_values device f32[N]
+ *   adv, ret                device f32[T][N] outputs (may not alias the inputs)
+ *   normalize  0: no statistics; 1: compute the whole-batch mean and population std of A and overwrite
+ *              adv with (A - mean) / (std + 1e-8); 2: compute the statistics only (adv stays raw) so that
+ *              rl_ppo_loss can normalise on the fly. ret always uses the raw A.
+ *   adv_stats  device f64[3] = {count, mean, std}, written when normalize != 0 (may be NULL for 0).
+ *   ws         device workspace of rl_gae_workspace_bytes(T, N) bytes, 8-byte aligned, zero-filled before
+ *              its first use; every call leaves it zero-filled again. Calls sharing a workspace must not
+ *              overlap.
+ * Statistics are reduced in a fixed order, so results are identical from run to run. */
+int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values,
+           int32_t T, int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize,
+           double* adv_stats, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes rl_ppo_loss needs for B samples in minibatches of mb. */
+int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
+
+/* PPO loss forward per minibatch ("Teaching Mario to speedrun", s.6 Don't move too far at once; the
+ * coefficients of PlayTrain Table 8 are the usual arguments). Minibatch m holds samples
+ * i = perm[m*mb + k], k < mb (i = m*mb + k when perm is NULL); for each:
+ *   logp = logits[i][actions[i]] - logsumexp(logits[i]),  ratio = exp(logp - old_logp[i])
+ *   pg = -min(ratio * A, clip(ratio, 1 - clip_eps, 1 + clip_eps) * A),  v = (new_values[i] - ret[i])^2,
+ *   H = entropy of softmax(logits[i]),  with A = adv[i], or (adv[i] - mean) / (std + 1e-8) from
+ *   adv_stats when adv_stats is not NULL.
+ *   out  device f32[B/mb][4] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}.
+ *   logits device f32[B][A] (16-byte aligned rows need A % 4 == 0; any A in 1..64 is accepted);
+ *   actions device int32[B] in [0, A); old_logp, adv, ret, new_values device f32[B]; perm device
+ *   int32[B], a permutation of 0..B-1, or NULL.
+ *   B % mb must be 0. ws as for rl_gae (rl_ppo_loss_workspace_bytes bytes, zero-filled before first use,
+ *   left zero-filled). Reductions use float64 partials in a fixed order. */
+int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                const float* ret, const float* new_values, const int32_t* perm, const double* adv_stats,
+                int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef, float ent_coef,
+                float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* rl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RL_H */

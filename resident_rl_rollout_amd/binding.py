@@ -1,0 +1,242 @@
+"""Python binding of librl.so: argument marshalling only.
+
+Every function here forwards to the C ABI declared in include/rl.h with the same name. PyTorch is used
+only to own device memory (tensors) and to name the stream (the current HIP stream); every step of the
+rollout path runs in the library's HIP kernels. If librl.so is missing the binding raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librl.so")
+
+OBS_TILES, OBS_PIXELS = 0, 1
+STATE_FIELDS = 16
+OBS_TILES_SIZE = 1397
+OBS_PIXELS_SIZE = 28224
+
+_lib = None
+
+
+class RLError(RuntimeError):
+    """A non-zero status from the library, with its rl_last_error() text."""
+
+
+class EnvConfig(ctypes.Structure):
+    _fields_ = [("num_envs", ctypes.c_int32), ("num_maps", ctypes.c_int32), ("map_h", ctypes.c_int32),
+                ("map_w", ctypes.c_int32), ("num_ckpts", ctypes.c_int32), ("frame_skip", ctypes.c_int32),
+                ("time_limit", ctypes.c_int32), ("obs_mode", ctypes.c_int32), ("obs_stride", ctypes.c_int64)]
+
+
+# (name, restype, argtypes) of every symbol include/rl.h declares.
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_CFG = ctypes.POINTER(EnvConfig)
+SIGNATURES = [
+    ("rl_env_state_bytes", ctypes.c_int, [_CFG, ctypes.POINTER(_SZ)]),
+    ("rl_env_obs_size", ctypes.c_int, [_CFG, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+    ("rl_step_layout", ctypes.c_int, [_CFG, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+    ("rl_env_create", ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    ("rl_env_reset", ctypes.c_int, [_P, _P, _P, _P]),
+    ("rl_env_step", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
+    ("rl_env_get_step_counter", ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
+    ("rl_env_set_step_counter", ctypes.c_int, [_P, _I64]),
+    ("rl_env_destroy", None, [_P]),
+    ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
+    ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
+    ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P, _P,
+                                   _SZ, _P]),
+    ("rl_last_error", ctypes.c_char_p, []),
+]
+
+
+def lib():
+    """The loaded library with every signature declared; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m resident_rl_rollout_amd.build` "
+                           "(there is no non-HIP fallback)")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, res, args in SIGNATURES:
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = handle
+    return handle
+
+
+def check(rc: int) -> None:
+    if rc != 0:
+        raise RLError(f"status {rc}: {lib().rl_last_error().decode()}")
+
+
+def stream_ptr(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dptr(t, dtype=None, what="tensor"):
+    """Device pointer of a contiguous CUDA tensor (None passes through as NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(x, dtype, device):
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    return x.to(device=device, dtype=dtype).contiguous()
+
+
+_workspaces: dict = {}
+
+
+def workspace(kind: str, nbytes: int, device) -> torch.Tensor:
+    """A zero-filled device workspace per (kind, size, device). The library leaves it zero-filled after
+    every call, so it is reused as is; calls sharing one must not overlap."""
+    key = (kind, int(nbytes), str(device))
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros(max(int(nbytes), 8), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+class Env:
+    """A batch of platformer envs over a device state buffer owned by this object."""
+
+    def __init__(self, maps, ckpts, spawns, num_envs, *, frame_skip=3, time_limit=2000, obs_mode=OBS_TILES,
+                 sprites=None, obs_stride=None, device="cuda", stream=None):
+        L = lib()
+        self.device = torch.device(device)
+        self.maps = _dev(maps, torch.uint8, self.device)
+        m, h, w = self.maps.shape
+        ck = _dev(ckpts, torch.int32, self.device).reshape(m, -1, 2)
+        self.ckpts = ck
+        self.spawns = _dev(spawns, torch.int32, self.device).reshape(m, 2)
+        self.sprites = None if sprites is None else _dev(sprites, torch.uint8, self.device).reshape(16, 8, 8)
+        self.obs_mode = obs_mode
+        size = OBS_TILES_SIZE if obs_mode == OBS_TILES else OBS_PIXELS_SIZE
+        self.obs_stride = size if obs_stride is None else int(obs_stride)
+        self.cfg = EnvConfig(num_envs, m, h, w, ck.shape[1], frame_skip, time_limit, obs_mode, self.obs_stride)
+        nbytes = ctypes.c_size_t()
+        check(L.rl_env_state_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
+        self.state = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+        self.num_envs = num_envs
+        self._handle = ctypes.c_void_p()
+        check(L.rl_env_create(ctypes.byref(self.cfg), dptr(self.maps), dptr(self.ckpts) if ck.numel() else None,
+                              dptr(self.spawns), dptr(self.sprites), dptr(self.state), nbytes.value,
+                              stream_ptr(stream), ctypes.byref(self._handle)))
+
+    @property
+    def obs_dtype(self):
+        return torch.float32 if self.obs_mode == OBS_TILES else torch.uint8
+
+    def new_obs(self, steps=None):
+        shape = (self.num_envs, self.obs_stride) if steps is None else (steps, self.num_envs, self.obs_stride)
+        return torch.empty(shape, dtype=self.obs_dtype, device=self.device)
+
+    def reset(self, obs=None, mask=None, stream=None):
+        check(lib().rl_env_reset(self._handle, dptr(mask, torch.uint8, "mask"), dptr(obs, self.obs_dtype, "obs"),
+                                 stream_ptr(stream)))
+
+    def step(self, actions, obs, rewards, dones, stream=None):
+        check(lib().rl_env_step(self._handle, dptr(actions, torch.int32, "actions"),
+                                dptr(obs, self.obs_dtype, "obs"), dptr(rewards, torch.float32, "rewards"),
+                                dptr(dones, torch.float32, "dones"), stream_ptr(stream)))
+
+    def read_state(self, stream=None):
+        out = torch.empty((self.num_envs, STATE_FIELDS), dtype=torch.int32, device=self.device)
+        check(lib().rl_env_read_state(self._handle, dptr(out), stream_ptr(stream)))
+        return out
+
+    @property
+    def step_counter(self) -> int:
+        c = ctypes.c_int64()
+        check(lib().rl_env_get_step_counter(self._handle, ctypes.byref(c)))
+        return c.value
+
+    @step_counter.setter
+    def step_counter(self, value: int):
+        check(lib().rl_env_set_step_counter(self._handle, int(value)))
+
+    def step_layout(self):
+        offs = (ctypes.c_size_t * 4)()
+        total = ctypes.c_size_t()
+        check(lib().rl_step_layout(ctypes.byref(self.cfg), offs, ctypes.byref(total)))
+        return list(offs), total.value
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            lib().rl_env_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gae_workspace_bytes(t: int, n: int) -> int:
+    b = ctypes.c_size_t()
+    check(lib().rl_gae_workspace_bytes(t, n, ctypes.byref(b)))
+    return b.value
+
+
+def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, ret=None, adv_stats=None,
+        ws=None, stream=None):
+    """rl_gae over [T][N] float32 device tensors; returns (adv, ret, adv_stats)."""
+    t, n = rewards.shape
+    dev = rewards.device
+    adv = torch.empty((t, n), dtype=torch.float32, device=dev) if adv is None else adv
+    ret = torch.empty((t, n), dtype=torch.float32, device=dev) if ret is None else ret
+    if normalize and adv_stats is None:
+        adv_stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    if normalize and ws is None:
+        ws = workspace("gae", gae_workspace_bytes(t, n), dev)
+    check(lib().rl_gae(dptr(rewards, torch.float32, "rewards"), dptr(values, torch.float32, "values"),
+                       dptr(dones, torch.float32, "dones"), dptr(last_values, torch.float32, "last_values"),
+                       t, n, float(gamma), float(lam), dptr(adv, torch.float32, "adv"),
+                       dptr(ret, torch.float32, "ret"), int(normalize),
+                       dptr(adv_stats, torch.float64, "adv_stats"), dptr(ws), 0 if ws is None else ws.numel(),
+                       stream_ptr(stream)))
+    return adv, ret, adv_stats
+
+
+def ppo_loss_workspace_bytes(b: int, mb: int) -> int:
+    nb = ctypes.c_size_t()
+    check(lib().rl_ppo_loss_workspace_bytes(b, mb, ctypes.byref(nb)))
+    return nb.value
+
+
+def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2, vf_coef=0.5,
+             ent_coef=0.01, adv_stats=None, out=None, ws=None, stream=None):
+    """rl_ppo_loss; returns out float32[B/minibatch][4] = (pg, value, entropy, total) per minibatch."""
+    b, a = logits.shape
+    dev = logits.device
+    out = torch.empty((b // minibatch, 4), dtype=torch.float32, device=dev) if out is None else out
+    if ws is None:
+        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev)
+    check(lib().rl_ppo_loss(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
+                            dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
+                            dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),
+                            dptr(perm, torch.int32, "perm"), dptr(adv_stats, torch.float64, "adv_stats"),
+                            b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
+                            dptr(out, torch.float32, "out"), dptr(ws), ws.numel(), stream_ptr(stream)))
+    return out

@@ -1,0 +1,737 @@
+// The batched tile platformer: device state layout, map padding, reset, step and observation kernels,
+// and the rl_env_* entry points.
+//
+// What a step computes follows the pages named in rl.h: the platformer step of "Teaching Mario to
+// speedrun" s.7 (a frame-skip loop of physics ticks, progress paid on a new best x, a terminal tick ends
+// the loop), the DDNet post's tick protocol (frame-skip 3, rewards summed between decisions), its
+// observation (43x31 tile window, 15-dim state x 4 frames, 4 checkpoint dims) and its reward (+10 per
+// checkpoint in order, high-water-mark progress, time penalty, +100 finish), and PlayTrain's Table 4
+// (terminated or truncated at the time limit). The pages leave the mechanics open; the constants and
+// the tick order below are the reading used throughout (positions in sub-units of 1/256 tile).
+//
+// Device layout (inside the caller's state buffer, every region 256-byte aligned, Np = N rounded up to
+// 64 so that every array row starts on a 256-byte boundary):
+//   slots  int32[4][5][Np]  ring of the last 4 frames; slot s, word w of env n at (s*5 + w)*Np + n.
+//                           Words: x, y, (vx & 0xffff) | vy << 16, flags / counters, tick. The newest
+//                           slot is the current state; the decision counter mod 4 names it.
+//   extra  int32[2][Np]     next checkpoint index, best x.
+//   map    u8[M][H+32][Wp]  the maps with a 16-row / 32-column solid border, Wp = round_up(W+64, 64),
+//                           so that every read of the step and observation kernels stays inside.
+//   ckpt   int32[M][K][2], spawn int32[M][2], sprites u8[16][8][8].
+// Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
+
+#include "rl_internal.hpp"
+
+namespace {
+
+constexpr int kTile = 256;
+constexpr int kBox = 192;
+constexpr int kHalfBox = 96;
+constexpr int kGravity = 12;
+constexpr int kMaxFall = 160;
+constexpr int kJumpV = 120;
+constexpr int kMaxVx = 48;
+constexpr int kAccGround = 8;
+constexpr int kAccAir = 4;
+constexpr int kFreezeTicks = 30;
+constexpr int kUnitsCkpt = 10240;     // +10 reward, 1024 units per reward
+constexpr int kUnitsFinish = 102400;  // +100 reward
+constexpr int kNumActions = 12;
+
+constexpr int kWinW = 43;
+constexpr int kWinH = 31;
+constexpr int kWinCx = 21;
+constexpr int kWinCy = 15;
+constexpr int kWinSize = kWinW * kWinH;                       // 1333
+constexpr int kStack = 4;
+constexpr int kFrameDims = 15;
+constexpr int kObsTiles = kWinSize + kStack * kFrameDims + 4;  // 1397
+constexpr int kPix = 84;
+constexpr int kPixFrame = kPix * kPix;                         // 7056
+constexpr int kPixFrameDwords = kPixFrame / 4;                 // 1764
+constexpr int kPixRowDwords = kPix / 4;                        // 21
+
+constexpr int kPadX = 32;
+constexpr int kPadY = 16;
+constexpr int kSlotWords = 5;
+constexpr uint8_t kSolid = 1;
+constexpr uint8_t kPlatform = 2;
+constexpr uint8_t kFreeze = 3;
+
+// Bits of the flags / counters word.
+constexpr uint32_t kFacingRight = 1u << 0;
+constexpr uint32_t kGroundedBit = 1u << 1;
+constexpr uint32_t kJumpHeldBit = 1u << 2;
+constexpr uint32_t kHookHeldBit = 1u << 3;
+constexpr uint32_t kWallLBit = 1u << 4;
+constexpr uint32_t kWallRBit = 1u << 5;
+constexpr int kFreezeShift = 8;   // 5 bits, 0..30
+constexpr int kHookShift = 16;    // 8 bits, 0..255
+constexpr int kActionShift = 24;  // 4 bits, 0..11
+
+struct Layout {
+    size_t slots, extra, map, ckpt, spawn, sprites, total;
+    int64_t np, hp, wp;
+};
+
+struct EnvDev {
+    int32_t* slots;
+    int32_t* extra;
+    const uint8_t* map;
+    const int32_t* ckpt;
+    const int32_t* spawn;
+    const uint8_t* sprites;
+    int32_t n, m, h, w, k, fs, time_limit;
+    int64_t np, hp, wp;
+};
+
+int validate_cfg(const rl_env_config* c)
+{
+    if (!c) return rl::fail(RL_EINVAL, "config is NULL");
+    if (c->num_envs < 1 || c->num_envs > (1 << 24))
+        return rl::fail(RL_EINVAL, "num_envs %d outside [1, 2^24]", c->num_envs);
+    if (c->num_maps < 1 || c->num_maps > 65536)
+        return rl::fail(RL_EINVAL, "num_maps %d outside [1, 65536]", c->num_maps);
+    if (c->map_h < 1 || c->map_h > 4096) return rl::fail(RL_EINVAL, "map_h %d outside [1, 4096]", c->map_h);
+    if (c->map_w < 1 || c->map_w > 65536) return rl::fail(RL_EINVAL, "map_w %d outside [1, 65536]", c->map_w);
+    if (c->num_ckpts < 0 || c->num_ckpts > (1 << 20))
+        return rl::fail(RL_EINVAL, "num_ckpts %d outside [0, 2^20]", c->num_ckpts);
+    if (c->frame_skip < 1 || c->frame_skip > RL_MAX_FRAME_SKIP)
+        return rl::fail(RL_EINVAL, "frame_skip %d outside [1, %d]", c->frame_skip, RL_MAX_FRAME_SKIP);
+    if (c->time_limit < 1) return rl::fail(RL_EINVAL, "time_limit %d < 1", c->time_limit);
+    if (c->obs_mode != RL_OBS_TILES && c->obs_mode != RL_OBS_PIXELS)
+        return rl::fail(RL_EINVAL, "obs_mode %d is neither tiles (0) nor pixels (1)", c->obs_mode);
+    const int64_t size = c->obs_mode == RL_OBS_TILES ? kObsTiles : kStack * kPixFrame;
+    if (c->obs_stride < size)
+        return rl::fail(RL_EINVAL, "obs_stride %lld < observation size %lld", (long long)c->obs_stride,
+                        (long long)size);
+    if (c->obs_mode == RL_OBS_PIXELS && c->obs_stride % 4 != 0)
+        return rl::fail(RL_EALIGN, "pixel obs_stride %lld is not a multiple of 4", (long long)c->obs_stride);
+    return RL_OK;
+}
+
+Layout layout_of(const rl_env_config* c)
+{
+    Layout l{};
+    l.np = (int64_t)rl::round_up((size_t)c->num_envs, 64);
+    l.hp = (int64_t)c->map_h + 2 * kPadY;
+    l.wp = (int64_t)rl::round_up((size_t)c->map_w + 2 * kPadX, 64);
+    size_t off = 0;
+    l.slots = off;
+    off = rl::round_up(off + sizeof(int32_t) * kStack * kSlotWords * l.np, 256);
+    l.extra = off;
+    off = rl::round_up(off + sizeof(int32_t) * 2 * l.np, 256);
+    l.map = off;
+    off = rl::round_up(off + (size_t)c->num_maps * l.hp * l.wp, 256);
+    l.ckpt = off;
+    off = rl::round_up(off + sizeof(int32_t) * 2 * (size_t)c->num_maps * (c->num_ckpts > 0 ? c->num_ckpts : 1), 256);
+    l.spawn = off;
+    off = rl::round_up(off + sizeof(int32_t) * 2 * (size_t)c->num_maps, 256);
+    l.sprites = off;
+    off = rl::round_up(off + 16 * 64, 256);
+    l.total = off;
+    return l;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Device helpers
+// ------------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ int32_t& slot_word(const EnvDev& d, int s, int w, int n)
+{
+    return d.slots[((int64_t)s * kSlotWords + w) * d.np + n];
+}
+
+__device__ __forceinline__ const uint8_t* map_base(const EnvDev& d, int m)
+{
+    return d.map + (int64_t)m * d.hp * d.wp;
+}
+
+// Address of tile (row, col) of padded map m; row/col are map coordinates (may be in the border).
+__device__ __forceinline__ const uint8_t* tile_ptr(const EnvDev& d, int m, int row, int col)
+{
+    return map_base(d, m) + (int64_t)(row + kPadY) * d.wp + (col + kPadX);
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Observation value of frame dimension `dim` from a slot's five words (all conversions exact).
+__device__ __forceinline__ float frame_dim(int dim, int32_t x, int32_t y, int32_t vxy, uint32_t misc,
+                                           int32_t tick)
+{
+    switch (dim) {
+    case 0: return (float)x * 0x1p-8f;
+    case 1: return (float)y * 0x1p-8f;
+    case 2: return (float)(int16_t)(vxy & 0xffff) * 0x1p-8f;
+    case 3: return (float)(vxy >> 16) * 0x1p-8f;
+    case 4: return (misc & kGroundedBit) ? 1.0f : 0.0f;
+    case 5: return (misc & kFacingRight) ? 1.0f : -1.0f;
+    case 6: return ((misc >> kFreezeShift) & 31u) ? 1.0f : 0.0f;
+    case 7: return (float)((misc >> kFreezeShift) & 31u);
+    case 8: return (misc & kHookHeldBit) ? 1.0f : 0.0f;
+    case 9: return (float)((misc >> kHookShift) & 255u);
+    case 10: return (misc & kJumpHeldBit) ? 1.0f : 0.0f;
+    case 11: return (misc & kWallLBit) ? 1.0f : 0.0f;
+    case 12: return (misc & kWallRBit) ? 1.0f : 0.0f;
+    case 13: return (float)tick * 0x1p-11f;
+    default: return (float)((misc >> kActionShift) & 15u);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Set-up kernels
+// ------------------------------------------------------------------------------------------------
+
+// Padded map copy, one dword of the destination per thread; cells outside the source map are solid.
+__global__ __launch_bounds__(256) void k_pad_maps(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                  int32_t m_count, int32_t h, int32_t w, int64_t hp, int64_t wp)
+{
+    const int64_t dwords = (int64_t)m_count * hp * wp / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < dwords;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t byte0 = i * 4;
+        const int64_t m = byte0 / (hp * wp);
+        const int64_t rem = byte0 - m * hp * wp;
+        const int64_t row = rem / wp - kPadY;
+        const int64_t col0 = rem % wp - kPadX;
+        uint32_t word = 0;
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = col0 + j;
+            uint32_t t = kSolid;
+            if (row >= 0 && row < h && col >= 0 && col < w) t = src[(m * h + row) * w + col];
+            word |= t << (8 * j);
+        }
+        reinterpret_cast<uint32_t*>(dst)[i] = word;
+    }
+}
+
+__device__ __forceinline__ void write_spawn(const EnvDev& d, int n)
+{
+    const int m = n % d.m;
+    const int32_t x = d.spawn[2 * m], y = d.spawn[2 * m + 1];
+    for (int s = 0; s < kStack; ++s) {
+        slot_word(d, s, 0, n) = x;
+        slot_word(d, s, 1, n) = y;
+        slot_word(d, s, 2, n) = 0;
+        slot_word(d, s, 3, n) = (int32_t)(kFacingRight | kGroundedBit);
+        slot_word(d, s, 4, n) = 0;
+    }
+    d.extra[n] = 0;
+    d.extra[d.np + n] = x;
+}
+
+__global__ __launch_bounds__(256) void k_reset(EnvDev d, const uint8_t* __restrict__ mask)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= d.n) return;
+    if (mask && !mask[n]) return;
+    write_spawn(d, n);
+}
+
+// ------------------------------------------------------------------------------------------------
+// env_step: one lane per env.
+// ------------------------------------------------------------------------------------------------
+
+// Solid / freeze bits of the 8x8 tiles around the player at the start of a decision: bit
+// (row - rb) * 8 + (col - cb). With |vx| <= 48 and -108 <= vy <= 160 per tick, up to 5 ticks keep every
+// probe of the decision inside rows r0-3 .. r0+4 and columns c0-2 .. c0+5 of the starting box corner.
+struct Neighbourhood {
+    uint64_t solid, freeze;
+    int rb, cb;
+    __device__ __forceinline__ uint32_t s(int row, int col) const
+    {
+        return (uint32_t)(solid >> ((row - rb) * 8 + (col - cb))) & 1u;
+    }
+    __device__ __forceinline__ uint32_t f(int row, int col) const
+    {
+        return (uint32_t)(freeze >> ((row - rb) * 8 + (col - cb))) & 1u;
+    }
+};
+
+__device__ __forceinline__ Neighbourhood load_neighbourhood(const EnvDev& d, int m, int32_t x, int32_t y)
+{
+    Neighbourhood nb;
+    // Clamping only matters for a spawn placed outside the map; it keeps every read in the border.
+    nb.rb = clampi(y >> 8, 0, d.h - 1) - 3;
+    nb.cb = clampi(x >> 8, 0, d.w - 1) - 2;
+    uint64_t rows[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_memcpy(&rows[i], tile_ptr(d, m, nb.rb + i, nb.cb), 8);
+    uint64_t s = 0, f = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t t = (uint32_t)(rows[i] >> (8 * j)) & 0xffu;
+            s |= (uint64_t)(t == kSolid || t == kPlatform) << (i * 8 + j);
+            f |= (uint64_t)(t == kFreeze) << (i * 8 + j);
+        }
+    }
+    nb.solid = s;
+    nb.freeze = f;
+    return nb;
+}
+
+__global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restrict__ actions,
+                                              float* __restrict__ rewards, float* __restrict__ dones,
+                                              int head_prev, int head_new)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= d.n) return;
+    const int m = n % d.m;
+
+    int32_t x = slot_word(d, head_prev, 0, n);
+    int32_t y = slot_word(d, head_prev, 1, n);
+    const int32_t vxy = slot_word(d, head_prev, 2, n);
+    const uint32_t misc = (uint32_t)slot_word(d, head_prev, 3, n);
+    int32_t tick = slot_word(d, head_prev, 4, n);
+    int32_t next = d.extra[n];
+    int32_t best_x = d.extra[d.np + n];
+    int32_t a = actions[n];
+    if (a < 0 || a >= kNumActions) a = 0;
+
+    int32_t vx = (int16_t)(vxy & 0xffff);
+    int32_t vy = vxy >> 16;
+    int32_t facing = (misc & kFacingRight) ? 1 : -1;
+    uint32_t grounded = (misc & kGroundedBit) ? 1u : 0u;
+    int32_t freeze = (int32_t)((misc >> kFreezeShift) & 31u);
+    int32_t hook_ticks = (int32_t)((misc >> kHookShift) & 255u);
+    uint32_t wall_l = (misc & kWallLBit) ? 1u : 0u, wall_r = (misc & kWallRBit) ? 1u : 0u;
+    uint32_t jump_held = (misc & kJumpHeldBit) ? 1u : 0u, hook_held = (misc & kHookHeldBit) ? 1u : 0u;
+
+    const Neighbourhood nb = load_neighbourhood(d, m, x, y);
+    const int32_t* ck = d.ckpt + (int64_t)m * d.k * 2;
+    int32_t ck_col = next < d.k ? ck[2 * next] : 0;
+
+    const int dir = a >> 2;
+    const int jump_in = (a >> 1) & 1;
+    const int hook_in = a & 1;
+
+    int32_t units = 0;
+    bool terminated = false, truncated = false;
+    for (int i = 0; i < d.fs && !terminated && !truncated; ++i) {
+        // 1. a frozen player's input is ignored
+        const bool frozen = freeze > 0;
+        const int sign = frozen ? 0 : (dir == 1 ? -1 : (dir == 2 ? 1 : 0));
+        const int jump = frozen ? 0 : jump_in;
+        const int hook = frozen ? 0 : hook_in;
+        // 2. horizontal velocity moves toward sign * MAX_VX without overshoot
+        const int32_t target = sign * kMaxVx;
+        const int32_t acc = grounded ? kAccGround : kAccAir;
+        vx = vx < target ? min(vx + acc, target) : (vx > target ? max(vx - acc, target) : vx);
+        if (sign != 0) facing = sign;
+        // 3-4. jump from the ground, gravity, terminal fall speed
+        if (jump && grounded) vy = -kJumpV;
+        vy = min(vy + kGravity, kMaxFall);
+        // 5. x move against the rows of the box before the y move
+        {
+            int32_t nx = x + vx;
+            const int r0 = y >> 8, r1 = (y + kBox - 1) >> 8;
+            if (vx > 0) {
+                const int col = (nx + kBox - 1) >> 8;
+                if (nb.s(r0, col) | nb.s(r1, col)) { nx = col * kTile - kBox; vx = 0; }
+            } else if (vx < 0) {
+                const int col = nx >> 8;
+                if (nb.s(r0, col) | nb.s(r1, col)) { nx = (col + 1) * kTile; vx = 0; }
+            }
+            x = nx;
+        }
+        // 6. y move against the columns of the box after the x move
+        {
+            int32_t ny = y + vy;
+            const int c0 = x >> 8, c1 = (x + kBox - 1) >> 8;
+            if (vy > 0) {
+                const int row = (ny + kBox - 1) >> 8;
+                if (nb.s(row, c0) | nb.s(row, c1)) { ny = row * kTile - kBox; vy = 0; }
+            } else if (vy < 0) {
+                const int row = ny >> 8;
+                if (nb.s(row, c0) | nb.s(row, c1)) { ny = (row + 1) * kTile; vy = 0; }
+            }
+            y = ny;
+        }
+        // 7-8. contacts of the final box; touching a freeze tile re-arms the counter
+        {
+            const int c0 = x >> 8, c1 = (x + kBox - 1) >> 8;
+            const int r0 = y >> 8, r1 = (y + kBox - 1) >> 8;
+            const int below = (y + kBox) >> 8;
+            grounded = nb.s(below, c0) | nb.s(below, c1);
+            const int cl = (x - 1) >> 8, cr = (x + kBox) >> 8;
+            wall_l = nb.s(r0, cl) | nb.s(r1, cl);
+            wall_r = nb.s(r0, cr) | nb.s(r1, cr);
+            const uint32_t touching = nb.f(r0, c0) | nb.f(r0, c1) | nb.f(r1, c0) | nb.f(r1, c1);
+            freeze = touching ? kFreezeTicks : (freeze > 0 ? freeze - 1 : 0);
+        }
+        // 9. hook and jump state
+        hook_ticks = hook ? min(hook_ticks + 1, 255) : 0;
+        hook_held = (uint32_t)hook;
+        jump_held = (uint32_t)jump;
+        // 10. progress past the high-water mark
+        if (x > best_x) { units += x - best_x; best_x = x; }
+        // 11. checkpoints in order; the last one is the finish
+        if (next < d.k && ((x + kHalfBox) >> 8) >= ck_col) {
+            units += kUnitsCkpt;
+            next += 1;
+            if (next == d.k) { units += kUnitsFinish; terminated = true; }
+            else ck_col = ck[2 * next];
+        }
+        // 12. time
+        tick += 1;
+        units -= 1;
+        if (tick >= d.time_limit) truncated = true;
+    }
+
+    rewards[n] = (float)units * 0x1p-10f;
+    const bool done = terminated || truncated;
+    dones[n] = done ? 1.0f : 0.0f;
+    if (done) {
+        write_spawn(d, n);
+        return;
+    }
+    const uint32_t new_misc = (facing > 0 ? kFacingRight : 0u) | (grounded ? kGroundedBit : 0u) |
+                              (jump_held ? kJumpHeldBit : 0u) | (hook_held ? kHookHeldBit : 0u) |
+                              (wall_l ? kWallLBit : 0u) | (wall_r ? kWallRBit : 0u) |
+                              ((uint32_t)freeze << kFreezeShift) | ((uint32_t)hook_ticks << kHookShift) |
+                              ((uint32_t)a << kActionShift);
+    slot_word(d, head_new, 0, n) = x;
+    slot_word(d, head_new, 1, n) = y;
+    slot_word(d, head_new, 2, n) = (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16));
+    slot_word(d, head_new, 3, n) = (int32_t)new_misc;
+    slot_word(d, head_new, 4, n) = tick;
+    d.extra[n] = next;
+    d.extra[d.np + n] = best_x;
+}
+
+// ------------------------------------------------------------------------------------------------
+// obs_gather, tile mode: one wave per env writes its 1397 floats as 22 fully coalesced 256-byte rows.
+// ------------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__ obs, int64_t stride, int head)
+{
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= d.n) return;
+    const int m = n % d.m;
+    const int32_t x = slot_word(d, head, 0, n);
+    const int32_t y = slot_word(d, head, 1, n);
+    const int pcol = clampi((x + kHalfBox) >> 8, 0, d.w - 1);
+    const int prow = clampi((y + kHalfBox) >> 8, 0, d.h - 1);
+    const uint8_t* win = tile_ptr(d, m, prow - kWinCy, pcol - kWinCx);
+    float* o = obs + (int64_t)n * stride;
+
+    // element k = lane + 64 i sits at window row r, column c; stepping k by 64 = 43 + 21 moves one row
+    // down and 21 columns right (wrapping into the next row).
+    int r = lane >= kWinW ? 1 : 0;
+    int c = lane - r * kWinW;
+#pragma unroll
+    for (int i = 0; i < (kObsTiles + 63) / 64; ++i) {
+        const int k = lane + 64 * i;
+        if (k < kWinSize) {
+            o[k] = (float)win[(int64_t)r * d.wp + c];
+        } else if (k < kObsTiles) {
+            const int t = k - kWinSize;
+            float v;
+            if (t < kStack * kFrameDims) {
+                const int f = t / kFrameDims, dim = t - f * kFrameDims;
+                const int s = (head - f) & 3;
+                v = frame_dim(dim, slot_word(d, s, 0, n), slot_word(d, s, 1, n), slot_word(d, s, 2, n),
+                              (uint32_t)slot_word(d, s, 3, n), slot_word(d, s, 4, n));
+            } else {
+                const int q = t - kStack * kFrameDims;
+                const int32_t next = d.extra[n];
+                if (q == 0 || q == 1) {
+                    if (next < d.k) {
+                        const int32_t* ckp = d.ckpt + ((int64_t)m * d.k + next) * 2;
+                        v = q == 0 ? (float)(ckp[0] * kTile + kTile / 2 - (x + kHalfBox)) * 0x1p-8f
+                                   : (float)(ckp[1] * kTile + kTile / 2 - (y + kHalfBox)) * 0x1p-8f;
+                    } else {
+                        v = 0.0f;
+                    }
+                } else if (q == 2) {
+                    v = (float)next;
+                } else {
+                    v = (float)d.extra[d.np + n] * 0x1p-8f;
+                }
+            }
+            o[k] = v;
+        }
+        r += 1;
+        c += 64 - kWinW;
+        if (c >= kWinW) { c -= kWinW; r += 1; }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// obs_gather, pixel mode: one block per env, one wave per stacked frame. Each frame is re-rendered from
+// the position kept in its ring slot (recomputing 7 KB from the L2-resident map is cheaper than storing
+// and re-reading it). Four pixels are packed per dword store.
+// ------------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restrict__ obs, int64_t stride, int head)
+{
+    __shared__ uint8_t spr[16 * 64];
+    reinterpret_cast<uint32_t*>(spr)[threadIdx.x] = reinterpret_cast<const uint32_t*>(d.sprites)[threadIdx.x];
+    __syncthreads();
+    const int n = blockIdx.x;
+    const int f = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int m = n % d.m;
+    const int s = (head - f) & 3;
+    const int32_t x = clampi(slot_word(d, s, 0, n), 0, d.w * kTile - 1);
+    const int32_t y = clampi(slot_word(d, s, 1, n), 0, d.h * kTile - 1);
+    const int cam_x = ((x + kHalfBox) >> 5) - kPix / 2;
+    const int cam_y = ((y + kHalfBox) >> 5) - kPix / 2;
+    const int bx0 = x >> 5, bx1 = (x + kBox - 1) >> 5;
+    const int by0 = y >> 5, by1 = (y + kBox - 1) >> 5;
+    uint32_t* o = reinterpret_cast<uint32_t*>(obs + (int64_t)n * stride + (int64_t)f * kPixFrame);
+
+    int py = lane / kPixRowDwords;
+    int qc = lane - py * kPixRowDwords;
+    for (int q = lane; q < kPixFrameDwords; q += 64) {
+        const int wy = cam_y + py;
+        const uint8_t* row = tile_ptr(d, m, wy >> 3, 0);
+        const int sy = (wy & 7) << 3;
+        const bool in_by = wy >= by0 && wy <= by1;
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int wx = cam_x + qc * 4 + j;
+            const uint32_t t = row[wx >> 3];
+            uint32_t v = spr[((t & 15u) << 6) | sy | (wx & 7)];
+            if (in_by && wx >= bx0 && wx <= bx1) v = 255u;
+            word |= v << (8 * j);
+        }
+        o[q] = word;
+        // q += 64 = 3 rows of 21 dwords + 1
+        py += 3;
+        qc += 1;
+        if (qc >= kPixRowDwords) { qc -= kPixRowDwords; py += 1; }
+    }
+}
+
+// Decode the newest slot and the extras into the canonical int32[N][16] state.
+__global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restrict__ out, int head)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= d.n) return;
+    const int32_t vxy = slot_word(d, head, 2, n);
+    const uint32_t misc = (uint32_t)slot_word(d, head, 3, n);
+    int32_t* o = out + (int64_t)n * RL_STATE_FIELDS;
+    o[0] = slot_word(d, head, 0, n);
+    o[1] = slot_word(d, head, 1, n);
+    o[2] = (int16_t)(vxy & 0xffff);
+    o[3] = vxy >> 16;
+    o[4] = (misc & kFacingRight) ? 1 : -1;
+    o[5] = (int32_t)((misc >> kFreezeShift) & 31u);
+    o[6] = (int32_t)((misc >> kHookShift) & 255u);
+    o[7] = (misc & kHookHeldBit) ? 1 : 0;
+    o[8] = (misc & kJumpHeldBit) ? 1 : 0;
+    o[9] = (misc & kGroundedBit) ? 1 : 0;
+    o[10] = (misc & kWallLBit) ? 1 : 0;
+    o[11] = (misc & kWallRBit) ? 1 : 0;
+    o[12] = slot_word(d, head, 4, n);
+    o[13] = d.extra[n];
+    o[14] = d.extra[d.np + n];
+    o[15] = (int32_t)((misc >> kActionShift) & 15u);
+}
+
+}  // namespace
+
+struct rl_env {
+    rl_env_config cfg;
+    Layout lay;
+    uint8_t* base;
+    int64_t counter;
+};
+
+namespace {
+
+EnvDev dev_of(const rl_env* e)
+{
+    EnvDev d;
+    d.slots = reinterpret_cast<int32_t*>(e->base + e->lay.slots);
+    d.extra = reinterpret_cast<int32_t*>(e->base + e->lay.extra);
+    d.map = e->base + e->lay.map;
+    d.ckpt = reinterpret_cast<const int32_t*>(e->base + e->lay.ckpt);
+    d.spawn = reinterpret_cast<const int32_t*>(e->base + e->lay.spawn);
+    d.sprites = e->base + e->lay.sprites;
+    d.n = e->cfg.num_envs;
+    d.m = e->cfg.num_maps;
+    d.h = e->cfg.map_h;
+    d.w = e->cfg.map_w;
+    d.k = e->cfg.num_ckpts;
+    d.fs = e->cfg.frame_skip;
+    d.time_limit = e->cfg.time_limit;
+    d.np = e->lay.np;
+    d.hp = e->lay.hp;
+    d.wp = e->lay.wp;
+    return d;
+}
+
+int launch_obs(const rl_env* e, void* obs, hipStream_t st, int head)
+{
+    const EnvDev d = dev_of(e);
+    if (e->cfg.obs_mode == RL_OBS_TILES) {
+        hipLaunchKernelGGL(k_obs_tiles, dim3((d.n + 3) / 4), dim3(256), 0, st, d, static_cast<float*>(obs),
+                           e->cfg.obs_stride, head);
+    } else {
+        hipLaunchKernelGGL(k_obs_pixels, dim3(d.n), dim3(256), 0, st, d, static_cast<uint8_t*>(obs),
+                           e->cfg.obs_stride, head);
+    }
+    return rl::check_launch("obs_gather");
+}
+
+int check_obs_ptr(const rl_env* e, const void* obs)
+{
+    if (!obs) return rl::fail(RL_EINVAL, "obs is NULL");
+    if (!rl::aligned(obs, 4)) return rl::fail(RL_EALIGN, "obs is not 4-byte aligned");
+    (void)e;
+    return RL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rl_env_state_bytes(const rl_env_config* cfg, size_t* bytes)
+{
+    if (int rc = validate_cfg(cfg)) return rc;
+    if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
+    *bytes = layout_of(cfg).total;
+    return RL_OK;
+}
+
+int rl_env_obs_size(const rl_env_config* cfg, size_t* elems, size_t* elem_bytes)
+{
+    if (int rc = validate_cfg(cfg)) return rc;
+    if (!elems || !elem_bytes) return rl::fail(RL_EINVAL, "output pointer is NULL");
+    *elems = cfg->obs_mode == RL_OBS_TILES ? kObsTiles : (size_t)kStack * kPixFrame;
+    *elem_bytes = cfg->obs_mode == RL_OBS_TILES ? 4 : 1;
+    return RL_OK;
+}
+
+int rl_step_layout(const rl_env_config* cfg, size_t offsets[4], size_t* block_bytes)
+{
+    if (int rc = validate_cfg(cfg)) return rc;
+    if (!offsets || !block_bytes) return rl::fail(RL_EINVAL, "output pointer is NULL");
+    const size_t n = (size_t)cfg->num_envs;
+    const size_t esz = cfg->obs_mode == RL_OBS_TILES ? 4 : 1;
+    offsets[0] = 0;
+    offsets[1] = rl::round_up(n * 4, 256);
+    offsets[2] = rl::round_up(offsets[1] + n * (size_t)cfg->obs_stride * esz, 256);
+    offsets[3] = rl::round_up(offsets[2] + n * 4, 256);
+    *block_bytes = rl::round_up(offsets[3] + n * 4, 256);
+    return RL_OK;
+}
+
+int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* ckpts, const int32_t* spawns,
+                  const uint8_t* sprites, void* state, size_t state_bytes, void* stream, rl_env** out)
+{
+    if (int rc = validate_cfg(cfg)) return rc;
+    if (!out) return rl::fail(RL_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!maps || !spawns || !state) return rl::fail(RL_EINVAL, "maps, spawns and state must be non-NULL");
+    if (cfg->num_ckpts > 0 && !ckpts) return rl::fail(RL_EINVAL, "ckpts is NULL with num_ckpts > 0");
+    if (cfg->obs_mode == RL_OBS_PIXELS && !sprites) return rl::fail(RL_EINVAL, "pixel mode needs sprites");
+    if (!rl::aligned(state, 256)) return rl::fail(RL_EALIGN, "state buffer is not 256-byte aligned");
+    if (!rl::aligned(ckpts, 4) || !rl::aligned(spawns, 4))
+        return rl::fail(RL_EALIGN, "ckpts / spawns are not 4-byte aligned");
+    const Layout lay = layout_of(cfg);
+    if (state_bytes < lay.total)
+        return rl::fail(RL_ESIZE, "state buffer has %zu bytes, needs %zu", state_bytes, lay.total);
+
+    rl_env* e = new (std::nothrow) rl_env;
+    if (!e) return rl::fail(RL_EINVAL, "out of host memory");
+    e->cfg = *cfg;
+    e->lay = lay;
+    e->base = static_cast<uint8_t*>(state);
+    e->counter = 0;
+    hipStream_t st = rl::as_stream(stream);
+    uint8_t* base = e->base;
+
+    const int64_t dwords = (int64_t)cfg->num_maps * lay.hp * lay.wp / 4;
+    const int blocks = (int)std::min<int64_t>((dwords + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_pad_maps, dim3(blocks), dim3(256), 0, st, maps, base + lay.map, cfg->num_maps,
+                       cfg->map_h, cfg->map_w, lay.hp, lay.wp);
+    int rc = rl::check_launch("pad_maps");
+    hipError_t he = hipSuccess;
+    if (rc == RL_OK && cfg->num_ckpts > 0)
+        he = hipMemcpyAsync(base + lay.ckpt, ckpts, sizeof(int32_t) * 2 * (size_t)cfg->num_maps * cfg->num_ckpts,
+                            hipMemcpyDeviceToDevice, st);
+    if (rc == RL_OK && he == hipSuccess)
+        he = hipMemcpyAsync(base + lay.spawn, spawns, sizeof(int32_t) * 2 * (size_t)cfg->num_maps,
+                            hipMemcpyDeviceToDevice, st);
+    if (rc == RL_OK && he == hipSuccess && cfg->obs_mode == RL_OBS_PIXELS)
+        he = hipMemcpyAsync(base + lay.sprites, sprites, 16 * 64, hipMemcpyDeviceToDevice, st);
+    if (rc == RL_OK && he != hipSuccess) rc = rl::fail(RL_EHIP, "table copy: %s", hipGetErrorString(he));
+    if (rc == RL_OK) {
+        const EnvDev d = dev_of(e);
+        hipLaunchKernelGGL(k_reset, dim3((cfg->num_envs + 255) / 256), dim3(256), 0, st, d,
+                           static_cast<const uint8_t*>(nullptr));
+        rc = rl::check_launch("reset");
+    }
+    if (rc != RL_OK) {
+        delete e;
+        return rc;
+    }
+    *out = e;
+    return RL_OK;
+}
+
+int rl_env_reset(rl_env* e, const uint8_t* mask, void* obs, void* stream)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (obs)
+        if (int rc = check_obs_ptr(e, obs)) return rc;
+    hipStream_t st = rl::as_stream(stream);
+    const EnvDev d = dev_of(e);
+    hipLaunchKernelGGL(k_reset, dim3((d.n + 255) / 256), dim3(256), 0, st, d, mask);
+    if (int rc = rl::check_launch("reset")) return rc;
+    if (obs) return launch_obs(e, obs, st, (int)(e->counter & 3));
+    return RL_OK;
+}
+
+int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, float* dones, void* stream)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (!actions || !rewards || !dones) return rl::fail(RL_EINVAL, "actions, rewards and dones must be non-NULL");
+    if (!rl::aligned(actions, 4) || !rl::aligned(rewards, 4) || !rl::aligned(dones, 4))
+        return rl::fail(RL_EALIGN, "actions / rewards / dones are not 4-byte aligned");
+    if (int rc = check_obs_ptr(e, obs)) return rc;
+    hipStream_t st = rl::as_stream(stream);
+    const EnvDev d = dev_of(e);
+    const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
+    hipLaunchKernelGGL(k_step, dim3((d.n + 255) / 256), dim3(256), 0, st, d, actions, rewards, dones, head_prev,
+                       head_new);
+    if (int rc = rl::check_launch("env_step")) return rc;
+    e->counter += 1;
+    return launch_obs(e, obs, st, head_new);
+}
+
+int rl_env_read_state(const rl_env* e, int32_t* out, void* stream)
+{
+    if (!e || !out) return rl::fail(RL_EINVAL, "env and out must be non-NULL");
+    if (!rl::aligned(out, 4)) return rl::fail(RL_EALIGN, "out is not 4-byte aligned");
+    const EnvDev d = dev_of(e);
+    hipLaunchKernelGGL(k_read_state, dim3((d.n + 255) / 256), dim3(256), 0, rl::as_stream(stream), d, out,
+                       (int)(e->counter & 3));
+    return rl::check_launch("read_state");
+}
+
+int rl_env_get_step_counter(const rl_env* e, int64_t* counter)
+{
+    if (!e || !counter) return rl::fail(RL_EINVAL, "env and counter must be non-NULL");
+    *counter = e->counter;
+    return RL_OK;
+}
+
+int rl_env_set_step_counter(rl_env* e, int64_t counter)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (counter < 0) return rl::fail(RL_EINVAL, "counter %lld < 0", (long long)counter);
+    e->counter = counter;
+    return RL_OK;
+}
+
+void rl_env_destroy(rl_env* e) { delete e; }
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// GAE reverse scan over a [T][N] rollout, whole-batch advantage statistics and normalisation.
+//
+// The recurrence ("Teaching Mario to speedrun", s.6 Better advantages; the done mask cuts an episode
+// where it ended):
+//   delta_t = r_t + gamma * V_{t+1} * (1 - d_t) - V_t,   A_t = delta_t + c_t * A_{t+1},
+//   c_t = gamma * lambda * (1 - d_t),  A_T = 0,  R_t = A_t + V_t.
+// It is a first-order linear recurrence, so a run of steps composes into one affine map
+// A_in = b + c * A_out. The chunked kernel splits T into C chunks per env: each thread loads its chunk
+// once into registers, reduces it to (b, c), the C maps are composed through LDS to give every chunk its
+// incoming A, and each thread then replays its chunk from registers. Every input is read once and every
+// output written once (20 bytes per element), with C times the lane parallelism of one lane per env;
+// each row [t][n0 .. n0+E) is a coalesced segment.
+//
+// Statistics: per-thread float64 sums of A and A^2, a block reduction, per-block partials in the
+// workspace, and the last block to finish (an atomic ticket) reduces the partials in block order. No
+// floating-point atomics: results are identical from run to run.
+
+#include <algorithm>
+
+#include "rl_internal.hpp"
+
+namespace {
+
+constexpr double kNormEps = 1e-8;
+constexpr size_t kHeaderBytes = 256;   // ticket counter lives at the start of the workspace
+
+struct StatsOut {
+    double* partials;     // [grid][2]
+    unsigned* ticket;
+    double* stats;        // {count, mean, std}
+    double count;
+};
+
+// Sum of a double across the block (256 threads), the same fixed order on every run.
+__device__ __forceinline__ double block_sum(double v, double* lds)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += lds[i];
+    return s;
+}
+
+// Publish this block's (sum A, sum A^2); the last block to arrive reduces all partials in block order
+// and writes {count, mean, population std}, then re-arms the ticket.
+__device__ void finish_stats(double s1, double s2, const StatsOut& so)
+{
+    __shared__ double lds[8];
+    __shared__ bool last;
+    s1 = block_sum(s1, lds);
+    s2 = block_sum(s2, lds + 4);
+    if (threadIdx.x == 0) {
+        so.partials[2 * blockIdx.x] = s1;
+        so.partials[2 * blockIdx.x + 1] = s2;
+        __threadfence();
+        const unsigned t = atomicAdd(so.ticket, 1u);
+        last = (t == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    double a = 0.0, b = 0.0;
+    for (unsigned i = threadIdx.x; i < gridDim.x; i += blockDim.x) {
+        a += so.partials[2 * i];
+        b += so.partials[2 * i + 1];
+    }
+    a = block_sum(a, lds);
+    b = block_sum(b, lds + 4);
+    if (threadIdx.x == 0) {
+        const double mean = a / so.count;
+        double var = b / so.count - mean * mean;
+        var = var > 0.0 ? var : 0.0;
+        so.stats[0] = so.count;
+        so.stats[1] = mean;
+        so.stats[2] = sqrt(var);
+        *so.ticket = 0u;
+        __threadfence();
+    }
+}
+
+// Block = E envs x (256 / E) chunks of L <= LMAX steps. Thread (e, ch) owns env blockIdx.x*E + e and
+// steps [ch*L, min(T, ch*L + L)).
+template <int E, int LMAX>
+__global__ __launch_bounds__(256) void k_gae_chunked(const float* __restrict__ rew, const float* __restrict__ val,
+                                                     const float* __restrict__ done, const float* __restrict__ vlast,
+                                                     int T, int N, int L, float gamma, float gl,
+                                                     float* __restrict__ adv, float* __restrict__ ret,
+                                                     int want_stats, StatsOut so)
+{
+    constexpr int C = 256 / E;
+    __shared__ float sb[C][E];
+    __shared__ float sc[C][E];
+    const int e = threadIdx.x % E;
+    const int ch = threadIdx.x / E;
+    const int n = blockIdx.x * E + e;
+    const bool valid = n < N;
+    const int t0 = ch * L;
+    const int len = valid ? max(0, min(L, T - t0)) : 0;
+
+    float delta[LMAX], cf[LMAX], vv[LMAX];
+#pragma unroll
+    for (int j = 0; j < LMAX; ++j) {
+        if (j < len) {
+            const int64_t idx = (int64_t)(t0 + j) * N + n;
+            vv[j] = val[idx];
+            delta[j] = rew[idx];
+            cf[j] = 1.0f - done[idx];
+        }
+    }
+    float vnext_tail = 0.0f;
+    if (len > 0) vnext_tail = (t0 + len < T) ? val[(int64_t)(t0 + len) * N + n] : vlast[n];
+
+    float b = 0.0f, c = 1.0f;
+#pragma unroll
+    for (int j = LMAX - 1; j >= 0; --j) {
+        if (j < len) {
+            const float vn = (j + 1 < len) ? vv[j + 1 < LMAX ? j + 1 : j] : vnext_tail;
+            const float notdone = cf[j];
+            delta[j] = delta[j] + gamma * vn * notdone - vv[j];
+            cf[j] = gl * notdone;
+            b = delta[j] + cf[j] * b;
+            c = cf[j] * c;
+        }
+    }
+    sb[ch][e] = b;
+    sc[ch][e] = c;
+    __syncthreads();
+
+    float a = 0.0f;
+    for (int k = C - 1; k > ch; --k) a = sb[k][e] + sc[k][e] * a;
+
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int j = LMAX - 1; j >= 0; --j) {
+        if (j < len) {
+            a = delta[j] + cf[j] * a;
+            const int64_t idx = (int64_t)(t0 + j) * N + n;
+            adv[idx] = a;
+            ret[idx] = a + vv[j];
+            s1 += (double)a;
+            s2 += (double)a * (double)a;
+        }
+    }
+    if (want_stats) finish_stats(s1, s2, so);
+}
+
+// One lane per env walking t = T-1 .. 0: the fallback for horizons longer than the chunked kernels hold.
+__global__ __launch_bounds__(256) void k_gae_seq(const float* __restrict__ rew, const float* __restrict__ val,
+                                                 const float* __restrict__ done, const float* __restrict__ vlast,
+                                                 int T, int N, float gamma, float gl, float* __restrict__ adv,
+                                                 float* __restrict__ ret, int want_stats, StatsOut so)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    double s1 = 0.0, s2 = 0.0;
+    if (n < N) {
+        float a = 0.0f, vn = vlast[n];
+        for (int t = T - 1; t >= 0; --t) {
+            const int64_t idx = (int64_t)t * N + n;
+            const float v = val[idx];
+            const float nd = 1.0f - done[idx];
+            const float delta = rew[idx] + gamma * vn * nd - v;
+            a = delta + gl * nd * a;
+            adv[idx] = a;
+            ret[idx] = a + v;
+            s1 += (double)a;
+            s2 += (double)a * (double)a;
+            vn = v;
+        }
+    }
+    if (want_stats) finish_stats(s1, s2, so);
+}
+
+__global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int64_t count, const double* __restrict__ stats)
+{
+    const float mean = (float)stats[1];
+    const float scale = (float)(1.0 / (stats[2] + kNormEps));
+    const int64_t n4 = count / 4;
+    float4* a4 = reinterpret_cast<float4*>(adv);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 v = a4[i];
+        v.x = (v.x - mean) * scale;
+        v.y = (v.y - mean) * scale;
+        v.z = (v.z - mean) * scale;
+        v.w = (v.w - mean) * scale;
+        a4[i] = v;
+    }
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        adv[i] = (adv[i] - mean) * scale;
+}
+
+enum class GaeKernel { C64x4_32, C32x8_16, C16x16_8, C16x16_32, C16x16_64, Seq };
+
+GaeKernel pick(int T, int N)
+{
+    if (T <= 128) {
+        if ((N + 63) / 64 >= 512) return GaeKernel::C64x4_32;
+        if ((N + 31) / 32 >= 512) return GaeKernel::C32x8_16;
+        return GaeKernel::C16x16_8;
+    }
+    if (T <= 512) return GaeKernel::C16x16_32;
+    if (T <= 1024) return GaeKernel::C16x16_64;
+    return GaeKernel::Seq;
+}
+
+int blocks_of(GaeKernel k, int N)
+{
+    switch (k) {
+    case GaeKernel::C64x4_32: return (N + 63) / 64;
+    case GaeKernel::C32x8_16: return (N + 31) / 32;
+    case GaeKernel::Seq: return (N + 255) / 256;
+    default: return (N + 15) / 16;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes)
+{
+    if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
+    if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
+    *bytes = kHeaderBytes + sizeof(double) * 2 * (size_t)((N + 15) / 16);
+    return RL_OK;
+}
+
+int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values, int32_t T,
+           int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize, double* adv_stats,
+           void* ws, size_t ws_bytes, void* stream)
+{
+    if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
+    if ((int64_t)T * N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "T*N too large");
+    if (!rewards || !values || !dones || !last_values || !adv || !ret)
+        return rl::fail(RL_EINVAL, "rewards, values, dones, last_values, adv and ret must be non-NULL");
+    if (normalize < 0 || normalize > 2) return rl::fail(RL_EINVAL, "normalize %d outside {0, 1, 2}", normalize);
+    if (normalize != 0 && (!adv_stats || !ws)) return rl::fail(RL_EINVAL, "normalize needs adv_stats and ws");
+    const void* ptrs[] = {rewards, values, dones, last_values, adv, ret};
+    for (const void* p : ptrs)
+        if (!rl::aligned(p, 4)) return rl::fail(RL_EALIGN, "a float array is not 4-byte aligned");
+    if (normalize == 1 && !rl::aligned(adv, 16)) return rl::fail(RL_EALIGN, "adv must be 16-byte aligned to normalize");
+    size_t need = 0;
+    rl_gae_workspace_bytes(T, N, &need);
+    if (normalize != 0) {
+        if (!rl::aligned(ws, 8) || !rl::aligned(adv_stats, 8)) return rl::fail(RL_EALIGN, "ws / adv_stats not 8-byte aligned");
+        if (ws_bytes < need) return rl::fail(RL_ESIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    }
+    hipStream_t st = rl::as_stream(stream);
+    const float gl = gamma * lambda;
+    StatsOut so{};
+    if (normalize != 0) {
+        so.ticket = static_cast<unsigned*>(ws);
+        so.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kHeaderBytes);
+        so.stats = adv_stats;
+        so.count = (double)T * (double)N;
+    }
+    const int want = normalize != 0 ? 1 : 0;
+    const GaeKernel k = pick(T, N);
+    const dim3 grid(blocks_of(k, N)), block(256);
+    switch (k) {
+    case GaeKernel::C64x4_32:
+        hipLaunchKernelGGL((k_gae_chunked<64, 32>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+                           (T + 3) / 4, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::C32x8_16:
+        hipLaunchKernelGGL((k_gae_chunked<32, 16>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+                           (T + 7) / 8, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::C16x16_8:
+        hipLaunchKernelGGL((k_gae_chunked<16, 8>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+                           (T + 15) / 16, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::C16x16_32:
+        hipLaunchKernelGGL((k_gae_chunked<16, 32>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+                           (T + 15) / 16, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::C16x16_64:
+        hipLaunchKernelGGL((k_gae_chunked<16, 64>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+                           (T + 15) / 16, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::Seq:
+        hipLaunchKernelGGL(k_gae_seq, grid, block, 0, st, rewards, values, dones, last_values, T, N, gamma, gl, adv,
+                           ret, want, so);
+        break;
+    }
+    if (int rc = rl::check_launch("gae_scan")) return rc;
+    if (normalize == 1) {
+        const int64_t count = (int64_t)T * N;
+        const int nb = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 8192);
+        hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, st, adv, count, adv_stats);
+        if (int rc = rl::check_launch("adv_normalize")) return rc;
+    }
+    return RL_OK;
+}
+
+}  // extern "C"

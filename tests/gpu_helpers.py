@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU parity tests: tolerance checks and paired GPU / oracle env batches."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from resident_rl_rollout_amd import binding, inputs
+
+
+def assert_gae_close(got, ref, what, rel=1e-5):
+    """|g - o| <= rel * (|o| + rms(o)) per element: the scale floor keeps the bound meaningful for
+    values near zero (normalised advantages have mean 0)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    bound = rel * (np.abs(ref) + rms)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at {i}: "
+                             f"got {got[i]!r} want {ref[i]!r} (bound {bound[i]:.3g})")
+
+
+def assert_loss_close(got, ref, scale, what, rel=1e-4):
+    """|g - o| <= rel * (|o| + mean |summand|) per minibatch scalar."""
+    got = np.asarray(got, np.float64)
+    bound = rel * (np.abs(ref) + scale)
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), f"{what}: err {err[err > bound]} bound {bound[err > bound]}"
+
+
+class PairedEnvs:
+    """The same env batch on the GPU (through the C ABI) and in the oracle, stepped with the same actions."""
+
+    def __init__(self, ms: inputs.MapSet, n, *, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_TILES,
+                 sprites=None, obs_stride=None):
+        self.gpu = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip, time_limit=time_limit,
+                               obs_mode=obs_mode, sprites=sprites, obs_stride=obs_stride)
+        self.ora = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip,
+                                    time_limit=time_limit, sprites=sprites)
+        self.ora.reset()
+        self.n = n
+        self.obs_mode = obs_mode
+        self.obs = self.gpu.new_obs()
+        self.rew = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.done = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.gpu.reset(self.obs)
+
+    def oracle_obs(self):
+        if self.obs_mode == binding.OBS_TILES:
+            return self.ora.obs_tiles()
+        return self.ora.obs_pixels().reshape(self.n, -1)
+
+    def gpu_obs(self):
+        size = binding.OBS_TILES_SIZE if self.obs_mode == binding.OBS_TILES else binding.OBS_PIXELS_SIZE
+        return self.obs[:, :size].cpu().numpy()
+
+    def step(self, actions_np):
+        a = torch.from_numpy(np.ascontiguousarray(actions_np, np.int32)).cuda()
+        self.gpu.step(a, self.obs, self.rew, self.done)
+        r, d = self.ora.step(actions_np)
+        return r, d
+
+    def check_state(self, what):
+        got = self.gpu.read_state().cpu().numpy()
+        if not np.array_equal(got, self.ora.state):
+            bad = np.argwhere(got != self.ora.state)
+            e, f = bad[0]
+            raise AssertionError(f"{what}: state differs in {len(bad)} fields; first env {e} field "
+                                 f"{oracle.STATE_FIELDS[f]}: gpu {got[e]} oracle {self.ora.state[e]}")
+
+    def check_step(self, r, d, what):
+        np.testing.assert_array_equal(self.rew.cpu().numpy(), r, err_msg=f"{what}: rewards")
+        np.testing.assert_array_equal(self.done.cpu().numpy(), d, err_msg=f"{what}: dones")
+
+    def check_obs(self, what, envs=None):
+        got = self.gpu_obs()
+        ref = self.oracle_obs()
+        if envs is not None:
+            got, ref = got[envs], ref[envs]
+        if not np.array_equal(got.view(np.uint8), ref.view(np.uint8)):
+            bad = np.argwhere(got != ref)
+            raise AssertionError(f"{what}: obs differ at {len(bad)} elements, first {bad[:5].tolist()}")

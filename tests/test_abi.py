@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: librl.so loads, exports every function include/rl.h declares, and rejects
+invalid arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from resident_rl_rollout_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rl.h")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(rl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("rl_env_create", "rl_env_reset", "rl_env_step", "rl_env_destroy", "rl_gae", "rl_ppo_loss",
+                     "rl_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(n for n, _, _ in binding.SIGNATURES) == declared_functions()
+
+
+def _cfg(**kw):
+    base = dict(num_envs=64, num_maps=1, map_h=32, map_w=128, num_ckpts=7, frame_skip=3, time_limit=2000,
+                obs_mode=0, obs_stride=1397)
+    base.update(kw)
+    return binding.EnvConfig(*[base[k] for k, _ in binding.EnvConfig._fields_])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(num_envs=0), -1, "num_envs"), (dict(num_maps=0), -1, "num_maps"), (dict(map_h=0), -1, "map_h"),
+    (dict(map_w=70000), -1, "map_w"), (dict(num_ckpts=-1), -1, "num_ckpts"), (dict(frame_skip=0), -1, "frame_skip"),
+    (dict(frame_skip=6), -1, "frame_skip"), (dict(time_limit=0), -1, "time_limit"), (dict(obs_mode=2), -1, "obs_mode"),
+    (dict(obs_stride=1396), -1, "obs_stride"), (dict(obs_mode=1, obs_stride=28226), -2, "multiple of 4"),
+])
+def test_config_validation(kw, code, msg):
+    lib = binding.lib()
+    n = ctypes.c_size_t()
+    assert lib.rl_env_state_bytes(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == code
+    assert msg in lib.rl_last_error().decode()
+
+
+def test_sizes_and_layout():
+    lib = binding.lib()
+    n, e, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.rl_env_obs_size(ctypes.byref(_cfg()), ctypes.byref(n), ctypes.byref(e)) == 0
+    assert (n.value, e.value) == (1397, 4)
+    assert lib.rl_env_obs_size(ctypes.byref(_cfg(obs_mode=1, obs_stride=28224)), ctypes.byref(n), ctypes.byref(e)) == 0
+    assert (n.value, e.value) == (28224, 1)
+    offs = (ctypes.c_size_t * 4)()
+    assert lib.rl_step_layout(ctypes.byref(_cfg(num_envs=65536)), offs, ctypes.byref(b)) == 0
+    assert list(offs) == [0, 262144, 262144 + 65536 * 5588, 262144 + 65536 * 5588 + 262144]
+    assert b.value == offs[3] + 262144
+    assert lib.rl_env_state_bytes(ctypes.byref(_cfg()), ctypes.byref(n)) == 0 and n.value % 256 == 0
+
+
+def test_entry_points_reject_before_any_hip_call():
+    lib = binding.lib()
+    out = ctypes.c_void_p()
+    fake = ctypes.c_void_p(4096)
+    # rl_env_create: NULL maps, misaligned state, too-small state
+    assert lib.rl_env_create(ctypes.byref(_cfg()), None, fake, fake, None, fake, 1 << 30, None, ctypes.byref(out)) == -1
+    assert lib.rl_env_create(ctypes.byref(_cfg()), fake, fake, fake, None, ctypes.c_void_p(4100), 1 << 30, None,
+                             ctypes.byref(out)) == -2
+    assert lib.rl_env_create(ctypes.byref(_cfg()), fake, fake, fake, None, fake, 100, None, ctypes.byref(out)) == -3
+    assert lib.rl_env_create(ctypes.byref(_cfg(obs_mode=1, obs_stride=28224)), fake, fake, fake, None, fake, 1 << 30,
+                             None, ctypes.byref(out)) == -1
+    assert lib.rl_env_step(None, fake, fake, fake, fake, None) == -1
+    assert lib.rl_env_reset(None, None, None, None) == -1
+    # rl_gae: sizes, NULLs, enum, workspace
+    assert lib.rl_gae(fake, fake, fake, fake, 0, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
+    assert lib.rl_gae(None, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
+    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 3, fake, fake, 1 << 20, None) == -1
+    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 1, fake, fake, 8, None) == -3
+    assert lib.rl_gae(fake, ctypes.c_void_p(4098), fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -2
+    # rl_ppo_loss: B % mb, A range, alignment, workspace
+    args = [fake] * 6 + [None, None]
+    assert lib.rl_ppo_loss(*args, 100, 12, 30, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
+    assert "multiple" in lib.rl_last_error().decode()
+    assert lib.rl_ppo_loss(*args, 100, 65, 10, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
+    assert lib.rl_ppo_loss(ctypes.c_void_p(4100), *args[1:], 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 1 << 20,
+                           None) == -2
+    assert lib.rl_ppo_loss(*args, 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 8, None) == -3
+    need = ctypes.c_size_t()
+    assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
+    assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 256 + 16 * 128

@@ -1,0 +1,95 @@
+"""GPU parity of ppo_loss against the float64 oracle.
+
+Tolerance: |g - o| <= 1e-4 (|o| + mean_i |summand_i|) per minibatch scalar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from resident_rl_rollout_amd import binding, inputs
+from tests.gpu_helpers import assert_loss_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _case(seed, b, a=12):
+    pi = inputs.make_policy_inputs(seed, b, a)
+    rng = np.random.default_rng(seed + 1)
+    adv = rng.standard_normal(b).astype(np.float32)
+    ret = rng.standard_normal(b).astype(np.float32)
+    return pi, adv, ret
+
+
+def _gpu(pi, adv, ret, mb, use_perm=True, stats=None, a=12):
+    out = binding.ppo_loss(_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret),
+                           _dev(pi.new_values), _dev(pi.perm) if use_perm else None, mb,
+                           adv_stats=None if stats is None else _dev(stats))
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("b,mb,use_perm,a", [(262144, 8192, True, 12), (262144, 8192, False, 12),
+                                             (4096, 4096, True, 12), (1000, 10, True, 12), (7, 1, True, 12),
+                                             (30000, 3000, True, 5), (8192, 1024, False, 64), (600, 200, True, 3)])
+def test_loss_matches_oracle(b, mb, use_perm, a, gpu_lib):
+    pi, adv, ret = _case(b + mb + a, b, a)
+    got = _gpu(pi, adv, ret, mb, use_perm)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values,
+                                 pi.perm if use_perm else None, mb)
+    assert got.shape == ref.shape
+    assert_loss_close(got, ref, scale, f"B={b} mb={mb} perm={use_perm} A={a}")
+
+
+def test_inline_normalisation_matches_normalised_input(gpu_lib):
+    b, mb = 65536, 8192
+    pi, adv, ret = _case(3, b)
+    raw = (adv * 2.5 + 0.3).astype(np.float32)
+    norm, mean, std = oracle.normalize(raw.astype(np.float64))
+    stats = np.array([b, mean, std], np.float64)
+    got = _gpu(pi, raw, ret, mb, stats=stats)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, norm, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(got, ref, scale, "inline normalisation")
+
+
+def test_full_rollout_batch_sixteen_minibatches(gpu_lib):
+    # The bench's launch configuration: B = 128 x 65536 samples in 16 shuffled minibatches.
+    b, mb = 128 * 65536, 524288
+    pi, adv, ret = _case(20, b)
+    got = _gpu(pi, adv, ret, mb)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(got, ref, scale, "16 minibatches")
+
+
+def test_clip_and_entropy_special_cases(gpu_lib):
+    # uniform logits: entropy ln 12; ratio set on both sides of the clip band
+    b = 256
+    logits = np.zeros((b, 12), np.float32)
+    actions = (np.arange(b) % 12).astype(np.int32)
+    ratios = np.where(np.arange(b) % 2 == 0, 1.5, 0.5)
+    old_logp = (-np.log(12.0) - np.log(ratios)).astype(np.float32)
+    adv = np.where(np.arange(b) % 4 < 2, 1.0, -1.0).astype(np.float32)
+    ret = np.zeros(b, np.float32)
+    nv = np.zeros(b, np.float32)
+    pi = inputs.PolicyInputs(logits, actions, old_logp, nv, np.arange(b, dtype=np.int32))
+    got = _gpu(pi, adv, ret, b)
+    ref, scale = oracle.ppo_loss(logits, actions, old_logp, adv, ret, nv, None, b)
+    assert_loss_close(got, ref, scale, "clip cases")
+    assert got[0, 2] == pytest.approx(np.log(12.0), rel=1e-6)
+    assert got[0, 1] == 0.0
+
+
+def test_deterministic(gpu_lib):
+    pi, adv, ret = _case(9, 100000)
+    o1 = _gpu(pi, adv, ret, 10000)
+    o2 = _gpu(pi, adv, ret, 10000)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_rejects_bad_arguments(gpu_lib):
+    pi, adv, ret = _case(1, 100)
+    with pytest.raises(binding.RLError, match="multiple"):
+        _gpu(pi, adv, ret, 30)
