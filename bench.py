@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10, help="timed rollouts")
     p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-envs", type=int, default=8192, help="envs in the oracle's bounded sample")
+    p.add_argument("--cpu-envs", type=int, default=16384, help="envs in the oracle's bounded sample")
     return p.parse_args()
 
 

@@ -152,9 +152,8 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes);
  *              adv with (A - mean) / (std + 1e-8); 2: compute the statistics only (adv stays raw) so that
  *              rl_ppo_loss can normalise on the fly. ret always uses the raw A.
  *   adv_stats  device f64[3] = {count, mean, std}, written when normalize != 0 (may be NULL for 0).
- *   ws         device workspace of rl_gae_workspace_bytes(T, N) bytes, 8-byte aligned, zero-filled before
- *              its first use; every call leaves it zero-filled again. Calls sharing a workspace must not
- *              overlap.
+ *   ws         device workspace of rl_gae_workspace_bytes(T, N) bytes, 8-byte aligned (any contents; used
+ *              when normalize != 0, may be NULL otherwise). Calls sharing a workspace must not overlap.
  * Statistics are reduced in a fixed order, so results are identical from run to run. */
 int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values,
            int32_t T, int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize,
@@ -174,8 +173,8 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   logits device f32[B][A] (16-byte aligned rows need A % 4 == 0; any A in 1..64 is accepted);
  *   actions device int32[B] in [0, A); old_logp, adv, ret, new_values device f32[B]; perm device
  *   int32[B], a permutation of 0..B-1, or NULL.
- *   B % mb must be 0. ws as for rl_gae (rl_ppo_loss_workspace_bytes bytes, zero-filled before first use,
- *   left zero-filled). Reductions use float64 partials in a fixed order. */
+ *   B % mb must be 0. ws: device workspace of rl_ppo_loss_workspace_bytes(B, mb) bytes, 8-byte aligned (any
+ *   contents); calls sharing it must not overlap. Reductions use float64 partials in a fixed order. */
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
                 const float* ret, const float* new_values, const int32_t* perm, const double* adv_stats,
                 int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef, float ent_coef,

@@ -107,8 +107,8 @@ _workspaces: dict = {}
 
 
 def workspace(kind: str, nbytes: int, device) -> torch.Tensor:
-    """A zero-filled device workspace per (kind, size, device). The library leaves it zero-filled after
-    every call, so it is reused as is; calls sharing one must not overlap."""
+    """A device workspace per (kind, size, device), reused by every call of that kind (calls on one
+    stream never overlap)."""
     key = (kind, int(nbytes), str(device))
     ws = _workspaces.get(key)
     if ws is None:

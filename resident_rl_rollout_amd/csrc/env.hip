@@ -272,22 +272,36 @@ __device__ __forceinline__ Neighbourhood load_neighbourhood(const EnvDev& d, int
     return nb;
 }
 
-__global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restrict__ actions,
-                                              float* __restrict__ rewards, float* __restrict__ dones,
-                                              int head_prev, int head_new)
-{
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= d.n) return;
-    const int m = n % d.m;
+// The five words of one ring slot.
+struct SlotWords {
+    int32_t x, y, vxy, misc, tick;
+};
 
-    int32_t x = slot_word(d, head_prev, 0, n);
-    int32_t y = slot_word(d, head_prev, 1, n);
-    const int32_t vxy = slot_word(d, head_prev, 2, n);
-    const uint32_t misc = (uint32_t)slot_word(d, head_prev, 3, n);
-    int32_t tick = slot_word(d, head_prev, 4, n);
-    int32_t next = d.extra[n];
-    int32_t best_x = d.extra[d.np + n];
-    int32_t a = actions[n];
+__device__ __forceinline__ SlotWords load_slot(const EnvDev& d, int s, int n)
+{
+    return SlotWords{slot_word(d, s, 0, n), slot_word(d, s, 1, n), slot_word(d, s, 2, n), slot_word(d, s, 3, n),
+                     slot_word(d, s, 4, n)};
+}
+
+// The words of the newest ring slot after a decision, plus the extras and whether the env was reset.
+struct Decision {
+    int32_t x, y, vxy, misc, tick, next, best_x;
+    bool done;
+};
+
+// One decision of env n from its current slot `cur` and extras: decode the action, run up to frame_skip
+// ticks, write the reward and done, and store the new state in ring slot head_new (or the spawn state in
+// all four slots after a terminal tick).
+__device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a, const SlotWords& cur, int32_t next,
+                                               int32_t best_x, float* __restrict__ rewards,
+                                               float* __restrict__ dones, int head_new)
+{
+    const int m = n % d.m;
+    int32_t x = cur.x;
+    int32_t y = cur.y;
+    const int32_t vxy = cur.vxy;
+    const uint32_t misc = (uint32_t)cur.misc;
+    int32_t tick = cur.tick;
     if (a < 0 || a >= kNumActions) a = 0;
 
     int32_t vx = (int16_t)(vxy & 0xffff);
@@ -385,7 +399,8 @@ __global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restric
     dones[n] = done ? 1.0f : 0.0f;
     if (done) {
         write_spawn(d, n);
-        return;
+        const int32_t* sp = d.spawn + 2 * m;
+        return Decision{sp[0], sp[1], 0, (int32_t)(kFacingRight | kGroundedBit), 0, 0, sp[0], true};
     }
     const uint32_t new_misc = (facing > 0 ? kFacingRight : 0u) | (grounded ? kGroundedBit : 0u) |
                               (jump_held ? kJumpHeldBit : 0u) | (hook_held ? kHookHeldBit : 0u) |
@@ -399,6 +414,18 @@ __global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restric
     slot_word(d, head_new, 4, n) = tick;
     d.extra[n] = next;
     d.extra[d.np + n] = best_x;
+    return Decision{x, y, (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16)), (int32_t)new_misc, tick,
+                    next, best_x, false};
+}
+
+// env_step alone (the pixel path renders in its own kernel): one lane per env.
+__global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restrict__ actions,
+                                              float* __restrict__ rewards, float* __restrict__ dones,
+                                              int head_prev, int head_new)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= d.n) return;
+    env_decide(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n], rewards, dones, head_new);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -457,6 +484,148 @@ __global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__
         r += 1;
         c += 64 - kWinW;
         if (c >= kWinW) { c -= kWinW; r += 1; }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// env_step + obs_gather fused, tile mode. A block owns E consecutive envs.
+//   Phase A (threads 0 .. E-1, one env each): the decision, then the env's 64 non-window observation
+//   values (4 frames of 15, newest first, and the 4 checkpoint dims) and the address of its window's
+//   top-left tile go to LDS.
+//   Phase B (all 256 threads): the E observation rows. When rows are packed (stride 1397) and the buffer
+//   is 16-byte aligned, the block's rows form one contiguous region written as aligned float4 stores,
+//   the densest store stream the memory system takes; four window values come from one unaligned dword
+//   of the map row (merged with the next row's first bytes where the four straddle a row end).
+//   Otherwise each wave writes whole rows with dword stores.
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kTail = kObsTiles - kWinSize;   // 64
+#ifndef RL_STEP_TILES_ENVS
+#define RL_STEP_TILES_ENVS 32
+#endif
+constexpr int kStepTilesEnvs = RL_STEP_TILES_ENVS;   // envs per block of the fused tile kernel
+static_assert(kStepTilesEnvs % 16 == 0 && kStepTilesEnvs <= 256, "a block's rows must start 16-byte aligned");
+
+__device__ __forceinline__ void put_frame(float* t, int32_t x, int32_t y, int32_t vxy, uint32_t misc, int32_t tick)
+{
+#pragma unroll
+    for (int dim = 0; dim < kFrameDims; ++dim) t[dim] = frame_dim(dim, x, y, vxy, misc, tick);
+}
+
+// Observation element k (< 1397) of staged env e.
+__device__ __forceinline__ float obs_elem(const EnvDev& d, const int64_t* wbase, const float (*tail)[kTail], int e,
+                                          int k)
+{
+    if (k < kWinSize) {
+        const int r = k / kWinW, c = k - r * kWinW;
+        return (float)d.map[wbase[e] + (int64_t)r * d.wp + c];
+    }
+    return tail[e][k - kWinSize];
+}
+
+#ifndef RL_STEP_TILES_MIN_WAVES
+#define RL_STEP_TILES_MIN_WAVES 1
+#endif
+
+template <int E, bool FLAT>
+__global__ __launch_bounds__(256, RL_STEP_TILES_MIN_WAVES) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+                                                    float* __restrict__ rewards, float* __restrict__ dones,
+                                                    float* __restrict__ obs, int64_t stride, int head_prev,
+                                                    int head_new)
+{
+    __shared__ float tail[E][kTail];
+    __shared__ int64_t wbase[E];
+    const int n0 = blockIdx.x * E;
+    const int ne = min(E, d.n - n0);
+
+    if ((int)threadIdx.x < ne) {
+        const int e = threadIdx.x;
+        const int n = n0 + e;
+        const int m = n % d.m;
+        // Every load that does not depend on the physics is issued first: the action, the current slot
+        // (frame 1 of the new stack), the two slots before it (frames 2 and 3) and the extras.
+        const int32_t a = actions[n];
+        const SlotWords cur = load_slot(d, head_prev, n);
+        const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
+        const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
+        const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
+        const Decision s = env_decide(d, n, a, cur, next0, best0, rewards, dones, head_new);
+        float* t = tail[e];
+        put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
+        if (s.done) {
+#pragma unroll
+            for (int f = 1; f < kStack; ++f)
+#pragma unroll
+                for (int dim = 0; dim < kFrameDims; ++dim) t[f * kFrameDims + dim] = t[dim];
+        } else {
+            put_frame(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
+            put_frame(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
+            put_frame(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
+        }
+        float* ck = t + kStack * kFrameDims;
+        if (s.next < d.k) {
+            const int32_t* p = d.ckpt + ((int64_t)m * d.k + s.next) * 2;
+            ck[0] = (float)(p[0] * kTile + kTile / 2 - (s.x + kHalfBox)) * 0x1p-8f;
+            ck[1] = (float)(p[1] * kTile + kTile / 2 - (s.y + kHalfBox)) * 0x1p-8f;
+        } else {
+            ck[0] = 0.0f;
+            ck[1] = 0.0f;
+        }
+        ck[2] = (float)s.next;
+        ck[3] = (float)s.best_x * 0x1p-8f;
+        const int pcol = clampi((s.x + kHalfBox) >> 8, 0, d.w - 1);
+        const int prow = clampi((s.y + kHalfBox) >> 8, 0, d.h - 1);
+        wbase[e] = tile_ptr(d, m, prow - kWinCy, pcol - kWinCx) - d.map;
+    }
+    __syncthreads();
+
+    if constexpr (FLAT) {
+        const int total = ne * kObsTiles;
+        float* base = obs + (int64_t)n0 * kObsTiles;
+        const int nq = total >> 2;
+        for (int q = threadIdx.x; q < nq; q += 256) {
+            const int f = q << 2;
+            const int e = f / kObsTiles;
+            const int k = f - e * kObsTiles;
+            float4 v;
+            if (k + 3 < kWinSize) {
+                const int r = k / kWinW, c = k - r * kWinW;
+                const uint8_t* p = d.map + wbase[e] + (int64_t)r * d.wp + c;
+                uint32_t w;
+                __builtin_memcpy(&w, p, 4);
+                const int avail = kWinW - c;      // bytes of row r from column c on
+                if (avail < 4) {
+                    uint32_t w1;                   // row r+1, starting 'avail' bytes before its column 0
+                    __builtin_memcpy(&w1, p + d.wp - kWinW, 4);
+                    const uint32_t keep = (1u << (8 * min(avail, 3))) - 1u;
+                    w = (w & keep) | (w1 & ~keep);
+                }
+                v.x = (float)(w & 0xffu);
+                v.y = (float)((w >> 8) & 0xffu);
+                v.z = (float)((w >> 16) & 0xffu);
+                v.w = (float)(w >> 24);
+            } else {
+                float vv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int kk = k + j, ee = e;
+                    if (kk >= kObsTiles) { kk -= kObsTiles; ee += 1; }
+                    vv[j] = obs_elem(d, wbase, tail, ee, kk);
+                }
+                v = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            }
+            reinterpret_cast<float4*>(base)[q] = v;
+        }
+        for (int f = (nq << 2) + threadIdx.x; f < total; f += 256) {
+            const int e = f / kObsTiles;
+            base[f] = obs_elem(d, wbase, tail, e, f - e * kObsTiles);
+        }
+    } else {
+        const int lane = threadIdx.x & 63;
+        for (int e = threadIdx.x >> 6; e < ne; e += 4) {
+            float* o = obs + (int64_t)(n0 + e) * stride;
+            for (int k = lane; k < kObsTiles; k += 64) o[k] = obs_elem(d, wbase, tail, e, k);
+        }
     }
 }
 
@@ -700,6 +869,19 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
     hipStream_t st = rl::as_stream(stream);
     const EnvDev d = dev_of(e);
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
+    if (e->cfg.obs_mode == RL_OBS_TILES) {
+        float* o = static_cast<float*>(obs);
+        const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs);
+        if (e->cfg.obs_stride == kObsTiles && rl::aligned(obs, 16))
+            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, true>), grid, dim3(256), 0, st, d, actions, rewards,
+                               dones, o, e->cfg.obs_stride, head_prev, head_new);
+        else
+            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, false>), grid, dim3(256), 0, st, d, actions, rewards,
+                               dones, o, e->cfg.obs_stride, head_prev, head_new);
+        if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
+        e->counter += 1;
+        return RL_OK;
+    }
     hipLaunchKernelGGL(k_step, dim3((d.n + 255) / 256), dim3(256), 0, st, d, actions, rewards, dones, head_prev,
                        head_new);
     if (int rc = rl::check_launch("env_step")) return rc;

@@ -12,8 +12,9 @@
 // each row [t][n0 .. n0+E) is a coalesced segment.
 //
 // Statistics: per-thread float64 sums of A and A^2, a block reduction, per-block partials in the
-// workspace, and the last block to finish (an atomic ticket) reduces the partials in block order. No
-// floating-point atomics: results are identical from run to run.
+// workspace, then a one-block finalise kernel reduces the partials in block order (the kernel boundary
+// makes every block's partial visible; no device-wide fence or atomic per block). No floating-point
+// atomics: results are identical from run to run.
 
 #include <algorithm>
 
@@ -22,13 +23,9 @@
 namespace {
 
 constexpr double kNormEps = 1e-8;
-constexpr size_t kHeaderBytes = 256;   // ticket counter lives at the start of the workspace
 
 struct StatsOut {
-    double* partials;     // [grid][2]
-    unsigned* ticket;
-    double* stats;        // {count, mean, std}
-    double count;
+    double* partials;     // [grid][2]: sum A, sum A^2 of each block
 };
 
 // Sum of a double across the block (256 threads), the same fixed order on every run.
@@ -45,53 +42,50 @@ __device__ __forceinline__ double block_sum(double v, double* lds)
     return s;
 }
 
-// Publish this block's (sum A, sum A^2); the last block to arrive reduces all partials in block order
-// and writes {count, mean, population std}, then re-arms the ticket.
-__device__ void finish_stats(double s1, double s2, const StatsOut& so)
+// Publish this block's (sum A, sum A^2).
+__device__ void publish_stats(double s1, double s2, const StatsOut& so)
 {
-    __shared__ double lds[8];
-    __shared__ bool last;
+    __shared__ double lds[32];
     s1 = block_sum(s1, lds);
-    s2 = block_sum(s2, lds + 4);
+    s2 = block_sum(s2, lds + 16);
     if (threadIdx.x == 0) {
         so.partials[2 * blockIdx.x] = s1;
         so.partials[2 * blockIdx.x + 1] = s2;
-        __threadfence();
-        const unsigned t = atomicAdd(so.ticket, 1u);
-        last = (t == gridDim.x - 1);
     }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
+
+// One block: reduce the per-block partials in block order into {count, mean, population std}.
+__global__ __launch_bounds__(256) void k_stats_finalize(const double* __restrict__ partials, int blocks, double count,
+                                                        double* __restrict__ stats)
+{
+    __shared__ double lds[8];
     double a = 0.0, b = 0.0;
-    for (unsigned i = threadIdx.x; i < gridDim.x; i += blockDim.x) {
-        a += so.partials[2 * i];
-        b += so.partials[2 * i + 1];
+    for (int i = threadIdx.x; i < blocks; i += blockDim.x) {
+        a += partials[2 * i];
+        b += partials[2 * i + 1];
     }
     a = block_sum(a, lds);
     b = block_sum(b, lds + 4);
     if (threadIdx.x == 0) {
-        const double mean = a / so.count;
-        double var = b / so.count - mean * mean;
+        const double mean = a / count;
+        double var = b / count - mean * mean;
         var = var > 0.0 ? var : 0.0;
-        so.stats[0] = so.count;
-        so.stats[1] = mean;
-        so.stats[2] = sqrt(var);
-        *so.ticket = 0u;
-        __threadfence();
+        stats[0] = count;
+        stats[1] = mean;
+        stats[2] = sqrt(var);
     }
 }
 
-// Block = E envs x (256 / E) chunks of L <= LMAX steps. Thread (e, ch) owns env blockIdx.x*E + e and
+// Block = E envs x (BLOCK / E) chunks of L <= LMAX steps. Thread (e, ch) owns env blockIdx.x*E + e and
 // steps [ch*L, min(T, ch*L + L)).
-template <int E, int LMAX>
-__global__ __launch_bounds__(256) void k_gae_chunked(const float* __restrict__ rew, const float* __restrict__ val,
+template <int E, int LMAX, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__ rew, const float* __restrict__ val,
                                                      const float* __restrict__ done, const float* __restrict__ vlast,
                                                      int T, int N, int L, float gamma, float gl,
                                                      float* __restrict__ adv, float* __restrict__ ret,
                                                      int want_stats, StatsOut so)
 {
-    constexpr int C = 256 / E;
+    constexpr int C = BLOCK / E;
     __shared__ float sb[C][E];
     __shared__ float sc[C][E];
     const int e = threadIdx.x % E;
@@ -101,18 +95,19 @@ __global__ __launch_bounds__(256) void k_gae_chunked(const float* __restrict__ r
     const int t0 = ch * L;
     const int len = valid ? max(0, min(L, T - t0)) : 0;
 
+    // Loads are unconditional (indices clamped into the arrays) so that all of a thread's loads issue
+    // back to back; only the arithmetic and the stores are predicated on the chunk's length.
+    const int nn = min(n, N - 1);
     float delta[LMAX], cf[LMAX], vv[LMAX];
 #pragma unroll
     for (int j = 0; j < LMAX; ++j) {
-        if (j < len) {
-            const int64_t idx = (int64_t)(t0 + j) * N + n;
-            vv[j] = val[idx];
-            delta[j] = rew[idx];
-            cf[j] = 1.0f - done[idx];
-        }
+        const int64_t idx = (int64_t)min(t0 + j, T - 1) * N + nn;
+        vv[j] = val[idx];
+        delta[j] = rew[idx];
+        cf[j] = 1.0f - done[idx];
     }
-    float vnext_tail = 0.0f;
-    if (len > 0) vnext_tail = (t0 + len < T) ? val[(int64_t)(t0 + len) * N + n] : vlast[n];
+    const float v_after = val[(int64_t)min(t0 + len, T - 1) * N + nn];
+    const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
 
     float b = 0.0f, c = 1.0f;
 #pragma unroll
@@ -145,7 +140,7 @@ __global__ __launch_bounds__(256) void k_gae_chunked(const float* __restrict__ r
             s2 += (double)a * (double)a;
         }
     }
-    if (want_stats) finish_stats(s1, s2, so);
+    if (want_stats) publish_stats(s1, s2, so);
 }
 
 // One lane per env walking t = T-1 .. 0: the fallback for horizons longer than the chunked kernels hold.
@@ -171,7 +166,7 @@ __global__ __launch_bounds__(256) void k_gae_seq(const float* __restrict__ rew, 
             vn = v;
         }
     }
-    if (want_stats) finish_stats(s1, s2, so);
+    if (want_stats) publish_stats(s1, s2, so);
 }
 
 __global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int64_t count, const double* __restrict__ stats)
@@ -193,10 +188,16 @@ __global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int6
         adv[i] = (adv[i] - mean) * scale;
 }
 
-enum class GaeKernel { C64x4_32, C32x8_16, C16x16_8, C16x16_32, C16x16_64, Seq };
+enum class GaeKernel { C64x4_32, C32x8_16, C16x16_8, C16x16_32, C16x16_64, C256x4_32, Seq };
+
+#ifndef RL_GAE_FORCE
+#define RL_GAE_FORCE -1
+#endif
 
 GaeKernel pick(int T, int N)
 {
+    if (RL_GAE_FORCE >= 0 && T <= 128) return (GaeKernel)RL_GAE_FORCE;
+    if (T <= 128 && (N + 255) / 256 >= 128) return GaeKernel::C256x4_32;
     if (T <= 128) {
         if ((N + 63) / 64 >= 512) return GaeKernel::C64x4_32;
         if ((N + 31) / 32 >= 512) return GaeKernel::C32x8_16;
@@ -212,6 +213,7 @@ int blocks_of(GaeKernel k, int N)
     switch (k) {
     case GaeKernel::C64x4_32: return (N + 63) / 64;
     case GaeKernel::C32x8_16: return (N + 31) / 32;
+    case GaeKernel::C256x4_32: return (N + 255) / 256;
     case GaeKernel::Seq: return (N + 255) / 256;
     default: return (N + 15) / 16;
     }
@@ -225,7 +227,7 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes)
 {
     if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
     if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
-    *bytes = kHeaderBytes + sizeof(double) * 2 * (size_t)((N + 15) / 16);
+    *bytes = sizeof(double) * 2 * (size_t)((N + 15) / 16);
     return RL_OK;
 }
 
@@ -252,35 +254,34 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     hipStream_t st = rl::as_stream(stream);
     const float gl = gamma * lambda;
     StatsOut so{};
-    if (normalize != 0) {
-        so.ticket = static_cast<unsigned*>(ws);
-        so.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kHeaderBytes);
-        so.stats = adv_stats;
-        so.count = (double)T * (double)N;
-    }
+    if (normalize != 0) so.partials = static_cast<double*>(ws);
     const int want = normalize != 0 ? 1 : 0;
     const GaeKernel k = pick(T, N);
     const dim3 grid(blocks_of(k, N)), block(256);
     switch (k) {
     case GaeKernel::C64x4_32:
-        hipLaunchKernelGGL((k_gae_chunked<64, 32>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<64, 32, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 3) / 4, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C32x8_16:
-        hipLaunchKernelGGL((k_gae_chunked<32, 16>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<32, 16, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 7) / 8, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_8:
-        hipLaunchKernelGGL((k_gae_chunked<16, 8>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 8, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_32:
-        hipLaunchKernelGGL((k_gae_chunked<16, 32>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 32, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_64:
-        hipLaunchKernelGGL((k_gae_chunked<16, 64>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 64, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
+        break;
+    case GaeKernel::C256x4_32:
+        hipLaunchKernelGGL((k_gae_chunked<256, 32, 1024>), grid, dim3(1024), 0, st, rewards, values, dones,
+                           last_values, T, N, (T + 3) / 4, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::Seq:
         hipLaunchKernelGGL(k_gae_seq, grid, block, 0, st, rewards, values, dones, last_values, T, N, gamma, gl, adv,
@@ -288,6 +289,11 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
         break;
     }
     if (int rc = rl::check_launch("gae_scan")) return rc;
+    if (normalize != 0) {
+        hipLaunchKernelGGL(k_stats_finalize, dim3(1), dim3(256), 0, st, static_cast<const double*>(ws),
+                           blocks_of(k, N), (double)T * (double)N, adv_stats);
+        if (int rc = rl::check_launch("adv_stats")) return rc;
+    }
     if (normalize == 1) {
         const int64_t count = (int64_t)T * N;
         const int nb = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 8192);

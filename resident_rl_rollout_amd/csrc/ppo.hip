@@ -4,9 +4,9 @@
 // their minibatch means and the weighted total.
 //
 // Grid: (blocks per minibatch, minibatches). Each thread accumulates its samples in float64; a block
-// reduction (shuffles, then LDS) gives per-block partials, and the last block of each minibatch to finish
-// (an atomic ticket per minibatch) reduces them in block order and writes the four scalars. No
-// floating-point atomics, so results are identical from run to run.
+// reduction (shuffles, then LDS) gives per-block partials, and a finalise kernel with one block per
+// minibatch reduces them in block order and writes the four scalars. No floating-point atomics, so
+// results are identical from run to run.
 
 #include <algorithm>
 
@@ -17,7 +17,6 @@ namespace {
 constexpr double kNormEps = 1e-8;
 constexpr int kSamplesPerThread = 8;
 constexpr int kMaxBlocksPerMb = 4096;
-constexpr size_t kHeaderAlign = 256;
 
 struct LossArgs {
     const float* logits;
@@ -32,8 +31,6 @@ struct LossArgs {
     int A;
     float clip_lo, clip_hi, vf, ent;
     double* partials;   // [num_mb][bpm][3]
-    unsigned* tickets;  // [num_mb]
-    float* out;         // [num_mb][4]
 };
 
 __device__ __forceinline__ double block_sum(double v, double* lds)
@@ -105,7 +102,6 @@ template <int AC>
 __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 {
     __shared__ double lds[12];
-    __shared__ bool last;
     const int m = blockIdx.y;
     const int64_t base = (int64_t)m * p.mb;
     float mean = 0.0f, scale = 1.0f;
@@ -135,21 +131,23 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     s_pg = block_sum(s_pg, lds);
     s_v = block_sum(s_v, lds + 4);
     s_h = block_sum(s_h, lds + 8);
-    const int bpm = gridDim.x;
     if (threadIdx.x == 0) {
-        double* part = p.partials + ((int64_t)m * bpm + blockIdx.x) * 3;
+        double* part = p.partials + ((int64_t)m * gridDim.x + blockIdx.x) * 3;
         part[0] = s_pg;
         part[1] = s_v;
         part[2] = s_h;
-        __threadfence();
-        last = atomicAdd(&p.tickets[m], 1u) == (unsigned)bpm - 1;
     }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
+
+// One block per minibatch: reduce its per-block partials in block order and write the four scalars.
+__global__ __launch_bounds__(256) void k_ppo_finalize(const double* __restrict__ partials, int bpm, int64_t mb,
+                                                      float vf, float ent, float* __restrict__ out)
+{
+    __shared__ double lds[12];
+    const int m = blockIdx.x;
     double a = 0.0, b = 0.0, c = 0.0;
     for (int j = threadIdx.x; j < bpm; j += blockDim.x) {
-        const double* part = p.partials + ((int64_t)m * bpm + j) * 3;
+        const double* part = partials + ((int64_t)m * bpm + j) * 3;
         a += part[0];
         b += part[1];
         c += part[2];
@@ -158,14 +156,12 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     b = block_sum(b, lds + 4);
     c = block_sum(c, lds + 8);
     if (threadIdx.x == 0) {
-        const double inv = 1.0 / (double)p.mb;
+        const double inv = 1.0 / (double)mb;
         const double pg = a * inv, v = b * inv, h = c * inv;
-        p.out[4 * m + 0] = (float)pg;
-        p.out[4 * m + 1] = (float)v;
-        p.out[4 * m + 2] = (float)h;
-        p.out[4 * m + 3] = (float)(pg + (double)p.vf * v - (double)p.ent * h);
-        p.tickets[m] = 0u;
-        __threadfence();
+        out[4 * m + 0] = (float)pg;
+        out[4 * m + 1] = (float)v;
+        out[4 * m + 2] = (float)h;
+        out[4 * m + 3] = (float)(pg + (double)vf * v - (double)ent * h);
     }
 }
 
@@ -174,8 +170,6 @@ int blocks_per_mb(int64_t mb)
     const int64_t per_block = 256 * kSamplesPerThread;
     return (int)std::max<int64_t>(1, std::min<int64_t>((mb + per_block - 1) / per_block, kMaxBlocksPerMb));
 }
-
-size_t ticket_bytes(int64_t num_mb) { return rl::round_up(sizeof(unsigned) * (size_t)num_mb, kHeaderAlign); }
 
 }  // namespace
 
@@ -187,7 +181,7 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     if (B % mb != 0) return rl::fail(RL_EINVAL, "B %lld is not a multiple of mb %d", (long long)B, mb);
     if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
     const int64_t num_mb = B / mb;
-    *bytes = ticket_bytes(num_mb) + sizeof(double) * 3 * (size_t)num_mb * (size_t)blocks_per_mb(mb);
+    *bytes = sizeof(double) * 3 * (size_t)num_mb * (size_t)blocks_per_mb(mb);
     return RL_OK;
 }
 
@@ -229,16 +223,17 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
     p.clip_hi = 1.0f + clip_eps;
     p.vf = vf_coef;
     p.ent = ent_coef;
-    p.tickets = static_cast<unsigned*>(ws);
-    p.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + ticket_bytes(num_mb));
-    p.out = out;
+    p.partials = static_cast<double*>(ws);
     const dim3 grid(blocks_per_mb(mb), (unsigned)num_mb), block(256);
     hipStream_t st = rl::as_stream(stream);
     if (A == 12)
         hipLaunchKernelGGL(k_ppo_loss<12>, grid, block, 0, st, p);
     else
         hipLaunchKernelGGL(k_ppo_loss<0>, grid, block, 0, st, p);
-    return rl::check_launch("ppo_loss");
+    if (int rc = rl::check_launch("ppo_loss")) return rc;
+    hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), block, 0, st, static_cast<const double*>(ws),
+                       (int)grid.x, (int64_t)mb, vf_coef, ent_coef, out);
+    return rl::check_launch("ppo_finalize");
 }
 
 }  // extern "C"

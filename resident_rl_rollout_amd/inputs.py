@@ -125,22 +125,32 @@ class PolicyInputs:
     perm: np.ndarray         # int32[B], a seeded shuffle of 0..B-1
 
 
-def make_policy_inputs(seed: int, b: int, a: int = NUM_ACTIONS, delta: float = 0.3) -> PolicyInputs:
+def make_policy_inputs(seed: int, b: int, a: int = NUM_ACTIONS, delta: float = 0.3,
+                       chunk: int = 1 << 20) -> PolicyInputs:
     """Stand-in policy outputs: old logits ~ N(0,1), new = old + U(-delta, delta); the action is sampled
     from the old logits by Gumbel-max and its old log-probability recorded (float64, rounded to f32);
-    new values ~ N(0,1); a seeded permutation for minibatch shuffling."""
+    new values ~ N(0,1); a seeded permutation for minibatch shuffling. Rows are drawn in chunks of
+    `chunk` (old logits, then the perturbation, then the Gumbel noise, per chunk) to bound temporaries."""
     rng = np.random.default_rng(seed)
-    old = rng.standard_normal((b, a), dtype=np.float32)
-    new = (old + rng.uniform(-delta, delta, size=(b, a)).astype(np.float32)).astype(np.float32)
-    gumbel = -np.log(-np.log(rng.random((b, a))))
-    act = np.argmax(old.astype(np.float64) + gumbel, axis=1).astype(np.int32)
-    o64 = old.astype(np.float64)
-    m = o64.max(axis=1, keepdims=True)
-    lse = m[:, 0] + np.log(np.exp(o64 - m).sum(axis=1))
-    old_logp = (o64[np.arange(b), act] - lse).astype(np.float32)
+    new = np.empty((b, a), np.float32)
+    act = np.empty(b, np.int32)
+    old_logp = np.empty(b, np.float32)
+    for lo in range(0, b, chunk):
+        hi = min(b, lo + chunk)
+        rows = hi - lo
+        old = rng.standard_normal((rows, a), dtype=np.float32)
+        pert = rng.random((rows, a), dtype=np.float32) * np.float32(2 * delta) - np.float32(delta)
+        new[lo:hi] = old + pert
+        gumbel = -np.log(-np.log(rng.random((rows, a))))
+        o64 = old.astype(np.float64)
+        k = np.argmax(o64 + gumbel, axis=1)
+        m = o64.max(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(np.exp(o64 - m).sum(axis=1))
+        act[lo:hi] = k
+        old_logp[lo:hi] = o64[np.arange(rows), k] - lse
     new_v = rng.standard_normal(b, dtype=np.float32)
     perm = rng.permutation(b).astype(np.int32)
-    return PolicyInputs(np.ascontiguousarray(new), act, old_logp, new_v, perm)
+    return PolicyInputs(new, act, old_logp, new_v, perm)
 
 
 def make_values(seed: int, t: int, n: int):
