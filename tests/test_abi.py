@@ -93,4 +93,4 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_ppo_loss(*args, 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 8, None) == -3
     need = ctypes.c_size_t()
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
-    assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 256 + 16 * 128
+    assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128
