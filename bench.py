@@ -34,8 +34,9 @@ GAMMA, LAMBDA = 0.99, 0.95
 ENV_STEP_BYTES = 4 + 20 + 8 + 20 + 8 + 4 + 4          # action, slot read, extras r/w, slot write, reward, done
 OBS_TILE_BYTES = 1397 * 4 + 4 * 20 + 8                # observation write + 4 ring slots + extras read
 ENV_BYTES_PER_ENV_STEP = ENV_STEP_BYTES + OBS_TILE_BYTES
-GAE_BYTES_PER_ELEM = 5 * 4 + 2 * 4                    # r, v, d in; adv, ret out; normalise: adv in + out
-LOSS_BYTES_PER_SAMPLE = 12 * 4 + 6 * 4                # logits row; action, old logp, adv, ret, value, perm
+GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
+LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
+                         "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
 
 
 def parse():
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-envs", type=int, default=16384, help="envs in the oracle's bounded sample")
+    p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
+                   help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
 
 
@@ -130,6 +133,7 @@ def main():
     actions.copy_(torch.from_numpy(policy_actions))
     t_ = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     logits, old_logp, new_v, perm = t_(pi.new_logits), t_(pi.old_logp), t_(pi.new_values), t_(pi.perm)
+    mb_index = t_(inputs.minibatch_index(pi.perm, b // MINIBATCHES))
     values_d, last_d = t_(values), t_(last_values)
     adv = torch.empty((HORIZON, N_ENVS), dtype=torch.float32, device=dev)
     ret = torch.empty_like(adv)
@@ -148,12 +152,16 @@ def main():
                 ev["env"][t][1].record()
         if ev is not None:
             ev["gae"][0].record()
-        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=1, adv=adv, ret=ret, adv_stats=stats)
+        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
         if ev is not None:
             ev["gae"][1].record()
             ev["loss"][0].record()
-        binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, perm, mb,
-                         out=loss_out)
+        if args.loss_mode == "stream":
+            binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
+                             adv_stats=stats, out=loss_out, mb_index=mb_index)
+        else:
+            binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, perm, mb,
+                             adv_stats=stats, out=loss_out)
         if ev is not None:
             ev["loss"][1].record()
 
@@ -180,7 +188,7 @@ def main():
     env_avg_s = float(env_ms.mean()) * 1e-3
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
-    loss_bytes = b * LOSS_BYTES_PER_SAMPLE
+    loss_bytes = b * LOSS_BYTES_PER_SAMPLE[args.loss_mode]
     gae_gbs = gae_bytes / (float(gae_ms.mean()) * 1e-3) / 1e9
     loss_gbs = loss_bytes / (float(loss_ms.mean()) * 1e-3) / 1e9
     gl_gbs = (gae_bytes + loss_bytes) / (float((gae_ms + loss_ms).mean()) * 1e-3) / 1e9
@@ -210,7 +218,8 @@ def main():
         "config": {"workload": "full rollout: 65536 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
                                "tile obs (31x43 + 4x15 + 4) into a resident rollout buffer, GAE + whole-batch "
                                "normalisation, PPO loss over 16 shuffled minibatches of 524288",
-                   "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES},
+                   "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES,
+                   "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss"},
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic("env_step+obs_gather"),

@@ -163,22 +163,28 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
 int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
 
 /* PPO loss forward per minibatch ("Teaching Mario to speedrun", s.6 Don't move too far at once; the
- * coefficients of PlayTrain Table 8 are the usual arguments). Minibatch m holds samples
- * i = perm[m*mb + k], k < mb (i = m*mb + k when perm is NULL); for each:
+ * coefficients of PlayTrain Table 8 are the usual arguments). Minibatch m is a set of mb samples given by
+ * one of:
+ *   perm      device int32[B], a permutation of 0..B-1: minibatch m = {perm[m*mb + k], k < mb};
+ *   mb_index  device u16[B]: sample i belongs to minibatch mb_index[i] (each of 0 .. B/mb - 1 taken
+ *             exactly mb times; at most 64 minibatches; values past the last minibatch count as the last);
+ *   neither   minibatch m = samples m*mb .. m*mb + mb - 1.
+ * (perm and mb_index describe the same split when mb_index[perm[p]] = p / mb.) For each sample i:
  *   logp = logits[i][actions[i]] - logsumexp(logits[i]),  ratio = exp(logp - old_logp[i])
  *   pg = -min(ratio * A, clip(ratio, 1 - clip_eps, 1 + clip_eps) * A),  v = (new_values[i] - ret[i])^2,
  *   H = entropy of softmax(logits[i]),  with A = adv[i], or (adv[i] - mean) / (std + 1e-8) from
  *   adv_stats when adv_stats is not NULL.
  *   out  device f32[B/mb][4] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}.
- *   logits device f32[B][A] (16-byte aligned rows need A % 4 == 0; any A in 1..64 is accepted);
- *   actions device int32[B] in [0, A); old_logp, adv, ret, new_values device f32[B]; perm device
- *   int32[B], a permutation of 0..B-1, or NULL.
+ *   logits device f32[B][A], A in 1..64 (16-byte aligned when A % 4 == 0); actions device int32[B] in
+ *   [0, A) (other values read logit 0); old_logp, adv, ret, new_values device f32[B].
  *   B % mb must be 0. ws: device workspace of rl_ppo_loss_workspace_bytes(B, mb) bytes, 8-byte aligned (any
- *   contents); calls sharing it must not overlap. Reductions use float64 partials in a fixed order. */
+ *   contents); calls sharing it must not overlap. The per-sample terms are reduced through float64
+ *   partials in a fixed order (identical results from run to run). With mb_index every input is read
+ *   once, in storage order; with perm every read is a gather. */
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
-                const float* ret, const float* new_values, const int32_t* perm, const double* adv_stats,
-                int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef, float ent_coef,
-                float* out, void* ws, size_t ws_bytes, void* stream);
+                const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                float ent_coef, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* rl_last_error(void);

@@ -51,8 +51,8 @@ SIGNATURES = [
     ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
     ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
     ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
-    ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P, _P,
-                                   _SZ, _P]),
+    ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P,
+                                   _P, _SZ, _P]),
     ("rl_last_error", ctypes.c_char_p, []),
 ]
 
@@ -226,8 +226,10 @@ def ppo_loss_workspace_bytes(b: int, mb: int) -> int:
 
 
 def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2, vf_coef=0.5,
-             ent_coef=0.01, adv_stats=None, out=None, ws=None, stream=None):
-    """rl_ppo_loss; returns out float32[B/minibatch][4] = (pg, value, entropy, total) per minibatch."""
+             ent_coef=0.01, adv_stats=None, out=None, ws=None, stream=None, mb_index=None):
+    """rl_ppo_loss; returns out float32[B/minibatch][4] = (pg, value, entropy, total) per minibatch.
+    Minibatches come from `perm` (int32 gather), or from `mb_index` (uint16 minibatch of each sample,
+    read in storage order), or are contiguous when both are None."""
     b, a = logits.shape
     dev = logits.device
     out = torch.empty((b // minibatch, 4), dtype=torch.float32, device=dev) if out is None else out
@@ -236,7 +238,8 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
     check(lib().rl_ppo_loss(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
                             dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
                             dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),
-                            dptr(perm, torch.int32, "perm"), dptr(adv_stats, torch.float64, "adv_stats"),
+                            dptr(perm, torch.int32, "perm"), dptr(mb_index, torch.uint16, "mb_index"),
+                            dptr(adv_stats, torch.float64, "adv_stats"),
                             b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
                             dptr(out, torch.float32, "out"), dptr(ws), ws.numel(), stream_ptr(stream)))
     return out

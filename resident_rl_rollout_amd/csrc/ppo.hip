@@ -3,10 +3,15 @@
 // recorded old log-probability, the clipped surrogate, the squared value error and the policy entropy;
 // their minibatch means and the weighted total.
 //
-// Grid: (blocks per minibatch, minibatches). Each thread accumulates its samples in float64; a block
-// reduction (shuffles, then LDS) gives per-block partials, and a finalise kernel with one block per
-// minibatch reduces them in block order and writes the four scalars. No floating-point atomics, so
-// results are identical from run to run.
+// Two ways to visit the samples, both ending in per-block float64 partials that a finalise kernel (one
+// block per minibatch) reduces in block order; no floating-point atomics, so results are identical from
+// run to run.
+//   Gather (perm or contiguous): grid (blocks per minibatch, minibatches); thread k of minibatch m reads
+//   sample perm[m*mb + k]. Shuffled indices make every per-sample read a random access.
+//   Stream (mb_index): each minibatch's scalars are means over its set of samples, so one pass over the
+//   batch in storage order serves all minibatches at once: every read is coalesced and each sample is
+//   read exactly once. Each thread adds its samples' terms into its own per-minibatch slots in LDS
+//   (private, so no atomics and a fixed order), and the block then sums the slots thread by thread.
 
 #include <algorithm>
 
@@ -30,7 +35,10 @@ struct LossArgs {
     int64_t mb;
     int A;
     float clip_lo, clip_hi, vf, ent;
-    double* partials;   // [num_mb][bpm][3]
+    double* partials;   // [num_mb][blocks][3]
+    const uint16_t* mb_index;
+    int64_t B;
+    int num_mb;
 };
 
 __device__ __forceinline__ double block_sum(double v, double* lds)
@@ -98,6 +106,25 @@ __device__ __forceinline__ void row_stats(const float* __restrict__ row, int A, 
     }
 }
 
+// The three per-sample terms: clipped surrogate, squared value error, entropy.
+template <int AC>
+__device__ __forceinline__ void sample_terms(const LossArgs& p, int64_t i, float mean, float scale, float* pg,
+                                             float* v, float* h)
+{
+    const int a = p.actions[i];
+    float log_s, mean_u, u_a;
+    row_stats<AC>(p.logits + i * (AC > 0 ? AC : p.A), p.A, a, &log_s, &mean_u, &u_a);
+    const float logp = u_a - log_s;
+    *h = log_s - mean_u;
+    const float ratio = expf(logp - p.old_logp[i]);
+    float adv = p.adv[i];
+    if (p.stats) adv = (adv - mean) * scale;
+    const float clipped = fminf(fmaxf(ratio, p.clip_lo), p.clip_hi);
+    *pg = -fminf(ratio * adv, clipped * adv);
+    const float dv = p.new_v[i] - p.ret[i];
+    *v = dv * dv;
+}
+
 template <int AC>
 __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 {
@@ -113,20 +140,11 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < p.mb; k += step) {
         const int64_t i = p.perm ? (int64_t)p.perm[base + k] : base + k;
-        const int a = p.actions[i];
-        float log_s, mean_u, u_a;
-        row_stats<AC>(p.logits + i * (AC > 0 ? AC : p.A), p.A, a, &log_s, &mean_u, &u_a);
-        const float logp = u_a - log_s;
-        const float entropy = log_s - mean_u;
-        const float ratio = expf(logp - p.old_logp[i]);
-        float adv = p.adv[i];
-        if (p.stats) adv = (adv - mean) * scale;
-        const float clipped = fminf(fmaxf(ratio, p.clip_lo), p.clip_hi);
-        const float pg = -fminf(ratio * adv, clipped * adv);
-        const float dv = p.new_v[i] - p.ret[i];
+        float pg, v, h;
+        sample_terms<AC>(p, i, mean, scale, &pg, &v, &h);
         s_pg += (double)pg;
-        s_v += (double)(dv * dv);
-        s_h += (double)entropy;
+        s_v += (double)v;
+        s_h += (double)h;
     }
     s_pg = block_sum(s_pg, lds);
     s_v = block_sum(s_v, lds + 4);
@@ -136,6 +154,41 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
         part[0] = s_pg;
         part[1] = s_v;
         part[2] = s_h;
+    }
+}
+
+// Stream mode: block b visits samples [b*chunk, min(B, (b+1)*chunk)) in storage order. THREADS * NB * 3
+// floats of LDS hold each thread's private per-minibatch sums (slot (j*3 + s)*THREADS + thread).
+template <int AC, int NB, int THREADS>
+__global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t chunk)
+{
+    __shared__ float acc[NB * 3 * THREADS];
+    const int t = threadIdx.x;
+    for (int j = t; j < NB * 3 * THREADS; j += THREADS) acc[j] = 0.0f;
+    __syncthreads();
+    float mean = 0.0f, scale = 1.0f;
+    if (p.stats) {
+        mean = (float)p.stats[1];
+        scale = (float)(1.0 / (p.stats[2] + kNormEps));
+    }
+    const int64_t lo = (int64_t)blockIdx.x * chunk;
+    const int64_t hi = min(p.B, lo + chunk);
+    for (int64_t i = lo + t; i < hi; i += THREADS) {
+        const int mbi = min((int)p.mb_index[i], NB - 1);
+        float pg, v, h;
+        sample_terms<AC>(p, i, mean, scale, &pg, &v, &h);
+        float* slot = acc + (mbi * 3) * THREADS + t;
+        slot[0] += pg;
+        slot[THREADS] += v;
+        slot[2 * THREADS] += h;
+    }
+    __syncthreads();
+    // thread j < num_mb * 3 sums slot row j over the threads in order
+    for (int j = t; j < p.num_mb * 3; j += THREADS) {
+        const float* row = acc + j * THREADS;
+        double sum = 0.0;
+        for (int u = 0; u < THREADS; ++u) sum += (double)row[u];
+        p.partials[((int64_t)(j / 3) * gridDim.x + blockIdx.x) * 3 + (j % 3)] = sum;
     }
 }
 
@@ -171,6 +224,17 @@ int blocks_per_mb(int64_t mb)
     return (int)std::max<int64_t>(1, std::min<int64_t>((mb + per_block - 1) / per_block, kMaxBlocksPerMb));
 }
 
+constexpr int kStreamMaxMinibatches = 64;
+constexpr int kStreamBlocks = 2048;
+
+// Stream-mode grid: blocks of `chunk` samples, at most kStreamBlocks of them.
+int stream_blocks(int64_t B, int64_t* chunk)
+{
+    const int64_t c = std::max<int64_t>(256, (B + kStreamBlocks - 1) / kStreamBlocks);
+    *chunk = c;
+    return (int)((B + c - 1) / c);
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,12 +245,15 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     if (B % mb != 0) return rl::fail(RL_EINVAL, "B %lld is not a multiple of mb %d", (long long)B, mb);
     if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
     const int64_t num_mb = B / mb;
-    *bytes = sizeof(double) * 3 * (size_t)num_mb * (size_t)blocks_per_mb(mb);
+    int64_t chunk = 0;
+    const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, &chunk) : 0);
+    *bytes = sizeof(double) * 3 * (size_t)num_mb * blocks;
     return RL_OK;
 }
 
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv, const float* ret,
-                const float* new_values, const int32_t* perm, const double* adv_stats, int64_t B, int32_t A,
+                const float* new_values, const int32_t* perm, const uint16_t* mb_index, const double* adv_stats,
+                int64_t B, int32_t A,
                 int32_t mb, float clip_eps, float vf_coef, float ent_coef, float* out, void* ws, size_t ws_bytes,
                 void* stream)
 {
@@ -201,6 +268,11 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
     for (const void* q : ptrs)
         if (!rl::aligned(q, 4)) return rl::fail(RL_EALIGN, "an array is not 4-byte aligned");
     if (perm && !rl::aligned(perm, 4)) return rl::fail(RL_EALIGN, "perm is not 4-byte aligned");
+    if (perm && mb_index) return rl::fail(RL_EINVAL, "pass perm or mb_index, not both");
+    if (mb_index && !rl::aligned(mb_index, 2)) return rl::fail(RL_EALIGN, "mb_index is not 2-byte aligned");
+    if (mb_index && B / mb > kStreamMaxMinibatches)
+        return rl::fail(RL_EINVAL, "mb_index supports at most %d minibatches, got %lld", kStreamMaxMinibatches,
+                        (long long)(B / mb));
     if (A % 4 == 0 && !rl::aligned(logits, 16)) return rl::fail(RL_EALIGN, "logits must be 16-byte aligned when A %% 4 == 0");
     if (!rl::aligned(ws, 8) || (adv_stats && !rl::aligned(adv_stats, 8)))
         return rl::fail(RL_EALIGN, "ws / adv_stats not 8-byte aligned");
@@ -224,15 +296,37 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
     p.vf = vf_coef;
     p.ent = ent_coef;
     p.partials = static_cast<double*>(ws);
-    const dim3 grid(blocks_per_mb(mb), (unsigned)num_mb), block(256);
+    p.mb_index = mb_index;
+    p.B = B;
+    p.num_mb = (int)num_mb;
     hipStream_t st = rl::as_stream(stream);
-    if (A == 12)
-        hipLaunchKernelGGL(k_ppo_loss<12>, grid, block, 0, st, p);
-    else
-        hipLaunchKernelGGL(k_ppo_loss<0>, grid, block, 0, st, p);
+    const dim3 block(256);
+    int nblk;
+    if (mb_index) {
+        int64_t chunk = 0;
+        nblk = stream_blocks(B, &chunk);
+        const dim3 grid(nblk);
+        if (num_mb <= 16) {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256>), grid, dim3(256), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256>), grid, dim3(256), 0, st, p, chunk);
+        } else if (num_mb <= 32) {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128>), grid, dim3(128), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128>), grid, dim3(128), 0, st, p, chunk);
+        } else {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64>), grid, dim3(64), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64>), grid, dim3(64), 0, st, p, chunk);
+        }
+    } else {
+        nblk = blocks_per_mb(mb);
+        const dim3 grid(nblk, (unsigned)num_mb);
+        if (A == 12)
+            hipLaunchKernelGGL(k_ppo_loss<12>, grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL(k_ppo_loss<0>, grid, block, 0, st, p);
+    }
     if (int rc = rl::check_launch("ppo_loss")) return rc;
-    hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), block, 0, st, static_cast<const double*>(ws),
-                       (int)grid.x, (int64_t)mb, vf_coef, ent_coef, out);
+    hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), block, 0, st, static_cast<const double*>(ws), nblk,
+                       (int64_t)mb, vf_coef, ent_coef, out);
     return rl::check_launch("ppo_finalize");
 }
 

@@ -153,6 +153,14 @@ def make_policy_inputs(seed: int, b: int, a: int = NUM_ACTIONS, delta: float = 0
     return PolicyInputs(new, act, old_logp, new_v, perm)
 
 
+def minibatch_index(perm: np.ndarray, mb: int) -> np.ndarray:
+    """The same minibatch split as `perm` (minibatch m = perm[m*mb : (m+1)*mb]) as the minibatch number of
+    every sample, uint16[B]."""
+    idx = np.empty(perm.shape[0], np.uint16)
+    idx[perm] = (np.arange(perm.shape[0]) // mb).astype(np.uint16)
+    return idx
+
+
 def make_values(seed: int, t: int, n: int):
     """Stand-in value head outputs: values f32[T][N] and bootstrap values f32[N], both ~ N(0,1)."""
     rng = np.random.default_rng(seed)

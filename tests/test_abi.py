@@ -84,13 +84,19 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 1, fake, fake, 8, None) == -3
     assert lib.rl_gae(fake, ctypes.c_void_p(4098), fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -2
     # rl_ppo_loss: B % mb, A range, alignment, workspace
-    args = [fake] * 6 + [None, None]
+    args = [fake] * 6 + [None, None, None]
     assert lib.rl_ppo_loss(*args, 100, 12, 30, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
     assert "multiple" in lib.rl_last_error().decode()
     assert lib.rl_ppo_loss(*args, 100, 65, 10, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
     assert lib.rl_ppo_loss(ctypes.c_void_p(4100), *args[1:], 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 1 << 20,
                            None) == -2
     assert lib.rl_ppo_loss(*args, 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 8, None) == -3
+    both = [fake] * 8 + [None]
+    assert lib.rl_ppo_loss(*both, 100, 12, 10, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
+    assert "not both" in lib.rl_last_error().decode()
+    idx = [fake] * 6 + [None, fake, None]
+    assert lib.rl_ppo_loss(*idx, 6500, 12, 100, 0.2, 0.5, 0.01, fake, fake, 1 << 30, None) == -1
+    assert "at most 64" in lib.rl_last_error().decode()
     need = ctypes.c_size_t()
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
     assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128

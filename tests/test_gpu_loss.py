@@ -25,10 +25,11 @@ def _case(seed, b, a=12):
     return pi, adv, ret
 
 
-def _gpu(pi, adv, ret, mb, use_perm=True, stats=None, a=12):
+def _gpu(pi, adv, ret, mb, use_perm=True, stats=None, a=12, stream=False):
+    idx = _dev(inputs.minibatch_index(pi.perm, mb)) if stream else None
     out = binding.ppo_loss(_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret),
-                           _dev(pi.new_values), _dev(pi.perm) if use_perm else None, mb,
-                           adv_stats=None if stats is None else _dev(stats))
+                           _dev(pi.new_values), _dev(pi.perm) if (use_perm and not stream) else None, mb,
+                           adv_stats=None if stats is None else _dev(stats), mb_index=idx)
     return out.cpu().numpy()
 
 
@@ -42,6 +43,29 @@ def test_loss_matches_oracle(b, mb, use_perm, a, gpu_lib):
                                  pi.perm if use_perm else None, mb)
     assert got.shape == ref.shape
     assert_loss_close(got, ref, scale, f"B={b} mb={mb} perm={use_perm} A={a}")
+
+
+@pytest.mark.parametrize("b,mb,a", [(262144, 8192, 12), (30000, 3000, 5), (600, 200, 3), (64000, 1000, 12),
+                                    (40000, 2500, 12), (1, 1, 12), (4096, 4096, 7)])
+def test_stream_mode_matches_oracle(b, mb, a, gpu_lib):
+    # the minibatch split given as each sample's minibatch number, read in storage order
+    pi, adv, ret = _case(b + 7 * mb + a, b, a)
+    got = _gpu(pi, adv, ret, mb, stream=True)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(got, ref, scale, f"stream B={b} mb={mb} A={a}")
+
+
+def test_stream_mode_inline_normalisation_full_batch(gpu_lib):
+    # the bench's configuration: 128 x 65536 samples, 16 minibatches, normalisation applied on the fly
+    b, mb = 128 * 65536, 524288
+    pi, adv, ret = _case(21, b)
+    raw = (adv * 1.7 - 0.4).astype(np.float32)
+    norm, mean, std = oracle.normalize(raw.astype(np.float64))
+    got = _gpu(pi, raw, ret, mb, stats=np.array([b, mean, std]), stream=True)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, norm, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(got, ref, scale, "stream + inline normalisation")
+    got2 = _gpu(pi, raw, ret, mb, stats=np.array([b, mean, std]), stream=True)
+    np.testing.assert_array_equal(got, got2)
 
 
 def test_inline_normalisation_matches_normalised_input(gpu_lib):
