@@ -30,10 +30,10 @@ HBM_PEAK_GBS = 8000.0
 N_ENVS, HORIZON, N_MAPS, MAP_H, MAP_W, MINIBATCHES = 65536, 128, 64, 256, 1024, 16
 GAMMA, LAMBDA = 0.99, 0.95
 
-# Algorithmic HBM bytes per unit (state layout of the env kernels: 5 ring words + 2 extra words per env).
-ENV_STEP_BYTES = 4 + 20 + 8 + 20 + 8 + 4 + 4          # action, slot read, extras r/w, slot write, reward, done
-OBS_TILE_BYTES = 1397 * 4 + 4 * 20 + 8                # observation write + 4 ring slots + extras read
-ENV_BYTES_PER_ENV_STEP = ENV_STEP_BYTES + OBS_TILE_BYTES
+# Algorithmic HBM bytes per unit. The fused tile step per env: the observation row, the action, the
+# current ring slot (5 words) and the two slots before it, the two extra words read and written, the new
+# slot, the reward and the done.
+ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
 GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
                          "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-envs", type=int, default=16384, help="envs in the oracle's bounded sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run one plain 1 GiB device-to-device copy, whose rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                        "scale the counters of the other kernels")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
@@ -142,6 +145,12 @@ def main():
     mb = b // MINIBATCHES
     env.reset(obs[0])
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def rollout(ev=None):
         for t in range(HORIZON):
