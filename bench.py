@@ -7,8 +7,10 @@ with whole-batch advantage normalisation, then the PPO clipped-surrogate / value
 shuffled minibatches of 524288 samples. Policy outputs (actions sampled from seeded old logits, new
 logits, values) are seeded N(0,1) stand-ins, generated before timing and resident in HBM.
 
-Prints one JSON line: env-steps/s of the whole job, the roofline of the env step (the dominant kernels),
-GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: env-steps/s of the whole job, the roofline of the env step (the dominant kernel),
+GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same workload. GAE and loss GB/s come
+from separate repetitions after a read-only cache flush (their own HBM efficiency); their times inside the
+rollout, which also absorb the write-back of the rollout's last observations, are reported beside them.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -46,6 +48,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-envs", type=int, default=16384, help="envs in the oracle's bounded sample")
+    p.add_argument("--iso-reps", type=int, default=7, help="isolated GAE / loss repetitions (median reported)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy, whose rocprofv3 FETCH_SIZE / WRITE_SIZE "
                         "scale the counters of the other kernels")
@@ -187,6 +190,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
+    # GAE and loss alone: before each repetition a 1 GiB read evicts the 256 MB Infinity Cache without
+    # leaving dirty lines behind (a write-based flush, or the rollout's observation writes, leaves up to
+    # 256 MB to be written back during the next kernel).
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush.zero_()
+    iso_gae, iso_loss = [], []
+    for rep in range(args.iso_reps):
+        for which in ("gae", "loss"):
+            flush.sum()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if which == "gae":
+                binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret,
+                            adv_stats=stats)
+            elif args.loss_mode == "stream":
+                binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
+                                 adv_stats=stats, out=loss_out, mb_index=mb_index)
+            else:
+                binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, perm, mb,
+                                 adv_stats=stats, out=loss_out)
+            z.record()
+            torch.cuda.synchronize()
+            (iso_gae if which == "gae" else iso_loss).append(a.elapsed_time(z))
+    del flush
+
     env_ms = np.array([[s.elapsed_time(e) for s, e in ev["env"]] for ev in events])   # [K][T]
     gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
     loss_ms = np.array([ev["loss"][0].elapsed_time(ev["loss"][1]) for ev in events])
@@ -198,9 +226,10 @@ def main():
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
     loss_bytes = b * LOSS_BYTES_PER_SAMPLE[args.loss_mode]
-    gae_gbs = gae_bytes / (float(gae_ms.mean()) * 1e-3) / 1e9
-    loss_gbs = loss_bytes / (float(loss_ms.mean()) * 1e-3) / 1e9
-    gl_gbs = (gae_bytes + loss_bytes) / (float((gae_ms + loss_ms).mean()) * 1e-3) / 1e9
+    gae_s, loss_s = float(np.median(iso_gae)) * 1e-3, float(np.median(iso_loss)) * 1e-3
+    gae_gbs = gae_bytes / gae_s / 1e9
+    loss_gbs = loss_bytes / loss_s / 1e9
+    gl_gbs = (gae_bytes + loss_bytes) / (gae_s + loss_s) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,8 +263,10 @@ def main():
                      "traffic": load_traffic("env_step+obs_gather"),
                      "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
         "env_step_us": float(env_ms.mean()) * 1e3,
-        "gae": {"us": float(gae_ms.mean()) * 1e3, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS},
-        "loss": {"us": float(loss_ms.mean()) * 1e3, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS},
+        "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
+                "us_in_rollout": float(gae_ms.mean()) * 1e3},
+        "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
+                 "us_in_rollout": float(loss_ms.mean()) * 1e3},
         "gae_loss_GB/s": gl_gbs,
         "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
         "loss_check": loss_out[0].tolist(),

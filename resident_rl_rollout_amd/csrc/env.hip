@@ -488,23 +488,30 @@ __global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__
 }
 
 // ------------------------------------------------------------------------------------------------
-// env_step + obs_gather fused, tile mode. A block owns E consecutive envs.
-//   Phase A (threads 0 .. E-1, one env each): the decision, then the env's 64 non-window observation
-//   values (4 frames of 15, newest first, and the 4 checkpoint dims) and the address of its window's
-//   top-left tile go to LDS.
-//   Phase B (all 256 threads): the E observation rows. When rows are packed (stride 1397) and the buffer
-//   is 16-byte aligned, the block's rows form one contiguous region written as aligned float4 stores,
-//   the densest store stream the memory system takes; four window values come from one unaligned dword
-//   of the map row (merged with the next row's first bytes where the four straddle a row end).
-//   Otherwise each wave writes whole rows with dword stores.
+// env_step + obs_gather fused, tile mode. A block of 256 threads owns E consecutive envs.
+//   Phase A (threads 0 .. E-1, one env each): every physics-independent load first (action, current
+//   ring slot, the two older slots, extras), then the decision. The env's 64 non-window observation
+//   values (4 frames of 15, newest first, and 4 checkpoint dims) and its window's top-left address go
+//   to LDS.
+//   Phase B (wave w writes the rows of envs w, w+4, ...): each env's 31-row window is read from the
+//   padded map into registers one env ahead (11 unaligned dwords per row, about 6 per lane) and parked
+//   in a per-wave LDS buffer as 44-byte rows. The row is written with wave-wide 16-byte stores from its
+//   first 16-byte boundary (scalar head and tail elements around them), so any stride works. Four
+//   window values come from two LDS dwords and one byte permute, which also skips the spare 44th byte
+//   when the four straddle a window row; indices advance incrementally. The next env's map loads are
+//   issued before this env's stores, and the store loop itself reads only LDS.
 // ------------------------------------------------------------------------------------------------
 
-constexpr int kTail = kObsTiles - kWinSize;   // 64
+constexpr int kTail = kObsTiles - kWinSize;       // 64
+constexpr int kRowBytes = 44;                     // a window row in LDS: 43 tiles + 1 spare byte
+constexpr int kRowDwords = kRowBytes / 4;         // 11
+constexpr int kWinDwords = kWinH * kRowDwords;    // 341 per env
+constexpr int kWinPerLane = (kWinDwords + 63) / 64;   // 6
 #ifndef RL_STEP_TILES_ENVS
 #define RL_STEP_TILES_ENVS 32
 #endif
 constexpr int kStepTilesEnvs = RL_STEP_TILES_ENVS;   // envs per block of the fused tile kernel
-static_assert(kStepTilesEnvs % 16 == 0 && kStepTilesEnvs <= 256, "a block's rows must start 16-byte aligned");
+static_assert(kStepTilesEnvs >= 1 && kStepTilesEnvs <= 256, "one lane per env in phase A");
 
 __device__ __forceinline__ void put_frame(float* t, int32_t x, int32_t y, int32_t vxy, uint32_t misc, int32_t tick)
 {
@@ -512,27 +519,75 @@ __device__ __forceinline__ void put_frame(float* t, int32_t x, int32_t y, int32_
     for (int dim = 0; dim < kFrameDims; ++dim) t[dim] = frame_dim(dim, x, y, vxy, misc, tick);
 }
 
-// Observation element k (< 1397) of staged env e.
-__device__ __forceinline__ float obs_elem(const EnvDev& d, const int64_t* wbase, const float (*tail)[kTail], int e,
-                                          int k)
+// Observation element k (< 1397) from a staged window and the staged frame / checkpoint values.
+__device__ __forceinline__ float staged_elem(const uint8_t* win, const float* tail, int k)
 {
     if (k < kWinSize) {
-        const int r = k / kWinW, c = k - r * kWinW;
-        return (float)d.map[wbase[e] + (int64_t)r * d.wp + c];
+        const int r = k / kWinW;
+        return (float)win[r * kRowBytes + (k - r * kWinW)];
     }
-    return tail[e][k - kWinSize];
+    return tail[k - kWinSize];
 }
 
-#ifndef RL_STEP_TILES_MIN_WAVES
-#define RL_STEP_TILES_MIN_WAVES 1
-#endif
+// One observation row from a staged window (w32, 31 rows of 44 bytes) and staged tail values, written by
+// one wave.
+__device__ __forceinline__ void write_row(const uint32_t* w32, const float* te, float* row, int lane)
+{
+    const uint8_t* win = reinterpret_cast<const uint8_t*>(w32);
+    const int h = (int)((4 - ((reinterpret_cast<uintptr_t>(row) >> 2) & 3)) & 3);  // scalars before 16 B
+    const int nq = (kObsTiles - h) >> 2;                                           // aligned float4s
+    if (lane < h) row[lane] = staged_elem(win, te, lane);
+    int k = h + 4 * lane;
+    int r = k / kWinW;
+    int c = k - r * kWinW;
+    for (int q = lane; q < nq; q += 64) {
+        float4 o;
+        if (k + 3 < kWinSize) {
+            const int D = r * kRowBytes + c;              // byte of (r, c) in the staged rows
+            const uint32_t lo = w32[D >> 2], hi = w32[(D >> 2) + 1];
+            uint32_t sel = (uint32_t)(D & 3) * 0x01010101u + 0x03020100u;
+            const int avail = kWinW - c;                  // tiles left in row r from column c
+            if (avail < 4) sel += 0x01010101u << (8 * avail);   // skip the spare byte
+            const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel);
+            o.x = (float)(w & 0xffu);
+            o.y = (float)((w >> 8) & 0xffu);
+            o.z = (float)((w >> 16) & 0xffu);
+            o.w = (float)(w >> 24);
+        } else {
+            o.x = staged_elem(win, te, k);
+            o.y = staged_elem(win, te, k + 1);
+            o.z = staged_elem(win, te, k + 2);
+            o.w = staged_elem(win, te, k + 3);
+        }
+        *reinterpret_cast<float4*>(row + k) = o;
+        // k += 256 = 5 rows of 43 plus 41 columns
+        k += 256;
+        r += 5;
+        c += 256 - 5 * kWinW;
+        if (c >= kWinW) { c -= kWinW; r += 1; }
+    }
+    const int t0 = h + 4 * nq;
+    if (lane < kObsTiles - t0) row[t0 + lane] = staged_elem(win, te, t0 + lane);
+}
 
-template <int E, bool FLAT>
-__global__ __launch_bounds__(256, RL_STEP_TILES_MIN_WAVES) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+// This lane's share of an env's window: dwords lane, lane + 64, ... of its 31 rows of 11.
+__device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int lane, uint32_t (&v)[kWinPerLane])
+{
+#pragma unroll
+    for (int j = 0; j < kWinPerLane; ++j) {
+        const int i = min(lane + 64 * j, kWinDwords - 1);
+        const int r = i / kRowDwords, c4 = i - r * kRowDwords;
+        __builtin_memcpy(&v[j], d.map + base + (int64_t)r * d.wp + 4 * c4, 4);
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
                                                     int head_new)
 {
+    __shared__ uint32_t wwin[4][kWinDwords + 1];
     __shared__ float tail[E][kTail];
     __shared__ int64_t wbase[E];
     const int n0 = blockIdx.x * E;
@@ -542,8 +597,6 @@ __global__ __launch_bounds__(256, RL_STEP_TILES_MIN_WAVES) void k_step_tiles(Env
         const int e = threadIdx.x;
         const int n = n0 + e;
         const int m = n % d.m;
-        // Every load that does not depend on the physics is issued first: the action, the current slot
-        // (frame 1 of the new stack), the two slots before it (frames 2 and 3) and the extras.
         const int32_t a = actions[n];
         const SlotWords cur = load_slot(d, head_prev, n);
         const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
@@ -579,53 +632,22 @@ __global__ __launch_bounds__(256, RL_STEP_TILES_MIN_WAVES) void k_step_tiles(Env
     }
     __syncthreads();
 
-    if constexpr (FLAT) {
-        const int total = ne * kObsTiles;
-        float* base = obs + (int64_t)n0 * kObsTiles;
-        const int nq = total >> 2;
-        for (int q = threadIdx.x; q < nq; q += 256) {
-            const int f = q << 2;
-            const int e = f / kObsTiles;
-            const int k = f - e * kObsTiles;
-            float4 v;
-            if (k + 3 < kWinSize) {
-                const int r = k / kWinW, c = k - r * kWinW;
-                const uint8_t* p = d.map + wbase[e] + (int64_t)r * d.wp + c;
-                uint32_t w;
-                __builtin_memcpy(&w, p, 4);
-                const int avail = kWinW - c;      // bytes of row r from column c on
-                if (avail < 4) {
-                    uint32_t w1;                   // row r+1, starting 'avail' bytes before its column 0
-                    __builtin_memcpy(&w1, p + d.wp - kWinW, 4);
-                    const uint32_t keep = (1u << (8 * min(avail, 3))) - 1u;
-                    w = (w & keep) | (w1 & ~keep);
-                }
-                v.x = (float)(w & 0xffu);
-                v.y = (float)((w >> 8) & 0xffu);
-                v.z = (float)((w >> 16) & 0xffu);
-                v.w = (float)(w >> 24);
-            } else {
-                float vv[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t* w32 = wwin[wave];
+    uint32_t v[kWinPerLane];
+    if (wave < ne) load_window(d, wbase[wave], lane, v);
+    for (int e = wave; e < ne; e += 4) {
+        // park this env's window in the wave's buffer; the wave's reads of the previous env are done
+        // (their results fed its stores)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    int kk = k + j, ee = e;
-                    if (kk >= kObsTiles) { kk -= kObsTiles; ee += 1; }
-                    vv[j] = obs_elem(d, wbase, tail, ee, kk);
-                }
-                v = make_float4(vv[0], vv[1], vv[2], vv[3]);
-            }
-            reinterpret_cast<float4*>(base)[q] = v;
-        }
-        for (int f = (nq << 2) + threadIdx.x; f < total; f += 256) {
-            const int e = f / kObsTiles;
-            base[f] = obs_elem(d, wbase, tail, e, f - e * kObsTiles);
-        }
-    } else {
-        const int lane = threadIdx.x & 63;
-        for (int e = threadIdx.x >> 6; e < ne; e += 4) {
-            float* o = obs + (int64_t)(n0 + e) * stride;
-            for (int k = lane; k < kObsTiles; k += 64) o[k] = obs_elem(d, wbase, tail, e, k);
-        }
+        for (int j = 0; j < kWinPerLane; ++j)
+            if (lane + 64 * j < kWinDwords) w32[lane + 64 * j] = v[j];
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes have landed
+        __builtin_amdgcn_wave_barrier();
+        if (e + 4 < ne) load_window(d, wbase[e + 4], lane, v);
+        write_row(w32, tail[e], obs + (int64_t)(n0 + e) * stride, lane);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -870,14 +892,9 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
     const EnvDev d = dev_of(e);
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
-        float* o = static_cast<float*>(obs);
         const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs);
-        if (e->cfg.obs_stride == kObsTiles && rl::aligned(obs, 16))
-            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, true>), grid, dim3(256), 0, st, d, actions, rewards,
-                               dones, o, e->cfg.obs_stride, head_prev, head_new);
-        else
-            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, false>), grid, dim3(256), 0, st, d, actions, rewards,
-                               dones, o, e->cfg.obs_stride, head_prev, head_new);
+        hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs>), grid, dim3(256), 0, st, d, actions, rewards, dones,
+                           static_cast<float*>(obs), e->cfg.obs_stride, head_prev, head_new);
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
         e->counter += 1;
         return RL_OK;
