@@ -653,15 +653,23 @@ __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __r
 
 // ------------------------------------------------------------------------------------------------
 // obs_gather, pixel mode: one block per env, one wave per stacked frame. Each frame is re-rendered from
-// the position kept in its ring slot (recomputing 7 KB from the L2-resident map is cheaper than storing
-// and re-reading it). Four pixels are packed per dword store.
+// the position kept in its ring slot (recomputing 7 KB from the cached map is cheaper than storing and
+// re-reading it). The wave first stages the frame's camera tiles (at most 12 x 12; 12 rows of 16
+// bytes) in LDS beside the block's sprite table. Lanes then own (row offset, pixel dword) pairs, 3 rows
+// of 21 dwords per pass, so a lane's tile column, sub-tile shift and player-box column mask are fixed
+// for the whole frame. A pixel dword (4 pixels of one row) takes two tile codes and their two 8-pixel
+// sprite rows from LDS and one byte-align; the player box is OR-ed in as a byte mask. Each pass stores
+// 3 consecutive rows (252 bytes) per wave.
 // ------------------------------------------------------------------------------------------------
+
+constexpr int kCamTiles = 12;      // tile rows / columns a camera row / column can touch (84 px span 11-12)
+constexpr int kCamTileStride = 16; // bytes per staged tile row
 
 __global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restrict__ obs, int64_t stride, int head)
 {
-    __shared__ uint8_t spr[16 * 64];
+    __shared__ uint2 spr[16 * 8];                                  // sprite rows, 8 pixels each
+    __shared__ uint32_t cam[4][kCamTiles * kCamTileStride / 4];    // each frame's camera tiles
     reinterpret_cast<uint32_t*>(spr)[threadIdx.x] = reinterpret_cast<const uint32_t*>(d.sprites)[threadIdx.x];
-    __syncthreads();
     const int n = blockIdx.x;
     const int f = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -671,31 +679,41 @@ __global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restric
     const int32_t y = clampi(slot_word(d, s, 1, n), 0, d.h * kTile - 1);
     const int cam_x = ((x + kHalfBox) >> 5) - kPix / 2;
     const int cam_y = ((y + kHalfBox) >> 5) - kPix / 2;
+    const int tx0 = cam_x >> 3, ty0 = cam_y >> 3;
     const int bx0 = x >> 5, bx1 = (x + kBox - 1) >> 5;
     const int by0 = y >> 5, by1 = (y + kBox - 1) >> 5;
+    // stage tiles: lane < 48 copies 4 bytes of staged row lane / 4 (unaligned map read, in the border)
+    if (lane < kCamTiles * kCamTileStride / 4) {
+        const int r = lane >> 2, c4 = lane & 3;
+        uint32_t w;
+        __builtin_memcpy(&w, tile_ptr(d, m, ty0 + r, tx0 + 4 * c4), 4);
+        cam[f][lane] = w;
+    }
+    __syncthreads();
+    const uint8_t* tiles = reinterpret_cast<const uint8_t*>(cam[f]);
     uint32_t* o = reinterpret_cast<uint32_t*>(obs + (int64_t)n * stride + (int64_t)f * kPixFrame);
 
-    int py = lane / kPixRowDwords;
-    int qc = lane - py * kPixRowDwords;
-    for (int q = lane; q < kPixFrameDwords; q += 64) {
+    // lane -> (row offset rl in 0..2, dword jl in 0..20 of the row); lane 63 idles. Everything that
+    // depends only on the column is fixed for the frame.
+    const int rl = lane / kPixRowDwords, jl = lane - rl * kPixRowDwords;
+    if (lane >= 3 * kPixRowDwords) return;
+    const int wx = cam_x + 4 * jl;
+    const int tc = (wx >> 3) - tx0;                  // 0 .. 10
+    const int ofs = wx & 7;                          // first pixel's column inside tile tc
+    const bool upper = ofs >= 4;
+    const uint32_t shift = (uint32_t)(ofs & 3);
+    const int lo_b = max(bx0 - wx, 0), hi_b = min(bx1 - wx, 3);
+    const uint32_t boxmask =
+        lo_b <= hi_b ? (0xffffffffu >> (8 * (3 - hi_b))) & (0xffffffffu << (8 * lo_b)) : 0u;
+    for (int py = rl; py < kPix; py += 3) {
         const int wy = cam_y + py;
-        const uint8_t* row = tile_ptr(d, m, wy >> 3, 0);
-        const int sy = (wy & 7) << 3;
-        const bool in_by = wy >= by0 && wy <= by1;
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int wx = cam_x + qc * 4 + j;
-            const uint32_t t = row[wx >> 3];
-            uint32_t v = spr[((t & 15u) << 6) | sy | (wx & 7)];
-            if (in_by && wx >= bx0 && wx <= bx1) v = 255u;
-            word |= v << (8 * j);
-        }
-        o[q] = word;
-        // q += 64 = 3 rows of 21 dwords + 1
-        py += 3;
-        qc += 1;
-        if (qc >= kPixRowDwords) { qc -= kPixRowDwords; py += 1; }
+        const int sy = wy & 7;
+        const uint8_t* trow = tiles + ((wy >> 3) - ty0) * kCamTileStride + tc;
+        const uint2 a = spr[(trow[0] & 15u) * 8 + sy];
+        const uint2 b = spr[(trow[1] & 15u) * 8 + sy];
+        uint32_t w = __builtin_amdgcn_alignbyte(upper ? b.x : a.y, upper ? a.y : a.x, shift);
+        if (wy >= by0 && wy <= by1) w |= boxmask;
+        o[py * kPixRowDwords + jl] = w;
     }
 }
 

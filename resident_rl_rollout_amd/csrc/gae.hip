@@ -143,96 +143,6 @@ __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__
     if (want_stats) publish_stats(s1, s2, so);
 }
 
-// Float4 variant for N % 4 == 0: thread (q, ch) owns the 4 adjacent envs 4(blockIdx.x*Q + q) .. +3 and
-// steps [ch*L, min(T, ch*L + L)). Every load and store moves 16 bytes, so one wave instruction covers a
-// 1 KB row segment, and a wave touches only L rows of each array.
-template <int Q, int L, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_gae_quad(const float* __restrict__ rew, const float* __restrict__ val,
-                                                     const float* __restrict__ done, const float* __restrict__ vlast,
-                                                     int T, int N, float gamma, float gl, float* __restrict__ adv,
-                                                     float* __restrict__ ret, int want_stats, StatsOut so)
-{
-    constexpr int C = BLOCK / Q;
-    __shared__ float sb[C][4 * Q];
-    __shared__ float sc[C][4 * Q];
-    const int q = threadIdx.x % Q;
-    const int ch = threadIdx.x / Q;
-    const int n4 = blockIdx.x * Q + q;           // index of this thread's env quad
-    const int nq = N >> 2;
-    const bool valid = n4 < nq;
-    const int t0 = ch * L;
-    const int len = valid ? max(0, min(L, T - t0)) : 0;
-    const int nn = min(n4, nq - 1);
-    const float4* r4 = reinterpret_cast<const float4*>(rew);
-    const float4* v4 = reinterpret_cast<const float4*>(val);
-    const float4* d4 = reinterpret_cast<const float4*>(done);
-
-    float delta[L][4], cf[L][4], vv[L][4];
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        const int64_t idx = (int64_t)min(t0 + j, T - 1) * nq + nn;
-        const float4 a = v4[idx], b = r4[idx], c = d4[idx];
-        vv[j][0] = a.x; vv[j][1] = a.y; vv[j][2] = a.z; vv[j][3] = a.w;
-        delta[j][0] = b.x; delta[j][1] = b.y; delta[j][2] = b.z; delta[j][3] = b.w;
-        cf[j][0] = 1.0f - c.x; cf[j][1] = 1.0f - c.y; cf[j][2] = 1.0f - c.z; cf[j][3] = 1.0f - c.w;
-    }
-    const float4 va = v4[(int64_t)min(t0 + len, T - 1) * nq + nn];
-    const float4 vl = reinterpret_cast<const float4*>(vlast)[nn];
-    const bool tail_in_t = t0 + len < T;
-    float vnt[4] = {tail_in_t ? va.x : vl.x, tail_in_t ? va.y : vl.y, tail_in_t ? va.z : vl.z,
-                    tail_in_t ? va.w : vl.w};
-
-    float b[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-#pragma unroll
-    for (int j = L - 1; j >= 0; --j) {
-        if (j < len) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float vn = (j + 1 < len) ? vv[j + 1 < L ? j + 1 : j][u] : vnt[u];
-                const float notdone = cf[j][u];
-                delta[j][u] = delta[j][u] + gamma * vn * notdone - vv[j][u];
-                cf[j][u] = gl * notdone;
-                b[u] = delta[j][u] + cf[j][u] * b[u];
-                c[u] = cf[j][u] * c[u];
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        sb[ch][4 * q + u] = b[u];
-        sc[ch][4 * q + u] = c[u];
-    }
-    __syncthreads();
-
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = C - 1; k > ch; --k)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = sb[k][4 * q + u] + sc[k][4 * q + u] * a[u];
-
-    double s1 = 0.0, s2 = 0.0;
-    float4* adv4 = reinterpret_cast<float4*>(adv);
-    float4* ret4 = reinterpret_cast<float4*>(ret);
-#pragma unroll
-    for (int j = L - 1; j >= 0; --j) {
-        if (j < len) {
-            float4 o, p;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = delta[j][u] + cf[j][u] * a[u];
-            o = make_float4(a[0], a[1], a[2], a[3]);
-            p = make_float4(a[0] + vv[j][0], a[1] + vv[j][1], a[2] + vv[j][2], a[3] + vv[j][3]);
-            const int64_t idx = (int64_t)(t0 + j) * nq + n4;
-            adv4[idx] = o;
-            ret4[idx] = p;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                s1 += (double)a[u];
-                s2 += (double)a[u] * (double)a[u];
-            }
-        }
-    }
-    if (want_stats) publish_stats(s1, s2, so);
-}
-
 // One lane per env walking t = T-1 .. 0: the fallback for horizons longer than the chunked kernels hold.
 __global__ __launch_bounds__(256) void k_gae_seq(const float* __restrict__ rew, const float* __restrict__ val,
                                                  const float* __restrict__ done, const float* __restrict__ vlast,
@@ -278,18 +188,15 @@ __global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int6
         adv[i] = (adv[i] - mean) * scale;
 }
 
-enum class GaeKernel { C64x4_32, C32x8_16, C16x16_8, C16x16_32, C16x16_64, C256x4_32, C128x8_16, C64x16_8, Q64x16_8, Q32x16_8, Q64x8_16, Seq };
+enum class GaeKernel { C32x8_16, C16x16_8, C16x16_32, C16x16_64, C256x4_32, Seq };
 
-#ifndef RL_GAE_FORCE
-#define RL_GAE_FORCE -1
-#endif
-
+// Shapes by horizon and batch width. Wide batches take 256 envs x 4 chunks (1 KB row segments per block;
+// measured fastest at 65536 x 128 against 64 x 4, 32 x 8, 128 x 8, 64 x 16 and float4 variants); narrow
+// batches trade row width for more chunks so that enough lanes are busy.
 GaeKernel pick(int T, int N)
 {
-    if (RL_GAE_FORCE >= 0 && T <= 128) return (GaeKernel)RL_GAE_FORCE;
     if (T <= 128 && (N + 255) / 256 >= 128) return GaeKernel::C256x4_32;
     if (T <= 128) {
-        if ((N + 63) / 64 >= 512) return GaeKernel::C64x4_32;
         if ((N + 31) / 32 >= 512) return GaeKernel::C32x8_16;
         return GaeKernel::C16x16_8;
     }
@@ -301,14 +208,8 @@ GaeKernel pick(int T, int N)
 int blocks_of(GaeKernel k, int N)
 {
     switch (k) {
-    case GaeKernel::C64x4_32: return (N + 63) / 64;
     case GaeKernel::C32x8_16: return (N + 31) / 32;
     case GaeKernel::C256x4_32: return (N + 255) / 256;
-    case GaeKernel::C128x8_16: return (N + 127) / 128;
-    case GaeKernel::C64x16_8: return (N + 63) / 64;
-    case GaeKernel::Q64x16_8: return (N / 4 + 63) / 64;
-    case GaeKernel::Q32x16_8: return (N / 4 + 31) / 32;
-    case GaeKernel::Q64x8_16: return (N / 4 + 63) / 64;
     case GaeKernel::Seq: return (N + 255) / 256;
     default: return (N + 15) / 16;
     }
@@ -354,10 +255,6 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     const GaeKernel k = pick(T, N);
     const dim3 grid(blocks_of(k, N)), block(256);
     switch (k) {
-    case GaeKernel::C64x4_32:
-        hipLaunchKernelGGL((k_gae_chunked<64, 32, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
-                           (T + 3) / 4, gamma, gl, adv, ret, want, so);
-        break;
     case GaeKernel::C32x8_16:
         hipLaunchKernelGGL((k_gae_chunked<32, 16, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
                            (T + 7) / 8, gamma, gl, adv, ret, want, so);
@@ -377,26 +274,6 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     case GaeKernel::C256x4_32:
         hipLaunchKernelGGL((k_gae_chunked<256, 32, 1024>), grid, dim3(1024), 0, st, rewards, values, dones,
                            last_values, T, N, (T + 3) / 4, gamma, gl, adv, ret, want, so);
-        break;
-    case GaeKernel::C128x8_16:
-        hipLaunchKernelGGL((k_gae_chunked<128, 16, 1024>), grid, dim3(1024), 0, st, rewards, values, dones,
-                           last_values, T, N, (T + 7) / 8, gamma, gl, adv, ret, want, so);
-        break;
-    case GaeKernel::C64x16_8:
-        hipLaunchKernelGGL((k_gae_chunked<64, 8, 1024>), grid, dim3(1024), 0, st, rewards, values, dones,
-                           last_values, T, N, (T + 15) / 16, gamma, gl, adv, ret, want, so);
-        break;
-    case GaeKernel::Q64x16_8:
-        hipLaunchKernelGGL((k_gae_quad<64, 8, 1024>), grid, dim3(1024), 0, st, rewards, values, dones, last_values,
-                           T, N, gamma, gl, adv, ret, want, so);
-        break;
-    case GaeKernel::Q32x16_8:
-        hipLaunchKernelGGL((k_gae_quad<32, 8, 512>), grid, dim3(512), 0, st, rewards, values, dones, last_values,
-                           T, N, gamma, gl, adv, ret, want, so);
-        break;
-    case GaeKernel::Q64x8_16:
-        hipLaunchKernelGGL((k_gae_quad<64, 16, 512>), grid, dim3(512), 0, st, rewards, values, dones, last_values,
-                           T, N, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::Seq:
         hipLaunchKernelGGL(k_gae_seq, grid, block, 0, st, rewards, values, dones, last_values, T, N, gamma, gl, adv,

@@ -33,7 +33,7 @@ def _oracle(gi, cols=None):
 
 
 @pytest.mark.parametrize("t,n", [(128, 2048), (128, 64), (1, 1), (37, 1000), (128, 70000), (300, 513),
-                                 (700, 100), (1500, 33), (129, 4096)])
+                                 (700, 100), (1500, 33), (129, 4096), (128, 20000)])
 def test_gae_matches_oracle(t, n, gpu_lib):
     gi = inputs.make_gae_inputs(10 + t + n, t, n)
     adv, ret, _ = _run(gi, 0)
