@@ -264,9 +264,10 @@ def main():
                      "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
         "env_step_us": float(env_ms.mean()) * 1e3,
         "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
-                "us_in_rollout": float(gae_ms.mean()) * 1e3},
+                "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_traffic": load_traffic("gae_scan")},
         "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
-                 "us_in_rollout": float(loss_ms.mean()) * 1e3},
+                 "us_in_rollout": float(loss_ms.mean()) * 1e3,
+                 "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
         "gae_loss_GB/s": gl_gbs,
         "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
         "loss_check": loss_out[0].tolist(),

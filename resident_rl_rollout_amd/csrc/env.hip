@@ -48,7 +48,6 @@ constexpr int kFrameDims = 15;
 constexpr int kObsTiles = kWinSize + kStack * kFrameDims + 4;  // 1397
 constexpr int kPix = 84;
 constexpr int kPixFrame = kPix * kPix;                         // 7056
-constexpr int kPixFrameDwords = kPixFrame / 4;                 // 1764
 constexpr int kPixRowDwords = kPix / 4;                        // 21
 
 constexpr int kPadX = 32;
@@ -418,8 +417,9 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
                     next, best_x, false};
 }
 
-// env_step alone (the pixel path renders in its own kernel): one lane per env.
-__global__ __launch_bounds__(256) void k_step(EnvDev d, const int32_t* __restrict__ actions,
+// env_step alone (the pixel path renders in its own kernel): one lane per env, one-wave blocks so that a
+// small batch still spreads over every CU (the kernel is latency-bound: a few waves per CU at most).
+__global__ __launch_bounds__(64) void k_step(EnvDev d, const int32_t* __restrict__ actions,
                                               float* __restrict__ rewards, float* __restrict__ dones,
                                               int head_prev, int head_new)
 {
@@ -493,13 +493,13 @@ __global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__
 //   ring slot, the two older slots, extras), then the decision. The env's 64 non-window observation
 //   values (4 frames of 15, newest first, and 4 checkpoint dims) and its window's top-left address go
 //   to LDS.
-//   Phase B (wave w writes the rows of envs w, w+4, ...): each env's 31-row window is read from the
-//   padded map into registers one env ahead (11 unaligned dwords per row, about 6 per lane) and parked
-//   in a per-wave LDS buffer as 44-byte rows. The row is written with wave-wide 16-byte stores from its
-//   first 16-byte boundary (scalar head and tail elements around them), so any stride works. Four
-//   window values come from two LDS dwords and one byte permute, which also skips the spare 44th byte
-//   when the four straddle a window row; indices advance incrementally. The next env's map loads are
-//   issued before this env's stores, and the store loop itself reads only LDS.
+//   Phase B (wave w writes the rows of envs w, w+4, ...): the wave first reads every one of its envs'
+//   31-row windows from the padded map (11 unaligned dwords per row, about 6 per lane and env) and parks
+//   them in LDS as 44-byte rows; only then does it store. Loads and stores share one in-order completion
+//   counter, so a load issued after a store could only be waited for together with that store. Each row
+//   is written with wave-wide 16-byte stores from its first 16-byte boundary (scalar head and tail
+//   elements around them), so any stride works. Four window values come from two LDS dwords and one
+//   byte permute, which also skips the spare 44th byte when the four straddle a window row.
 // ------------------------------------------------------------------------------------------------
 
 constexpr int kTail = kObsTiles - kWinSize;       // 64
@@ -507,11 +507,7 @@ constexpr int kRowBytes = 44;                     // a window row in LDS: 43 til
 constexpr int kRowDwords = kRowBytes / 4;         // 11
 constexpr int kWinDwords = kWinH * kRowDwords;    // 341 per env
 constexpr int kWinPerLane = (kWinDwords + 63) / 64;   // 6
-#ifndef RL_STEP_TILES_ENVS
-#define RL_STEP_TILES_ENVS 32
-#endif
-constexpr int kStepTilesEnvs = RL_STEP_TILES_ENVS;   // envs per block of the fused tile kernel
-static_assert(kStepTilesEnvs >= 1 && kStepTilesEnvs <= 256, "one lane per env in phase A");
+constexpr int kStepTilesEnvs = 16;                // envs per block of the fused tile kernel
 
 __device__ __forceinline__ void put_frame(float* t, int32_t x, int32_t y, int32_t vxy, uint32_t misc, int32_t tick)
 {
@@ -530,41 +526,44 @@ __device__ __forceinline__ float staged_elem(const uint8_t* win, const float* ta
 }
 
 // One observation row from a staged window (w32, 31 rows of 44 bytes) and staged tail values, written by
-// one wave.
+// one wave. The float4s that lie wholly in the window take six fixed passes whose LDS reads are all
+// issued before the first store; the few that reach into the tail follow in one pass.
 __device__ __forceinline__ void write_row(const uint32_t* w32, const float* te, float* row, int lane)
 {
     const uint8_t* win = reinterpret_cast<const uint8_t*>(w32);
     const int h = (int)((4 - ((reinterpret_cast<uintptr_t>(row) >> 2) & 3)) & 3);  // scalars before 16 B
     const int nq = (kObsTiles - h) >> 2;                                           // aligned float4s
+    const int nwin = (kWinSize - h) >> 2;                                          // ... inside the window
+    constexpr int kPasses = (kWinSize / 4 + 63) / 64;                              // 6
     if (lane < h) row[lane] = staged_elem(win, te, lane);
-    int k = h + 4 * lane;
-    int r = k / kWinW;
-    int c = k - r * kWinW;
-    for (int q = lane; q < nq; q += 64) {
-        float4 o;
-        if (k + 3 < kWinSize) {
-            const int D = r * kRowBytes + c;              // byte of (r, c) in the staged rows
-            const uint32_t lo = w32[D >> 2], hi = w32[(D >> 2) + 1];
-            uint32_t sel = (uint32_t)(D & 3) * 0x01010101u + 0x03020100u;
-            const int avail = kWinW - c;                  // tiles left in row r from column c
-            if (avail < 4) sel += 0x01010101u << (8 * avail);   // skip the spare byte
-            const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel);
-            o.x = (float)(w & 0xffu);
-            o.y = (float)((w >> 8) & 0xffu);
-            o.z = (float)((w >> 16) & 0xffu);
-            o.w = (float)(w >> 24);
-        } else {
-            o.x = staged_elem(win, te, k);
-            o.y = staged_elem(win, te, k + 1);
-            o.z = staged_elem(win, te, k + 2);
-            o.w = staged_elem(win, te, k + 3);
+    uint32_t w[kPasses];
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+        const int k = h + 4 * min(lane + 64 * j, nwin - 1);
+        const int r = k / kWinW;
+        const int c = k - r * kWinW;
+        const int D = k + r;                                  // byte of (r, c) in the staged rows
+        uint32_t sel = (uint32_t)(D & 3) * 0x01010101u + 0x03020100u;
+        const int avail = kWinW - c;
+        if (avail < 4) sel += 0x01010101u << (8 * avail);    // skip the spare byte
+        w[j] = __builtin_amdgcn_perm(w32[(D >> 2) + 1], w32[D >> 2], sel);
+    }
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+        const int q = lane + 64 * j;
+        if (q < nwin) {
+            float4 o;
+            o.x = (float)(w[j] & 0xffu);
+            o.y = (float)((w[j] >> 8) & 0xffu);
+            o.z = (float)((w[j] >> 16) & 0xffu);
+            o.w = (float)(w[j] >> 24);
+            *reinterpret_cast<float4*>(row + h + 4 * q) = o;
         }
-        *reinterpret_cast<float4*>(row + k) = o;
-        // k += 256 = 5 rows of 43 plus 41 columns
-        k += 256;
-        r += 5;
-        c += 256 - 5 * kWinW;
-        if (c >= kWinW) { c -= kWinW; r += 1; }
+    }
+    if (nwin + lane < nq) {
+        const int k = h + 4 * (nwin + lane);
+        *reinterpret_cast<float4*>(row + k) = make_float4(staged_elem(win, te, k), staged_elem(win, te, k + 1),
+                                                          staged_elem(win, te, k + 2), staged_elem(win, te, k + 3));
     }
     const int t0 = h + 4 * nq;
     if (lane < kObsTiles - t0) row[t0 + lane] = staged_elem(win, te, t0 + lane);
@@ -587,7 +586,8 @@ __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __r
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
                                                     int head_new)
 {
-    __shared__ uint32_t wwin[4][kWinDwords + 1];
+    static_assert(E % 4 == 0 && E <= 64, "whole envs per wave; one lane per env in phase A");
+    __shared__ uint32_t wwin[E][kWinDwords + 1];
     __shared__ float tail[E][kTail];
     __shared__ int64_t wbase[E];
     const int n0 = blockIdx.x * E;
@@ -634,21 +634,26 @@ __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __r
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint32_t* w32 = wwin[wave];
-    uint32_t v[kWinPerLane];
-    if (wave < ne) load_window(d, wbase[wave], lane, v);
-    for (int e = wave; e < ne; e += 4) {
-        // park this env's window in the wave's buffer; the wave's reads of the previous env are done
-        // (their results fed its stores)
+    constexpr int EW = E / 4;                 // envs per wave
+    constexpr int EB = EW <= 6 ? EW : 4;      // windows in registers at once
+    static_assert(EW % EB == 0, "whole batches");
+#pragma unroll 1
+    for (int b = 0; b < EW; b += EB) {
+        uint32_t v[EB][kWinPerLane];
 #pragma unroll
-        for (int j = 0; j < kWinPerLane; ++j)
-            if (lane + 64 * j < kWinDwords) w32[lane + 64 * j] = v[j];
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes have landed
-        __builtin_amdgcn_wave_barrier();
-        if (e + 4 < ne) load_window(d, wbase[e + 4], lane, v);
-        write_row(w32, tail[e], obs + (int64_t)(n0 + e) * stride, lane);
-        __builtin_amdgcn_wave_barrier();
+        for (int i = 0; i < EB; ++i)
+            if (wave + 4 * (b + i) < ne) load_window(d, wbase[wave + 4 * (b + i)], lane, v[i]);
+#pragma unroll
+        for (int i = 0; i < EB; ++i)
+            if (wave + 4 * (b + i) < ne) {
+#pragma unroll
+                for (int j = 0; j < kWinPerLane; ++j)
+                    if (lane + 64 * j < kWinDwords) wwin[wave + 4 * (b + i)][lane + 64 * j] = v[i][j];
+            }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    for (int e = wave; e < ne; e += 4) write_row(wwin[e], tail[e], obs + (int64_t)(n0 + e) * stride, lane);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -917,7 +922,7 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
         e->counter += 1;
         return RL_OK;
     }
-    hipLaunchKernelGGL(k_step, dim3((d.n + 255) / 256), dim3(256), 0, st, d, actions, rewards, dones, head_prev,
+    hipLaunchKernelGGL(k_step, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
                        head_new);
     if (int rc = rl::check_launch("env_step")) return rc;
     e->counter += 1;
