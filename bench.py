@@ -12,7 +12,7 @@ GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same worklo
 from separate repetitions after a read-only cache flush (their own HBM efficiency); their times inside the
 rollout, which also absorb the write-back of the rollout's last observations, are reported beside them.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload rollout|pixels]
 """
 from __future__ import annotations
 
@@ -36,6 +36,11 @@ GAMMA, LAMBDA = 0.99, 0.95
 # current ring slot (5 words) and the two slots before it, the two extra words read and written, the new
 # slot, the reward and the done.
 ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
+# The pixel step per env (two kernels): the physics reads the action, the current slot and the extras and
+# writes the new slot, the extras, the reward and the done; the render reads (x, y) of the four stacked
+# slots and writes the 4 x 84 x 84 frame bytes.
+PIX_ENVS = 16384
+PIX_BYTES_PER_ENV_STEP = 4 * 84 * 84 + (4 + 20 + 8) + (20 + 8 + 4 + 4) + 4 * 8   # 28324
 GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
                          "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
@@ -47,11 +52,15 @@ def parse():
     p.add_argument("--steps", type=int, default=10, help="timed rollouts")
     p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-envs", type=int, default=16384, help="envs in the oracle's bounded sample")
+    p.add_argument("--cpu-envs", type=int, default=None,
+                   help="envs in the oracle's bounded sample (default 16384 for the rollout, 512 for pixels)")
     p.add_argument("--iso-reps", type=int, default=7, help="isolated GAE / loss repetitions (median reported)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy, whose rocprofv3 FETCH_SIZE / WRITE_SIZE "
                         "scale the counters of the other kernels")
+    p.add_argument("--workload", choices=("rollout", "pixels"), default="rollout",
+                   help="rollout: the tile-observation full rollout (the default bench line); pixels: 16384 envs "
+                        "x 128 steps rendering 4 x 84 x 84 u8 frames, then GAE")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
@@ -105,11 +114,143 @@ def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
     return b / dt, dt
 
 
+def calibration_copy(torch, dev):
+    """One plain device-to-device copy of 1 GiB: the known byte count that scales the HBM counters."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n):
+    """The oracle, single-threaded, on the first n envs of the pixel workload: 128 steps with pixel
+    observations, then GAE by its definition with normalisation. Returns env-steps/s."""
+    import oracle
+    t0 = time.perf_counter()
+    env = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, sprites=sprites)
+    env.reset()
+    obs = np.empty((n, 4 * 84 * 84), np.uint8)
+    rew = np.empty((HORIZON, n), np.float32)
+    dn = np.empty((HORIZON, n), np.float32)
+    for t in range(HORIZON):
+        rew[t], dn[t] = env.step(policy_actions[t, :n])
+        env.obs_pixels(obs)
+    adv, _ = oracle.gae(rew, values[:, :n], dn, last_values[:n], float(np.float32(GAMMA)), float(np.float32(LAMBDA)))
+    oracle.normalize(adv)
+    dt = time.perf_counter() - t0
+    return HORIZON * n / dt, dt
+
+
+def main_pixels(args):
+    import torch
+
+    from resident_rl_rollout_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+    n = PIX_ENVS
+    ms = inputs.make_mapset(range(100, 100 + N_MAPS), MAP_H, MAP_W)
+    sprites = inputs.make_sprites(30)
+    policy_actions = inputs.make_actions(22, HORIZON, n)
+    values, last_values = inputs.make_values(23, HORIZON, n)
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_PIXELS,
+                      sprites=sprites, device=dev)
+    # rollout buffer: one allocation of [actions T*N | obs T*N*28224 (u8) | rewards T*N | dones T*N]
+    a_bytes = HORIZON * n * 4
+    o_bytes = HORIZON * n * 4 * 84 * 84
+    offs = [0, a_bytes, a_bytes + o_bytes, a_bytes + o_bytes + a_bytes]
+    buf = torch.empty(offs[3] + a_bytes, dtype=torch.uint8, device=dev)
+    actions = buf[offs[0]:offs[1]].view(torch.int32).view(HORIZON, n)
+    obs = buf[offs[1]:offs[2]].view(HORIZON, n, 4 * 84 * 84)
+    rewards = buf[offs[2]:offs[3]].view(torch.float32).view(HORIZON, n)
+    dones = buf[offs[3]:].view(torch.float32).view(HORIZON, n)
+    actions.copy_(torch.from_numpy(policy_actions))
+    values_d = torch.from_numpy(values).to(dev)
+    last_d = torch.from_numpy(last_values).to(dev)
+    adv = torch.empty((HORIZON, n), dtype=torch.float32, device=dev)
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    env.reset(obs[0])
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
+
+    def rollout(ev=None):
+        for t in range(HORIZON):
+            if ev is not None:
+                ev["env"][t][0].record()
+            env.step(actions[t], obs[t], rewards[t], dones[t])
+            if ev is not None:
+                ev["env"][t][1].record()
+        if ev is not None:
+            ev["gae"][0].record()
+        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
+        if ev is not None:
+            ev["gae"][1].record()
+
+    for _ in range(args.warmup):
+        rollout()
+    torch.cuda.synchronize()
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    events = [{"env": [mk() for _ in range(HORIZON)], "gae": mk()} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        rollout(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    env_ms = np.array([[s_.elapsed_time(e_) for s_, e_ in ev["env"]] for ev in events])
+    gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
+    env_avg_s = float(env_ms.mean()) * 1e-3
+    launch_bytes = n * PIX_BYTES_PER_ENV_STEP
+    achieved = launch_bytes / env_avg_s / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_s = min(args.cpu_envs, n)
+        rate, dt = cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n_s)
+        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} of the 16384 envs x 128 steps (env step + 4 x 84 x 84 pixel render), GAE + "
+                         f"normalisation over [128][{n_s}]; {dt:.1f} s single-threaded"}
+    out = {
+        "metric": "env-steps/s incl. 84x84 u8 pixel obs write at 16384 envs",
+        "value": args.steps * HORIZON * n / wall,
+        "unit": "env-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i32+u8+f32",
+        "data": "synthetic",
+        "config": {"workload": "pixel rollout: 16384 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
+                               "4 x 84 x 84 u8 frames from 16 seeded 8x8 sprites into a resident rollout buffer, "
+                               "then GAE with whole-batch statistics",
+                   "num_envs": n, "horizon": HORIZON},
+        "roofline": {"kernel": "env_step + pixel render (one rl_env_step: k_step, k_obs_pixels)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("env_step+pixels"), "bytes_per_launch": launch_bytes,
+                     "avg_launch_us": env_avg_s * 1e6},
+        "gae_us_in_rollout": float(gae_ms.mean()) * 1e3,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_envs is None:
+        args.cpu_envs = 512 if args.workload == "pixels" else 16384
+    if args.workload == "pixels":
+        return main_pixels(args)
     import torch
 
     from resident_rl_rollout_amd import binding, inputs
@@ -149,11 +290,7 @@ def main():
     env.reset(obs[0])
     torch.cuda.synchronize()
     if args.calibrate_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, dev)
 
     def rollout(ev=None):
         for t in range(HORIZON):
@@ -195,15 +332,17 @@ def main():
     # 256 MB to be written back during the next kernel).
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     flush.zero_()
-    iso_gae, iso_loss = [], []
+    iso = {"gae": [], "scan": [], "loss": []}
     for rep in range(args.iso_reps):
-        for which in ("gae", "loss"):
+        for which in ("gae", "scan", "loss"):
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             if which == "gae":
                 binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret,
                             adv_stats=stats)
+            elif which == "scan":   # the scan kernel alone: no statistics, no second launch
+                binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=0, adv=adv, ret=ret)
             elif args.loss_mode == "stream":
                 binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
                                  adv_stats=stats, out=loss_out, mb_index=mb_index)
@@ -212,7 +351,7 @@ def main():
                                  adv_stats=stats, out=loss_out)
             z.record()
             torch.cuda.synchronize()
-            (iso_gae if which == "gae" else iso_loss).append(a.elapsed_time(z))
+            iso[which].append(a.elapsed_time(z))
     del flush
 
     env_ms = np.array([[s.elapsed_time(e) for s, e in ev["env"]] for ev in events])   # [K][T]
@@ -226,7 +365,9 @@ def main():
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
     loss_bytes = b * LOSS_BYTES_PER_SAMPLE[args.loss_mode]
-    gae_s, loss_s = float(np.median(iso_gae)) * 1e-3, float(np.median(iso_loss)) * 1e-3
+    gae_s, loss_s = float(np.median(iso["gae"])) * 1e-3, float(np.median(iso["loss"])) * 1e-3
+    scan_s = float(np.median(iso["scan"])) * 1e-3
+    scan_gbs = gae_bytes / scan_s / 1e9
     gae_gbs = gae_bytes / gae_s / 1e9
     loss_gbs = loss_bytes / loss_s / 1e9
     gl_gbs = (gae_bytes + loss_bytes) / (gae_s + loss_s) / 1e9
@@ -264,7 +405,8 @@ def main():
                      "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
         "env_step_us": float(env_ms.mean()) * 1e3,
         "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
-                "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_traffic": load_traffic("gae_scan")},
+                "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_us": scan_s * 1e6, "scan_GB/s": scan_gbs,
+                "scan_frac": scan_gbs / HBM_PEAK_GBS, "scan_traffic": load_traffic("gae_scan")},
         "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
                  "us_in_rollout": float(loss_ms.mean()) * 1e3,
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
