@@ -42,6 +42,7 @@ ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
 PIX_ENVS = 16384
 PIX_BYTES_PER_ENV_STEP = 4 * 84 * 84 + (4 + 20 + 8) + (20 + 8 + 4 + 4) + 4 * 8   # 28324
 GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
+GRAD_BYTES_PER_SAMPLE = 12 * 4 + 4                   # the gradient row and the value gradient, written
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
                          "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
 
@@ -286,6 +287,8 @@ def main():
     ret = torch.empty_like(adv)
     stats = torch.zeros(3, dtype=torch.float64, device=dev)
     loss_out = torch.empty((MINIBATCHES, 4), dtype=torch.float32, device=dev)
+    dlogits = torch.empty((b, 12), dtype=torch.float32, device=dev)
+    dvalues = torch.empty(b, dtype=torch.float32, device=dev)
     mb = b // MINIBATCHES
     env.reset(obs[0])
     torch.cuda.synchronize()
@@ -332,9 +335,9 @@ def main():
     # 256 MB to be written back during the next kernel).
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     flush.zero_()
-    iso = {"gae": [], "scan": [], "loss": []}
+    iso = {"gae": [], "scan": [], "loss": [], "grad": []}
     for rep in range(args.iso_reps):
-        for which in ("gae", "scan", "loss"):
+        for which in ("gae", "scan", "loss", "grad"):
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -343,6 +346,10 @@ def main():
                             adv_stats=stats)
             elif which == "scan":   # the scan kernel alone: no statistics, no second launch
                 binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=0, adv=adv, ret=ret)
+            elif which == "grad":   # the loss with its per-sample gradient in the same pass (stream mode)
+                binding.ppo_loss_grad(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None,
+                                      mb, adv_stats=stats, out=loss_out, dlogits=dlogits, dvalues=dvalues,
+                                      mb_index=mb_index)
             elif args.loss_mode == "stream":
                 binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
                                  adv_stats=stats, out=loss_out, mb_index=mb_index)
@@ -367,6 +374,9 @@ def main():
     loss_bytes = b * LOSS_BYTES_PER_SAMPLE[args.loss_mode]
     gae_s, loss_s = float(np.median(iso["gae"])) * 1e-3, float(np.median(iso["loss"])) * 1e-3
     scan_s = float(np.median(iso["scan"])) * 1e-3
+    grad_s = float(np.median(iso["grad"])) * 1e-3
+    grad_bytes = b * (LOSS_BYTES_PER_SAMPLE["stream"] + GRAD_BYTES_PER_SAMPLE)
+    grad_gbs = grad_bytes / grad_s / 1e9
     scan_gbs = gae_bytes / scan_s / 1e9
     gae_gbs = gae_bytes / gae_s / 1e9
     loss_gbs = loss_bytes / loss_s / 1e9
@@ -410,6 +420,8 @@ def main():
         "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
                  "us_in_rollout": float(loss_ms.mean()) * 1e3,
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
+        "loss_grad": {"us": grad_s * 1e6, "GB/s": grad_gbs, "frac": grad_gbs / HBM_PEAK_GBS, "bytes": grad_bytes,
+                      "traffic": load_traffic("ppo_loss_grad")},
         "gae_loss_GB/s": gl_gbs,
         "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
         "loss_check": loss_out[0].tolist(),

@@ -6,7 +6,8 @@
  *      dones into caller-owned device buffers (rl_env_*);
  *   2. the GAE reverse scan over a [T][N] rollout with optional whole-batch advantage normalisation
  *      (rl_gae);
- *   3. the PPO clipped-surrogate, value and entropy loss reductions per minibatch (rl_ppo_loss).
+ *   3. the PPO clipped-surrogate, value and entropy loss reductions per minibatch (rl_ppo_loss), and
+ *      the same reductions with each sample's loss gradient written in the same pass (rl_ppo_loss_grad).
  *
  * Sources (page, then section):
  *   "Teaching Mario to speedrun" (bigmah.com): s.4 the return; s.6 GAE, the clipped loss and the
@@ -176,7 +177,7 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   adv_stats when adv_stats is not NULL.
  *   out  device f32[B/mb][4] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}.
  *   logits device f32[B][A], A in 1..64 (16-byte aligned when A % 4 == 0); actions device int32[B] in
- *   [0, A) (other values read logit 0); old_logp, adv, ret, new_values device f32[B].
+ *   [0, A) (other values act as action 0); old_logp, adv, ret, new_values device f32[B].
  *   B % mb must be 0. ws: device workspace of rl_ppo_loss_workspace_bytes(B, mb) bytes, 8-byte aligned (any
  *   contents); calls sharing it must not overlap. The per-sample terms are reduced through float64
  *   partials in a fixed order (identical results from run to run). With mb_index every input is read
@@ -185,6 +186,27 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
                 const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
                 const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
                 float ent_coef, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* rl_ppo_loss plus, in the same pass, the gradient of each minibatch's total loss
+ * L_m = mean pg + vf_coef * mean v - ent_coef * mean H with respect to the logits and the value of every
+ * sample of m (the next step of the learn phase in "Teaching Mario to speedrun", s.6; the loss and its
+ * gradient computed in one pass as in the GPU-shader trainer of s.8). With p = softmax(logits[i]),
+ * a = actions[i], M = mb and A, ratio as above:
+ *   dlogits[i][j] = (1/M) (-u A ratio ([j == a] - p_j) + ent_coef p_j (log p_j + H)),
+ *   dvalues[i]    = (1/M) 2 vf_coef (new_values[i] - ret[i]),
+ * where u = 1 when ratio * A <= clip(ratio) * A (the minimum takes the unclipped term; inside the clip
+ * band both terms are equal) and u = 0 on the clipped side. Advantages (normalised or not) are constants.
+ *   dlogits  device f32[B][A] output, row i for sample i in storage order (16-byte aligned when A % 4 == 0);
+ *   dvalues  device f32[B] output.
+ * Every sample must belong to exactly one minibatch (perm a permutation; mb_index as above), so each
+ * row is written once; out-of-range actions act as action 0 in both the loss and its gradient. All other
+ * arguments, errors and the workspace are as for rl_ppo_loss; dlogits and dvalues must be non-NULL and
+ * may not alias an input. */
+int rl_ppo_loss_grad(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                     const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                     const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                     float ent_coef, float* out, float* dlogits, float* dvalues, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* rl_last_error(void);

@@ -60,8 +60,10 @@ def _load():
     lib.oracle_gae.argtypes = [p, p, p, p, i32, i32, f64, f64, p, p]
     lib.oracle_normalize.argtypes = [p, i64, f64, p, p, p]
     lib.oracle_ppo_loss.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p]
+    lib.oracle_ppo_loss_grad.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p, p, p, p, p]
     for fn in (lib.oracle_env_reset, lib.oracle_env_step, lib.oracle_env_obs_tiles,
-               lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss):
+               lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss,
+               lib.oracle_ppo_loss_grad):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -152,13 +154,13 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
              vf_coef=0.5, ent_coef=0.01):
     """Per-minibatch PPO loss scalars, float64. Returns (out[num_mb][4], scale[num_mb][4]) with columns
     (pg, value, entropy, total)."""
-    lg = _c(logits, np.float32)
+    lg = _c(logits, np.float64)
     b, a = lg.shape
     act = _c(actions, np.int32).reshape(b)
-    olp = _c(old_logp, np.float32).reshape(b)
+    olp = _c(old_logp, np.float64).reshape(b)
     ad = _c(adv, np.float64).reshape(b)
     rt = _c(ret, np.float64).reshape(b)
-    nv = _c(new_values, np.float32).reshape(b)
+    nv = _c(new_values, np.float64).reshape(b)
     pm = None if perm is None else _c(perm, np.int32).reshape(b)
     assert b % minibatch == 0
     nmb = b // minibatch
@@ -167,3 +169,31 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
     _load().oracle_ppo_loss(_ptr(lg), _ptr(act), _ptr(olp), _ptr(ad), _ptr(rt), _ptr(nv), _ptr(pm), b, a,
                             minibatch, float(clip_eps), float(vf_coef), float(ent_coef), _ptr(out), _ptr(scale))
     return out, scale
+
+
+class LossGrad:
+    """Per-sample gradient of each minibatch's total loss, float64, in storage order, with the tests'
+    extras (see oracle_ppo_loss_grad)."""
+
+    def __init__(self, dlogits, dvalues, gscale, vscale, dpg, ratio):
+        self.dlogits, self.dvalues, self.gscale, self.vscale, self.dpg, self.ratio = (
+            dlogits, dvalues, gscale, vscale, dpg, ratio)
+
+
+def ppo_loss_grad(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2,
+                  vf_coef=0.5, ent_coef=0.01):
+    """dL_m/dlogits [B][A] and dL_m/dV [B] for the minibatch m that holds each sample."""
+    lg = _c(logits, np.float64)
+    b, a = lg.shape
+    act = _c(actions, np.int32).reshape(b)
+    olp = _c(old_logp, np.float64).reshape(b)
+    ad = _c(adv, np.float64).reshape(b)
+    rt = _c(ret, np.float64).reshape(b)
+    nv = _c(new_values, np.float64).reshape(b)
+    pm = None if perm is None else _c(perm, np.int32).reshape(b)
+    assert b % minibatch == 0
+    g = LossGrad(np.empty((b, a)), np.empty(b), np.empty((b, a)), np.empty(b), np.empty((b, a)), np.empty(b))
+    _load().oracle_ppo_loss_grad(_ptr(lg), _ptr(act), _ptr(olp), _ptr(ad), _ptr(rt), _ptr(nv), _ptr(pm), b, a,
+                                 minibatch, float(clip_eps), float(vf_coef), float(ent_coef), _ptr(g.dlogits),
+                                 _ptr(g.dvalues), _ptr(g.gscale), _ptr(g.vscale), _ptr(g.dpg), _ptr(g.ratio))
+    return g

@@ -442,10 +442,11 @@ int oracle_normalize(const double *adv, int64_t n, double eps, double *out, doub
 /*   v_i     = (V_i - R_i)^2                                                                         */
 /*   H_i     = entropy of softmax(z_i)                                                               */
 /* out[m] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}; scale[m] holds */
-/* the mean absolute summand of each (the tolerance floor).                                          */
+/* the mean absolute summand of each (the tolerance floor). Inputs are float64 so that the loss can  */
+/* also be evaluated at perturbed points (finite differences); float32 data converts exactly.        */
 /* ---------------------------------------------------------------------------------------------- */
-int oracle_ppo_loss(const float *logits, const int32_t *actions, const float *old_logp, const double *adv,
-                    const double *ret, const float *new_values, const int32_t *perm, int64_t B, int32_t A,
+int oracle_ppo_loss(const double *logits, const int32_t *actions, const double *old_logp, const double *adv,
+                    const double *ret, const double *new_values, const int32_t *perm, int64_t B, int32_t A,
                     int32_t mb, double clip_eps, double vf_coef, double ent_coef, double *out, double *scale)
 {
     int64_t num_mb = B / mb;
@@ -453,23 +454,23 @@ int oracle_ppo_loss(const float *logits, const int32_t *actions, const float *ol
         double s_pg = 0, s_v = 0, s_h = 0, a_pg = 0, a_h = 0;
         for (int64_t k = 0; k < mb; ++k) {
             int64_t i = perm ? (int64_t)perm[m * mb + k] : m * mb + k;
-            const float *z = logits + (size_t)i * A;
+            const double *z = logits + (size_t)i * A;
             double zmax = z[0];
-            for (int j = 1; j < A; ++j) if ((double)z[j] > zmax) zmax = z[j];
+            for (int j = 1; j < A; ++j) if (z[j] > zmax) zmax = z[j];
             double sum = 0.0;
-            for (int j = 0; j < A; ++j) sum += exp((double)z[j] - zmax);
+            for (int j = 0; j < A; ++j) sum += exp(z[j] - zmax);
             double lse = zmax + log(sum);
             double ent = 0.0;  /* -sum p_j log p_j */
             for (int j = 0; j < A; ++j) {
-                double lp = (double)z[j] - lse;
+                double lp = z[j] - lse;
                 ent -= exp(lp) * lp;
             }
-            double logp = (double)z[actions[i]] - lse;
-            double ratio = exp(logp - (double)old_logp[i]);
+            double logp = z[actions[i]] - lse;
+            double ratio = exp(logp - old_logp[i]);
             double clipped = ratio < 1.0 - clip_eps ? 1.0 - clip_eps : (ratio > 1.0 + clip_eps ? 1.0 + clip_eps : ratio);
             double s1 = ratio * adv[i], s2 = clipped * adv[i];
             double pg = -(s1 < s2 ? s1 : s2);
-            double dv = (double)new_values[i] - ret[i];
+            double dv = new_values[i] - ret[i];
             double v = dv * dv;
             s_pg += pg; s_v += v; s_h += ent;
             a_pg += fabs(pg); a_h += fabs(ent);
@@ -485,6 +486,68 @@ int oracle_ppo_loss(const float *logits, const int32_t *actions, const float *ol
             scale[m * 4 + 2] = a_h / mb;
             scale[m * 4 + 3] = a_pg / mb + vf_coef * v + ent_coef * a_h / mb;
         }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------- */
+/* Gradient of each minibatch's total loss L_m = mean pg + vf_coef mean v - ent_coef mean H with     */
+/* respect to the logits and the value of every sample i of minibatch m (the step after the loss     */
+/* forward in the collect / judge / learn loop of [MARIO] s.6; computing it in the same pass as the  */
+/* loss follows the fused loss-and-gradient kernel described in [MARIO] s.8). With p = softmax(z_i),  */
+/* a = a_i, r = ratio_i, c = clip(r, 1 - eps, 1 + eps), M = mb:                                       */
+/*   d logp / d z_j = [j == a] - p_j,   d r / d z_j = r ([j == a] - p_j)                              */
+/*   -min(r A, c A) takes the unclipped term when r A <= c A (inside the band both terms are r A);    */
+/*   there its derivative in r is -A, otherwise 0 (c is constant outside the band)                    */
+/*   d H / d z_j = -p_j (log p_j + H)                                                                 */
+/*   dL_m / d z_j = (1/M) (-[r A <= c A] A r ([j == a] - p_j) + ent_coef p_j (log p_j + H))           */
+/*   dL_m / d V_i = (1/M) vf_coef 2 (V_i - R_i)                                                       */
+/* Advantages are constants (normalisation statistics included). Extra outputs for the tests:         */
+/*   gscale[i][j] = (1/M) (|A| r |[j == a] - p_j| + ent_coef p_j (|log p_j| + H)), vscale[i] =         */
+/*   (1/M) vf_coef 2 (|V_i| + |R_i|): the magnitudes of the summands (the tolerance floor);           */
+/*   dpg[i][j] = (1/M) (-A r ([j == a] - p_j)): the surrogate's part when the unclipped term is taken;  */
+/*   ratio[i] = r. A ratio within rounding of a band edge decides the surrogate's part either way.    */
+/* perm must be a permutation of [0, B) (each sample in one minibatch); NULL = contiguous minibatches. */
+/* ---------------------------------------------------------------------------------------------- */
+int oracle_ppo_loss_grad(const double *logits, const int32_t *actions, const double *old_logp,
+                         const double *adv, const double *ret, const double *new_values, const int32_t *perm,
+                         int64_t B, int32_t A, int32_t mb, double clip_eps, double vf_coef, double ent_coef,
+                         double *dlogits, double *dvalues, double *gscale, double *vscale, double *dpg,
+                         double *ratio_out)
+{
+    const double inv = 1.0 / (double)mb;
+    for (int64_t k = 0; k < B; ++k) {
+        int64_t i = perm ? (int64_t)perm[k] : k;
+        const double *z = logits + (size_t)i * A;
+        double zmax = z[0];
+        for (int j = 1; j < A; ++j) if (z[j] > zmax) zmax = z[j];
+        double sum = 0.0;
+        for (int j = 0; j < A; ++j) sum += exp(z[j] - zmax);
+        double lse = zmax + log(sum);
+        double ent = 0.0;
+        for (int j = 0; j < A; ++j) {
+            double lp = z[j] - lse;
+            ent -= exp(lp) * lp;
+        }
+        int a = actions[i];
+        double logp = z[a] - lse;
+        double ratio = exp(logp - old_logp[i]);
+        double clipped = ratio < 1.0 - clip_eps ? 1.0 - clip_eps : (ratio > 1.0 + clip_eps ? 1.0 + clip_eps : ratio);
+        int unclipped = ratio * adv[i] <= clipped * adv[i];
+        for (int j = 0; j < A; ++j) {
+            double lp = z[j] - lse;
+            double pj = exp(lp);
+            double onehot = j == a ? 1.0 : 0.0;
+            double g_pg = -adv[i] * ratio * (onehot - pj);
+            double g_h = ent_coef * pj * (lp + ent);
+            dlogits[(size_t)i * A + j] = inv * ((unclipped ? g_pg : 0.0) + g_h);
+            if (gscale) gscale[(size_t)i * A + j] = inv * (fabs(adv[i]) * ratio * fabs(onehot - pj) +
+                                                          ent_coef * pj * (fabs(lp) + ent));
+            if (dpg) dpg[(size_t)i * A + j] = inv * g_pg;
+        }
+        dvalues[i] = inv * vf_coef * 2.0 * (new_values[i] - ret[i]);
+        if (vscale) vscale[i] = inv * vf_coef * 2.0 * (fabs(new_values[i]) + fabs(ret[i]));
+        if (ratio_out) ratio_out[i] = ratio;
     }
     return 0;
 }

@@ -53,6 +53,8 @@ SIGNATURES = [
     ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
     ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P,
                                    _P, _SZ, _P]),
+    ("rl_ppo_loss_grad", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32,
+                                        _P, _P, _P, _P, _SZ, _P]),
     ("rl_last_error", ctypes.c_char_p, []),
 ]
 
@@ -243,3 +245,26 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
                             b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
                             dptr(out, torch.float32, "out"), dptr(ws), ws.numel(), stream_ptr(stream)))
     return out
+
+
+def ppo_loss_grad(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2, vf_coef=0.5,
+                  ent_coef=0.01, adv_stats=None, out=None, dlogits=None, dvalues=None, ws=None, stream=None,
+                  mb_index=None):
+    """rl_ppo_loss_grad; returns (out [B/minibatch][4], dlogits [B][A], dvalues [B]): the loss scalars and
+    the gradient of each minibatch's total with respect to its samples' logits and values."""
+    b, a = logits.shape
+    dev = logits.device
+    out = torch.empty((b // minibatch, 4), dtype=torch.float32, device=dev) if out is None else out
+    dlogits = torch.empty((b, a), dtype=torch.float32, device=dev) if dlogits is None else dlogits
+    dvalues = torch.empty(b, dtype=torch.float32, device=dev) if dvalues is None else dvalues
+    if ws is None:
+        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev)
+    check(lib().rl_ppo_loss_grad(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
+                                 dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
+                                 dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),
+                                 dptr(perm, torch.int32, "perm"), dptr(mb_index, torch.uint16, "mb_index"),
+                                 dptr(adv_stats, torch.float64, "adv_stats"),
+                                 b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
+                                 dptr(out, torch.float32, "out"), dptr(dlogits, torch.float32, "dlogits"),
+                                 dptr(dvalues, torch.float32, "dvalues"), dptr(ws), ws.numel(), stream_ptr(stream)))
+    return out, dlogits, dvalues

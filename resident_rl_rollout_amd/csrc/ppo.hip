@@ -12,6 +12,16 @@
 //   batch in storage order serves all minibatches at once: every read is coalesced and each sample is
 //   read exactly once. Each thread adds its samples' terms into its own per-minibatch slots in LDS
 //   (private, so no atomics and a fixed order), and the block then sums the slots thread by thread.
+//
+// With a gradient (rl_ppo_loss_grad), the same pass also writes each sample's row of dL_m/dlogits and its
+// dL_m/dV for the minibatch m that holds it: the fused loss-and-gradient step that the same page (s.8,
+// the port of the trainer to GPU shaders) describes. With p = softmax(z), r the ratio, c its clip and
+// M the minibatch size:
+//   dL/dz_j = (1/M) (-[r A <= c A] A r ([j == a] - p_j) + ent_coef p_j (log p_j + H)),
+//   dL/dV   = (1/M) 2 vf_coef (V - R).
+// The surrogate's minimum takes the unclipped term whenever r A <= c A (inside the clip band the two
+// terms are equal), where its derivative in r is -A; on the clipped side it is constant. Advantages,
+// normalised or not, are constants.
 
 #include <algorithm>
 
@@ -39,6 +49,10 @@ struct LossArgs {
     const uint16_t* mb_index;
     int64_t B;
     int num_mb;
+    float* dlogits;     // [B][A], or NULL without a gradient
+    float* dvalues;     // [B]
+    float inv_mb;       // 1 / M
+    float dv_coef;      // 2 vf / M
 };
 
 __device__ __forceinline__ double block_sum(double v, double* lds)
@@ -53,79 +67,112 @@ __device__ __forceinline__ double block_sum(double v, double* lds)
     return s;
 }
 
-// Logits row statistics for AC (compile-time action count; 0 = runtime A, read element by element):
-// returns log(sum exp(z - max)) in *log_s, (sum e_j (z_j - max)) / S in *mean_u, and z_a - max in *u_a.
+// The logits row of a sample in registers (AC = compile-time action count).
 template <int AC>
-__device__ __forceinline__ void row_stats(const float* __restrict__ row, int A, int a, float* log_s, float* mean_u,
-                                          float* u_a)
+__device__ __forceinline__ void load_row(const float* __restrict__ row, float (&z)[AC])
 {
-    if constexpr (AC > 0) {
-        float z[AC];
-        if constexpr (AC % 4 == 0) {
+    if constexpr (AC % 4 == 0) {
 #pragma unroll
-            for (int j = 0; j < AC / 4; ++j) {
-                const float4 q = reinterpret_cast<const float4*>(row)[j];
-                z[4 * j] = q.x;
-                z[4 * j + 1] = q.y;
-                z[4 * j + 2] = q.z;
-                z[4 * j + 3] = q.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < AC; ++j) z[j] = row[j];
+        for (int j = 0; j < AC / 4; ++j) {
+            const float4 q = reinterpret_cast<const float4*>(row)[j];
+            z[4 * j] = q.x;
+            z[4 * j + 1] = q.y;
+            z[4 * j + 2] = q.z;
+            z[4 * j + 3] = q.w;
         }
-        float mx = z[0];
-#pragma unroll
-        for (int j = 1; j < AC; ++j) mx = fmaxf(mx, z[j]);
-        float s = 0.0f, su = 0.0f, ua = z[0] - mx;
-#pragma unroll
-        for (int j = 0; j < AC; ++j) {
-            const float u = z[j] - mx;
-            const float ex = expf(u);
-            s += ex;
-            su += ex * u;
-            if (j == a) ua = u;
-        }
-        *log_s = logf(s);
-        *mean_u = su / s;
-        *u_a = ua;
     } else {
-        float mx = row[0];
-        for (int j = 1; j < A; ++j) mx = fmaxf(mx, row[j]);
-        float s = 0.0f, su = 0.0f, ua = row[0] - mx;
-        for (int j = 0; j < A; ++j) {
-            const float u = row[j] - mx;
-            const float ex = expf(u);
-            s += ex;
-            su += ex * u;
-            if (j == a) ua = u;
-        }
-        *log_s = logf(s);
-        *mean_u = su / s;
-        *u_a = ua;
+#pragma unroll
+        for (int j = 0; j < AC; ++j) z[j] = row[j];
     }
 }
 
-// The three per-sample terms: clipped surrogate, squared value error, entropy.
+// Row statistics: mx = max z, log_s = log(sum exp(z - mx)), mean_u = (sum e_j (z_j - mx)) / S, u_a = z_a - mx.
+// AC > 0 reads the registers z; AC = 0 (runtime A) reads the row element by element.
 template <int AC>
+__device__ __forceinline__ void row_stats(const float* z, const float* __restrict__ row, int A, int a, float* mx_out,
+                                          float* log_s, float* mean_u, float* u_a)
+{
+    const int n = AC > 0 ? AC : A;
+    auto at = [&](int j) { return AC > 0 ? z[j] : row[j]; };
+    float mx = at(0);
+#pragma unroll
+    for (int j = 1; j < (AC > 0 ? AC : 64); ++j)
+        if (AC > 0 || j < n) mx = fmaxf(mx, at(j));
+    float s = 0.0f, su = 0.0f, ua = at(0) - mx;
+#pragma unroll
+    for (int j = 0; j < (AC > 0 ? AC : 64); ++j) {
+        if (AC > 0 || j < n) {
+            const float u = at(j) - mx;
+            const float ex = expf(u);
+            s += ex;
+            su += ex * u;
+            if (j == a) ua = u;
+        }
+    }
+    *mx_out = mx;
+    *log_s = logf(s);
+    *mean_u = su / s;
+    *u_a = ua;
+}
+
+// The three per-sample terms: clipped surrogate, squared value error, entropy; with GRAD also the
+// sample's gradient row and value gradient.
+template <int AC, bool GRAD>
 __device__ __forceinline__ void sample_terms(const LossArgs& p, int64_t i, float mean, float scale, float* pg,
                                              float* v, float* h)
 {
-    const int a = p.actions[i];
-    float log_s, mean_u, u_a;
-    row_stats<AC>(p.logits + i * (AC > 0 ? AC : p.A), p.A, a, &log_s, &mean_u, &u_a);
+    const int A = AC > 0 ? AC : p.A;
+    int a = p.actions[i];
+    if (a < 0 || a >= A) a = 0;   // an out-of-range action reads logit 0
+    const float* row = p.logits + i * A;
+    float z[AC > 0 ? AC : 1];
+    if constexpr (AC > 0) load_row<AC>(row, z);
+    float mx, log_s, mean_u, u_a;
+    row_stats<AC>(z, row, A, a, &mx, &log_s, &mean_u, &u_a);
     const float logp = u_a - log_s;
     *h = log_s - mean_u;
     const float ratio = expf(logp - p.old_logp[i]);
     float adv = p.adv[i];
     if (p.stats) adv = (adv - mean) * scale;
     const float clipped = fminf(fmaxf(ratio, p.clip_lo), p.clip_hi);
-    *pg = -fminf(ratio * adv, clipped * adv);
+    const float s1 = ratio * adv, s2 = clipped * adv;
+    *pg = -fminf(s1, s2);
     const float dv = p.new_v[i] - p.ret[i];
     *v = dv * dv;
+    if constexpr (GRAD) {
+        const float c_pg = s1 <= s2 ? -adv * ratio * p.inv_mb : 0.0f;   // times ([j == a] - p_j)
+        const float c_h = p.ent * p.inv_mb;                               // times p_j (log p_j + H)
+        const float H = *h;
+        const float lse = mx + log_s;
+        float* g = p.dlogits + i * A;
+        if constexpr (AC > 0) {
+            float gz[AC];
+#pragma unroll
+            for (int j = 0; j < AC; ++j) {
+                const float lp = z[j] - lse;
+                const float pj = expf(lp);
+                gz[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * (lp + H);
+            }
+            if constexpr (AC % 4 == 0) {
+#pragma unroll
+                for (int j = 0; j < AC / 4; ++j)
+                    reinterpret_cast<float4*>(g)[j] = make_float4(gz[4 * j], gz[4 * j + 1], gz[4 * j + 2], gz[4 * j + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < AC; ++j) g[j] = gz[j];
+            }
+        } else {
+            for (int j = 0; j < A; ++j) {
+                const float lp = row[j] - lse;
+                const float pj = expf(lp);
+                g[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * (lp + H);
+            }
+        }
+        p.dvalues[i] = p.dv_coef * dv;
+    }
 }
 
-template <int AC>
+template <int AC, bool GRAD>
 __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 {
     __shared__ double lds[12];
@@ -141,7 +188,7 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < p.mb; k += step) {
         const int64_t i = p.perm ? (int64_t)p.perm[base + k] : base + k;
         float pg, v, h;
-        sample_terms<AC>(p, i, mean, scale, &pg, &v, &h);
+        sample_terms<AC, GRAD>(p, i, mean, scale, &pg, &v, &h);
         s_pg += (double)pg;
         s_v += (double)v;
         s_h += (double)h;
@@ -159,7 +206,7 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 
 // Stream mode: block b visits samples [b*chunk, min(B, (b+1)*chunk)) in storage order. THREADS * NB * 3
 // floats of LDS hold each thread's private per-minibatch sums (slot (j*3 + s)*THREADS + thread).
-template <int AC, int NB, int THREADS>
+template <int AC, int NB, int THREADS, bool GRAD>
 __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t chunk)
 {
     __shared__ float acc[NB * 3 * THREADS];
@@ -176,7 +223,7 @@ __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t
     for (int64_t i = lo + t; i < hi; i += THREADS) {
         const int mbi = min((int)p.mb_index[i], NB - 1);
         float pg, v, h;
-        sample_terms<AC>(p, i, mean, scale, &pg, &v, &h);
+        sample_terms<AC, GRAD>(p, i, mean, scale, &pg, &v, &h);
         float* slot = acc + (mbi * 3) * THREADS + t;
         slot[0] += pg;
         slot[THREADS] += v;
@@ -251,11 +298,36 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     return RL_OK;
 }
 
-int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv, const float* ret,
-                const float* new_values, const int32_t* perm, const uint16_t* mb_index, const double* adv_stats,
-                int64_t B, int32_t A,
-                int32_t mb, float clip_eps, float vf_coef, float ent_coef, float* out, void* ws, size_t ws_bytes,
-                void* stream)
+}  // extern "C"
+
+namespace {
+
+template <bool GRAD>
+void launch_loss(const LossArgs& p, int64_t num_mb, int A, bool stream_mode, int64_t chunk, int nblk, hipStream_t st)
+{
+    if (stream_mode) {
+        const dim3 grid(nblk);
+        if (num_mb <= 16) {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256, GRAD>), grid, dim3(256), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256, GRAD>), grid, dim3(256), 0, st, p, chunk);
+        } else if (num_mb <= 32) {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128, GRAD>), grid, dim3(128), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128, GRAD>), grid, dim3(128), 0, st, p, chunk);
+        } else {
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64, GRAD>), grid, dim3(64), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64, GRAD>), grid, dim3(64), 0, st, p, chunk);
+        }
+    } else {
+        const dim3 grid(nblk, (unsigned)num_mb);
+        if (A == 12) hipLaunchKernelGGL((k_ppo_loss<12, GRAD>), grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((k_ppo_loss<0, GRAD>), grid, dim3(256), 0, st, p);
+    }
+}
+
+int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                  const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                  const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                  float ent_coef, float* out, float* dlogits, float* dvalues, void* ws, size_t ws_bytes, void* stream)
 {
     size_t need = 0;
     if (int rc = rl_ppo_loss_workspace_bytes(B, mb, &need)) return rc;
@@ -274,6 +346,12 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
         return rl::fail(RL_EINVAL, "mb_index supports at most %d minibatches, got %lld", kStreamMaxMinibatches,
                         (long long)(B / mb));
     if (A % 4 == 0 && !rl::aligned(logits, 16)) return rl::fail(RL_EALIGN, "logits must be 16-byte aligned when A %% 4 == 0");
+    if (dlogits) {
+        if (!rl::aligned(dlogits, 4) || !rl::aligned(dvalues, 4))
+            return rl::fail(RL_EALIGN, "dlogits / dvalues are not 4-byte aligned");
+        if (A % 4 == 0 && !rl::aligned(dlogits, 16))
+            return rl::fail(RL_EALIGN, "dlogits must be 16-byte aligned when A %% 4 == 0");
+    }
     if (!rl::aligned(ws, 8) || (adv_stats && !rl::aligned(adv_stats, 8)))
         return rl::fail(RL_EALIGN, "ws / adv_stats not 8-byte aligned");
     if (ws_bytes < need) return rl::fail(RL_ESIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -299,35 +377,43 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
     p.mb_index = mb_index;
     p.B = B;
     p.num_mb = (int)num_mb;
+    p.dlogits = dlogits;
+    p.dvalues = dvalues;
+    p.inv_mb = (float)(1.0 / (double)mb);
+    p.dv_coef = (float)(2.0 * (double)vf_coef / (double)mb);
     hipStream_t st = rl::as_stream(stream);
-    const dim3 block(256);
-    int nblk;
-    if (mb_index) {
-        int64_t chunk = 0;
-        nblk = stream_blocks(B, &chunk);
-        const dim3 grid(nblk);
-        if (num_mb <= 16) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256>), grid, dim3(256), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256>), grid, dim3(256), 0, st, p, chunk);
-        } else if (num_mb <= 32) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128>), grid, dim3(128), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128>), grid, dim3(128), 0, st, p, chunk);
-        } else {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64>), grid, dim3(64), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64>), grid, dim3(64), 0, st, p, chunk);
-        }
-    } else {
-        nblk = blocks_per_mb(mb);
-        const dim3 grid(nblk, (unsigned)num_mb);
-        if (A == 12)
-            hipLaunchKernelGGL(k_ppo_loss<12>, grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL(k_ppo_loss<0>, grid, block, 0, st, p);
-    }
+    int64_t chunk = 0;
+    const int nblk = mb_index ? stream_blocks(B, &chunk) : blocks_per_mb(mb);
+    if (dlogits) launch_loss<true>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
+    else launch_loss<false>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
     if (int rc = rl::check_launch("ppo_loss")) return rc;
-    hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), block, 0, st, static_cast<const double*>(ws), nblk,
+    hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), dim3(256), 0, st, static_cast<const double*>(ws), nblk,
                        (int64_t)mb, vf_coef, ent_coef, out);
     return rl::check_launch("ppo_finalize");
+}
+
+}  // namespace
+
+extern "C" {
+
+int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv, const float* ret,
+                const float* new_values, const int32_t* perm, const uint16_t* mb_index, const double* adv_stats,
+                int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef, float ent_coef, float* out, void* ws,
+                size_t ws_bytes, void* stream)
+{
+    return ppo_loss_impl(logits, actions, old_logp, adv, ret, new_values, perm, mb_index, adv_stats, B, A, mb, clip_eps,
+                         vf_coef, ent_coef, out, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int rl_ppo_loss_grad(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                     const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                     const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                     float ent_coef, float* out, float* dlogits, float* dvalues, void* ws, size_t ws_bytes,
+                     void* stream)
+{
+    if (!dlogits || !dvalues) return rl::fail(RL_EINVAL, "dlogits and dvalues must be non-NULL");
+    return ppo_loss_impl(logits, actions, old_logp, adv, ret, new_values, perm, mb_index, adv_stats, B, A, mb, clip_eps,
+                         vf_coef, ent_coef, out, dlogits, dvalues, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,40 @@ def assert_loss_close(got, ref, scale, what, rel=1e-4):
     assert (err <= bound).all(), f"{what}: err {err[err > bound]} bound {bound[err > bound]}"
 
 
+def assert_grad_close(dlogits, dvalues, g, adv, what, rel=1e-4, clip_eps=0.2, edge_rel=1e-5):
+    """Loss-gradient parity against the oracle's LossGrad g: per element |got - want| <= rel * (|want| +
+    summand magnitudes). Where float rounding decides which side of the min a sample takes (its ratio
+    within edge_rel of the band edge that applies to its advantage's sign), the row may match either
+    side: the oracle's row, or that row with the surrogate's part switched."""
+    dl = np.asarray(dlogits, np.float64)
+    dv = np.asarray(dvalues, np.float64)
+    assert dl.shape == g.dlogits.shape and dv.shape == g.dvalues.shape, what
+    bound = rel * (np.abs(g.dlogits) + g.gscale)
+    ok = (np.abs(dl - g.dlogits) <= bound).all(axis=1)
+    edge = np.where(np.asarray(adv) >= 0, 1.0 + clip_eps, 1.0 - clip_eps)
+    ambiguous = np.abs(g.ratio - edge) <= edge_rel * edge
+    if (~ok & ambiguous).any():
+        rows = np.nonzero(~ok & ambiguous)[0]
+        # the other side of the min: remove the surrogate part if the oracle kept it, add it otherwise
+        sides = [g.dlogits[rows] - g.dpg[rows], g.dlogits[rows] + g.dpg[rows]]
+        alt_ok = np.zeros(rows.size, bool)
+        for alt in sides:
+            alt_ok |= (np.abs(dl[rows] - alt) <= rel * (np.abs(alt) + g.gscale[rows])).all(axis=1)
+        ok[rows] = alt_ok
+    if not ok.all():
+        i = int(np.nonzero(~ok)[0][0])
+        j = int(np.argmax(np.abs(dl[i] - g.dlogits[i]) - bound[i]))
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} gradient rows outside tolerance; first "
+                             f"sample {i} logit {j}: got {dl[i, j]!r} want {g.dlogits[i, j]!r} "
+                             f"(bound {bound[i, j]:.3g}, ratio {g.ratio[i]!r})")
+    vbound = rel * (np.abs(g.dvalues) + g.vscale)
+    verr = np.abs(dv - g.dvalues)
+    if (verr > vbound).any():
+        i = int(np.argmax(verr - vbound))
+        raise AssertionError(f"{what}: value gradient of sample {i}: got {dv[i]!r} want {g.dvalues[i]!r}")
+    return int(ambiguous.sum())
+
+
 class PairedEnvs:
     """The same env batch on the GPU (through the C ABI) and in the oracle, stepped with the same actions."""
 

@@ -97,6 +97,13 @@ def test_entry_points_reject_before_any_hip_call():
     idx = [fake] * 6 + [None, fake, None]
     assert lib.rl_ppo_loss(*idx, 6500, 12, 100, 0.2, 0.5, 0.01, fake, fake, 1 << 30, None) == -1
     assert "at most 64" in lib.rl_last_error().decode()
+    # rl_ppo_loss_grad: the gradient buffers are required; dlogits 16-byte aligned when A % 4 == 0
+    g = [fake] * 6 + [None, None, None]
+    assert lib.rl_ppo_loss_grad(*g, 100, 12, 10, 0.2, 0.5, 0.01, fake, None, fake, fake, 1 << 20, None) == -1
+    assert "dlogits" in lib.rl_last_error().decode()
+    assert lib.rl_ppo_loss_grad(*g, 100, 12, 10, 0.2, 0.5, 0.01, fake, ctypes.c_void_p(4100), fake, fake, 1 << 20,
+                                None) == -2
+    assert lib.rl_ppo_loss_grad(*g, 100, 12, 30, 0.2, 0.5, 0.01, fake, fake, fake, fake, 1 << 20, None) == -1
     need = ctypes.c_size_t()
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
     assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128
