@@ -61,9 +61,10 @@ def _load():
     lib.oracle_normalize.argtypes = [p, i64, f64, p, p, p]
     lib.oracle_ppo_loss.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p]
     lib.oracle_ppo_loss_grad.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p, p, p, p, p]
+    lib.oracle_vtrace.argtypes = [p, p, p, p, p, i32, i32, f64, f64, f64, f64, f64, p, p]
     for fn in (lib.oracle_env_reset, lib.oracle_env_step, lib.oracle_env_obs_tiles,
                lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss,
-               lib.oracle_ppo_loss_grad):
+               lib.oracle_ppo_loss_grad, lib.oracle_vtrace):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,3 +198,19 @@ def ppo_loss_grad(logits, actions, old_logp, adv, ret, new_values, perm, minibat
                                  minibatch, float(clip_eps), float(vf_coef), float(ent_coef), _ptr(g.dlogits),
                                  _ptr(g.dvalues), _ptr(g.gscale), _ptr(g.vscale), _ptr(g.dpg), _ptr(g.ratio))
     return g
+
+
+def vtrace(rewards, values, dones, last_values, log_rhos, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0,
+           pg_rho_bar=1.0):
+    """V-trace targets vs[T][N] and policy-gradient advantages pg[T][N], float64, by the definition sum."""
+    r = _c(rewards, np.float32)
+    t, n = r.shape
+    v = _c(values, np.float32)
+    d = _c(dones, np.float32)
+    lv = _c(last_values, np.float32).reshape(n)
+    lr = _c(log_rhos, np.float32)
+    vs = np.empty((t, n), np.float64)
+    pg = np.empty((t, n), np.float64)
+    _load().oracle_vtrace(_ptr(r), _ptr(v), _ptr(d), _ptr(lv), _ptr(lr), t, n, float(gamma), float(lam),
+                          float(rho_bar), float(c_bar), float(pg_rho_bar), _ptr(vs), _ptr(pg))
+    return vs, pg

@@ -551,3 +551,48 @@ int oracle_ppo_loss_grad(const double *logits, const int32_t *actions, const dou
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------------- */
+/* V-trace targets (the off-policy correction that PlayTrain's IMPALA trainer, App. C.3, takes from   */
+/* torchbeast; "Teaching Mario to speedrun" s.8 names it as the alternative to GAE for per-minibatch   */
+/* advantages). Restated from its published definition (Espeholt et al., 2018, IMPALA, eq. 1) with    */
+/* the done mask read as for GAE: the discount of step t is g_t = gamma (1 - d_t). With V_T = the      */
+/* bootstrap values and lr = log(pi / mu) of the taken action:                                         */
+/*   rho_t = min(rho_bar, exp(lr_t)),  c_t = lambda min(c_bar, exp(lr_t))                              */
+/*   delta_t = rho_t (r_t + g_t V_{t+1} - V_t)                                                         */
+/*   vs_s = V_s + sum_{t >= s} (prod_{i = s}^{t-1} g_i c_i) delta_t          (vs_T = V_T)              */
+/*   pg_s = min(pg_rho_bar, exp(lr_s)) (r_s + g_s vs_{s+1} - V_s)                                      */
+/* The sum is taken as written (O(T^2) per env), in float64.                                           */
+/* ---------------------------------------------------------------------------------------------- */
+int oracle_vtrace(const float *rewards, const float *values, const float *dones, const float *last_values,
+                  const float *log_rhos, int32_t T, int32_t N, double gamma, double lambda, double rho_bar,
+                  double c_bar, double pg_rho_bar, double *vs, double *pg_adv)
+{
+    for (int32_t n = 0; n < N; ++n) {
+        for (int32_t s = 0; s < T; ++s) {
+            double acc = 0.0, w = 1.0;
+            for (int32_t t = s; t < T; ++t) {
+                size_t k = (size_t)t * N + n;
+                double g = gamma * (1.0 - (double)dones[k]);
+                double vnext = t + 1 < T ? (double)values[k + N] : (double)last_values[n];
+                double ratio = exp((double)log_rhos[k]);
+                double rho = ratio < rho_bar ? ratio : rho_bar;
+                double delta = rho * ((double)rewards[k] + g * vnext - (double)values[k]);
+                acc += w * delta;
+                double c = lambda * (ratio < c_bar ? ratio : c_bar);
+                w *= g * c;
+                if (w == 0.0) break;
+            }
+            vs[(size_t)s * N + n] = (double)values[(size_t)s * N + n] + acc;
+        }
+        for (int32_t s = 0; s < T; ++s) {
+            size_t k = (size_t)s * N + n;
+            double g = gamma * (1.0 - (double)dones[k]);
+            double vs_next = s + 1 < T ? vs[k + N] : (double)last_values[n];
+            double ratio = exp((double)log_rhos[k]);
+            double rho_pg = ratio < pg_rho_bar ? ratio : pg_rho_bar;
+            pg_adv[k] = rho_pg * ((double)rewards[k] + g * vs_next - (double)values[k]);
+        }
+    }
+    return 0;
+}
