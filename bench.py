@@ -42,6 +42,7 @@ ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
 PIX_ENVS = 16384
 PIX_BYTES_PER_ENV_STEP = 4 * 84 * 84 + (4 + 20 + 8) + (20 + 8 + 4 + 4) + 4 * 8   # 28324
 GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
+VTRACE_BYTES_PER_ELEM = 6 * 4                        # r, v, d, log rho in; vs, pg advantage out
 GRAD_BYTES_PER_SAMPLE = 12 * 4 + 4                   # the gradient row and the value gradient, written
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
                          "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
@@ -288,6 +289,9 @@ def main():
     stats = torch.zeros(3, dtype=torch.float64, device=dev)
     loss_out = torch.empty((MINIBATCHES, 4), dtype=torch.float32, device=dev)
     dlogits = torch.empty((b, 12), dtype=torch.float32, device=dev)
+    log_rhos = torch.from_numpy(inputs.make_log_rhos(24, HORIZON, N_ENVS)).to(dev)
+    vs_out = torch.empty((HORIZON, N_ENVS), dtype=torch.float32, device=dev)
+    pgadv_out = torch.empty_like(vs_out)
     dvalues = torch.empty(b, dtype=torch.float32, device=dev)
     mb = b // MINIBATCHES
     env.reset(obs[0])
@@ -335,9 +339,9 @@ def main():
     # 256 MB to be written back during the next kernel).
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     flush.zero_()
-    iso = {"gae": [], "scan": [], "loss": [], "grad": []}
+    iso = {"gae": [], "scan": [], "loss": [], "grad": [], "vtrace": []}
     for rep in range(args.iso_reps):
-        for which in ("gae", "scan", "loss", "grad"):
+        for which in ("gae", "scan", "loss", "grad", "vtrace"):
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -346,6 +350,8 @@ def main():
                             adv_stats=stats)
             elif which == "scan":   # the scan kernel alone: no statistics, no second launch
                 binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=0, adv=adv, ret=ret)
+            elif which == "vtrace":  # V-trace targets and advantages over the same [T][N] rollout
+                binding.vtrace(rewards, values_d, dones, last_d, log_rhos, GAMMA, 1.0, vs=vs_out, pg_adv=pgadv_out)
             elif which == "grad":   # the loss with its per-sample gradient in the same pass (stream mode)
                 binding.ppo_loss_grad(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None,
                                       mb, adv_stats=stats, out=loss_out, dlogits=dlogits, dvalues=dvalues,
@@ -375,6 +381,9 @@ def main():
     gae_s, loss_s = float(np.median(iso["gae"])) * 1e-3, float(np.median(iso["loss"])) * 1e-3
     scan_s = float(np.median(iso["scan"])) * 1e-3
     grad_s = float(np.median(iso["grad"])) * 1e-3
+    vt_s = float(np.median(iso["vtrace"])) * 1e-3
+    vt_bytes = b * VTRACE_BYTES_PER_ELEM + N_ENVS * 4
+    vt_gbs = vt_bytes / vt_s / 1e9
     grad_bytes = b * (LOSS_BYTES_PER_SAMPLE["stream"] + GRAD_BYTES_PER_SAMPLE)
     grad_gbs = grad_bytes / grad_s / 1e9
     scan_gbs = gae_bytes / scan_s / 1e9
@@ -422,6 +431,8 @@ def main():
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
         "loss_grad": {"us": grad_s * 1e6, "GB/s": grad_gbs, "frac": grad_gbs / HBM_PEAK_GBS, "bytes": grad_bytes,
                       "traffic": load_traffic("ppo_loss_grad")},
+        "vtrace": {"us": vt_s * 1e6, "GB/s": vt_gbs, "frac": vt_gbs / HBM_PEAK_GBS, "bytes": vt_bytes,
+                   "traffic": load_traffic("vtrace")},
         "gae_loss_GB/s": gl_gbs,
         "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
         "loss_check": loss_out[0].tolist(),

@@ -5,7 +5,7 @@
  *   1. batched platformer stepping with frame-skip and auto-reset, writing observations, rewards and
  *      dones into caller-owned device buffers (rl_env_*);
  *   2. the GAE reverse scan over a [T][N] rollout with optional whole-batch advantage normalisation
- *      (rl_gae);
+ *      (rl_gae), and the V-trace scan for off-policy targets (rl_vtrace);
  *   3. the PPO clipped-surrogate, value and entropy loss reductions per minibatch (rl_ppo_loss), and
  *      the same reductions with each sample's loss gradient written in the same pass (rl_ppo_loss_grad).
  *
@@ -159,6 +159,22 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes);
 int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values,
            int32_t T, int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize,
            double* adv_stats, void* ws, size_t ws_bytes, void* stream);
+
+/* V-trace over a [T][N] rollout: the IMPALA off-policy targets and policy-gradient advantages (PlayTrain
+ * App. C.3 takes V-trace from torchbeast for its IMPALA trainer; "Teaching Mario to speedrun" s.8 names it
+ * beside GAE for per-minibatch advantages). Restated from the published definition (Espeholt et al. 2018,
+ * eq. 1) with the done mask as in rl_gae, g_t = gamma (1 - dones[t]):
+ *   ratio_t = exp(log_rhos[t]),  rho_t = min(rho_bar, ratio_t),  c_t = lambda min(c_bar, ratio_t),
+ *   vs[t] = V_t + sum_{u >= t} (prod_{i = t}^{u-1} g_i c_i) rho_u (r_u + g_u V_{u+1} - V_u),  V_T = last_values,
+ *   pg_adv[t] = min(pg_rho_bar, ratio_t) (r_t + g_t vs[t+1] - V_t),  vs[T] = last_values.
+ *   rewards, values, dones, log_rhos   device f32[T][N] (log_rhos = log pi(a_t) - log mu(a_t) of the taken
+ *                                      actions); last_values device f32[N];
+ *   vs, pg_adv                         device f32[T][N] outputs (may not alias the inputs);
+ *   rho_bar, c_bar, pg_rho_bar >= 0 (torchbeast uses 1, 1, 1 and lambda = 1).
+ * The scan runs in float32 (the same chunked affine-map scan as rl_gae); no workspace. */
+int rl_vtrace(const float* rewards, const float* values, const float* dones, const float* last_values,
+              const float* log_rhos, int32_t T, int32_t N, float gamma, float lambda, float rho_bar, float c_bar,
+              float pg_rho_bar, float* vs, float* pg_adv, void* stream);
 
 /* Workspace bytes rl_ppo_loss needs for B samples in minibatches of mb. */
 int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);

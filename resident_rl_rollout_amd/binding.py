@@ -50,6 +50,7 @@ SIGNATURES = [
     ("rl_env_destroy", None, [_P]),
     ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
     ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    ("rl_vtrace", ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _F32, _P, _P, _P]),
     ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
     ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P,
                                    _P, _SZ, _P]),
@@ -219,6 +220,20 @@ def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, 
                        dptr(adv_stats, torch.float64, "adv_stats"), dptr(ws), 0 if ws is None else ws.numel(),
                        stream_ptr(stream)))
     return adv, ret, adv_stats
+
+
+def vtrace(rewards, values, dones, last_values, log_rhos, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0,
+           vs=None, pg_adv=None, stream=None):
+    """rl_vtrace over [T][N]; returns (vs, pg_adv)."""
+    t, n = rewards.shape
+    vs = torch.empty_like(rewards) if vs is None else vs
+    pg_adv = torch.empty_like(rewards) if pg_adv is None else pg_adv
+    check(lib().rl_vtrace(dptr(rewards, torch.float32, "rewards"), dptr(values, torch.float32, "values"),
+                          dptr(dones, torch.float32, "dones"), dptr(last_values, torch.float32, "last_values"),
+                          dptr(log_rhos, torch.float32, "log_rhos"), t, n, float(gamma), float(lam), float(rho_bar),
+                          float(c_bar), float(pg_rho_bar), dptr(vs, torch.float32, "vs"),
+                          dptr(pg_adv, torch.float32, "pg_adv"), stream_ptr(stream)))
+    return vs, pg_adv
 
 
 def ppo_loss_workspace_bytes(b: int, mb: int) -> int:

@@ -188,6 +188,107 @@ __global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int6
         adv[i] = (adv[i] - mean) * scale;
 }
 
+// ------------------------------------------------------------------------------------------------
+// V-trace targets and policy-gradient advantages (the IMPALA off-policy correction that PlayTrain's
+// IMPALA trainer takes from torchbeast, App. C.3; "Teaching Mario to speedrun" s.8 names it beside GAE),
+// with the done mask read as for GAE: g_t = gamma (1 - d_t). With ratio_t = exp(log_rho_t),
+// rho_t = min(rho_bar, ratio_t), c_t = lambda min(c_bar, ratio_t), the TD error e_t = r_t + g_t V_{t+1} - V_t
+// and x_t = vs_t - V_t:
+//   x_t = rho_t e_t + g_t c_t x_{t+1}   (x_T = 0, V_T = bootstrap),      vs_t = V_t + x_t,
+//   pg_t = min(pg_rho_bar, ratio_t) (r_t + g_t vs_{t+1} - V_t) = min(pg_rho_bar, ratio_t) (e_t + g_t x_{t+1}).
+// The same first-order linear recurrence as GAE, so the same chunked scan: each thread holds e, ratio,
+// 1 - d and V of its chunk in registers, reduces the chunk to an affine map, the maps compose through
+// LDS, and the replay writes vs and pg (24 bytes per element: four inputs read, two outputs written).
+// ------------------------------------------------------------------------------------------------
+
+struct VtraceCoef {
+    float gamma, lambda, rho_bar, c_bar, pg_rho_bar;
+};
+
+template <int E, int LMAX, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restrict__ rew, const float* __restrict__ val,
+                                                        const float* __restrict__ done, const float* __restrict__ vlast,
+                                                        const float* __restrict__ lrho, int T, int N, int L,
+                                                        VtraceCoef k, float* __restrict__ vs, float* __restrict__ pg)
+{
+    constexpr int C = BLOCK / E;
+    __shared__ float sb[C][E];
+    __shared__ float sc[C][E];
+    const int e = threadIdx.x % E;
+    const int ch = threadIdx.x / E;
+    const int n = blockIdx.x * E + e;
+    const bool valid = n < N;
+    const int t0 = ch * L;
+    const int len = valid ? max(0, min(L, T - t0)) : 0;
+
+    const int nn = min(n, N - 1);
+    float td[LMAX], ratio[LMAX], nd[LMAX], vv[LMAX];
+#pragma unroll
+    for (int j = 0; j < LMAX; ++j) {
+        const int64_t idx = (int64_t)min(t0 + j, T - 1) * N + nn;
+        vv[j] = val[idx];
+        td[j] = rew[idx];
+        nd[j] = 1.0f - done[idx];
+        ratio[j] = lrho[idx];
+    }
+    const float v_after = val[(int64_t)min(t0 + len, T - 1) * N + nn];
+    const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
+
+    float b = 0.0f, c = 1.0f;
+#pragma unroll
+    for (int j = LMAX - 1; j >= 0; --j) {
+        if (j < len) {
+            const float vn = (j + 1 < len) ? vv[j + 1 < LMAX ? j + 1 : j] : vnext_tail;
+            const float g = k.gamma * nd[j];
+            ratio[j] = expf(ratio[j]);
+            td[j] = td[j] + g * vn - vv[j];
+            const float rho = fminf(k.rho_bar, ratio[j]);
+            const float gc = g * k.lambda * fminf(k.c_bar, ratio[j]);
+            b = rho * td[j] + gc * b;
+            c = gc * c;
+        }
+    }
+    sb[ch][e] = b;
+    sc[ch][e] = c;
+    __syncthreads();
+
+    float a = 0.0f;
+    for (int q = C - 1; q > ch; --q) a = sb[q][e] + sc[q][e] * a;
+
+#pragma unroll
+    for (int j = LMAX - 1; j >= 0; --j) {
+        if (j < len) {
+            const float g = k.gamma * nd[j];
+            const int64_t idx = (int64_t)(t0 + j) * N + n;
+            pg[idx] = fminf(k.pg_rho_bar, ratio[j]) * (td[j] + g * a);
+            a = fminf(k.rho_bar, ratio[j]) * td[j] + g * k.lambda * fminf(k.c_bar, ratio[j]) * a;
+            vs[idx] = a + vv[j];
+        }
+    }
+}
+
+// One lane per env walking t = T-1 .. 0: V-trace for horizons longer than the chunked kernels hold.
+__global__ __launch_bounds__(256) void k_vtrace_seq(const float* __restrict__ rew, const float* __restrict__ val,
+                                                    const float* __restrict__ done, const float* __restrict__ vlast,
+                                                    const float* __restrict__ lrho, int T, int N, VtraceCoef k,
+                                                    float* __restrict__ vs, float* __restrict__ pg)
+{
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float a = 0.0f, vn = vlast[n];
+    for (int t = T - 1; t >= 0; --t) {
+        const int64_t idx = (int64_t)t * N + n;
+        const float v = val[idx];
+        const float g = k.gamma * (1.0f - done[idx]);
+        const float ratio = expf(lrho[idx]);
+        const float td = rew[idx] + g * vn - v;
+        pg[idx] = fminf(k.pg_rho_bar, ratio) * (td + g * a);
+        a = fminf(k.rho_bar, ratio) * td + g * k.lambda * fminf(k.c_bar, ratio) * a;
+        vs[idx] = a + v;
+        vn = v;
+    }
+}
+
 enum class GaeKernel { C32x8_16, C16x16_8, C16x16_32, C16x16_64, C256x4_32, Seq };
 
 // Shapes by horizon and batch width. Wide batches take 256 envs x 4 chunks (1 KB row segments per block;
@@ -293,6 +394,41 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
         if (int rc = rl::check_launch("adv_normalize")) return rc;
     }
     return RL_OK;
+}
+
+int rl_vtrace(const float* rewards, const float* values, const float* dones, const float* last_values,
+              const float* log_rhos, int32_t T, int32_t N, float gamma, float lambda, float rho_bar, float c_bar,
+              float pg_rho_bar, float* vs, float* pg_adv, void* stream)
+{
+    if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
+    if ((int64_t)T * N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "T*N too large");
+    if (!rewards || !values || !dones || !last_values || !log_rhos || !vs || !pg_adv)
+        return rl::fail(RL_EINVAL, "rewards, values, dones, last_values, log_rhos, vs and pg_adv must be non-NULL");
+    if (!(rho_bar >= 0.0f) || !(c_bar >= 0.0f) || !(pg_rho_bar >= 0.0f))
+        return rl::fail(RL_EINVAL, "rho_bar, c_bar and pg_rho_bar must be >= 0");
+    const void* ptrs[] = {rewards, values, dones, last_values, log_rhos, vs, pg_adv};
+    for (const void* p : ptrs)
+        if (!rl::aligned(p, 4)) return rl::fail(RL_EALIGN, "a float array is not 4-byte aligned");
+    hipStream_t st = rl::as_stream(stream);
+    const VtraceCoef k{gamma, lambda, rho_bar, c_bar, pg_rho_bar};
+    if (T <= 128 && (N + 127) / 128 >= 256) {
+        hipLaunchKernelGGL((k_vtrace_chunked<128, 16, 1024>), dim3((N + 127) / 128), dim3(1024), 0, st, rewards, values,
+                           dones, last_values, log_rhos, T, N, (T + 7) / 8, k, vs, pg_adv);
+    } else if (T <= 128) {
+        hipLaunchKernelGGL((k_vtrace_chunked<16, 8, 256>), dim3((N + 15) / 16), dim3(256), 0, st, rewards, values,
+                           dones, last_values, log_rhos, T, N, (T + 15) / 16, k, vs, pg_adv);
+    } else if (T <= 256) {
+        hipLaunchKernelGGL((k_vtrace_chunked<16, 16, 256>), dim3((N + 15) / 16), dim3(256), 0, st, rewards, values,
+                           dones, last_values, log_rhos, T, N, (T + 15) / 16, k, vs, pg_adv);
+    } else if (T <= 512) {
+        // four per-step arrays of 32 steps would not fit the register file: 32 chunks of up to 16 steps
+        hipLaunchKernelGGL((k_vtrace_chunked<8, 16, 256>), dim3((N + 7) / 8), dim3(256), 0, st, rewards, values,
+                           dones, last_values, log_rhos, T, N, (T + 31) / 32, k, vs, pg_adv);
+    } else {
+        hipLaunchKernelGGL(k_vtrace_seq, dim3((N + 255) / 256), dim3(256), 0, st, rewards, values, dones, last_values,
+                           log_rhos, T, N, k, vs, pg_adv);
+    }
+    return rl::check_launch("vtrace");
 }
 
 }  // extern "C"

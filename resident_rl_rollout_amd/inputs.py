@@ -116,6 +116,14 @@ def make_gae_inputs(seed: int, t: int, n: int, p_spike: float = 0.05, p_done: fl
     return GaeInputs(r, v, d, vl)
 
 
+def make_log_rhos(seed: int, t: int, n: int, spread: float = 0.6) -> np.ndarray:
+    """Log importance ratios log pi - log mu of the taken actions, U(-spread, spread), float32: ratios from
+    0.55 to 1.82, so both sides of rho_bar = c_bar = 1 occur (the stand-in policy's new-minus-old logits
+    move by at most 0.3 each, which bounds the log-ratio by 0.6)."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(-spread, spread, (t, n)).astype(np.float32)
+
+
 @dataclasses.dataclass
 class PolicyInputs:
     new_logits: np.ndarray   # f32[B][A]

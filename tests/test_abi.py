@@ -83,6 +83,12 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 3, fake, fake, 1 << 20, None) == -1
     assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 1, fake, fake, 8, None) == -3
     assert lib.rl_gae(fake, ctypes.c_void_p(4098), fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -2
+    # rl_vtrace: sizes, NULLs, clip thresholds, alignment
+    assert lib.rl_vtrace(fake, fake, fake, fake, fake, 0, 5, 0.99, 1.0, 1.0, 1.0, 1.0, fake, fake, None) == -1
+    assert lib.rl_vtrace(fake, fake, fake, fake, None, 4, 5, 0.99, 1.0, 1.0, 1.0, 1.0, fake, fake, None) == -1
+    assert lib.rl_vtrace(fake, fake, fake, fake, fake, 4, 5, 0.99, 1.0, -1.0, 1.0, 1.0, fake, fake, None) == -1
+    assert lib.rl_vtrace(fake, fake, fake, fake, ctypes.c_void_p(4098), 4, 5, 0.99, 1.0, 1.0, 1.0, 1.0, fake, fake,
+                         None) == -2
     # rl_ppo_loss: B % mb, A range, alignment, workspace
     args = [fake] * 6 + [None, None, None]
     assert lib.rl_ppo_loss(*args, 100, 12, 30, 0.2, 0.5, 0.01, fake, fake, 1 << 20, None) == -1
