@@ -8,7 +8,9 @@ shuffled minibatches of 524288 samples. Policy outputs (actions sampled from see
 logits, values) are seeded N(0,1) stand-ins, generated before timing and resident in HBM.
 
 Prints one JSON line: env-steps/s of the whole job, the roofline of the env step (the dominant kernel),
-GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same workload. GAE and loss GB/s come
+GAE + loss GB/s, and the CPU oracle timed on a bounded sample of the same workload, single-threaded and in
+one process per host core of the GPU's share (the oracle itself is unchanged; envs and minibatches are
+independent). GAE and loss GB/s come
 from separate repetitions after a read-only cache flush (their own HBM efficiency); their times inside the
 rollout, which also absorb the write-back of the rollout's last observations, are reported beside them.
 
@@ -116,6 +118,67 @@ def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
     return b / dt, dt
 
 
+CPU_WORKERS = 16     # the host-core share of one GPU
+_SHARED = {}         # inputs the forked workers read (copy-on-write)
+
+
+def _env_shard(lo_hi):
+    """Worker: the oracle's env step + tile observations for envs [lo, hi), then GAE over the shard."""
+    import oracle
+    lo, hi = lo_hi
+    g = _SHARED
+    n = hi - lo
+    env = oracle.OracleEnv(g["ms"].maps, g["ms"].ckpts, g["ms"].spawns, n, env_offset=lo)
+    env.reset()
+    obs = np.empty((n, 1397), np.float32)
+    rew = np.empty((HORIZON, n), np.float32)
+    dn = np.empty((HORIZON, n), np.float32)
+    for t in range(HORIZON):
+        rew[t], dn[t] = env.step(g["actions"][t, lo:hi])
+        env.obs_tiles(obs)
+    adv, ret = oracle.gae(rew, g["values"][:, lo:hi], dn, g["last_values"][lo:hi], float(np.float32(GAMMA)),
+                          float(np.float32(LAMBDA)))
+    return adv, ret
+
+
+def _loss_minibatch(args):
+    """Worker: the oracle's loss for one minibatch (its sample indices into the rollout batch)."""
+    import oracle
+    rows, adv, ret = args
+    g = _SHARED
+    pi = g["pi"]
+    out, _ = oracle.ppo_loss(pi.new_logits[rows], g["actions"].reshape(-1)[rows], pi.old_logp[rows], adv, ret,
+                             pi.new_values[rows], None, rows.size)
+    return out[0]
+
+
+def cpu_baseline_all_cores(ms, policy_actions, values, last_values, pi, n, workers):
+    """The same bounded sample as cpu_baseline, with the single-threaded oracle run in `workers` forked
+    processes: envs are independent (env shards with GAE per shard), and so are the loss minibatches."""
+    import multiprocessing as mp
+
+    import oracle
+    _SHARED.update(ms=ms, actions=policy_actions, values=values, last_values=last_values, pi=pi)
+    t0 = time.perf_counter()
+    bounds = np.linspace(0, n, workers + 1).astype(int)
+    with mp.get_context("fork").Pool(workers) as pool:
+        parts = pool.map(_env_shard, [(int(a), int(z)) for a, z in zip(bounds[:-1], bounds[1:])])
+        adv = np.concatenate([p[0] for p in parts], axis=1)
+        ret = np.concatenate([p[1] for p in parts], axis=1)
+        na, _, _ = oracle.normalize(adv)
+        b = HORIZON * n
+        sel = (np.arange(HORIZON)[:, None] * N_ENVS + np.arange(n)[None, :]).reshape(-1)
+        perm = np.random.default_rng(5).permutation(b)
+        mb = b // MINIBATCHES
+        tasks = []
+        for m in range(MINIBATCHES):
+            k = perm[m * mb:(m + 1) * mb]
+            tasks.append((sel[k], na.reshape(-1)[k], ret.reshape(-1)[k]))
+        pool.map(_loss_minibatch, tasks)
+    dt = time.perf_counter() - t0
+    return b / dt, dt
+
+
 def calibration_copy(torch, dev):
     """One plain device-to-device copy of 1 GiB: the known byte count that scales the HBM counters."""
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -144,20 +207,70 @@ def cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n):
     return HORIZON * n / dt, dt
 
 
+def _pix_shard(lo_hi):
+    """Worker: the oracle's env step + pixel render for envs [lo, hi), then GAE over the shard."""
+    import oracle
+    lo, hi = lo_hi
+    g = _SHARED
+    n = hi - lo
+    env = oracle.OracleEnv(g["ms"].maps, g["ms"].ckpts, g["ms"].spawns, n, sprites=g["sprites"], env_offset=lo)
+    env.reset()
+    obs = np.empty((n, 4 * 84 * 84), np.uint8)
+    rew = np.empty((HORIZON, n), np.float32)
+    dn = np.empty((HORIZON, n), np.float32)
+    for t in range(HORIZON):
+        rew[t], dn[t] = env.step(g["actions"][t, lo:hi])
+        env.obs_pixels(obs)
+    adv, _ = oracle.gae(rew, g["values"][:, lo:hi], dn, g["last_values"][lo:hi], float(np.float32(GAMMA)),
+                        float(np.float32(LAMBDA)))
+    return adv
+
+
+def cpu_baseline_pixels_all_cores(ms, sprites, policy_actions, values, last_values, n, workers):
+    """cpu_baseline_pixels' sample in `workers` forked processes of the single-threaded oracle."""
+    import multiprocessing as mp
+
+    import oracle
+    _SHARED.update(ms=ms, sprites=sprites, actions=policy_actions, values=values, last_values=last_values)
+    t0 = time.perf_counter()
+    bounds = np.linspace(0, n, workers + 1).astype(int)
+    with mp.get_context("fork").Pool(workers) as pool:
+        parts = pool.map(_pix_shard, [(int(a), int(z)) for a, z in zip(bounds[:-1], bounds[1:])])
+    oracle.normalize(np.concatenate(parts, axis=1))
+    dt = time.perf_counter() - t0
+    return HORIZON * n / dt, dt
+
+
 def main_pixels(args):
-    import torch
+    from resident_rl_rollout_amd import inputs
 
-    from resident_rl_rollout_amd import binding, inputs
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    binding.lib()
     n = PIX_ENVS
     ms = inputs.make_mapset(range(100, 100 + N_MAPS), MAP_H, MAP_W)
     sprites = inputs.make_sprites(30)
     policy_actions = inputs.make_actions(22, HORIZON, n)
     values, last_values = inputs.make_values(23, HORIZON, n)
+    # CPU legs first: no fork after the GPU runtime is initialised
+    cpu = cpu_all = None
+    if not args.no_cpu_baseline:
+        n_s = min(args.cpu_envs, n)
+        rate, dt = cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n_s)
+        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} of the 16384 envs x 128 steps (env step + 4 x 84 x 84 pixel render), GAE + "
+                         f"normalisation over [128][{n_s}]; {dt:.1f} s single-threaded"}
+        workers = min(CPU_WORKERS, os.cpu_count() or 1)
+        rate, dt = cpu_baseline_pixels_all_cores(ms, sprites, policy_actions, values, last_values, n_s, workers)
+        cpu_all = {"value": rate, "unit": "env-steps/s", "cores": workers, "kind": "oracle",
+                   "sample": f"the same sample in {workers} processes of the single-threaded oracle (env shards); "
+                             f"{dt:.1f} s wall"}
+
+    import torch
+
+    from resident_rl_rollout_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
     env = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_PIXELS,
                       sprites=sprites, device=dev)
     # rollout buffer: one allocation of [actions T*N | obs T*N*28224 (u8) | rewards T*N | dones T*N]
@@ -210,13 +323,6 @@ def main_pixels(args):
     env_avg_s = float(env_ms.mean()) * 1e-3
     launch_bytes = n * PIX_BYTES_PER_ENV_STEP
     achieved = launch_bytes / env_avg_s / 1e9
-    cpu = None
-    if not args.no_cpu_baseline:
-        n_s = min(args.cpu_envs, n)
-        rate, dt = cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n_s)
-        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {n_s} of the 16384 envs x 128 steps (env step + 4 x 84 x 84 pixel render), GAE + "
-                         f"normalisation over [128][{n_s}]; {dt:.1f} s single-threaded"}
     out = {
         "metric": "env-steps/s incl. 84x84 u8 pixel obs write at 16384 envs",
         "value": args.steps * HORIZON * n / wall,
@@ -240,6 +346,7 @@ def main_pixels(args):
                      "avg_launch_us": env_avg_s * 1e6},
         "gae_us_in_rollout": float(gae_ms.mean()) * 1e3,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(out), flush=True)
 
@@ -253,21 +360,39 @@ def main():
         args.cpu_envs = 512 if args.workload == "pixels" else 16384
     if args.workload == "pixels":
         return main_pixels(args)
-    import torch
+    from resident_rl_rollout_amd import inputs
 
-    from resident_rl_rollout_amd import binding, inputs
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    binding.lib()
-
-    # ---- seeded inputs, made resident before timing ----
+    # ---- seeded inputs (host) ----
     ms = inputs.make_mapset(range(100, 100 + N_MAPS), MAP_H, MAP_W)
     b = HORIZON * N_ENVS
     pi = inputs.make_policy_inputs(20, b)
     values, last_values = inputs.make_values(21, HORIZON, N_ENVS)
     policy_actions = pi.actions.reshape(HORIZON, N_ENVS)
+
+    # The CPU legs run before this process first touches the GPU: the all-core leg forks workers, and a
+    # process whose GPU runtime is initialised must not fork them.
+    cpu = cpu_all = None
+    if not args.no_cpu_baseline:
+        n_s = min(args.cpu_envs, N_ENVS)
+        rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
+        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} of the 65536 envs x 128 steps (env step + tile obs), GAE + normalisation "
+                         f"over [128][{n_s}], loss over the sample's {HORIZON * n_s} samples in 16 minibatches; "
+                         f"{dt:.1f} s single-threaded"}
+        workers = min(CPU_WORKERS, os.cpu_count() or 1)
+        rate, dt = cpu_baseline_all_cores(ms, policy_actions, values, last_values, pi, n_s, workers)
+        cpu_all = {"value": rate, "unit": "env-steps/s", "cores": workers, "kind": "oracle",
+                   "sample": f"the same sample in {workers} processes of the single-threaded oracle: env shards, "
+                             f"GAE per shard, one process per loss minibatch; {dt:.1f} s wall"}
+
+    import torch
+
+    from resident_rl_rollout_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
 
     env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev)
     # rollout buffer: one allocation of [actions T*N | obs T*N*1397 | rewards T*N | dones T*N]
@@ -391,15 +516,6 @@ def main():
     loss_gbs = loss_bytes / loss_s / 1e9
     gl_gbs = (gae_bytes + loss_bytes) / (gae_s + loss_s) / 1e9
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        n_s = min(args.cpu_envs, N_ENVS)
-        rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
-        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {n_s} of the 65536 envs x 128 steps (env step + tile obs), GAE + normalisation "
-                         f"over [128][{n_s}], loss over the sample's {HORIZON * n_s} samples in 16 minibatches; "
-                         f"{dt:.1f} s single-threaded"}
-
     out = {
         "metric": "env-steps/s incl. obs write at 65536 envs; GAE+loss GB/s vs HBM peak",
         "value": value,
@@ -437,6 +553,7 @@ def main():
         "gae_loss_frac": gl_gbs / HBM_PEAK_GBS,
         "loss_check": loss_out[0].tolist(),
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(out), flush=True)
 
