@@ -294,13 +294,14 @@ def main_pixels(args):
         calibration_copy(torch, dev)
 
     def rollout(ev=None):
-        for t in range(HORIZON):
-            if ev is not None:
-                ev["env"][t][0].record()
-            env.step(actions[t], obs[t], rewards[t], dones[t])
-            if ev is not None:
-                ev["env"][t][1].record()
+        # one event pair around the 128 back-to-back env launches: events between launches would add
+        # their own barrier and timestamp packets to every step
         if ev is not None:
+            ev["env"][0].record()
+        for t in range(HORIZON):
+            env.step(actions[t], obs[t], rewards[t], dones[t])
+        if ev is not None:
+            ev["env"][1].record()
             ev["gae"][0].record()
         binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
         if ev is not None:
@@ -310,7 +311,7 @@ def main_pixels(args):
         rollout()
     torch.cuda.synchronize()
     mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    events = [{"env": [mk() for _ in range(HORIZON)], "gae": mk()} for _ in range(args.steps)]
+    events = [{"env": mk(), "gae": mk()} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -318,7 +319,7 @@ def main_pixels(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    env_ms = np.array([[s_.elapsed_time(e_) for s_, e_ in ev["env"]] for ev in events])
+    env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
     gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
     env_avg_s = float(env_ms.mean()) * 1e-3
     launch_bytes = n * PIX_BYTES_PER_ENV_STEP
@@ -425,13 +426,14 @@ def main():
         calibration_copy(torch, dev)
 
     def rollout(ev=None):
-        for t in range(HORIZON):
-            if ev is not None:
-                ev["env"][t][0].record()
-            env.step(actions[t], obs[t], rewards[t], dones[t])
-            if ev is not None:
-                ev["env"][t][1].record()
+        # one event pair around the 128 back-to-back env launches: events between launches would add
+        # their own barrier and timestamp packets to every step
         if ev is not None:
+            ev["env"][0].record()
+        for t in range(HORIZON):
+            env.step(actions[t], obs[t], rewards[t], dones[t])
+        if ev is not None:
+            ev["env"][1].record()
             ev["gae"][0].record()
         binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
         if ev is not None:
@@ -451,7 +453,7 @@ def main():
     torch.cuda.synchronize()
 
     mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    events = [{"env": [mk() for _ in range(HORIZON)], "gae": mk(), "loss": mk()} for _ in range(args.steps)]
+    events = [{"env": mk(), "gae": mk(), "loss": mk()} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -492,7 +494,7 @@ def main():
             iso[which].append(a.elapsed_time(z))
     del flush
 
-    env_ms = np.array([[s.elapsed_time(e) for s, e in ev["env"]] for ev in events])   # [K][T]
+    env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
     gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
     loss_ms = np.array([ev["loss"][0].elapsed_time(ev["loss"][1]) for ev in events])
     env_steps = args.steps * HORIZON * N_ENVS
