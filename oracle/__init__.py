@@ -19,13 +19,13 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-NF = 16            # canonical state fields per env
+NF = 17            # canonical state fields per env
 STACK = 4
 FRAME_DIMS = 15
 OBS_TILES = 31 * 43 + STACK * FRAME_DIMS + 4   # 1397
 PIX = 84
 STATE_FIELDS = ("x", "y", "vx", "vy", "facing", "freeze_ticks", "hook_ticks", "hook_held", "jump_held",
-                "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action")
+                "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action", "path")
 
 
 def build() -> str:
@@ -40,7 +40,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("num_envs", "env_offset", "num_maps", "map_h", "map_w", "num_ckpts", "frame_skip",
-                 "time_limit")]
+                 "time_limit", "reward_mode", "max_waypoints")]
 
 
 def _load():
@@ -54,7 +54,8 @@ def _load():
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     cfgp = ctypes.POINTER(_Cfg)
     lib.oracle_env_reset.argtypes = [cfgp, p, p, p, p]
-    lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p]
+    lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p, p, p]
+    lib.oracle_bfs_path.argtypes = [p, i32, i32, i32, i32, i32, i32, p, i32, p, p]
     lib.oracle_env_obs_tiles.argtypes = [cfgp, p, p, p, p, p, i64]
     lib.oracle_env_obs_pixels.argtypes = [cfgp, p, p, p, p]
     lib.oracle_gae.argtypes = [p, p, p, p, i32, i32, f64, f64, p, p]
@@ -64,7 +65,7 @@ def _load():
     lib.oracle_vtrace.argtypes = [p, p, p, p, p, i32, i32, f64, f64, f64, f64, f64, p, p]
     for fn in (lib.oracle_env_reset, lib.oracle_env_step, lib.oracle_env_obs_tiles,
                lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss,
-               lib.oracle_ppo_loss_grad, lib.oracle_vtrace):
+               lib.oracle_ppo_loss_grad, lib.oracle_vtrace, lib.oracle_bfs_path):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -83,13 +84,21 @@ class OracleEnv:
     f32[N][4][15] (newest first)."""
 
     def __init__(self, maps, ckpts, spawns, num_envs, frame_skip=3, time_limit=2000, sprites=None,
-                 env_offset=0):
+                 env_offset=0, reward_mode=0, waypoints=None, wp_lens=None):
         self.maps = _c(maps, np.uint8)
         self.ckpts = _c(ckpts, np.int32).reshape(self.maps.shape[0], -1, 2)
         self.spawns = _c(spawns, np.int32).reshape(self.maps.shape[0], 2)
         self.sprites = None if sprites is None else _c(sprites, np.uint8)
         m, h, w = self.maps.shape
-        self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit)
+        if reward_mode == 1:
+            self.waypoints = _c(waypoints, np.int32).reshape(m, -1, 2)
+            self.wp_lens = _c(wp_lens, np.int32).reshape(m)
+            assert (self.wp_lens >= 1).all() and (self.wp_lens <= self.waypoints.shape[1]).all()
+            kw = self.waypoints.shape[1]
+        else:
+            self.waypoints = self.wp_lens = None
+            kw = 0
+        self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit, reward_mode, kw)
         self.n = num_envs
         self.state = np.zeros((num_envs, NF), np.int32)
         self.stack = np.zeros((num_envs, STACK, FRAME_DIMS), np.float32)
@@ -107,8 +116,8 @@ class OracleEnv:
         rew = np.empty(self.n, np.float32)
         done = np.empty(self.n, np.float32)
         self._lib.oracle_env_step(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.ckpts),
-                                  _ptr(self.spawns), _ptr(actions), _ptr(self.state), _ptr(self.stack),
-                                  _ptr(rew), _ptr(done))
+                                  _ptr(self.spawns), _ptr(self.waypoints), _ptr(self.wp_lens), _ptr(actions),
+                                  _ptr(self.state), _ptr(self.stack), _ptr(rew), _ptr(done))
         return rew, done
 
     def obs_tiles(self, out=None):
@@ -127,6 +136,24 @@ class OracleEnv:
         self._lib.oracle_env_obs_pixels(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.sprites),
                                         _ptr(self.stack), _ptr(out))
         return out
+
+
+def bfs_path(grid, start, goal, max_len=None):
+    """The oracle's BFS tile path over one map grid u8[H][W] from start (col, row) to goal (col, row):
+    int32[L][2] of (col, row), or None when unreachable / blocked. Raises if longer than max_len."""
+    g = _c(grid, np.uint8)
+    h, w = g.shape
+    max_len = h * w if max_len is None else max_len
+    path = np.empty((max_len, 2), np.int32)
+    n = ctypes.c_int32()
+    scratch = np.empty(2 * h * w, np.int32)
+    rc = _load().oracle_bfs_path(_ptr(g), h, w, int(start[0]), int(start[1]), int(goal[0]), int(goal[1]),
+                                 _ptr(path), max_len, ctypes.byref(n), _ptr(scratch))
+    if rc == -1:
+        return None
+    if rc == -3:
+        raise ValueError("path longer than max_len")
+    return path[:n.value].copy()
 
 
 def gae(rewards, values, dones, last_values, gamma, lam):

@@ -49,6 +49,11 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 #define FREEZE_TICKS 30
 #define UNITS_CHECKPOINT 10240   /* +10 reward   (1 reward = 1024 units) */
 #define UNITS_FINISH 102400      /* +100 reward */
+/* Waypoint-path reward ([DDNET] "Reward Engineering", Version 2; readings): */
+#define WP_AHEAD 8               /* the nearest waypoint is searched at the high-water index and 8 past it */
+#define UNITS_WAYPOINT 256       /* progress: one tile of path = 256 units, V1's one unit per sub-unit */
+#define WP_GRACE 1024            /* the 128-unit (about 4 tile) grace zone, in sub-units */
+#define WP_PENALTY_SHIFT 4       /* beyond the grace zone: one unit per 16 sub-units of distance per tick */
 #define WIN_W 43            /* tile window: 43 columns ... */
 #define WIN_H 31            /* ... by 31 rows */
 #define WIN_CX 21           /* the player's tile sits at window column 21, row 15 */
@@ -61,7 +66,7 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 /* Canonical state layout: int32[N][NF] in this field order. */
 enum {
     F_X, F_Y, F_VX, F_VY, F_FACING, F_FREEZE, F_HOOK_TICKS, F_HOOK_HELD, F_JUMP_HELD, F_GROUNDED,
-    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, NF
+    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, F_PATH, NF
 };
 
 typedef struct {
@@ -69,12 +74,21 @@ typedef struct {
     int32_t env_offset;  /* global index of the first of them (env n plays map n mod num_maps) */
     int32_t num_maps, map_h, map_w, num_ckpts;
     int32_t frame_skip, time_limit;
+    int32_t reward_mode;    /* 0: checkpoint rewards (Version 1); 1: waypoint path (Version 2) */
+    int32_t max_waypoints;  /* row length of the waypoint table (reward_mode 1) */
 } oracle_cfg;
 
 typedef struct {
     int32_t x, y, vx, vy, facing, freeze, hook_ticks, hook_held, jump_held, grounded;
-    int32_t wall_l, wall_r, tick, next, best_x, last_action;
+    int32_t wall_l, wall_r, tick, next, best_x, last_action, path;
 } env_t;
+
+/* The waypoint path of every map: waypoints[m][k] = (col, row) of the k-th tile of map m's path,
+ * k < lens[m] <= max_waypoints. */
+typedef struct {
+    const int32_t *waypoints;
+    const int32_t *lens;
+} path_t;
 
 static void load_env(const int32_t *s, env_t *e)
 {
@@ -82,7 +96,7 @@ static void load_env(const int32_t *s, env_t *e)
     e->facing = s[F_FACING]; e->freeze = s[F_FREEZE]; e->hook_ticks = s[F_HOOK_TICKS];
     e->hook_held = s[F_HOOK_HELD]; e->jump_held = s[F_JUMP_HELD]; e->grounded = s[F_GROUNDED];
     e->wall_l = s[F_WALL_L]; e->wall_r = s[F_WALL_R]; e->tick = s[F_TICK]; e->next = s[F_NEXT];
-    e->best_x = s[F_BEST_X]; e->last_action = s[F_LAST_ACTION];
+    e->best_x = s[F_BEST_X]; e->last_action = s[F_LAST_ACTION]; e->path = s[F_PATH];
 }
 
 static void store_env(const env_t *e, int32_t *s)
@@ -91,7 +105,7 @@ static void store_env(const env_t *e, int32_t *s)
     s[F_FACING] = e->facing; s[F_FREEZE] = e->freeze; s[F_HOOK_TICKS] = e->hook_ticks;
     s[F_HOOK_HELD] = e->hook_held; s[F_JUMP_HELD] = e->jump_held; s[F_GROUNDED] = e->grounded;
     s[F_WALL_L] = e->wall_l; s[F_WALL_R] = e->wall_r; s[F_TICK] = e->tick; s[F_NEXT] = e->next;
-    s[F_BEST_X] = e->best_x; s[F_LAST_ACTION] = e->last_action;
+    s[F_BEST_X] = e->best_x; s[F_LAST_ACTION] = e->last_action; s[F_PATH] = e->path;
 }
 
 /* Mathematical floor of a / b for b > 0 (C's '/' truncates toward zero). */
@@ -161,6 +175,43 @@ static void make_frame(const env_t *e, float *f)
     f[14] = (float)e->last_action;
 }
 
+/* floor(sqrt(v)) for v >= 0, by the digit-by-digit (binary) method. */
+static int64_t isqrt64(int64_t v)
+{
+    uint64_t x = (uint64_t)v, r = 0, bit = (uint64_t)1 << 62;
+    while (bit > x) bit >>= 2;
+    while (bit != 0) {
+        if (x >= r + bit) { x -= r + bit; r = (r >> 1) + bit; }
+        else r >>= 1;
+        bit >>= 2;
+    }
+    return (int64_t)r;
+}
+
+/* Version 2 progress and distance terms of one tick ([DDNET] "Reward Engineering", Version 2): the
+ * waypoint nearest to the box centre among the high-water index and the WP_AHEAD after it (the lowest
+ * index on a tie); moving the high-water mark forward pays UNITS_WAYPOINT per waypoint (no backtrack
+ * penalty); a distance d beyond the grace zone costs (d - WP_GRACE) >> WP_PENALTY_SHIFT units. */
+static int32_t waypoint_units(const oracle_cfg *c, const path_t *pt, int m, env_t *e)
+{
+    const int32_t *wp = pt->waypoints + (size_t)m * c->max_waypoints * 2;
+    int32_t len = pt->lens[m];
+    int64_t cx = (int64_t)e->x + BOX / 2, cy = (int64_t)e->y + BOX / 2;
+    int32_t best = e->path;
+    int64_t best_d2 = -1;
+    for (int32_t k = e->path; k <= e->path + WP_AHEAD && k < len; ++k) {
+        int64_t dx = cx - ((int64_t)wp[2 * k] * TILE + TILE / 2);
+        int64_t dy = cy - ((int64_t)wp[2 * k + 1] * TILE + TILE / 2);
+        int64_t d2 = dx * dx + dy * dy;
+        if (best_d2 < 0 || d2 < best_d2) { best_d2 = d2; best = k; }
+    }
+    int32_t units = 0;
+    if (best > e->path) { units += (best - e->path) * UNITS_WAYPOINT; e->path = best; }
+    int64_t d = isqrt64(best_d2);
+    if (d > WP_GRACE) units -= (int32_t)((d - WP_GRACE) >> WP_PENALTY_SHIFT);
+    return units;
+}
+
 /* Move v toward target by at most acc. */
 static int32_t approach(int32_t v, int32_t target, int32_t acc)
 {
@@ -170,8 +221,8 @@ static int32_t approach(int32_t v, int32_t target, int32_t acc)
 }
 
 /* One physics tick (all integer). Adds the tick's reward units to *units; returns 1 on the finish. */
-static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts, int m,
-                        env_t *e, int dir, int jump, int hook, int32_t *units)
+static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts, const path_t *pt,
+                        int m, env_t *e, int dir, int jump, int hook, int32_t *units)
 {
     /* 1. a frozen player's input is ignored */
     if (e->freeze > 0) { dir = 0; jump = 0; hook = 0; }
@@ -236,23 +287,29 @@ static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t 
     e->hook_held = hook;
     e->jump_held = jump;
 
-    /* 10. progress reward: one unit per sub-unit past the high-water mark, no backtrack penalty */
-    if (e->x > e->best_x) { *units += e->x - e->best_x; e->best_x = e->x; }
+    /* 10. progress reward. Version 1: one unit per sub-unit past the high-water mark of x, no backtrack
+     * penalty. Version 2: the waypoint path's progress and distance terms. best_x is kept in both (it is
+     * an observation dim). */
+    if (c->reward_mode == 1) *units += waypoint_units(c, pt, m, e);
+    if (e->x > e->best_x) {
+        if (c->reward_mode == 0) *units += e->x - e->best_x;
+        e->best_x = e->x;
+    }
 
-    /* 11. checkpoints in order; passing the last one is the finish */
+    /* 11. checkpoints in order (+10 each in Version 1); passing the last one is the finish (+100) */
     int finished = 0;
     if (e->next < c->num_ckpts) {
         const int32_t *ck = ckpts + ((size_t)m * c->num_ckpts + e->next) * 2;
         if (floordiv(e->x + BOX / 2, TILE) >= ck[0]) {
-            *units += UNITS_CHECKPOINT;
+            if (c->reward_mode == 0) *units += UNITS_CHECKPOINT;
             e->next += 1;
             if (e->next == c->num_ckpts) { *units += UNITS_FINISH; finished = 1; }
         }
     }
 
-    /* 12. time: one unit per tick */
+    /* 12. time: one unit per tick in Version 1 (Version 2 lists no time penalty) */
     e->tick += 1;
-    *units -= 1;
+    if (c->reward_mode == 0) *units -= 1;
     return finished;
 }
 
@@ -280,9 +337,10 @@ int oracle_env_reset(const oracle_cfg *c, const int32_t *spawns, const uint8_t *
  * reward and done describe the episode that ended while the state and stack are the new episode's.
  * Otherwise the new frame is pushed onto the stack (newest first). */
 int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts,
-                    const int32_t *spawns, const int32_t *actions, int32_t *state, float *stack,
-                    float *rewards, float *dones)
+                    const int32_t *spawns, const int32_t *waypoints, const int32_t *wp_lens,
+                    const int32_t *actions, int32_t *state, float *stack, float *rewards, float *dones)
 {
+    const path_t pt = {waypoints, wp_lens};
     for (int n = 0; n < c->num_envs; ++n) {
         int m = map_of(c, n);
         env_t e;
@@ -294,7 +352,7 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
         int32_t units = 0;
         int terminated = 0, truncated = 0;
         for (int i = 0; i < c->frame_skip && !terminated && !truncated; ++i) {
-            terminated = physics_tick(c, maps, ckpts, m, &e, dir, jump, hook, &units);
+            terminated = physics_tick(c, maps, ckpts, &pt, m, &e, dir, jump, hook, &units);
             if (e.tick >= c->time_limit) truncated = 1;
         }
         e.last_action = a;
@@ -312,6 +370,51 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
             make_frame(&e, st);
         }
         store_env(&e, state + (size_t)n * NF);
+    }
+    return 0;
+}
+
+/* Tile path for the waypoint reward ([DDNET] "Reward Engineering", Version 2: a tile-level BFS
+ * pathfinder over the map). Breadth-first search over the tiles a box can pass through (not SOLID or
+ * PLATFORM, inside the map) with 4-neighbour moves tried in the order right, up, down, left; each tile
+ * keeps the first tile that reached it, so the path is the one shortest path this order picks. Writes
+ * (col, row) pairs from start to goal inclusive into path[max_len][2] and their count into *len.
+ * Returns 0, -1 when start or goal is blocked or outside the map or the goal is unreachable, -3 when
+ * the path needs more than max_len tiles. */
+int oracle_bfs_path(const uint8_t *map, int32_t h, int32_t w, int32_t c0, int32_t r0, int32_t c1, int32_t r1,
+                    int32_t *path, int32_t max_len, int32_t *len, int32_t *scratch)
+{
+    /* scratch: int32[2 * h * w] = queue, then the parent of every tile (-1 unvisited, -2 start) */
+    int32_t *queue = scratch, *parent = scratch + (size_t)h * w;
+#define PASSABLE(r, cc) ((r) >= 0 && (r) < h && (cc) >= 0 && (cc) < w && \
+                         map[(size_t)(r) * w + (cc)] != SOLID && map[(size_t)(r) * w + (cc)] != PLATFORM)
+    if (!PASSABLE(r0, c0) || !PASSABLE(r1, c1)) return -1;
+    for (size_t i = 0; i < (size_t)h * w; ++i) parent[i] = -1;
+    int32_t head = 0, tail = 0;
+    parent[(size_t)r0 * w + c0] = -2;
+    queue[tail++] = r0 * w + c0;
+    static const int dc[4] = {1, 0, 0, -1}, dr[4] = {0, -1, 1, 0};
+    while (head < tail) {
+        int32_t cur = queue[head++];
+        if (cur == r1 * w + c1) break;
+        int32_t r = cur / w, cc = cur % w;
+        for (int k = 0; k < 4; ++k) {
+            int32_t nr = r + dr[k], nc = cc + dc[k];
+            if (!PASSABLE(nr, nc) || parent[(size_t)nr * w + nc] != -1) continue;
+            parent[(size_t)nr * w + nc] = cur;
+            queue[tail++] = nr * w + nc;
+        }
+    }
+#undef PASSABLE
+    if (parent[(size_t)r1 * w + c1] == -1) return -1;
+    int32_t n = 0;
+    for (int32_t t = r1 * w + c1; t != -2; t = parent[t]) ++n;
+    if (n > max_len) return -3;
+    *len = n;
+    int32_t k = n - 1;
+    for (int32_t t = r1 * w + c1; t != -2; t = parent[t], --k) {
+        path[2 * k] = t % w;
+        path[2 * k + 1] = t / w;
     }
     return 0;
 }
