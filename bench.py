@@ -38,6 +38,7 @@ GAMMA, LAMBDA = 0.99, 0.95
 # current ring slot (5 words) and the two slots before it, the two extra words read and written, the new
 # slot, the reward and the done.
 ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
+ENV_BYTES_WAYPOINTS = 4 + 4   # the path index, read and written (the 0.5 MB waypoint table stays in cache)
 # The pixel step per env (two kernels): the physics reads the action, the current slot and the extras and
 # writes the new slot, the extras, the reward and the done; the render reads (x, y) of the four stacked
 # slots and writes the 4 x 84 x 84 frame bytes.
@@ -65,6 +66,9 @@ def parse():
     p.add_argument("--workload", choices=("rollout", "pixels"), default="rollout",
                    help="rollout: the tile-observation full rollout (the default bench line); pixels: 16384 envs "
                         "x 128 steps rendering 4 x 84 x 84 u8 frames, then GAE")
+    p.add_argument("--reward", choices=("checkpoints", "waypoints"), default="checkpoints",
+                   help="the rollout's reward: checkpoints (+10 each, x progress, time penalty) or the waypoint "
+                        "path (progress along each map's BFS tile path, grace-zone distance penalty)")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
@@ -90,6 +94,39 @@ def load_traffic(kernel_key):
     return rec["hbm_bytes_per_launch"]
 
 
+def path_goal(grid, col, row):
+    """A map's path goal: the finish checkpoint's tile, or the nearest tile above it in its column that a
+    box can pass (a platform may cover the checkpoint's tile; the finish itself is reached by column)."""
+    while row > 0 and grid[row, col] in (1, 2):
+        row -= 1
+    return col, row
+
+
+def path_ends(ms, m):
+    x, y = ms.spawns[m]
+    start = ((int(x) + 96) >> 8, (int(y) + 96) >> 8)
+    return start, path_goal(ms.maps[m], int(ms.ckpts[m, -1, 0]), int(ms.ckpts[m, -1, 1]))
+
+
+def pad_paths(paths):
+    kw = max(len(p) for p in paths)
+    table = np.zeros((len(paths), kw, 2), np.int32)
+    for m, p in enumerate(paths):
+        table[m, :len(p)] = p
+        table[m, len(p):] = p[-1]
+    return table, np.array([len(p) for p in paths], np.int32)
+
+
+def oracle_waypoints(ms):
+    """The oracle's own BFS paths, for the CPU leg."""
+    import oracle
+    return pad_paths([oracle.bfs_path(ms.maps[m], *path_ends(ms, m)) for m in range(ms.maps.shape[0])])
+
+
+def _env_kw():
+    return {k: _SHARED[k] for k in ("reward_mode", "waypoints", "wp_lens") if k in _SHARED}
+
+
 def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
     """The oracle as it stands, single-threaded, on the first n_sample envs of the same workload: 128
     steps with tile observations, GAE by its definition with normalisation, and the loss over the
@@ -97,7 +134,7 @@ def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
     import oracle
     n = n_sample
     t0 = time.perf_counter()
-    env = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n)
+    env = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, **_env_kw())
     env.reset()
     obs = np.empty((n, 1397), np.float32)
     rew = np.empty((HORIZON, n), np.float32)
@@ -128,7 +165,7 @@ def _env_shard(lo_hi):
     lo, hi = lo_hi
     g = _SHARED
     n = hi - lo
-    env = oracle.OracleEnv(g["ms"].maps, g["ms"].ckpts, g["ms"].spawns, n, env_offset=lo)
+    env = oracle.OracleEnv(g["ms"].maps, g["ms"].ckpts, g["ms"].spawns, n, env_offset=lo, **_env_kw())
     env.reset()
     obs = np.empty((n, 1397), np.float32)
     rew = np.empty((HORIZON, n), np.float32)
@@ -373,7 +410,11 @@ def main():
     # The CPU legs run before this process first touches the GPU: the all-core leg forks workers, and a
     # process whose GPU runtime is initialised must not fork them.
     cpu = cpu_all = None
+    waypoints = args.reward == "waypoints"
     if not args.no_cpu_baseline:
+        if waypoints:
+            table, lens = oracle_waypoints(ms)
+            _SHARED.update(reward_mode=1, waypoints=table, wp_lens=lens)
         n_s = min(args.cpu_envs, N_ENVS)
         rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
         cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
@@ -395,7 +436,11 @@ def main():
     torch.cuda.set_device(dev)
     binding.lib()
 
-    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev)
+    wp_kw = {}
+    if waypoints:   # the library's host BFS: each map's tile path from the spawn to the finish
+        table, lens = pad_paths([binding.waypoint_path(ms.maps[m], *path_ends(ms, m)) for m in range(N_MAPS)])
+        wp_kw = dict(reward_mode=binding.REWARD_WAYPOINTS, waypoints=table, wp_lens=lens)
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev, **wp_kw)
     # rollout buffer: one allocation of [actions T*N | obs T*N*1397 | rewards T*N | dones T*N]
     a_bytes = HORIZON * N_ENVS * 4
     o_bytes = HORIZON * N_ENVS * 1397 * 4
@@ -500,7 +545,7 @@ def main():
     env_steps = args.steps * HORIZON * N_ENVS
     value = env_steps / wall
 
-    env_launch_bytes = N_ENVS * ENV_BYTES_PER_ENV_STEP
+    env_launch_bytes = N_ENVS * (ENV_BYTES_PER_ENV_STEP + (ENV_BYTES_WAYPOINTS if waypoints else 0))
     env_avg_s = float(env_ms.mean()) * 1e-3
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
@@ -533,9 +578,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "full rollout: 65536 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
                                "tile obs (31x43 + 4x15 + 4) into a resident rollout buffer, GAE + whole-batch "
-                               "normalisation, PPO loss over 16 shuffled minibatches of 524288",
+                               "normalisation, PPO loss over 16 shuffled minibatches of 524288"
+                               + (", waypoint-path reward" if waypoints else ""),
                    "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES,
-                   "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss"},
+                   "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss",
+                   "reward": args.reward},
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic("env_step+obs_gather"),

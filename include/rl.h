@@ -55,8 +55,9 @@ enum {
 };
 
 enum { RL_OBS_TILES = 0, RL_OBS_PIXELS = 1 };
+enum { RL_REWARD_CHECKPOINTS = 0, RL_REWARD_WAYPOINTS = 1 };
 
-#define RL_STATE_FIELDS 16      /* canonical state fields per env, see rl_env_read_state */
+#define RL_STATE_FIELDS 17      /* canonical state fields per env, see rl_env_read_state */
 #define RL_OBS_TILES_SIZE 1397  /* f32 elements: 31*43 window + 4*15 frames + 4 checkpoint dims */
 #define RL_OBS_PIXELS_SIZE 28224 /* u8 elements: 4 frames of 84*84 */
 #define RL_MAX_FRAME_SKIP 5
@@ -75,6 +76,8 @@ typedef struct rl_env_config {
     int32_t obs_mode;    /* RL_OBS_TILES (f32 observations) or RL_OBS_PIXELS (u8 observations) */
     int64_t obs_stride;  /* elements from one env's observation to the next, >= the observation size;
                             tiles: a multiple of 1 f32, pixels: a multiple of 4 u8 */
+    int32_t reward_mode; /* RL_REWARD_CHECKPOINTS or RL_REWARD_WAYPOINTS (see rl_env_step) */
+    int32_t max_waypoints; /* waypoints per map path, 1 .. 2^20, with RL_REWARD_WAYPOINTS (else ignored) */
 } rl_env_config;
 
 typedef struct rl_env rl_env;   /* opaque host handle */
@@ -114,12 +117,36 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
  * env's observation to obs (device, [N][obs_stride] of the mode's element type). */
 int rl_env_reset(rl_env* env, const uint8_t* mask, void* obs, void* stream);
 
+/* The waypoint path of every map, for RL_REWARD_WAYPOINTS ("boesch.dev DDNet RL post", Reward Engineering,
+ * Version 2: progress along a path traced through the map, e.g. by rl_waypoint_path). Copies
+ *   waypoints  device int32[M][max_waypoints][2] (column, row) of the path's tiles, in order, and
+ *   lens       device int32[M] path length of each map (values outside 1 .. max_waypoints are clamped)
+ * into the state buffer on `stream`; the inputs may be freed once the stream has passed this call. Must
+ * be called before the first rl_env_step of a waypoint-reward env (the step fails otherwise); RL_EINVAL
+ * for a checkpoint-reward env. */
+int rl_env_set_waypoints(rl_env* env, const int32_t* waypoints, const int32_t* lens, void* stream);
+
+/* Host helper for the waypoint path: the tile-level BFS pathfinder of the same post. Breadth-first
+ * search over the tiles of one map (host u8[h][w]) that a box can pass (not solid or platform) with
+ * 4-neighbour moves tried in the order right, up, down, left, each tile keeping the first tile that
+ * reached it: the one shortest path from (c0, r0) to (c1, r1) that this order selects. Writes (column,
+ * row) pairs from start to goal inclusive to path (host int32[max_len][2]) and the count to *len.
+ * RL_EINVAL if an end is blocked or outside the map or the goal is unreachable; RL_ESIZE if the path
+ * needs more than max_len tiles. Uses about 8 h w bytes of host memory. */
+int rl_waypoint_path(const uint8_t* map, int32_t h, int32_t w, int32_t c0, int32_t r0, int32_t c1, int32_t r1,
+                     int32_t* path, int32_t max_len, int32_t* len);
+
 /* One decision of every env (the pages' step: read actions, advance, write observations / rewards /
  * terminals). For env n: decode actions[n] in [0, 12) as direction = a / 4 (none, left, right),
  * jump = bit 1, hook = bit 0 (other values act as 0); run up to frame_skip ticks, stopping after a
- * terminal tick; rewards[n] = the summed reward units times 2^-10 (progress past the best x, +10 per
- * checkpoint in order, +100 at the finish, -2^-10 per tick); dones[n] = 1 if the episode finished or hit
- * the time limit, else 0. A done env is reset in place: its reward and done describe the episode that
+ * terminal tick; rewards[n] = the summed reward units times 2^-10. RL_REWARD_CHECKPOINTS (Version 1 of
+ * the post's reward): progress past the best x (one unit per sub-unit), +10 per checkpoint in order, +100
+ * at the finish, -1 unit per tick. RL_REWARD_WAYPOINTS (Version 2): each tick the waypoint nearest to the
+ * box centre among the path's high-water index and the 8 after it (lowest index on a tie); moving the
+ * high-water index forward pays 256 units per waypoint, a distance d = floor(sqrt(squared distance in
+ * sub-units)) beyond 1024 (the 128-unit grace zone) costs (d - 1024) >> 4 units, +100 at the finish, no
+ * checkpoint bonus and no time penalty. dones[n] = 1 if the episode finished (passed its last checkpoint)
+ * or hit the time limit, else 0. A done env is reset in place: its reward and done describe the episode that
  * ended, its observation is the new episode's first. Observations (tiles: the 31x43 window around the
  * player's tile, the last 4 frames newest first, next checkpoint dx / dy, checkpoints passed, best x;
  * pixels: 4 frames of 84x84, newest first) go to obs.
@@ -129,7 +156,8 @@ int rl_env_step(rl_env* env, const int32_t* actions, void* obs, float* rewards, 
 
 /* Decode the state of every env into device int32[N][RL_STATE_FIELDS] with fields in the order
  * x, y, vx, vy, facing (+1/-1), freeze_ticks, hook_ticks, hook_held, jump_held, grounded, wall_left,
- * wall_right, tick, next_ckpt, best_x, last_action. */
+ * wall_right, tick, next_ckpt, best_x, last_action, path (the waypoint high-water index; 0 with
+ * checkpoint rewards). */
 int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
 
 /* The decision counter, whose value mod 4 selects the frame ring's newest slot. Saving the state

@@ -196,6 +196,7 @@ static int32_t waypoint_units(const oracle_cfg *c, const path_t *pt, int m, env_
 {
     const int32_t *wp = pt->waypoints + (size_t)m * c->max_waypoints * 2;
     int32_t len = pt->lens[m];
+    if (e->path > len - 1) e->path = len - 1;   /* a shorter table than the index reached */
     int64_t cx = (int64_t)e->x + BOX / 2, cy = (int64_t)e->y + BOX / 2;
     int32_t best = e->path;
     int64_t best_d2 = -1;

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librl.so")
 
 OBS_TILES, OBS_PIXELS = 0, 1
-STATE_FIELDS = 16
+STATE_FIELDS = 17
+REWARD_CHECKPOINTS, REWARD_WAYPOINTS = 0, 1
 OBS_TILES_SIZE = 1397
 OBS_PIXELS_SIZE = 28224
 
@@ -31,7 +32,8 @@ class RLError(RuntimeError):
 class EnvConfig(ctypes.Structure):
     _fields_ = [("num_envs", ctypes.c_int32), ("num_maps", ctypes.c_int32), ("map_h", ctypes.c_int32),
                 ("map_w", ctypes.c_int32), ("num_ckpts", ctypes.c_int32), ("frame_skip", ctypes.c_int32),
-                ("time_limit", ctypes.c_int32), ("obs_mode", ctypes.c_int32), ("obs_stride", ctypes.c_int64)]
+                ("time_limit", ctypes.c_int32), ("obs_mode", ctypes.c_int32), ("obs_stride", ctypes.c_int64),
+                ("reward_mode", ctypes.c_int32), ("max_waypoints", ctypes.c_int32)]
 
 
 # (name, restype, argtypes) of every symbol include/rl.h declares.
@@ -43,6 +45,8 @@ SIGNATURES = [
     ("rl_step_layout", ctypes.c_int, [_CFG, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     ("rl_env_create", ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P)]),
     ("rl_env_reset", ctypes.c_int, [_P, _P, _P, _P]),
+    ("rl_env_set_waypoints", ctypes.c_int, [_P, _P, _P, _P]),
+    ("rl_waypoint_path", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_I32)]),
     ("rl_env_step", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
     ("rl_env_get_step_counter", ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
@@ -124,7 +128,10 @@ class Env:
     """A batch of platformer envs over a device state buffer owned by this object."""
 
     def __init__(self, maps, ckpts, spawns, num_envs, *, frame_skip=3, time_limit=2000, obs_mode=OBS_TILES,
-                 sprites=None, obs_stride=None, device="cuda", stream=None):
+                 sprites=None, obs_stride=None, device="cuda", stream=None, reward_mode=REWARD_CHECKPOINTS,
+                 waypoints=None, wp_lens=None):
+        """reward_mode REWARD_WAYPOINTS needs waypoints int32[M][KW][2] and wp_lens int32[M] (copied to the
+        device and set on the env after creation)."""
         L = lib()
         self.device = torch.device(device)
         self.maps = _dev(maps, torch.uint8, self.device)
@@ -136,7 +143,12 @@ class Env:
         self.obs_mode = obs_mode
         size = OBS_TILES_SIZE if obs_mode == OBS_TILES else OBS_PIXELS_SIZE
         self.obs_stride = size if obs_stride is None else int(obs_stride)
-        self.cfg = EnvConfig(num_envs, m, h, w, ck.shape[1], frame_skip, time_limit, obs_mode, self.obs_stride)
+        kw = 0
+        if reward_mode == REWARD_WAYPOINTS:
+            wpt = _dev(waypoints, torch.int32, self.device).reshape(m, -1, 2)
+            kw = wpt.shape[1]
+        self.cfg = EnvConfig(num_envs, m, h, w, ck.shape[1], frame_skip, time_limit, obs_mode, self.obs_stride,
+                             reward_mode, kw)
         nbytes = ctypes.c_size_t()
         check(L.rl_env_state_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
         self.state = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
@@ -145,6 +157,10 @@ class Env:
         check(L.rl_env_create(ctypes.byref(self.cfg), dptr(self.maps), dptr(self.ckpts) if ck.numel() else None,
                               dptr(self.spawns), dptr(self.sprites), dptr(self.state), nbytes.value,
                               stream_ptr(stream), ctypes.byref(self._handle)))
+        if reward_mode == REWARD_WAYPOINTS:
+            self.waypoints = wpt
+            self.wp_lens = _dev(wp_lens, torch.int32, self.device).reshape(m)
+            check(L.rl_env_set_waypoints(self._handle, dptr(self.waypoints), dptr(self.wp_lens), stream_ptr(stream)))
 
     @property
     def obs_dtype(self):
@@ -194,6 +210,20 @@ class Env:
             self.close()
         except Exception:
             pass
+
+
+def waypoint_path(grid, start, goal, max_len=None):
+    """rl_waypoint_path on one host map grid u8[H][W]: the BFS tile path from start (col, row) to goal
+    (col, row) as int32[L][2] (col, row) pairs."""
+    import numpy as np
+    g = np.ascontiguousarray(grid, np.uint8)
+    h, w = g.shape
+    max_len = h * w if max_len is None else int(max_len)
+    out = np.empty((max_len, 2), np.int32)
+    n = ctypes.c_int32()
+    check(lib().rl_waypoint_path(g.ctypes.data_as(_P), h, w, int(start[0]), int(start[1]), int(goal[0]),
+                                 int(goal[1]), out.ctypes.data_as(_P), max_len, ctypes.byref(n)))
+    return out[:n.value].copy()
 
 
 def gae_workspace_bytes(t: int, n: int) -> int:

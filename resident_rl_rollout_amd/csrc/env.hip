@@ -20,6 +20,8 @@
 //   ckpt   int32[M][K][2], spawn int32[M][2], sprites u8[16][8][8].
 // Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
 
+#include <vector>
+
 #include "rl_internal.hpp"
 
 namespace {
@@ -37,6 +39,11 @@ constexpr int kFreezeTicks = 30;
 constexpr int kUnitsCkpt = 10240;     // +10 reward, 1024 units per reward
 constexpr int kUnitsFinish = 102400;  // +100 reward
 constexpr int kNumActions = 12;
+// waypoint-path reward ("Reward Engineering", Version 2; readings)
+constexpr int kWpAhead = 8;           // the nearest waypoint is searched at the high-water index and 8 past it
+constexpr int kUnitsWaypoint = 256;   // one tile of path = 256 units
+constexpr int kWpGrace = 1024;        // the 128-unit (about 4 tile) grace zone, sub-units
+constexpr int kWpPenaltyShift = 4;    // beyond it: one unit per 16 sub-units of distance per tick
 
 constexpr int kWinW = 43;
 constexpr int kWinH = 31;
@@ -69,7 +76,7 @@ constexpr int kHookShift = 16;    // 8 bits, 0..255
 constexpr int kActionShift = 24;  // 4 bits, 0..11
 
 struct Layout {
-    size_t slots, extra, map, ckpt, spawn, sprites, total;
+    size_t slots, extra, map, ckpt, spawn, sprites, waypoints, wplens, total;
     int64_t np, hp, wp;
 };
 
@@ -80,7 +87,9 @@ struct EnvDev {
     const int32_t* ckpt;
     const int32_t* spawn;
     const uint8_t* sprites;
-    int32_t n, m, h, w, k, fs, time_limit;
+    const int32_t* wpt;     // [M][kw][2] waypoint path (column, row), reward mode 1
+    const int32_t* wplen;   // [M]
+    int32_t n, m, h, w, k, fs, time_limit, kw;
     int64_t np, hp, wp;
 };
 
@@ -106,6 +115,10 @@ int validate_cfg(const rl_env_config* c)
                         (long long)size);
     if (c->obs_mode == RL_OBS_PIXELS && c->obs_stride % 4 != 0)
         return rl::fail(RL_EALIGN, "pixel obs_stride %lld is not a multiple of 4", (long long)c->obs_stride);
+    if (c->reward_mode != RL_REWARD_CHECKPOINTS && c->reward_mode != RL_REWARD_WAYPOINTS)
+        return rl::fail(RL_EINVAL, "reward_mode %d is neither checkpoints (0) nor waypoints (1)", c->reward_mode);
+    if (c->reward_mode == RL_REWARD_WAYPOINTS && (c->max_waypoints < 1 || c->max_waypoints > (1 << 20)))
+        return rl::fail(RL_EINVAL, "max_waypoints %d outside [1, 2^20]", c->max_waypoints);
     return RL_OK;
 }
 
@@ -119,7 +132,7 @@ Layout layout_of(const rl_env_config* c)
     l.slots = off;
     off = rl::round_up(off + sizeof(int32_t) * kStack * kSlotWords * l.np, 256);
     l.extra = off;
-    off = rl::round_up(off + sizeof(int32_t) * 2 * l.np, 256);
+    off = rl::round_up(off + sizeof(int32_t) * 3 * l.np, 256);
     l.map = off;
     off = rl::round_up(off + (size_t)c->num_maps * l.hp * l.wp, 256);
     l.ckpt = off;
@@ -128,6 +141,11 @@ Layout layout_of(const rl_env_config* c)
     off = rl::round_up(off + sizeof(int32_t) * 2 * (size_t)c->num_maps, 256);
     l.sprites = off;
     off = rl::round_up(off + 16 * 64, 256);
+    const size_t kw = c->reward_mode == RL_REWARD_WAYPOINTS ? (size_t)c->max_waypoints : 0;
+    l.waypoints = off;
+    off = rl::round_up(off + sizeof(int32_t) * 2 * kw * (size_t)c->num_maps, 256);
+    l.wplens = off;
+    off = rl::round_up(off + (kw ? sizeof(int32_t) * (size_t)c->num_maps : 0), 256);
     l.total = off;
     return l;
 }
@@ -217,6 +235,7 @@ __device__ __forceinline__ void write_spawn(const EnvDev& d, int n)
     }
     d.extra[n] = 0;
     d.extra[d.np + n] = x;
+    d.extra[2 * d.np + n] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_reset(EnvDev d, const uint8_t* __restrict__ mask)
@@ -288,11 +307,49 @@ struct Decision {
     bool done;
 };
 
-// One decision of env n from its current slot `cur` and extras: decode the action, run up to frame_skip
-// ticks, write the reward and done, and store the new state in ring slot head_new (or the spawn state in
-// all four slots after a terminal tick).
+// Reward mode 1's progress and distance terms of one tick: the waypoint nearest to the box centre among
+// the high-water index and the kWpAhead after it (the lowest index on a tie); moving the high-water index
+// forward pays kUnitsWaypoint per waypoint; a distance d = floor(sqrt(d2)) beyond the grace zone costs
+// (d - kWpGrace) >> kWpPenaltyShift units. The candidates are loaded unconditionally (indices clamped to
+// the path's end) so that the loads issue together; d2 is exact in int64, d is needed only past the zone.
+__device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_t x, int32_t y, int32_t& path)
+{
+    const int32_t len = clampi(d.wplen[m], 1, d.kw);
+    if (path > len - 1) path = len - 1;
+    const int2* row = reinterpret_cast<const int2*>(d.wpt) + (int64_t)m * d.kw;
+    int2 w[kWpAhead + 1];
+#pragma unroll
+    for (int j = 0; j <= kWpAhead; ++j) w[j] = row[min(path + j, len - 1)];
+    const int64_t cx = (int64_t)x + kHalfBox, cy = (int64_t)y + kHalfBox;
+    int32_t best = path;
+    int64_t best_d2 = 0;
+#pragma unroll
+    for (int j = 0; j <= kWpAhead; ++j) {
+        const int64_t dx = cx - ((int64_t)w[j].x * kTile + kTile / 2);
+        const int64_t dy = cy - ((int64_t)w[j].y * kTile + kTile / 2);
+        const int64_t d2 = dx * dx + dy * dy;
+        if (j == 0 || (path + j < len && d2 < best_d2)) {
+            best_d2 = d2;
+            best = path + j;
+        }
+    }
+    int32_t units = 0;
+    if (best > path) {
+        units += (best - path) * kUnitsWaypoint;
+        path = best;
+    }
+    if (best_d2 >= (int64_t)(kWpGrace + 1) * (kWpGrace + 1)) {
+        int64_t r = (int64_t)sqrt((double)best_d2);   // then corrected to the exact integer floor
+        while (r * r > best_d2) --r;
+        while ((r + 1) * (r + 1) <= best_d2) ++r;
+        units -= (int32_t)((r - kWpGrace) >> kWpPenaltyShift);
+    }
+    return units;
+}
+
+template <int RM>
 __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a, const SlotWords& cur, int32_t next,
-                                               int32_t best_x, float* __restrict__ rewards,
+                                               int32_t best_x, int32_t path, float* __restrict__ rewards,
                                                float* __restrict__ dones, int head_new)
 {
     const int m = n % d.m;
@@ -378,18 +435,23 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         hook_ticks = hook ? min(hook_ticks + 1, 255) : 0;
         hook_held = (uint32_t)hook;
         jump_held = (uint32_t)jump;
-        // 10. progress past the high-water mark
-        if (x > best_x) { units += x - best_x; best_x = x; }
-        // 11. checkpoints in order; the last one is the finish
+        // 10. progress: past the high-water mark of x (mode 0), or along the waypoint path (mode 1); best x
+        // is kept in both (it is an observation dim)
+        if constexpr (RM == 1) units += waypoint_units(d, m, x, y, path);
+        if (x > best_x) {
+            if constexpr (RM == 0) units += x - best_x;
+            best_x = x;
+        }
+        // 11. checkpoints in order (+10 each in mode 0); the last one is the finish
         if (next < d.k && ((x + kHalfBox) >> 8) >= ck_col) {
-            units += kUnitsCkpt;
+            if constexpr (RM == 0) units += kUnitsCkpt;
             next += 1;
             if (next == d.k) { units += kUnitsFinish; terminated = true; }
             else ck_col = ck[2 * next];
         }
-        // 12. time
+        // 12. time (a penalty in mode 0 only)
         tick += 1;
-        units -= 1;
+        if constexpr (RM == 0) units -= 1;
         if (tick >= d.time_limit) truncated = true;
     }
 
@@ -413,19 +475,22 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     slot_word(d, head_new, 4, n) = tick;
     d.extra[n] = next;
     d.extra[d.np + n] = best_x;
+    if constexpr (RM == 1) d.extra[2 * d.np + n] = path;
     return Decision{x, y, (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16)), (int32_t)new_misc, tick,
                     next, best_x, false};
 }
 
 // env_step alone (the pixel path renders in its own kernel): one lane per env, one-wave blocks so that a
 // small batch still spreads over every CU (the kernel is latency-bound: a few waves per CU at most).
+template <int RM>
 __global__ __launch_bounds__(64) void k_step(EnvDev d, const int32_t* __restrict__ actions,
                                               float* __restrict__ rewards, float* __restrict__ dones,
                                               int head_prev, int head_new)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= d.n) return;
-    env_decide(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n], rewards, dones, head_new);
+    env_decide<RM>(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n],
+                   RM == 1 ? d.extra[2 * d.np + n] : 0, rewards, dones, head_new);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -580,7 +645,7 @@ __device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int l
     }
 }
 
-template <int E>
+template <int E, int RM>
 __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
@@ -602,7 +667,8 @@ __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __r
         const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
         const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
         const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
-        const Decision s = env_decide(d, n, a, cur, next0, best0, rewards, dones, head_new);
+        const int32_t path0 = RM == 1 ? d.extra[2 * d.np + n] : 0;
+        const Decision s = env_decide<RM>(d, n, a, cur, next0, best0, path0, rewards, dones, head_new);
         float* t = tail[e];
         put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
         if (s.done) {
@@ -745,6 +811,7 @@ __global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restric
     o[12] = slot_word(d, head, 4, n);
     o[13] = d.extra[n];
     o[14] = d.extra[d.np + n];
+    o[16] = d.extra[2 * d.np + n];
     o[15] = (int32_t)((misc >> kActionShift) & 15u);
 }
 
@@ -755,6 +822,7 @@ struct rl_env {
     Layout lay;
     uint8_t* base;
     int64_t counter;
+    bool waypoints_set;
 };
 
 namespace {
@@ -768,6 +836,9 @@ EnvDev dev_of(const rl_env* e)
     d.ckpt = reinterpret_cast<const int32_t*>(e->base + e->lay.ckpt);
     d.spawn = reinterpret_cast<const int32_t*>(e->base + e->lay.spawn);
     d.sprites = e->base + e->lay.sprites;
+    d.wpt = reinterpret_cast<const int32_t*>(e->base + e->lay.waypoints);
+    d.wplen = reinterpret_cast<const int32_t*>(e->base + e->lay.wplens);
+    d.kw = e->cfg.reward_mode == RL_REWARD_WAYPOINTS ? e->cfg.max_waypoints : 0;
     d.n = e->cfg.num_envs;
     d.m = e->cfg.num_maps;
     d.h = e->cfg.map_h;
@@ -859,6 +930,7 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
     e->lay = lay;
     e->base = static_cast<uint8_t*>(state);
     e->counter = 0;
+    e->waypoints_set = false;
     hipStream_t st = rl::as_stream(stream);
     uint8_t* base = e->base;
 
@@ -911,22 +983,97 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
     if (!rl::aligned(actions, 4) || !rl::aligned(rewards, 4) || !rl::aligned(dones, 4))
         return rl::fail(RL_EALIGN, "actions / rewards / dones are not 4-byte aligned");
     if (int rc = check_obs_ptr(e, obs)) return rc;
+    const bool wp = e->cfg.reward_mode == RL_REWARD_WAYPOINTS;
+    if (wp && !e->waypoints_set) return rl::fail(RL_EINVAL, "waypoint rewards need rl_env_set_waypoints first");
     hipStream_t st = rl::as_stream(stream);
     const EnvDev d = dev_of(e);
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
         const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs);
-        hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs>), grid, dim3(256), 0, st, d, actions, rewards, dones,
-                           static_cast<float*>(obs), e->cfg.obs_stride, head_prev, head_new);
+        float* o = static_cast<float*>(obs);
+        if (wp)
+            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 1>), grid, dim3(256), 0, st, d, actions, rewards, dones, o,
+                               e->cfg.obs_stride, head_prev, head_new);
+        else
+            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 0>), grid, dim3(256), 0, st, d, actions, rewards, dones, o,
+                               e->cfg.obs_stride, head_prev, head_new);
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
         e->counter += 1;
         return RL_OK;
     }
-    hipLaunchKernelGGL(k_step, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
-                       head_new);
+    if (wp)
+        hipLaunchKernelGGL(k_step<1>, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
+                           head_new);
+    else
+        hipLaunchKernelGGL(k_step<0>, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
+                           head_new);
     if (int rc = rl::check_launch("env_step")) return rc;
     e->counter += 1;
     return launch_obs(e, obs, st, head_new);
+}
+
+int rl_env_set_waypoints(rl_env* e, const int32_t* waypoints, const int32_t* lens, void* stream)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (e->cfg.reward_mode != RL_REWARD_WAYPOINTS) return rl::fail(RL_EINVAL, "the env does not use waypoint rewards");
+    if (!waypoints || !lens) return rl::fail(RL_EINVAL, "waypoints and lens must be non-NULL");
+    if (!rl::aligned(waypoints, 4) || !rl::aligned(lens, 4))
+        return rl::fail(RL_EALIGN, "waypoints / lens are not 4-byte aligned");
+    hipStream_t st = rl::as_stream(stream);
+    const size_t m = (size_t)e->cfg.num_maps;
+    hipError_t he = hipMemcpyAsync(e->base + e->lay.waypoints, waypoints,
+                                   sizeof(int32_t) * 2 * (size_t)e->cfg.max_waypoints * m, hipMemcpyDeviceToDevice, st);
+    if (he == hipSuccess)
+        he = hipMemcpyAsync(e->base + e->lay.wplens, lens, sizeof(int32_t) * m, hipMemcpyDeviceToDevice, st);
+    if (he != hipSuccess) return rl::fail(RL_EHIP, "waypoint copy: %s", hipGetErrorString(he));
+    e->waypoints_set = true;
+    return RL_OK;
+}
+
+int rl_waypoint_path(const uint8_t* map, int32_t h, int32_t w, int32_t c0, int32_t r0, int32_t c1, int32_t r1,
+                     int32_t* path, int32_t max_len, int32_t* len)
+{
+    if (!map || !path || !len) return rl::fail(RL_EINVAL, "map, path and len must be non-NULL");
+    if (h < 1 || w < 1 || (int64_t)h * w > ((int64_t)1 << 30)) return rl::fail(RL_EINVAL, "map size %d x %d", h, w);
+    if (max_len < 1) return rl::fail(RL_EINVAL, "max_len %d < 1", max_len);
+    const int64_t cells = (int64_t)h * w;
+    auto open = [&](int64_t r, int64_t c) {
+        if (r < 0 || r >= h || c < 0 || c >= w) return false;
+        const uint8_t t = map[r * w + c];
+        return t != kSolid && t != kPlatform;
+    };
+    if (!open(r0, c0) || !open(r1, c1)) return rl::fail(RL_EINVAL, "start or goal is blocked or outside the map");
+    // from[i]: the tile that first reached tile i (row-major), -1 unvisited; the start points to itself
+    std::vector<int32_t> from((size_t)cells, -1), frontier;
+    frontier.reserve(1024);
+    const int32_t start = r0 * w + c0, goal = r1 * w + c1;
+    from[(size_t)start] = start;
+    frontier.push_back(start);
+    static const int step_c[4] = {1, 0, 0, -1}, step_r[4] = {0, -1, 1, 0};   // right, up, down, left
+    for (size_t head = 0; head < frontier.size() && from[(size_t)goal] < 0; ++head) {
+        const int32_t cur = frontier[head];
+        const int32_t r = cur / w, c = cur - r * w;
+        for (int k = 0; k < 4; ++k) {
+            const int32_t nr = r + step_r[k], nc = c + step_c[k];
+            if (!open(nr, nc)) continue;
+            const int32_t nxt = nr * w + nc;
+            if (from[(size_t)nxt] >= 0) continue;
+            from[(size_t)nxt] = cur;
+            frontier.push_back(nxt);
+        }
+    }
+    if (from[(size_t)goal] < 0) return rl::fail(RL_EINVAL, "goal unreachable from start");
+    int32_t n = 1;
+    for (int32_t t = goal; t != start; t = from[(size_t)t]) ++n;
+    if (n > max_len) return rl::fail(RL_ESIZE, "path needs %d tiles, max_len is %d", n, max_len);
+    int32_t k = n - 1;
+    for (int32_t t = goal;; t = from[(size_t)t], --k) {
+        path[2 * k] = t % w;
+        path[2 * k + 1] = t / w;
+        if (t == start) break;
+    }
+    *len = n;
+    return RL_OK;
 }
 
 int rl_env_read_state(const rl_env* e, int32_t* out, void* stream)

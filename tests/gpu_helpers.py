@@ -66,15 +66,44 @@ def assert_grad_close(dlogits, dvalues, g, adv, what, rel=1e-4, clip_eps=0.2, ed
     return int(ambiguous.sum())
 
 
+def path_goal(grid, col, row):
+    """The finish tile, or the nearest tile above it in its column that a box can pass (a platform may
+    cover the finish checkpoint's tile; the finish itself is reached by column)."""
+    while row > 0 and grid[row, col] in (1, 2):
+        row -= 1
+    return col, row
+
+
+def waypoint_table(ms: inputs.MapSet):
+    """Each map's BFS tile path (the oracle's) from the spawn's box-centre tile to its finish tile (see
+    path_goal), padded to the longest: (int32[M][KW][2], int32[M])."""
+    paths = []
+    for m in range(ms.maps.shape[0]):
+        x, y = ms.spawns[m]
+        start = ((int(x) + 96) >> 8, (int(y) + 96) >> 8)
+        goal = path_goal(ms.maps[m], int(ms.ckpts[m, -1, 0]), int(ms.ckpts[m, -1, 1]))
+        p = oracle.bfs_path(ms.maps[m], start, goal)
+        assert p is not None, f"map {m}: finish unreachable"
+        paths.append(p)
+    kw = max(len(p) for p in paths)
+    table = np.zeros((len(paths), kw, 2), np.int32)
+    for m, p in enumerate(paths):
+        table[m, :len(p)] = p
+        table[m, len(p):] = p[-1]
+    return table, np.array([len(p) for p in paths], np.int32)
+
+
 class PairedEnvs:
     """The same env batch on the GPU (through the C ABI) and in the oracle, stepped with the same actions."""
 
     def __init__(self, ms: inputs.MapSet, n, *, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_TILES,
-                 sprites=None, obs_stride=None):
+                 sprites=None, obs_stride=None, reward_mode=0, waypoints=None, wp_lens=None):
         self.gpu = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip, time_limit=time_limit,
-                               obs_mode=obs_mode, sprites=sprites, obs_stride=obs_stride)
+                               obs_mode=obs_mode, sprites=sprites, obs_stride=obs_stride, reward_mode=reward_mode,
+                               waypoints=waypoints, wp_lens=wp_lens)
         self.ora = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip,
-                                    time_limit=time_limit, sprites=sprites)
+                                    time_limit=time_limit, sprites=sprites, reward_mode=reward_mode,
+                                    waypoints=waypoints, wp_lens=wp_lens)
         self.ora.reset()
         self.n = n
         self.obs_mode = obs_mode

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(**kw):
     base = dict(num_envs=64, num_maps=1, map_h=32, map_w=128, num_ckpts=7, frame_skip=3, time_limit=2000,
-                obs_mode=0, obs_stride=1397)
+                obs_mode=0, obs_stride=1397, reward_mode=0, max_waypoints=0)
     base.update(kw)
     return binding.EnvConfig(*[base[k] for k, _ in binding.EnvConfig._fields_])
 
@@ -42,6 +42,9 @@ def _cfg(**kw):
     (dict(map_w=70000), -1, "map_w"), (dict(num_ckpts=-1), -1, "num_ckpts"), (dict(frame_skip=0), -1, "frame_skip"),
     (dict(frame_skip=6), -1, "frame_skip"), (dict(time_limit=0), -1, "time_limit"), (dict(obs_mode=2), -1, "obs_mode"),
     (dict(obs_stride=1396), -1, "obs_stride"), (dict(obs_mode=1, obs_stride=28226), -2, "multiple of 4"),
+    (dict(num_envs=(1 << 24) + 1), -1, "num_envs"), (dict(reward_mode=2), -1, "reward_mode"),
+    (dict(reward_mode=1, max_waypoints=0), -1, "max_waypoints"),
+    (dict(reward_mode=1, max_waypoints=(1 << 20) + 1), -1, "max_waypoints"),
 ])
 def test_config_validation(kw, code, msg):
     lib = binding.lib()
@@ -76,6 +79,7 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_env_create(ctypes.byref(_cfg(obs_mode=1, obs_stride=28224)), fake, fake, fake, None, fake, 1 << 30,
                              None, ctypes.byref(out)) == -1
     assert lib.rl_env_step(None, fake, fake, fake, fake, None) == -1
+    assert lib.rl_env_set_waypoints(None, fake, fake, None) == -1
     assert lib.rl_env_reset(None, None, None, None) == -1
     # rl_gae: sizes, NULLs, enum, workspace
     assert lib.rl_gae(fake, fake, fake, fake, 0, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
@@ -113,3 +117,27 @@ def test_entry_points_reject_before_any_hip_call():
     need = ctypes.c_size_t()
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
     assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128
+
+
+def test_waypoint_path_host_bfs_matches_the_oracle():
+    # the library's BFS (host C++) and the oracle's, written apart, pick the same unique path
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(4)
+    for trial in range(8):
+        g = (rng.random((20, 40)) < 0.3).astype(np.uint8) * rng.integers(1, 4, (20, 40)).astype(np.uint8)
+        g[5, 0] = g[14, 39] = 0
+        ref = oracle.bfs_path(g, (0, 5), (39, 14))
+        if ref is None:
+            with pytest.raises(binding.RLError, match="unreachable"):
+                binding.waypoint_path(g, (0, 5), (39, 14))
+        else:
+            np.testing.assert_array_equal(binding.waypoint_path(g, (0, 5), (39, 14)), ref)
+    g = np.zeros((3, 3), np.uint8)
+    assert binding.waypoint_path(g, (0, 0), (2, 2)).tolist() == [[0, 0], [1, 0], [2, 0], [2, 1], [2, 2]]
+    with pytest.raises(binding.RLError, match="max_len"):
+        binding.waypoint_path(g, (0, 0), (2, 2), max_len=4)
+    g[1, 1] = 1
+    with pytest.raises(binding.RLError, match="blocked"):
+        binding.waypoint_path(g, (1, 1), (2, 2))
