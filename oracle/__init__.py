@@ -19,13 +19,15 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-NF = 17            # canonical state fields per env
+NF = 18            # canonical state fields per env
+RESPAWN_BUF = 64   # outcomes in each map's respawn buffer
 STACK = 4
 FRAME_DIMS = 15
 OBS_TILES = 31 * 43 + STACK * FRAME_DIMS + 4   # 1397
 PIX = 84
 STATE_FIELDS = ("x", "y", "vx", "vy", "facing", "freeze_ticks", "hook_ticks", "hook_held", "jump_held",
-                "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action", "path")
+                "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action", "path",
+                "from_start")
 
 
 def build() -> str:
@@ -40,7 +42,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("num_envs", "env_offset", "num_maps", "map_h", "map_w", "num_ckpts", "frame_skip",
-                 "time_limit", "reward_mode", "max_waypoints")]
+                 "time_limit", "reward_mode", "max_waypoints", "respawn_mode")]
 
 
 def _load():
@@ -54,8 +56,11 @@ def _load():
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     cfgp = ctypes.POINTER(_Cfg)
     lib.oracle_env_reset.argtypes = [cfgp, p, p, p, p]
-    lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p, p, p]
+    lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p, p, p, ctypes.c_uint64, i64, p,
+                                    p, p, p, p, p]
     lib.oracle_bfs_path.argtypes = [p, i32, i32, i32, i32, i32, i32, p, i32, p, p]
+    lib.oracle_respawn_draw.argtypes = [ctypes.c_uint64, i64, i32, i32]
+    lib.oracle_respawn_draw.restype = ctypes.c_uint64
     lib.oracle_env_obs_tiles.argtypes = [cfgp, p, p, p, p, p, i64]
     lib.oracle_env_obs_pixels.argtypes = [cfgp, p, p, p, p]
     lib.oracle_gae.argtypes = [p, p, p, p, i32, i32, f64, f64, p, p]
@@ -84,7 +89,8 @@ class OracleEnv:
     f32[N][4][15] (newest first)."""
 
     def __init__(self, maps, ckpts, spawns, num_envs, frame_skip=3, time_limit=2000, sprites=None,
-                 env_offset=0, reward_mode=0, waypoints=None, wp_lens=None):
+                 env_offset=0, reward_mode=0, waypoints=None, wp_lens=None, respawn_mode=0, ckpt_spawns=None,
+                 respawn_seed=0):
         self.maps = _c(maps, np.uint8)
         self.ckpts = _c(ckpts, np.int32).reshape(self.maps.shape[0], -1, 2)
         self.spawns = _c(spawns, np.int32).reshape(self.maps.shape[0], 2)
@@ -98,7 +104,18 @@ class OracleEnv:
         else:
             self.waypoints = self.wp_lens = None
             kw = 0
-        self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit, reward_mode, kw)
+        self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit, reward_mode, kw,
+                        respawn_mode)
+        # adaptive respawn: each map's outcome ring, fill, write position and frontier; the decision counter
+        self.ckpt_spawns = None if ckpt_spawns is None else _c(ckpt_spawns, np.int32).reshape(m, -1, 2)
+        assert respawn_mode == 0 or (self.ckpt_spawns is not None and self.ckpts.shape[1] >= 1)
+        self.ring = np.zeros((m, RESPAWN_BUF), np.int32)
+        self.fill = np.zeros(m, np.int32)
+        self.head = np.zeros(m, np.int32)
+        self.frontier = np.zeros(m, np.int32)
+        self.respawn_seed = int(respawn_seed) & (2 ** 64 - 1)
+        self.counter = 0
+        self.ended = np.zeros(num_envs, np.int32)
         self.n = num_envs
         self.state = np.zeros((num_envs, NF), np.int32)
         self.stack = np.zeros((num_envs, STACK, FRAME_DIMS), np.float32)
@@ -116,8 +133,11 @@ class OracleEnv:
         rew = np.empty(self.n, np.float32)
         done = np.empty(self.n, np.float32)
         self._lib.oracle_env_step(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.ckpts),
-                                  _ptr(self.spawns), _ptr(self.waypoints), _ptr(self.wp_lens), _ptr(actions),
-                                  _ptr(self.state), _ptr(self.stack), _ptr(rew), _ptr(done))
+                                  _ptr(self.spawns), _ptr(self.waypoints), _ptr(self.wp_lens),
+                                  _ptr(self.ckpt_spawns), _ptr(self.ring), _ptr(self.fill), _ptr(self.head),
+                                  _ptr(self.frontier), self.respawn_seed, self.counter, _ptr(self.ended),
+                                  _ptr(actions), _ptr(self.state), _ptr(self.stack), _ptr(rew), _ptr(done))
+        self.counter += 1
         return rew, done
 
     def obs_tiles(self, out=None):
@@ -241,3 +261,8 @@ def vtrace(rewards, values, dones, last_values, log_rhos, gamma, lam=1.0, rho_ba
     _load().oracle_vtrace(_ptr(r), _ptr(v), _ptr(d), _ptr(lv), _ptr(lr), t, n, float(gamma), float(lam),
                           float(rho_bar), float(c_bar), float(pg_rho_bar), _ptr(vs), _ptr(pg))
     return vs, pg
+
+
+def respawn_draw(seed, counter, n, i):
+    """The oracle's i-th respawn draw of global env n at decision `counter` (uint64)."""
+    return int(_load().oracle_respawn_draw(int(seed) & (2 ** 64 - 1), int(counter), int(n), int(i)))

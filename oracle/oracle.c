@@ -54,6 +54,9 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 #define UNITS_WAYPOINT 256       /* progress: one tile of path = 256 units, V1's one unit per sub-unit */
 #define WP_GRACE 1024            /* the 128-unit (about 4 tile) grace zone, in sub-units */
 #define WP_PENALTY_SHIFT 4       /* beyond the grace zone: one unit per 16 sub-units of distance per tick */
+/* Adaptive checkpoint respawn ([DDNET] "Checkpoint Respawning"; readings): */
+#define RESPAWN_BUF 64           /* the rolling buffer of episode outcomes, per map */
+#define RESPAWN_START_U32 858993459u  /* a draw below this (20% of 2^32) starts from the beginning */
 #define WIN_W 43            /* tile window: 43 columns ... */
 #define WIN_H 31            /* ... by 31 rows */
 #define WIN_CX 21           /* the player's tile sits at window column 21, row 15 */
@@ -66,7 +69,7 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 /* Canonical state layout: int32[N][NF] in this field order. */
 enum {
     F_X, F_Y, F_VX, F_VY, F_FACING, F_FREEZE, F_HOOK_TICKS, F_HOOK_HELD, F_JUMP_HELD, F_GROUNDED,
-    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, F_PATH, NF
+    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, F_PATH, F_FROM_START, NF
 };
 
 typedef struct {
@@ -76,12 +79,24 @@ typedef struct {
     int32_t frame_skip, time_limit;
     int32_t reward_mode;    /* 0: checkpoint rewards (Version 1); 1: waypoint path (Version 2) */
     int32_t max_waypoints;  /* row length of the waypoint table (reward_mode 1) */
+    int32_t respawn_mode;   /* 0: every episode starts at the spawn; 1: adaptive checkpoint respawn */
 } oracle_cfg;
 
 typedef struct {
     int32_t x, y, vx, vy, facing, freeze, hook_ticks, hook_held, jump_held, grounded;
-    int32_t wall_l, wall_r, tick, next, best_x, last_action, path;
+    int32_t wall_l, wall_r, tick, next, best_x, last_action, path, from_start;
 } env_t;
+
+/* Adaptive respawn state of every map: the ring of the last RESPAWN_BUF episode outcomes (checkpoints
+ * passed when the episode ended), how many are filled, the next write position, and the frontier (the
+ * most checkpoints an episode that started at the spawn has passed). */
+typedef struct {
+    const int32_t *ckpt_spawns;   /* [M][K][2] (x, y) standing spot at each checkpoint */
+    int32_t *ring;                /* [M][RESPAWN_BUF] */
+    int32_t *fill, *head, *frontier;   /* [M] */
+    uint64_t seed;
+    int64_t counter;              /* the decision counter of this step */
+} respawn_t;
 
 /* The waypoint path of every map: waypoints[m][k] = (col, row) of the k-th tile of map m's path,
  * k < lens[m] <= max_waypoints. */
@@ -97,6 +112,7 @@ static void load_env(const int32_t *s, env_t *e)
     e->hook_held = s[F_HOOK_HELD]; e->jump_held = s[F_JUMP_HELD]; e->grounded = s[F_GROUNDED];
     e->wall_l = s[F_WALL_L]; e->wall_r = s[F_WALL_R]; e->tick = s[F_TICK]; e->next = s[F_NEXT];
     e->best_x = s[F_BEST_X]; e->last_action = s[F_LAST_ACTION]; e->path = s[F_PATH];
+    e->from_start = s[F_FROM_START];
 }
 
 static void store_env(const env_t *e, int32_t *s)
@@ -106,6 +122,7 @@ static void store_env(const env_t *e, int32_t *s)
     s[F_HOOK_HELD] = e->hook_held; s[F_JUMP_HELD] = e->jump_held; s[F_GROUNDED] = e->grounded;
     s[F_WALL_L] = e->wall_l; s[F_WALL_R] = e->wall_r; s[F_TICK] = e->tick; s[F_NEXT] = e->next;
     s[F_BEST_X] = e->best_x; s[F_LAST_ACTION] = e->last_action; s[F_PATH] = e->path;
+    s[F_FROM_START] = e->from_start;
 }
 
 /* Mathematical floor of a / b for b > 0 (C's '/' truncates toward zero). */
@@ -152,6 +169,79 @@ static void spawn_env(const int32_t *spawns, int m, env_t *e)
     e->facing = 1;
     e->grounded = 1;
     e->best_x = e->x;
+    e->from_start = 1;
+}
+
+/* SplitMix64's output function (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", 2014). */
+static uint64_t mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+#define GOLDEN_GAMMA 0x9E3779B97F4A7C15ull
+
+/* The i-th draw (i = 1, 2) of global env n at decision `counter`: the i-th SplitMix64 output from the
+ * state seed + 2 * GOLDEN_GAMMA * (counter * 2^24 + n), i.e. mix64(state + i * GOLDEN_GAMMA). */
+static uint64_t respawn_draw(uint64_t seed, int64_t counter, int32_t n, int i)
+{
+    uint64_t key = (uint64_t)counter * ((uint64_t)1 << 24) + (uint64_t)n;
+    return mix64(seed + 2 * GOLDEN_GAMMA * key + (uint64_t)i * GOLDEN_GAMMA);
+}
+
+/* The draw above, for the tests. */
+uint64_t oracle_respawn_draw(uint64_t seed, int64_t counter, int32_t n, int32_t i)
+{
+    return respawn_draw(seed, counter, n, i);
+}
+
+/* The checkpoint an ended episode of global env n on map m restarts at (0 = the spawn), drawn from the
+ * map's outcome buffer as it stood at the start of the step ([DDNET] "Checkpoint Respawning"): 20% of
+ * resets, and every reset while the buffer is empty, start at the spawn; otherwise one entry of the top
+ * quarter of the buffer (the entries >= the highest outcome v that at least max(1, fill / 4) entries
+ * reach) is taken uniformly, capped at the frontier and at the last checkpoint before the finish. */
+static int32_t respawn_choice(const oracle_cfg *c, const respawn_t *rs, int m, int32_t n)
+{
+    int32_t fill = rs->fill[m];
+    if (fill == 0) return 0;
+    uint64_t u1 = respawn_draw(rs->seed, rs->counter, n, 1);
+    if ((uint32_t)(u1 >> 32) < RESPAWN_START_U32) return 0;
+    const int32_t *ring = rs->ring + (size_t)m * RESPAWN_BUF;
+    int32_t q = fill / 4 > 0 ? fill / 4 : 1;
+    int32_t cand = 0, thr = 0;
+    for (int32_t v = c->num_ckpts; v >= 0; --v) {
+        for (int32_t i = 0; i < fill; ++i) if (ring[i] == v) ++cand;
+        if (cand >= q) { thr = v; break; }
+    }
+    uint64_t u2 = respawn_draw(rs->seed, rs->counter, n, 2);
+    int32_t pick = (int32_t)((u2 >> 32) % (uint64_t)cand);
+    int32_t chosen = thr;
+    for (int32_t v = c->num_ckpts; v >= thr; --v) {
+        int32_t cv = 0;
+        for (int32_t i = 0; i < fill; ++i) if (ring[i] == v) ++cv;
+        if (pick < cv) { chosen = v; break; }
+        pick -= cv;
+    }
+    int32_t k = chosen < rs->frontier[m] ? chosen : rs->frontier[m];
+    if (k > c->num_ckpts - 1) k = c->num_ckpts - 1;
+    return k > 0 ? k : 0;
+}
+
+/* Start a new episode of map m at checkpoint k: the spawn for k = 0, else the standing spot of
+ * checkpoint k - 1 with k checkpoints counted as passed. */
+static void spawn_at(const oracle_cfg *c, const int32_t *spawns, const respawn_t *rs, int m, int32_t k,
+                     env_t *e)
+{
+    spawn_env(spawns, m, e);
+    if (k > 0) {
+        const int32_t *p = rs->ckpt_spawns + ((size_t)m * c->num_ckpts + (k - 1)) * 2;
+        e->x = p[0];
+        e->y = p[1];
+        e->best_x = e->x;
+        e->next = k;
+        e->from_start = 0;
+    }
 }
 
 /* The 15-dim frame of a state ("What the agent sees and does": position, velocity, hook state,
@@ -339,9 +429,12 @@ int oracle_env_reset(const oracle_cfg *c, const int32_t *spawns, const uint8_t *
  * Otherwise the new frame is pushed onto the stack (newest first). */
 int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts,
                     const int32_t *spawns, const int32_t *waypoints, const int32_t *wp_lens,
+                    const int32_t *ckpt_spawns, int32_t *ring, int32_t *fill, int32_t *head, int32_t *frontier,
+                    uint64_t seed, int64_t counter, int32_t *ended,
                     const int32_t *actions, int32_t *state, float *stack, float *rewards, float *dones)
 {
     const path_t pt = {waypoints, wp_lens};
+    const respawn_t rs = {ckpt_spawns, ring, fill, head, frontier, seed, counter};
     for (int n = 0; n < c->num_envs; ++n) {
         int m = map_of(c, n);
         env_t e;
@@ -361,8 +454,13 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
         dones[n] = (terminated || truncated) ? 1.0f : 0.0f;
 
         float *st = stack + (size_t)n * STACK * FRAME_DIMS;
+        if (ended) ended[n] = -1;
         if (terminated || truncated) {
-            spawn_env(spawns, m, &e);
+            /* the outcome for the respawn buffer: checkpoints passed, and whether the episode began at
+             * the spawn; the next episode starts from the buffer as it stood at the start of the step */
+            if (ended) ended[n] = e.next | (e.from_start ? (int32_t)1 << 30 : 0);
+            int32_t k = c->respawn_mode == 1 ? respawn_choice(c, &rs, m, c->env_offset + n) : 0;
+            spawn_at(c, spawns, &rs, m, k, &e);
             float f[FRAME_DIMS];
             make_frame(&e, f);
             for (int k = 0; k < STACK; ++k) memcpy(st + k * FRAME_DIMS, f, sizeof f);
@@ -372,6 +470,18 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
         }
         store_env(&e, state + (size_t)n * NF);
     }
+    /* after every env has stepped: the ended episodes' outcomes enter their map's ring in env order,
+     * and those that began at the spawn raise the frontier */
+    if (c->respawn_mode == 1)
+        for (int n = 0; n < c->num_envs; ++n) {
+            if (ended[n] < 0) continue;
+            int m = map_of(c, n);
+            int32_t outcome = ended[n] & (((int32_t)1 << 30) - 1);
+            ring[(size_t)m * RESPAWN_BUF + head[m]] = outcome;
+            head[m] = (head[m] + 1) % RESPAWN_BUF;
+            if (fill[m] < RESPAWN_BUF) fill[m] += 1;
+            if ((ended[n] >> 30) & 1 && outcome > frontier[m]) frontier[m] = outcome;
+        }
     return 0;
 }
 

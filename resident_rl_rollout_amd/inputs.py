@@ -28,6 +28,7 @@ class MapSet:
     maps: np.ndarray      # u8[M][H][W], row 0 at the top
     ckpts: np.ndarray     # int32[M][K][2] = (col, row)
     spawns: np.ndarray    # int32[M][2]    = (x, y) in sub-units
+    ckpt_spawns: np.ndarray = None   # int32[M][K][2] = (x, y) standing spot at each checkpoint
 
     @property
     def num_maps(self) -> int:
@@ -74,16 +75,26 @@ def make_mapset(seeds, h: int, w: int) -> MapSet:
     """Maps for the given seeds, with checkpoint k at column 16(k+1) on the row just above the floor
     (K = (w-1)//16 per map) and the spawn standing on the floor at column 1."""
     k = (w - 1) // 16
-    maps, ckpts, spawns = [], [], []
+    maps, ckpts, spawns, stands = [], [], [], []
     for s in seeds:
         tiles, heights = make_map(int(s), h, w)
         maps.append(tiles)
         cols = 16 * (np.arange(k) + 1)
         ckpts.append(np.stack([cols, h - heights[cols] - 1], axis=1))
         spawns.append([256, (h - int(heights[1])) * 256 - 192])
+        # standing spot at each checkpoint: the box centred in the checkpoint's column, on the floor or
+        # on the platform stack that covers it (tile codes 1 and 2 block)
+        st = []
+        for c in cols:
+            r = h - int(heights[c]) - 1
+            while r > 0 and tiles[r, c] in (1, 2):
+                r -= 1
+            st.append([int(c) * 256 + 32, (r + 1) * 256 - 192])
+        stands.append(st)
     return MapSet(np.ascontiguousarray(np.stack(maps)).astype(np.uint8),
                   np.asarray(ckpts, dtype=np.int32).reshape(len(seeds), k, 2),
-                  np.asarray(spawns, dtype=np.int32))
+                  np.asarray(spawns, dtype=np.int32),
+                  np.asarray(stands, dtype=np.int32).reshape(len(seeds), k, 2))
 
 
 def make_sprites(seed: int = 30) -> np.ndarray:
