@@ -39,6 +39,7 @@ GAMMA, LAMBDA = 0.99, 0.95
 # slot, the reward and the done.
 ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
 ENV_BYTES_WAYPOINTS = 4 + 4   # the path index, read and written (the 0.5 MB waypoint table stays in cache)
+ENV_BYTES_RESPAWN = 4 + 4 + 4  # the from-start flag read, the step's outcome written and read back by the append
 # The pixel step per env (two kernels): the physics reads the action, the current slot and the extras and
 # writes the new slot, the extras, the reward and the done; the render reads (x, y) of the four stacked
 # slots and writes the 4 x 84 x 84 frame bytes.
@@ -69,6 +70,8 @@ def parse():
     p.add_argument("--reward", choices=("checkpoints", "waypoints"), default="checkpoints",
                    help="the rollout's reward: checkpoints (+10 each, x progress, time penalty) or the waypoint "
                         "path (progress along each map's BFS tile path, grace-zone distance penalty)")
+    p.add_argument("--respawn", choices=("off", "adaptive"), default="off",
+                   help="adaptive checkpoint respawn (each map's outcome buffer, top-quarter restarts, frontier cap)")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
@@ -123,8 +126,12 @@ def oracle_waypoints(ms):
     return pad_paths([oracle.bfs_path(ms.maps[m], *path_ends(ms, m)) for m in range(ms.maps.shape[0])])
 
 
+RESPAWN_SEED = 2024
+
+
 def _env_kw():
-    return {k: _SHARED[k] for k in ("reward_mode", "waypoints", "wp_lens") if k in _SHARED}
+    return {k: _SHARED[k] for k in ("reward_mode", "waypoints", "wp_lens", "respawn_mode", "ckpt_spawns",
+                                    "respawn_seed") if k in _SHARED}
 
 
 def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
@@ -411,10 +418,13 @@ def main():
     # process whose GPU runtime is initialised must not fork them.
     cpu = cpu_all = None
     waypoints = args.reward == "waypoints"
+    respawn = args.respawn == "adaptive"
     if not args.no_cpu_baseline:
         if waypoints:
             table, lens = oracle_waypoints(ms)
             _SHARED.update(reward_mode=1, waypoints=table, wp_lens=lens)
+        if respawn:
+            _SHARED.update(respawn_mode=1, ckpt_spawns=ms.ckpt_spawns, respawn_seed=RESPAWN_SEED)
         n_s = min(args.cpu_envs, N_ENVS)
         rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
         cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
@@ -440,6 +450,8 @@ def main():
     if waypoints:   # the library's host BFS: each map's tile path from the spawn to the finish
         table, lens = pad_paths([binding.waypoint_path(ms.maps[m], *path_ends(ms, m)) for m in range(N_MAPS)])
         wp_kw = dict(reward_mode=binding.REWARD_WAYPOINTS, waypoints=table, wp_lens=lens)
+    if respawn:
+        wp_kw.update(respawn_mode=binding.RESPAWN_ADAPTIVE, ckpt_spawns=ms.ckpt_spawns, respawn_seed=RESPAWN_SEED)
     env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev, **wp_kw)
     # rollout buffer: one allocation of [actions T*N | obs T*N*1397 | rewards T*N | dones T*N]
     a_bytes = HORIZON * N_ENVS * 4
@@ -545,7 +557,8 @@ def main():
     env_steps = args.steps * HORIZON * N_ENVS
     value = env_steps / wall
 
-    env_launch_bytes = N_ENVS * (ENV_BYTES_PER_ENV_STEP + (ENV_BYTES_WAYPOINTS if waypoints else 0))
+    env_launch_bytes = N_ENVS * (ENV_BYTES_PER_ENV_STEP + (ENV_BYTES_WAYPOINTS if waypoints else 0)
+                                 + (ENV_BYTES_RESPAWN if respawn else 0))
     env_avg_s = float(env_ms.mean()) * 1e-3
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
@@ -579,10 +592,11 @@ def main():
         "config": {"workload": "full rollout: 65536 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
                                "tile obs (31x43 + 4x15 + 4) into a resident rollout buffer, GAE + whole-batch "
                                "normalisation, PPO loss over 16 shuffled minibatches of 524288"
-                               + (", waypoint-path reward" if waypoints else ""),
+                               + (", waypoint-path reward" if waypoints else "")
+                               + (", adaptive checkpoint respawn" if respawn else ""),
                    "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES,
                    "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss",
-                   "reward": args.reward},
+                   "reward": args.reward, "respawn": args.respawn},
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic("env_step+obs_gather"),

@@ -56,8 +56,10 @@ enum {
 
 enum { RL_OBS_TILES = 0, RL_OBS_PIXELS = 1 };
 enum { RL_REWARD_CHECKPOINTS = 0, RL_REWARD_WAYPOINTS = 1 };
+enum { RL_RESPAWN_OFF = 0, RL_RESPAWN_ADAPTIVE = 1 };
 
-#define RL_STATE_FIELDS 17      /* canonical state fields per env, see rl_env_read_state */
+#define RL_STATE_FIELDS 18      /* canonical state fields per env, see rl_env_read_state */
+#define RL_RESPAWN_BUF 64       /* episode outcomes kept per map for the adaptive respawn */
 #define RL_OBS_TILES_SIZE 1397  /* f32 elements: 31*43 window + 4*15 frames + 4 checkpoint dims */
 #define RL_OBS_PIXELS_SIZE 28224 /* u8 elements: 4 frames of 84*84 */
 #define RL_MAX_FRAME_SKIP 5
@@ -78,6 +80,8 @@ typedef struct rl_env_config {
                             tiles: a multiple of 1 f32, pixels: a multiple of 4 u8 */
     int32_t reward_mode; /* RL_REWARD_CHECKPOINTS or RL_REWARD_WAYPOINTS (see rl_env_step) */
     int32_t max_waypoints; /* waypoints per map path, 1 .. 2^20, with RL_REWARD_WAYPOINTS (else ignored) */
+    int32_t respawn_mode;  /* RL_RESPAWN_OFF or RL_RESPAWN_ADAPTIVE (1 .. 1024 checkpoints; see rl_env_step) */
+    uint64_t respawn_seed; /* seed of the adaptive respawn's draws */
 } rl_env_config;
 
 typedef struct rl_env rl_env;   /* opaque host handle */
@@ -126,6 +130,17 @@ int rl_env_reset(rl_env* env, const uint8_t* mask, void* obs, void* stream);
  * for a checkpoint-reward env. */
 int rl_env_set_waypoints(rl_env* env, const int32_t* waypoints, const int32_t* lens, void* stream);
 
+/* Standing spots for the adaptive respawn (RL_RESPAWN_ADAPTIVE): copies ckpt_spawns, device
+ * int32[M][K][2] = (x, y) in sub-units where an episode restarted at checkpoint k + 1 begins, into the
+ * state buffer on `stream` (the input may be freed once the stream has passed this call). Must be called
+ * before the first rl_env_step of such an env (the step fails otherwise); RL_EINVAL otherwise. */
+int rl_env_set_respawn_spots(rl_env* env, const int32_t* ckpt_spawns, void* stream);
+
+/* The adaptive respawn's per-map state into device outputs: ring int32[M][RL_RESPAWN_BUF] (the buffered
+ * outcomes), and int32[M] fill, head (next write position) and frontier. RL_EINVAL without respawn. */
+int rl_env_read_respawn(const rl_env* env, int32_t* ring, int32_t* fill, int32_t* head, int32_t* frontier,
+                        void* stream);
+
 /* Host helper for the waypoint path: the tile-level BFS pathfinder of the same post. Breadth-first
  * search over the tiles of one map (host u8[h][w]) that a box can pass (not solid or platform) with
  * 4-neighbour moves tried in the order right, up, down, left, each tile keeping the first tile that
@@ -146,7 +161,17 @@ int rl_waypoint_path(const uint8_t* map, int32_t h, int32_t w, int32_t c0, int32
  * high-water index forward pays 256 units per waypoint, a distance d = floor(sqrt(squared distance in
  * sub-units)) beyond 1024 (the 128-unit grace zone) costs (d - 1024) >> 4 units, +100 at the finish, no
  * checkpoint bonus and no time penalty. dones[n] = 1 if the episode finished (passed its last checkpoint)
- * or hit the time limit, else 0. A done env is reset in place: its reward and done describe the episode that
+ * or hit the time limit, else 0.
+ * RL_RESPAWN_ADAPTIVE ("boesch.dev DDNet RL post", Checkpoint Respawning): each map keeps its last
+ * RL_RESPAWN_BUF episode outcomes (checkpoints passed when the episode ended) and a frontier (the most
+ * checkpoints passed by an episode that began at the spawn). An ended episode of global env n at decision
+ * counter c restarts from the buffer as it stood at the start of the step: with the draws
+ * u_i = SplitMix64's i-th output from the state seed + 2 * 0x9E3779B97F4A7C15 * (c * 2^24 + n), an empty
+ * buffer or (u_1 >> 32) < 858993459 (20%) restarts at the spawn; otherwise the ((u_2 >> 32) mod cand)-th
+ * entry, counting from the largest, of the cand entries >= the buffer's max(1, fill / 4)-th largest is
+ * taken, capped at the frontier and at K - 1; k > 0 restarts at checkpoint k - 1's standing spot with k
+ * checkpoints passed. After the step the ended episodes' outcomes enter their map's buffer in env order,
+ * and those that began at the spawn raise its frontier. A done env is reset in place: its reward and done describe the episode that
  * ended, its observation is the new episode's first. Observations (tiles: the 31x43 window around the
  * player's tile, the last 4 frames newest first, next checkpoint dx / dy, checkpoints passed, best x;
  * pixels: 4 frames of 84x84, newest first) go to obs.
@@ -157,7 +182,7 @@ int rl_env_step(rl_env* env, const int32_t* actions, void* obs, float* rewards, 
 /* Decode the state of every env into device int32[N][RL_STATE_FIELDS] with fields in the order
  * x, y, vx, vy, facing (+1/-1), freeze_ticks, hook_ticks, hook_held, jump_held, grounded, wall_left,
  * wall_right, tick, next_ckpt, best_x, last_action, path (the waypoint high-water index; 0 with
- * checkpoint rewards). */
+ * checkpoint rewards), from_start (1 if the episode began at the spawn). */
 int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
 
 /* The decision counter, whose value mod 4 selects the frame ring's newest slot. Saving the state

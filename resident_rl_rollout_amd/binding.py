@@ -17,8 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librl.so")
 
 OBS_TILES, OBS_PIXELS = 0, 1
-STATE_FIELDS = 17
+STATE_FIELDS = 18
 REWARD_CHECKPOINTS, REWARD_WAYPOINTS = 0, 1
+RESPAWN_OFF, RESPAWN_ADAPTIVE = 0, 1
+RESPAWN_BUF = 64
 OBS_TILES_SIZE = 1397
 OBS_PIXELS_SIZE = 28224
 
@@ -33,7 +35,8 @@ class EnvConfig(ctypes.Structure):
     _fields_ = [("num_envs", ctypes.c_int32), ("num_maps", ctypes.c_int32), ("map_h", ctypes.c_int32),
                 ("map_w", ctypes.c_int32), ("num_ckpts", ctypes.c_int32), ("frame_skip", ctypes.c_int32),
                 ("time_limit", ctypes.c_int32), ("obs_mode", ctypes.c_int32), ("obs_stride", ctypes.c_int64),
-                ("reward_mode", ctypes.c_int32), ("max_waypoints", ctypes.c_int32)]
+                ("reward_mode", ctypes.c_int32), ("max_waypoints", ctypes.c_int32),
+                ("respawn_mode", ctypes.c_int32), ("respawn_seed", ctypes.c_uint64)]
 
 
 # (name, restype, argtypes) of every symbol include/rl.h declares.
@@ -46,6 +49,8 @@ SIGNATURES = [
     ("rl_env_create", ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P)]),
     ("rl_env_reset", ctypes.c_int, [_P, _P, _P, _P]),
     ("rl_env_set_waypoints", ctypes.c_int, [_P, _P, _P, _P]),
+    ("rl_env_set_respawn_spots", ctypes.c_int, [_P, _P, _P]),
+    ("rl_env_read_respawn", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     ("rl_waypoint_path", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_I32)]),
     ("rl_env_step", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
@@ -129,7 +134,7 @@ class Env:
 
     def __init__(self, maps, ckpts, spawns, num_envs, *, frame_skip=3, time_limit=2000, obs_mode=OBS_TILES,
                  sprites=None, obs_stride=None, device="cuda", stream=None, reward_mode=REWARD_CHECKPOINTS,
-                 waypoints=None, wp_lens=None):
+                 waypoints=None, wp_lens=None, respawn_mode=RESPAWN_OFF, ckpt_spawns=None, respawn_seed=0):
         """reward_mode REWARD_WAYPOINTS needs waypoints int32[M][KW][2] and wp_lens int32[M] (copied to the
         device and set on the env after creation)."""
         L = lib()
@@ -148,7 +153,7 @@ class Env:
             wpt = _dev(waypoints, torch.int32, self.device).reshape(m, -1, 2)
             kw = wpt.shape[1]
         self.cfg = EnvConfig(num_envs, m, h, w, ck.shape[1], frame_skip, time_limit, obs_mode, self.obs_stride,
-                             reward_mode, kw)
+                             reward_mode, kw, respawn_mode, int(respawn_seed) & (2 ** 64 - 1))
         nbytes = ctypes.c_size_t()
         check(L.rl_env_state_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
         self.state = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
@@ -161,6 +166,10 @@ class Env:
             self.waypoints = wpt
             self.wp_lens = _dev(wp_lens, torch.int32, self.device).reshape(m)
             check(L.rl_env_set_waypoints(self._handle, dptr(self.waypoints), dptr(self.wp_lens), stream_ptr(stream)))
+        self.respawn_mode = respawn_mode
+        if respawn_mode == RESPAWN_ADAPTIVE:
+            self.ckpt_spawns = _dev(ckpt_spawns, torch.int32, self.device).reshape(m, -1, 2)
+            check(L.rl_env_set_respawn_spots(self._handle, dptr(self.ckpt_spawns), stream_ptr(stream)))
 
     @property
     def obs_dtype(self):
@@ -183,6 +192,15 @@ class Env:
         out = torch.empty((self.num_envs, STATE_FIELDS), dtype=torch.int32, device=self.device)
         check(lib().rl_env_read_state(self._handle, dptr(out), stream_ptr(stream)))
         return out
+
+    def read_respawn(self, stream=None):
+        """(ring int32[M][64], fill, head, frontier int32[M]) of the adaptive respawn."""
+        m = self.maps.shape[0]
+        ring = torch.empty((m, RESPAWN_BUF), dtype=torch.int32, device=self.device)
+        meta = torch.empty((3, m), dtype=torch.int32, device=self.device)
+        check(lib().rl_env_read_respawn(self._handle, dptr(ring), dptr(meta[0]), dptr(meta[1]), dptr(meta[2]),
+                                        stream_ptr(stream)))
+        return ring, meta[0], meta[1], meta[2]
 
     @property
     def step_counter(self) -> int:

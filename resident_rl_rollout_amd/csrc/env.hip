@@ -44,6 +44,14 @@ constexpr int kWpAhead = 8;           // the nearest waypoint is searched at the
 constexpr int kUnitsWaypoint = 256;   // one tile of path = 256 units
 constexpr int kWpGrace = 1024;        // the 128-unit (about 4 tile) grace zone, sub-units
 constexpr int kWpPenaltyShift = 4;    // beyond it: one unit per 16 sub-units of distance per tick
+// adaptive checkpoint respawn ("Checkpoint Respawning"; readings)
+constexpr int kRespawnBuf = RL_RESPAWN_BUF;          // outcomes kept per map
+constexpr uint32_t kRespawnStartU32 = 858993459u;    // a draw below this (20% of 2^32) restarts at the spawn
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;  // SplitMix64's increment
+constexpr int kMaxRespawnCkpts = 1024;
+// the step kernels' variants: bit 0 = the waypoint-path reward, bit 1 = the adaptive respawn
+constexpr int kModeWaypoints = 1;
+constexpr int kModeRespawn = 2;
 
 constexpr int kWinW = 43;
 constexpr int kWinH = 31;
@@ -76,7 +84,7 @@ constexpr int kHookShift = 16;    // 8 bits, 0..255
 constexpr int kActionShift = 24;  // 4 bits, 0..11
 
 struct Layout {
-    size_t slots, extra, map, ckpt, spawn, sprites, waypoints, wplens, total;
+    size_t slots, extra, map, ckpt, spawn, sprites, waypoints, wplens, spots, ring, rmeta, rhist, total;
     int64_t np, hp, wp;
 };
 
@@ -89,6 +97,12 @@ struct EnvDev {
     const uint8_t* sprites;
     const int32_t* wpt;     // [M][kw][2] waypoint path (column, row), reward mode 1
     const int32_t* wplen;   // [M]
+    const int32_t* spots;   // [M][k][2] respawn standing spots
+    int32_t* ring;          // [M][kRespawnBuf] buffered outcomes
+    int32_t* rmeta;         // [M][4] fill, head, frontier, -
+    int32_t* rhist;         // [M][k + 1] counts of the buffered outcomes
+    uint64_t seed;          // respawn draws
+    int64_t counter;        // the decision counter of this step
     int32_t n, m, h, w, k, fs, time_limit, kw;
     int64_t np, hp, wp;
 };
@@ -119,6 +133,11 @@ int validate_cfg(const rl_env_config* c)
         return rl::fail(RL_EINVAL, "reward_mode %d is neither checkpoints (0) nor waypoints (1)", c->reward_mode);
     if (c->reward_mode == RL_REWARD_WAYPOINTS && (c->max_waypoints < 1 || c->max_waypoints > (1 << 20)))
         return rl::fail(RL_EINVAL, "max_waypoints %d outside [1, 2^20]", c->max_waypoints);
+    if (c->respawn_mode != RL_RESPAWN_OFF && c->respawn_mode != RL_RESPAWN_ADAPTIVE)
+        return rl::fail(RL_EINVAL, "respawn_mode %d is neither off (0) nor adaptive (1)", c->respawn_mode);
+    if (c->respawn_mode == RL_RESPAWN_ADAPTIVE && (c->num_ckpts < 1 || c->num_ckpts > kMaxRespawnCkpts))
+        return rl::fail(RL_EINVAL, "the adaptive respawn needs 1 .. %d checkpoints, got %d", kMaxRespawnCkpts,
+                        c->num_ckpts);
     return RL_OK;
 }
 
@@ -131,8 +150,8 @@ Layout layout_of(const rl_env_config* c)
     size_t off = 0;
     l.slots = off;
     off = rl::round_up(off + sizeof(int32_t) * kStack * kSlotWords * l.np, 256);
-    l.extra = off;
-    off = rl::round_up(off + sizeof(int32_t) * 3 * l.np, 256);
+    l.extra = off;   // next checkpoint, best x, path index, from-start flag, the step's ended outcome
+    off = rl::round_up(off + sizeof(int32_t) * 5 * l.np, 256);
     l.map = off;
     off = rl::round_up(off + (size_t)c->num_maps * l.hp * l.wp, 256);
     l.ckpt = off;
@@ -146,6 +165,16 @@ Layout layout_of(const rl_env_config* c)
     off = rl::round_up(off + sizeof(int32_t) * 2 * kw * (size_t)c->num_maps, 256);
     l.wplens = off;
     off = rl::round_up(off + (kw ? sizeof(int32_t) * (size_t)c->num_maps : 0), 256);
+    const bool rs = c->respawn_mode == RL_RESPAWN_ADAPTIVE;
+    const size_t mm = rs ? (size_t)c->num_maps : 0;
+    l.spots = off;
+    off = rl::round_up(off + sizeof(int32_t) * 2 * mm * (size_t)c->num_ckpts, 256);
+    l.ring = off;
+    off = rl::round_up(off + sizeof(int32_t) * kRespawnBuf * mm, 256);
+    l.rmeta = off;
+    off = rl::round_up(off + sizeof(int32_t) * 4 * mm, 256);
+    l.rhist = off;
+    off = rl::round_up(off + sizeof(int32_t) * mm * ((size_t)c->num_ckpts + 1), 256);
     l.total = off;
     return l;
 }
@@ -236,6 +265,7 @@ __device__ __forceinline__ void write_spawn(const EnvDev& d, int n)
     d.extra[n] = 0;
     d.extra[d.np + n] = x;
     d.extra[2 * d.np + n] = 0;
+    d.extra[3 * d.np + n] = 1;
 }
 
 __global__ __launch_bounds__(256) void k_reset(EnvDev d, const uint8_t* __restrict__ mask)
@@ -347,10 +377,152 @@ __device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_
     return units;
 }
 
-template <int RM>
+// ------------------------------------------------------------------------------------------------
+// Adaptive checkpoint respawn.
+// ------------------------------------------------------------------------------------------------
+
+// SplitMix64's output function (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+// 2014).
+__device__ __forceinline__ uint64_t splitmix_output(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// The checkpoint an ended episode of env n on map m restarts at (0 = the spawn), from the map's buffer as
+// it stood at the start of the step (the buffers change only in k_respawn_append, after the step). The
+// draws are SplitMix64's first and second outputs from the state seed + 2 golden (counter 2^24 + n). The
+// top quarter of the buffer is read off its histogram: the max(1, fill / 4)-th largest outcome thr, the
+// cand outcomes >= thr, and the (pick + 1)-th largest of them.
+__device__ int32_t respawn_choice(const EnvDev& d, int m, int n)
+{
+    const int32_t* meta = d.rmeta + 4 * m;
+    const int32_t fill = meta[0];
+    if (fill == 0) return 0;
+    const uint64_t key = (uint64_t)d.counter * ((uint64_t)1 << 24) + (uint64_t)n;
+    const uint64_t state = d.seed + 2 * kGolden * key;
+    if ((uint32_t)(splitmix_output(state + kGolden) >> 32) < kRespawnStartU32) return 0;
+    const int32_t* hist = d.rhist + (int64_t)m * (d.k + 1);
+    const int32_t q = max(1, fill / 4);
+    int32_t cand = 0, thr = 0;
+    for (int32_t v = d.k; v >= 0; --v) {
+        cand += hist[v];
+        if (cand >= q) {
+            thr = v;
+            break;
+        }
+    }
+    if (cand == 0) return 0;   // a histogram that disagrees with fill (not produced by this library)
+    const uint32_t pick = (uint32_t)(splitmix_output(state + 2 * kGolden) >> 32) % (uint32_t)cand;
+    int32_t acc = 0, chosen = thr;
+    for (int32_t v = d.k; v >= thr; --v) {
+        acc += hist[v];
+        if ((int32_t)pick < acc) {
+            chosen = v;
+            break;
+        }
+    }
+    return max(0, min(min(chosen, meta[2]), d.k - 1));
+}
+
+// Start a new episode of env n on map m at checkpoint k in all four ring slots and the extras: the spawn
+// for k = 0, else checkpoint k - 1's standing spot with k checkpoints passed. Returns its decision.
+__device__ __forceinline__ Decision spawn_at(const EnvDev& d, int n, int m, int32_t k)
+{
+    int32_t x = d.spawn[2 * m], y = d.spawn[2 * m + 1];
+    if (k > 0) {
+        const int32_t* p = d.spots + ((int64_t)m * d.k + (k - 1)) * 2;
+        x = p[0];
+        y = p[1];
+    }
+    const int32_t misc = (int32_t)(kFacingRight | kGroundedBit);
+    for (int s = 0; s < kStack; ++s) {
+        slot_word(d, s, 0, n) = x;
+        slot_word(d, s, 1, n) = y;
+        slot_word(d, s, 2, n) = 0;
+        slot_word(d, s, 3, n) = misc;
+        slot_word(d, s, 4, n) = 0;
+    }
+    d.extra[n] = k;
+    d.extra[d.np + n] = x;
+    d.extra[2 * d.np + n] = 0;
+    d.extra[3 * d.np + n] = k == 0 ? 1 : 0;
+    return Decision{x, y, 0, misc, 0, k, x, true};
+}
+
+// After the step: one block per map appends the step's ended outcomes to the map's ring in env order (only
+// the last kRespawnBuf survive), raises the frontier by those that began at the spawn, and recounts the
+// ring's histogram.
+__global__ __launch_bounds__(256) void k_respawn_append(EnvDev d)
+{
+    __shared__ int32_t part[256];
+    __shared__ int32_t fmax[256];
+    __shared__ int32_t hist[kMaxRespawnCkpts + 1];
+    const int m = blockIdx.x;
+    const int t = threadIdx.x;
+    const int cnt = m < d.n ? (d.n - m + d.m - 1) / d.m : 0;   // envs of map m: n = m + M i, i < cnt
+    const int per = (cnt + 255) / 256;
+    const int i0 = min(cnt, t * per), i1 = min(cnt, i0 + per);
+    const int32_t* ended = d.extra + 4 * d.np;
+    int32_t mine = 0, front = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int32_t e = ended[m + (int64_t)d.m * i];
+        if (e >= 0) {
+            ++mine;
+            if ((e >> 30) & 1) front = max(front, e & ((1 << 30) - 1));
+        }
+    }
+    part[t] = mine;
+    fmax[t] = front;
+    __syncthreads();
+    // inclusive scan of the per-thread counts (fixed order), and the frontier candidate
+    for (int off = 1; off < 256; off <<= 1) {
+        const int32_t a = t >= off ? part[t - off] : 0;
+        const int32_t b = t >= off ? fmax[t - off] : 0;
+        __syncthreads();
+        part[t] += a;
+        fmax[t] = max(fmax[t], b);
+        __syncthreads();
+    }
+    const int32_t total = part[255];
+    if (total == 0) return;                       // uniform: nothing ended on this map
+    int32_t* meta = d.rmeta + 4 * m;
+    int32_t* ring = d.ring + (int64_t)m * kRespawnBuf;
+    const int32_t head = meta[1];
+    int32_t p = part[t] - mine;                   // this thread's first append position
+    for (int i = i0; i < i1; ++i) {
+        const int32_t e = ended[m + (int64_t)d.m * i];
+        if (e >= 0) {
+            if (p >= total - kRespawnBuf) ring[(head + p) % kRespawnBuf] = e & ((1 << 30) - 1);
+            ++p;
+        }
+    }
+    for (int v = t; v <= d.k; v += 256) hist[v] = 0;
+    __syncthreads();                              // ring writes and the cleared histogram
+    const int32_t fill = min(meta[0] + total, kRespawnBuf);
+    if (t < fill) atomicAdd(&hist[min(max(ring[t], 0), d.k)], 1);
+    __syncthreads();
+    int32_t* gh = d.rhist + (int64_t)m * (d.k + 1);
+    for (int v = t; v <= d.k; v += 256) gh[v] = hist[v];
+    if (t == 0) {
+        meta[0] = fill;
+        meta[1] = (head + total) % kRespawnBuf;
+        meta[2] = max(meta[2], fmax[255]);
+    }
+}
+
+// Zero the respawn state (create).
+__global__ __launch_bounds__(256) void k_zero(int32_t* __restrict__ p, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+template <int MODE>
 __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a, const SlotWords& cur, int32_t next,
-                                               int32_t best_x, int32_t path, float* __restrict__ rewards,
-                                               float* __restrict__ dones, int head_new)
+                                               int32_t best_x, int32_t path, int32_t from_start,
+                                               float* __restrict__ rewards, float* __restrict__ dones, int head_new)
 {
     const int m = n % d.m;
     int32_t x = cur.x;
@@ -437,21 +609,21 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         jump_held = (uint32_t)jump;
         // 10. progress: past the high-water mark of x (mode 0), or along the waypoint path (mode 1); best x
         // is kept in both (it is an observation dim)
-        if constexpr (RM == 1) units += waypoint_units(d, m, x, y, path);
+        if constexpr ((MODE & kModeWaypoints) != 0) units += waypoint_units(d, m, x, y, path);
         if (x > best_x) {
-            if constexpr (RM == 0) units += x - best_x;
+            if constexpr ((MODE & kModeWaypoints) == 0) units += x - best_x;
             best_x = x;
         }
         // 11. checkpoints in order (+10 each in mode 0); the last one is the finish
         if (next < d.k && ((x + kHalfBox) >> 8) >= ck_col) {
-            if constexpr (RM == 0) units += kUnitsCkpt;
+            if constexpr ((MODE & kModeWaypoints) == 0) units += kUnitsCkpt;
             next += 1;
             if (next == d.k) { units += kUnitsFinish; terminated = true; }
             else ck_col = ck[2 * next];
         }
         // 12. time (a penalty in mode 0 only)
         tick += 1;
-        if constexpr (RM == 0) units -= 1;
+        if constexpr ((MODE & kModeWaypoints) == 0) units -= 1;
         if (tick >= d.time_limit) truncated = true;
     }
 
@@ -459,10 +631,14 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     const bool done = terminated || truncated;
     dones[n] = done ? 1.0f : 0.0f;
     if (done) {
-        write_spawn(d, n);
-        const int32_t* sp = d.spawn + 2 * m;
-        return Decision{sp[0], sp[1], 0, (int32_t)(kFacingRight | kGroundedBit), 0, 0, sp[0], true};
+        int32_t k = 0;
+        if constexpr ((MODE & kModeRespawn) != 0) {
+            d.extra[4 * d.np + n] = next | (from_start ? (1 << 30) : 0);   // the ended episode's outcome
+            k = respawn_choice(d, m, n);
+        }
+        return spawn_at(d, n, m, k);
     }
+    if constexpr ((MODE & kModeRespawn) != 0) d.extra[4 * d.np + n] = -1;
     const uint32_t new_misc = (facing > 0 ? kFacingRight : 0u) | (grounded ? kGroundedBit : 0u) |
                               (jump_held ? kJumpHeldBit : 0u) | (hook_held ? kHookHeldBit : 0u) |
                               (wall_l ? kWallLBit : 0u) | (wall_r ? kWallRBit : 0u) |
@@ -475,22 +651,23 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     slot_word(d, head_new, 4, n) = tick;
     d.extra[n] = next;
     d.extra[d.np + n] = best_x;
-    if constexpr (RM == 1) d.extra[2 * d.np + n] = path;
+    if constexpr ((MODE & kModeWaypoints) != 0) d.extra[2 * d.np + n] = path;
     return Decision{x, y, (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16)), (int32_t)new_misc, tick,
                     next, best_x, false};
 }
 
 // env_step alone (the pixel path renders in its own kernel): one lane per env, one-wave blocks so that a
 // small batch still spreads over every CU (the kernel is latency-bound: a few waves per CU at most).
-template <int RM>
+template <int MODE>
 __global__ __launch_bounds__(64) void k_step(EnvDev d, const int32_t* __restrict__ actions,
                                               float* __restrict__ rewards, float* __restrict__ dones,
                                               int head_prev, int head_new)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= d.n) return;
-    env_decide<RM>(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n],
-                   RM == 1 ? d.extra[2 * d.np + n] : 0, rewards, dones, head_new);
+    env_decide<MODE>(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n],
+                     (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0,
+                     (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1, rewards, dones, head_new);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -645,7 +822,7 @@ __device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int l
     }
 }
 
-template <int E, int RM>
+template <int E, int MODE>
 __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
@@ -667,8 +844,9 @@ __global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __r
         const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
         const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
         const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
-        const int32_t path0 = RM == 1 ? d.extra[2 * d.np + n] : 0;
-        const Decision s = env_decide<RM>(d, n, a, cur, next0, best0, path0, rewards, dones, head_new);
+        const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
+        const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
+        const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, rewards, dones, head_new);
         float* t = tail[e];
         put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
         if (s.done) {
@@ -788,7 +966,20 @@ __global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restric
     }
 }
 
-// Decode the newest slot and the extras into the canonical int32[N][16] state.
+// The adaptive respawn's per-map state, one block (64 lanes = the ring) per map.
+__global__ __launch_bounds__(64) void k_read_respawn(EnvDev d, int32_t* __restrict__ ring, int32_t* __restrict__ fill,
+                                                     int32_t* __restrict__ head, int32_t* __restrict__ frontier)
+{
+    const int m = blockIdx.x;
+    ring[(int64_t)m * kRespawnBuf + threadIdx.x] = d.ring[(int64_t)m * kRespawnBuf + threadIdx.x];
+    if (threadIdx.x == 0) {
+        fill[m] = d.rmeta[4 * m];
+        head[m] = d.rmeta[4 * m + 1];
+        frontier[m] = d.rmeta[4 * m + 2];
+    }
+}
+
+// Decode the newest slot and the extras into the canonical int32[N][RL_STATE_FIELDS] state.
 __global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restrict__ out, int head)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
@@ -812,6 +1003,7 @@ __global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restric
     o[13] = d.extra[n];
     o[14] = d.extra[d.np + n];
     o[16] = d.extra[2 * d.np + n];
+    o[17] = d.extra[3 * d.np + n];
     o[15] = (int32_t)((misc >> kActionShift) & 15u);
 }
 
@@ -823,6 +1015,7 @@ struct rl_env {
     uint8_t* base;
     int64_t counter;
     bool waypoints_set;
+    bool spots_set;
 };
 
 namespace {
@@ -839,6 +1032,12 @@ EnvDev dev_of(const rl_env* e)
     d.wpt = reinterpret_cast<const int32_t*>(e->base + e->lay.waypoints);
     d.wplen = reinterpret_cast<const int32_t*>(e->base + e->lay.wplens);
     d.kw = e->cfg.reward_mode == RL_REWARD_WAYPOINTS ? e->cfg.max_waypoints : 0;
+    d.spots = reinterpret_cast<const int32_t*>(e->base + e->lay.spots);
+    d.ring = reinterpret_cast<int32_t*>(e->base + e->lay.ring);
+    d.rmeta = reinterpret_cast<int32_t*>(e->base + e->lay.rmeta);
+    d.rhist = reinterpret_cast<int32_t*>(e->base + e->lay.rhist);
+    d.seed = e->cfg.respawn_seed;
+    d.counter = e->counter;
     d.n = e->cfg.num_envs;
     d.m = e->cfg.num_maps;
     d.h = e->cfg.map_h;
@@ -931,6 +1130,7 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
     e->base = static_cast<uint8_t*>(state);
     e->counter = 0;
     e->waypoints_set = false;
+    e->spots_set = false;
     hipStream_t st = rl::as_stream(stream);
     uint8_t* base = e->base;
 
@@ -949,6 +1149,13 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
     if (rc == RL_OK && he == hipSuccess && cfg->obs_mode == RL_OBS_PIXELS)
         he = hipMemcpyAsync(base + lay.sprites, sprites, 16 * 64, hipMemcpyDeviceToDevice, st);
     if (rc == RL_OK && he != hipSuccess) rc = rl::fail(RL_EHIP, "table copy: %s", hipGetErrorString(he));
+    if (rc == RL_OK && cfg->respawn_mode == RL_RESPAWN_ADAPTIVE) {
+        // ring, meta and histogram are contiguous: zero them together
+        const int64_t words = (int64_t)(lay.total - lay.ring) / 4;
+        hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)), dim3(256), 0, st,
+                           reinterpret_cast<int32_t*>(base + lay.ring), words);
+        rc = rl::check_launch("respawn state");
+    }
     if (rc == RL_OK) {
         const EnvDev d = dev_of(e);
         hipLaunchKernelGGL(k_reset, dim3((cfg->num_envs + 255) / 256), dim3(256), 0, st, d,
@@ -984,32 +1191,68 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
         return rl::fail(RL_EALIGN, "actions / rewards / dones are not 4-byte aligned");
     if (int rc = check_obs_ptr(e, obs)) return rc;
     const bool wp = e->cfg.reward_mode == RL_REWARD_WAYPOINTS;
+    const bool rs = e->cfg.respawn_mode == RL_RESPAWN_ADAPTIVE;
     if (wp && !e->waypoints_set) return rl::fail(RL_EINVAL, "waypoint rewards need rl_env_set_waypoints first");
+    if (rs && !e->spots_set) return rl::fail(RL_EINVAL, "the adaptive respawn needs rl_env_set_respawn_spots first");
     hipStream_t st = rl::as_stream(stream);
     const EnvDev d = dev_of(e);
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
+    const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
-        const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs);
+        const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs), block(256);
         float* o = static_cast<float*>(obs);
-        if (wp)
-            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 1>), grid, dim3(256), 0, st, d, actions, rewards, dones, o,
-                               e->cfg.obs_stride, head_prev, head_new);
-        else
-            hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 0>), grid, dim3(256), 0, st, d, actions, rewards, dones, o,
-                               e->cfg.obs_stride, head_prev, head_new);
+        const int64_t os = e->cfg.obs_stride;
+        switch (mode) {
+        case 0: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 0>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
+        case 1: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 1>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
+        case 2: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 2>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
+        default: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 3>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
+        }
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
-        e->counter += 1;
-        return RL_OK;
+    } else {
+        const dim3 grid((d.n + 63) / 64), block(64);
+        switch (mode) {
+        case 0: hipLaunchKernelGGL(k_step<0>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
+        case 1: hipLaunchKernelGGL(k_step<1>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
+        case 2: hipLaunchKernelGGL(k_step<2>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
+        default: hipLaunchKernelGGL(k_step<3>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
+        }
+        if (int rc = rl::check_launch("env_step")) return rc;
     }
-    if (wp)
-        hipLaunchKernelGGL(k_step<1>, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
-                           head_new);
-    else
-        hipLaunchKernelGGL(k_step<0>, dim3((d.n + 63) / 64), dim3(64), 0, st, d, actions, rewards, dones, head_prev,
-                           head_new);
-    if (int rc = rl::check_launch("env_step")) return rc;
+    if (rs) {
+        hipLaunchKernelGGL(k_respawn_append, dim3(d.m), dim3(256), 0, st, d);
+        if (int rc = rl::check_launch("respawn_append")) return rc;
+    }
     e->counter += 1;
+    if (e->cfg.obs_mode == RL_OBS_TILES) return RL_OK;
     return launch_obs(e, obs, st, head_new);
+}
+
+int rl_env_set_respawn_spots(rl_env* e, const int32_t* ckpt_spawns, void* stream)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (e->cfg.respawn_mode != RL_RESPAWN_ADAPTIVE) return rl::fail(RL_EINVAL, "the env does not use the adaptive respawn");
+    if (!ckpt_spawns) return rl::fail(RL_EINVAL, "ckpt_spawns is NULL");
+    if (!rl::aligned(ckpt_spawns, 4)) return rl::fail(RL_EALIGN, "ckpt_spawns is not 4-byte aligned");
+    const hipError_t he = hipMemcpyAsync(e->base + e->lay.spots, ckpt_spawns,
+                                         sizeof(int32_t) * 2 * (size_t)e->cfg.num_maps * e->cfg.num_ckpts,
+                                         hipMemcpyDeviceToDevice, rl::as_stream(stream));
+    if (he != hipSuccess) return rl::fail(RL_EHIP, "respawn spot copy: %s", hipGetErrorString(he));
+    e->spots_set = true;
+    return RL_OK;
+}
+
+int rl_env_read_respawn(const rl_env* e, int32_t* ring, int32_t* fill, int32_t* head, int32_t* frontier, void* stream)
+{
+    if (!e) return rl::fail(RL_EINVAL, "env is NULL");
+    if (e->cfg.respawn_mode != RL_RESPAWN_ADAPTIVE) return rl::fail(RL_EINVAL, "the env does not use the adaptive respawn");
+    if (!ring || !fill || !head || !frontier) return rl::fail(RL_EINVAL, "outputs must be non-NULL");
+    const void* outs[] = {ring, fill, head, frontier};
+    for (const void* q : outs)
+        if (!rl::aligned(q, 4)) return rl::fail(RL_EALIGN, "an output is not 4-byte aligned");
+    hipLaunchKernelGGL(k_read_respawn, dim3(e->cfg.num_maps), dim3(64), 0, rl::as_stream(stream), dev_of(e), ring, fill,
+                       head, frontier);
+    return rl::check_launch("read_respawn");
 }
 
 int rl_env_set_waypoints(rl_env* e, const int32_t* waypoints, const int32_t* lens, void* stream)

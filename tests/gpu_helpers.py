@@ -97,13 +97,17 @@ class PairedEnvs:
     """The same env batch on the GPU (through the C ABI) and in the oracle, stepped with the same actions."""
 
     def __init__(self, ms: inputs.MapSet, n, *, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_TILES,
-                 sprites=None, obs_stride=None, reward_mode=0, waypoints=None, wp_lens=None):
+                 sprites=None, obs_stride=None, reward_mode=0, waypoints=None, wp_lens=None, respawn_mode=0,
+                 respawn_seed=0):
+        spots = ms.ckpt_spawns if respawn_mode else None
         self.gpu = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip, time_limit=time_limit,
                                obs_mode=obs_mode, sprites=sprites, obs_stride=obs_stride, reward_mode=reward_mode,
-                               waypoints=waypoints, wp_lens=wp_lens)
+                               waypoints=waypoints, wp_lens=wp_lens, respawn_mode=respawn_mode, ckpt_spawns=spots,
+                               respawn_seed=respawn_seed)
         self.ora = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip,
                                     time_limit=time_limit, sprites=sprites, reward_mode=reward_mode,
-                                    waypoints=waypoints, wp_lens=wp_lens)
+                                    waypoints=waypoints, wp_lens=wp_lens, respawn_mode=respawn_mode,
+                                    ckpt_spawns=spots, respawn_seed=respawn_seed)
         self.ora.reset()
         self.n = n
         self.obs_mode = obs_mode
@@ -134,6 +138,15 @@ class PairedEnvs:
             e, f = bad[0]
             raise AssertionError(f"{what}: state differs in {len(bad)} fields; first env {e} field "
                                  f"{oracle.STATE_FIELDS[f]}: gpu {got[e]} oracle {self.ora.state[e]}")
+
+    def check_respawn(self, what):
+        ring, fill, head, front = (t.cpu().numpy() for t in self.gpu.read_respawn())
+        np.testing.assert_array_equal(fill, self.ora.fill, err_msg=f"{what}: respawn fill")
+        np.testing.assert_array_equal(head, self.ora.head, err_msg=f"{what}: respawn head")
+        np.testing.assert_array_equal(front, self.ora.frontier, err_msg=f"{what}: respawn frontier")
+        for m in range(len(fill)):
+            np.testing.assert_array_equal(ring[m, :fill[m]], self.ora.ring[m, :fill[m]],
+                                          err_msg=f"{what}: respawn ring of map {m}")
 
     def check_step(self, r, d, what):
         np.testing.assert_array_equal(self.rew.cpu().numpy(), r, err_msg=f"{what}: rewards")

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(**kw):
     base = dict(num_envs=64, num_maps=1, map_h=32, map_w=128, num_ckpts=7, frame_skip=3, time_limit=2000,
-                obs_mode=0, obs_stride=1397, reward_mode=0, max_waypoints=0)
+                obs_mode=0, obs_stride=1397, reward_mode=0, max_waypoints=0, respawn_mode=0, respawn_seed=0)
     base.update(kw)
     return binding.EnvConfig(*[base[k] for k, _ in binding.EnvConfig._fields_])
 
@@ -45,6 +45,8 @@ def _cfg(**kw):
     (dict(num_envs=(1 << 24) + 1), -1, "num_envs"), (dict(reward_mode=2), -1, "reward_mode"),
     (dict(reward_mode=1, max_waypoints=0), -1, "max_waypoints"),
     (dict(reward_mode=1, max_waypoints=(1 << 20) + 1), -1, "max_waypoints"),
+    (dict(respawn_mode=2), -1, "respawn_mode"), (dict(respawn_mode=1, num_ckpts=0), -1, "checkpoints"),
+    (dict(respawn_mode=1, num_ckpts=1025), -1, "checkpoints"),
 ])
 def test_config_validation(kw, code, msg):
     lib = binding.lib()
@@ -80,6 +82,8 @@ def test_entry_points_reject_before_any_hip_call():
                              None, ctypes.byref(out)) == -1
     assert lib.rl_env_step(None, fake, fake, fake, fake, None) == -1
     assert lib.rl_env_set_waypoints(None, fake, fake, None) == -1
+    assert lib.rl_env_set_respawn_spots(None, fake, None) == -1
+    assert lib.rl_env_read_respawn(None, fake, fake, fake, fake, None) == -1
     assert lib.rl_env_reset(None, None, None, None) == -1
     # rl_gae: sizes, NULLs, enum, workspace
     assert lib.rl_gae(fake, fake, fake, fake, 0, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
