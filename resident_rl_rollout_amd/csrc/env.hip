@@ -473,6 +473,7 @@ __global__ __launch_bounds__(256) void k_respawn_append(EnvDev d)
             if ((e >> 30) & 1) front = max(front, e & ((1 << 30) - 1));
         }
     }
+    if (!__syncthreads_or(mine)) return;          // uniform: nothing ended on this map this step
     part[t] = mine;
     fmax[t] = front;
     __syncthreads();
@@ -486,7 +487,6 @@ __global__ __launch_bounds__(256) void k_respawn_append(EnvDev d)
         __syncthreads();
     }
     const int32_t total = part[255];
-    if (total == 0) return;                       // uniform: nothing ended on this map
     int32_t* meta = d.rmeta + 4 * m;
     int32_t* ring = d.ring + (int64_t)m * kRespawnBuf;
     const int32_t head = meta[1];
