@@ -248,7 +248,8 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   logits device f32[B][A], A in 1..64 (16-byte aligned when A % 4 == 0); actions device int32[B] in
  *   [0, A) (other values act as action 0); old_logp, adv, ret, new_values device f32[B].
  *   B % mb must be 0. ws: device workspace of rl_ppo_loss_workspace_bytes(B, mb) bytes, 8-byte aligned (any
- *   contents); calls sharing it must not overlap. The per-sample terms are reduced through float64
+ *   contents); calls sharing it must not overlap. The per-sample terms are float32 (exponentials and
+ *   logarithms from the hardware's base-2 instructions, about 1 ulp each) and are reduced through float64
  *   partials in a fixed order (identical results from run to run). With mb_index every input is read
  *   once, in storage order; with perm every read is a gather. */
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,

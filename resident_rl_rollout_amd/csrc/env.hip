@@ -14,10 +14,15 @@
 //   slots  int32[4][5][Np]  ring of the last 4 frames; slot s, word w of env n at (s*5 + w)*Np + n.
 //                           Words: x, y, (vx & 0xffff) | vy << 16, flags / counters, tick. The newest
 //                           slot is the current state; the decision counter mod 4 names it.
-//   extra  int32[2][Np]     next checkpoint index, best x.
+//   extra  int32[5][Np]     next checkpoint index, best x, waypoint high-water index, began-at-spawn flag,
+//                           the step's ended outcome (checkpoints passed, bit 30 = began at the spawn;
+//                           -1 when the env did not end; written in respawn mode only).
 //   map    u8[M][H+32][Wp]  the maps with a 16-row / 32-column solid border, Wp = round_up(W+64, 64),
 //                           so that every read of the step and observation kernels stays inside.
 //   ckpt   int32[M][K][2], spawn int32[M][2], sprites u8[16][8][8].
+//   waypoints int32[M][Kw][2], wplens int32[M]            (waypoint reward only; empty otherwise)
+//   spots int32[M][K][2], ring int32[M][64], rmeta int32[M][4] (fill, head, frontier, spare),
+//   rhist int32[M][K+1]                                    (adaptive respawn only; empty otherwise)
 // Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
 
 #include <vector>

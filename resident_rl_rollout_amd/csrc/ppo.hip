@@ -86,72 +86,119 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, float (&
     }
 }
 
-// Row statistics: mx = max z, log_s = log(sum exp(z - mx)), mean_u = (sum e_j (z_j - mx)) / S, u_a = z_a - mx.
-// AC > 0 reads the registers z; AC = 0 (runtime A) reads the row element by element.
+// e^x and ln x from the hardware's base-2 exponential and logarithm (v_exp_f32 / v_log_f32, about one
+// ulp each): e^x = 2^(x log2 e), ln x = log2 x ln 2. The arguments here are u <= 0 (results in (0, 1]),
+// ratios' log differences, and sums >= 1, so no denormal scaling is needed.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+
+// Row statistics with u_j = z_j - max z: log_s = log(S), S = sum e^{u_j}, mean_u = (sum e^{u_j} u_j) / S
+// (the entropy is log_s - mean_u), u_a = u of the taken action.
+struct RowStats {
+    float mx, log_s, mean_u, u_a, inv_s;
+};
+
+// AC > 0: the row in registers z; the e^{u_j} stay in ex for the gradient.
 template <int AC>
-__device__ __forceinline__ void row_stats(const float* z, const float* __restrict__ row, int A, int a, float* mx_out,
-                                          float* log_s, float* mean_u, float* u_a)
+__device__ __forceinline__ RowStats row_stats(const float (&z)[AC], int a, float (&ex)[AC])
 {
-    const int n = AC > 0 ? AC : A;
-    auto at = [&](int j) { return AC > 0 ? z[j] : row[j]; };
-    float mx = at(0);
+    float mx = z[0];
 #pragma unroll
-    for (int j = 1; j < (AC > 0 ? AC : 64); ++j)
-        if (AC > 0 || j < n) mx = fmaxf(mx, at(j));
-    float s = 0.0f, su = 0.0f, ua = at(0) - mx;
+    for (int j = 1; j < AC; ++j) mx = fmaxf(mx, z[j]);
+    float s = 0.0f, su = 0.0f, ua = z[0] - mx;
 #pragma unroll
-    for (int j = 0; j < (AC > 0 ? AC : 64); ++j) {
-        if (AC > 0 || j < n) {
-            const float u = at(j) - mx;
-            const float ex = expf(u);
-            s += ex;
-            su += ex * u;
-            if (j == a) ua = u;
-        }
+    for (int j = 0; j < AC; ++j) {
+        const float u = z[j] - mx;
+        ex[j] = exp_hw(u);
+        s += ex[j];
+        su += ex[j] * u;
+        ua = j == a ? u : ua;
     }
-    *mx_out = mx;
-    *log_s = logf(s);
-    *mean_u = su / s;
-    *u_a = ua;
+    RowStats r;
+    r.mx = mx;
+    r.inv_s = __builtin_amdgcn_rcpf(s);
+    r.log_s = log_hw(s);
+    r.mean_u = su * r.inv_s;
+    r.u_a = ua;
+    return r;
 }
 
-// The three per-sample terms: clipped surrogate, squared value error, entropy; with GRAD also the
-// sample's gradient row and value gradient.
+// Runtime A: the row is read from memory.
+__device__ __forceinline__ RowStats row_stats_mem(const float* __restrict__ row, int A, int a)
+{
+    float mx = row[0];
+    for (int j = 1; j < A; ++j) mx = fmaxf(mx, row[j]);
+    float s = 0.0f, su = 0.0f;
+    for (int j = 0; j < A; ++j) {
+        const float u = row[j] - mx;
+        const float ex = exp_hw(u);
+        s += ex;
+        su += ex * u;
+    }
+    RowStats r;
+    r.mx = mx;
+    r.inv_s = __builtin_amdgcn_rcpf(s);
+    r.log_s = log_hw(s);
+    r.mean_u = su * r.inv_s;
+    r.u_a = row[a] - mx;
+    return r;
+}
+
+// A sample's inputs, loaded ahead of its arithmetic (AC = 0: the logits stay in memory).
+template <int AC>
+struct SampleIn {
+    float z[AC > 0 ? AC : 1];
+    int32_t a;
+    float old_logp, adv, ret, v;
+};
+
+template <int AC>
+__device__ __forceinline__ void load_sample(const LossArgs& p, int64_t i, SampleIn<AC>& s)
+{
+    if constexpr (AC > 0) load_row<AC>(p.logits + i * AC, s.z);
+    s.a = p.actions[i];
+    s.old_logp = p.old_logp[i];
+    s.adv = p.adv[i];
+    s.ret = p.ret[i];
+    s.v = p.new_v[i];
+}
+
+// The three per-sample terms of sample i (inputs s): clipped surrogate, squared value error, entropy;
+// with GRAD and `write` also the sample's gradient row and value gradient.
 template <int AC, bool GRAD>
-__device__ __forceinline__ void sample_terms(const LossArgs& p, int64_t i, float mean, float scale, float* pg,
-                                             float* v, float* h)
+__device__ __forceinline__ void terms_of(const LossArgs& p, int64_t i, bool write, const SampleIn<AC>& s, float mean,
+                                         float scale, float* pg, float* v, float* h)
 {
     const int A = AC > 0 ? AC : p.A;
-    int a = p.actions[i];
+    int a = s.a;
     if (a < 0 || a >= A) a = 0;   // an out-of-range action reads logit 0
     const float* row = p.logits + i * A;
-    float z[AC > 0 ? AC : 1];
-    if constexpr (AC > 0) load_row<AC>(row, z);
-    float mx, log_s, mean_u, u_a;
-    row_stats<AC>(z, row, A, a, &mx, &log_s, &mean_u, &u_a);
-    const float logp = u_a - log_s;
-    *h = log_s - mean_u;
-    const float ratio = expf(logp - p.old_logp[i]);
-    float adv = p.adv[i];
+    float ex[AC > 0 ? AC : 1];
+    RowStats r;
+    if constexpr (AC > 0) r = row_stats<AC>(s.z, a, ex);
+    else r = row_stats_mem(row, A, a);
+    const float logp = r.u_a - r.log_s;
+    *h = r.log_s - r.mean_u;
+    const float ratio = exp_hw(logp - s.old_logp);
+    float adv = s.adv;
     if (p.stats) adv = (adv - mean) * scale;
     const float clipped = fminf(fmaxf(ratio, p.clip_lo), p.clip_hi);
     const float s1 = ratio * adv, s2 = clipped * adv;
     *pg = -fminf(s1, s2);
-    const float dv = p.new_v[i] - p.ret[i];
+    const float dv = s.v - s.ret;
     *v = dv * dv;
     if constexpr (GRAD) {
+        if (!write) return;
+        // p_j = e^{u_j} / S, and log p_j + H = (u_j - log_s) + (log_s - mean_u) = u_j - mean_u
         const float c_pg = s1 <= s2 ? -adv * ratio * p.inv_mb : 0.0f;   // times ([j == a] - p_j)
         const float c_h = p.ent * p.inv_mb;                               // times p_j (log p_j + H)
-        const float H = *h;
-        const float lse = mx + log_s;
         float* g = p.dlogits + i * A;
         if constexpr (AC > 0) {
             float gz[AC];
 #pragma unroll
             for (int j = 0; j < AC; ++j) {
-                const float lp = z[j] - lse;
-                const float pj = expf(lp);
-                gz[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * (lp + H);
+                const float pj = ex[j] * r.inv_s;
+                gz[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * ((s.z[j] - r.mx) - r.mean_u);
             }
             if constexpr (AC % 4 == 0) {
 #pragma unroll
@@ -163,13 +210,22 @@ __device__ __forceinline__ void sample_terms(const LossArgs& p, int64_t i, float
             }
         } else {
             for (int j = 0; j < A; ++j) {
-                const float lp = row[j] - lse;
-                const float pj = expf(lp);
-                g[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * (lp + H);
+                const float u = row[j] - r.mx;
+                const float pj = exp_hw(u) * r.inv_s;
+                g[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * (u - r.mean_u);
             }
         }
         p.dvalues[i] = p.dv_coef * dv;
     }
+}
+
+template <int AC, bool GRAD>
+__device__ __forceinline__ void sample_terms(const LossArgs& p, int64_t i, float mean, float scale, float* pg,
+                                             float* v, float* h)
+{
+    SampleIn<AC> s;
+    load_sample<AC>(p, i, s);
+    terms_of<AC, GRAD>(p, i, true, s, mean, scale, pg, v, h);
 }
 
 template <int AC, bool GRAD>
@@ -205,8 +261,10 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 }
 
 // Stream mode: block b visits samples [b*chunk, min(B, (b+1)*chunk)) in storage order. THREADS * NB * 3
-// floats of LDS hold each thread's private per-minibatch sums (slot (j*3 + s)*THREADS + thread).
-template <int AC, int NB, int THREADS, bool GRAD>
+// floats of LDS hold each thread's private per-minibatch sums (slot (j*3 + s)*THREADS + thread). A
+// thread loads the inputs of its next U samples (indices clamped to the chunk, so the loads issue
+// together) before the arithmetic of the first; it still adds its samples in increasing index order.
+template <int AC, int NB, int THREADS, int U, bool GRAD>
 __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t chunk)
 {
     __shared__ float acc[NB * 3 * THREADS];
@@ -220,22 +278,52 @@ __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t
     }
     const int64_t lo = (int64_t)blockIdx.x * chunk;
     const int64_t hi = min(p.B, lo + chunk);
-    for (int64_t i = lo + t; i < hi; i += THREADS) {
-        const int mbi = min((int)p.mb_index[i], NB - 1);
-        float pg, v, h;
-        sample_terms<AC, GRAD>(p, i, mean, scale, &pg, &v, &h);
-        float* slot = acc + (mbi * 3) * THREADS + t;
-        slot[0] += pg;
-        slot[THREADS] += v;
-        slot[2 * THREADS] += h;
+    for (int64_t i0 = lo + t; i0 < hi; i0 += (int64_t)THREADS * U) {
+        SampleIn<AC> s[U];
+        int mbi[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = min(i0 + (int64_t)u * THREADS, hi - 1);
+            load_sample<AC>(p, i, s[u]);
+            mbi[u] = min((int)p.mb_index[i], NB - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // every sample's arithmetic runs (a clamped one on a copy of the chunk's last sample, which
+            // adds +0 to the sums and writes no gradient), so no load is moved behind a branch
+            const int64_t i = i0 + (int64_t)u * THREADS;
+            const bool valid = i < hi;
+            float pg, v, h;
+            terms_of<AC, GRAD>(p, min(i, hi - 1), valid, s[u], mean, scale, &pg, &v, &h);
+            float* slot = acc + (mbi[u] * 3) * THREADS + t;
+            slot[0] += valid ? pg : 0.0f;
+            slot[THREADS] += valid ? v : 0.0f;
+            slot[2 * THREADS] += valid ? h : 0.0f;
+        }
     }
     __syncthreads();
-    // thread j < num_mb * 3 sums slot row j over the threads in order
-    for (int j = t; j < p.num_mb * 3; j += THREADS) {
-        const float* row = acc + j * THREADS;
+    // Each slot row j < num_mb * 3 is summed over the threads in order: with enough threads, as four
+    // quarter sums (threads 4j .. 4j + 3, consecutive lanes of one wave) added left to right.
+    constexpr int Q = THREADS >= 4 * NB * 3 ? 4 : 1;
+    if constexpr (Q == 4) {
+        const int j = t >> 2, q = t & 3;
         double sum = 0.0;
-        for (int u = 0; u < THREADS; ++u) sum += (double)row[u];
-        p.partials[((int64_t)(j / 3) * gridDim.x + blockIdx.x) * 3 + (j % 3)] = sum;
+        if (j < p.num_mb * 3) {
+            const float* row = acc + j * THREADS + q * (THREADS / 4);
+            for (int u = 0; u < THREADS / 4; ++u) sum += (double)row[u];
+        }
+        const int first = (t & 63) & ~3;
+        const double q0 = __shfl(sum, first, 64), q1 = __shfl(sum, first + 1, 64);
+        const double q2 = __shfl(sum, first + 2, 64), q3 = __shfl(sum, first + 3, 64);
+        if (j < p.num_mb * 3 && q == 0)
+            p.partials[((int64_t)(j / 3) * gridDim.x + blockIdx.x) * 3 + (j % 3)] = ((q0 + q1) + q2) + q3;
+    } else {
+        for (int j = t; j < p.num_mb * 3; j += THREADS) {
+            const float* row = acc + j * THREADS;
+            double sum = 0.0;
+            for (int u = 0; u < THREADS; ++u) sum += (double)row[u];
+            p.partials[((int64_t)(j / 3) * gridDim.x + blockIdx.x) * 3 + (j % 3)] = sum;
+        }
     }
 }
 
@@ -272,7 +360,9 @@ int blocks_per_mb(int64_t mb)
 }
 
 constexpr int kStreamMaxMinibatches = 64;
-constexpr int kStreamBlocks = 2048;
+// Every stream variant holds 48 KB of LDS per block, so a CU keeps 3 blocks and 768 blocks are one
+// resident round on 256 CUs: no tail round of partly filled CUs.
+constexpr int kStreamBlocks = 768;
 
 // Stream-mode grid: blocks of `chunk` samples, at most kStreamBlocks of them.
 int stream_blocks(int64_t B, int64_t* chunk)
@@ -306,16 +396,18 @@ template <bool GRAD>
 void launch_loss(const LossArgs& p, int64_t num_mb, int A, bool stream_mode, int64_t chunk, int nblk, hipStream_t st)
 {
     if (stream_mode) {
+        // With 64 minibatches a CU holds 3 one-wave blocks, so each thread loads 4 samples ahead; with
+        // 8 or 12 waves per CU the loads of one sample per thread already keep HBM busy.
         const dim3 grid(nblk);
         if (num_mb <= 16) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256, GRAD>), grid, dim3(256), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256, GRAD>), grid, dim3(256), 0, st, p, chunk);
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256, 1, GRAD>), grid, dim3(256), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256, 1, GRAD>), grid, dim3(256), 0, st, p, chunk);
         } else if (num_mb <= 32) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128, GRAD>), grid, dim3(128), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128, GRAD>), grid, dim3(128), 0, st, p, chunk);
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128, 1, GRAD>), grid, dim3(128), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128, 1, GRAD>), grid, dim3(128), 0, st, p, chunk);
         } else {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64, GRAD>), grid, dim3(64), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64, GRAD>), grid, dim3(64), 0, st, p, chunk);
+            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64, 4, GRAD>), grid, dim3(64), 0, st, p, chunk);
+            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64, 1, GRAD>), grid, dim3(64), 0, st, p, chunk);
         }
     } else {
         const dim3 grid(nblk, (unsigned)num_mb);

@@ -46,7 +46,8 @@ def test_loss_matches_oracle(b, mb, use_perm, a, gpu_lib):
 
 
 @pytest.mark.parametrize("b,mb,a", [(262144, 8192, 12), (30000, 3000, 5), (600, 200, 3), (64000, 1000, 12),
-                                    (40000, 2500, 12), (1, 1, 12), (4096, 4096, 7)])
+                                    (40000, 2500, 12), (1, 1, 12), (4096, 4096, 7),
+                                    (3000000, 187500, 12)])   # blocks end partway through a load-ahead group
 def test_stream_mode_matches_oracle(b, mb, a, gpu_lib):
     # the minibatch split given as each sample's minibatch number, read in storage order
     pi, adv, ret = _case(b + 7 * mb + a, b, a)

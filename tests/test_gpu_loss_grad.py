@@ -50,7 +50,8 @@ def _check(pi, adv, ret, mb, mode, what, stats=None, adv_ref=None):
 @pytest.mark.parametrize("b,mb,a,mode", [
     (262144, 8192, 12, "stream"), (262144, 8192, 12, "perm"), (30000, 3000, 5, "stream"),
     (600, 200, 3, "stream"), (4096, 4096, 7, "stream"), (1, 1, 12, "stream"), (1000, 10, 12, "perm"),
-    (8192, 1024, 64, "contiguous"), (40000, 2500, 12, "stream"), (7, 1, 12, "perm")])
+    (8192, 1024, 64, "contiguous"), (40000, 2500, 12, "stream"), (7, 1, 12, "perm"),
+    (3000000, 187500, 12, "stream")])
 def test_grad_matches_oracle(b, mb, a, mode, gpu_lib):
     pi, adv, ret = _case(b + 3 * mb + a, b, a)
     _check(pi, adv, ret, mb, mode, f"grad {mode} B={b} mb={mb} A={a}")
