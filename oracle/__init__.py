@@ -68,9 +68,12 @@ def _load():
     lib.oracle_ppo_loss.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p]
     lib.oracle_ppo_loss_grad.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, f64, f64, f64, p, p, p, p, p, p]
     lib.oracle_vtrace.argtypes = [p, p, p, p, p, i32, i32, f64, f64, f64, f64, f64, p, p]
+    lib.oracle_policy_forward.argtypes = [p, i64, i64, p, p, ctypes.c_uint64, i64, i64, p, p, p]
+    lib.oracle_policy_gumbel.argtypes = [ctypes.c_uint64, i64, i64, i32, p]
+    lib.oracle_policy_gumbel.restype = f64
     for fn in (lib.oracle_env_reset, lib.oracle_env_step, lib.oracle_env_obs_tiles,
                lib.oracle_env_obs_pixels, lib.oracle_gae, lib.oracle_normalize, lib.oracle_ppo_loss,
-               lib.oracle_ppo_loss_grad, lib.oracle_vtrace, lib.oracle_bfs_path):
+               lib.oracle_ppo_loss_grad, lib.oracle_vtrace, lib.oracle_bfs_path, lib.oracle_policy_forward):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -266,3 +269,32 @@ def vtrace(rewards, values, dones, last_values, log_rhos, gamma, lam=1.0, rho_ba
 def respawn_draw(seed, counter, n, i):
     """The oracle's i-th respawn draw of global env n at decision `counter` (uint64)."""
     return int(_load().oracle_respawn_draw(int(seed) & (2 ** 64 - 1), int(counter), int(n), int(i)))
+
+
+POLICY_HIDDEN = 128
+POLICY_ACTIONS = 12
+
+
+def policy_forward(obs, enc_w, dec_w, seed, t, env_offset=0):
+    """The stand-in policy's inference for rows of obs (float32 [n][>= 1397]): returns (out float64
+    [n][13] = 12 logits then the value, actions int32 [n], logp float64 [n])."""
+    lib = _load()
+    obs = _c(obs, np.float32)
+    n, stride = obs.shape
+    enc_w = _c(enc_w, np.float32).reshape(POLICY_HIDDEN, OBS_TILES)
+    dec_w = _c(dec_w, np.float32).reshape(POLICY_ACTIONS + 1, POLICY_HIDDEN)
+    out = np.empty((n, POLICY_ACTIONS + 1), np.float64)
+    actions = np.empty(n, np.int32)
+    logp = np.empty(n, np.float64)
+    rc = lib.oracle_policy_forward(_ptr(obs), n, stride, _ptr(enc_w), _ptr(dec_w), int(seed) & ((1 << 64) - 1),
+                                   int(t), int(env_offset), _ptr(out), _ptr(actions), _ptr(logp))
+    if rc != 0:
+        raise ValueError("oracle_policy_forward rejected its arguments")
+    return out, actions, logp
+
+
+def policy_gumbel(seed, t, n, j):
+    """(g, u): the Gumbel variate of global env n, decision t, logit j, and its uniform draw."""
+    u = ctypes.c_double()
+    g = _load().oracle_policy_gumbel(int(seed) & ((1 << 64) - 1), int(t), int(n), int(j), ctypes.byref(u))
+    return g, u.value

@@ -11,7 +11,8 @@
  * Sources (page, then section):
  *   [MARIO]    "Teaching Mario to speedrun" (bigmah.com): s.4 Reward (the return G_t), s.5 (the reverse
  *              return loop), s.6 PPO (GAE, the clipped loss, the collect/judge/learn loop), s.7
- *              PufferLib (the four shared arrays, the vecenv step, the platformer step function).
+ *              PufferLib (the four shared arrays, the vecenv step, the platformer step function), s.8
+ *              (PufferLib 5.0's default policy: the shape of the stand-in inference).
  *   [DDNET]    boesch.dev DDNet RL post: "How it works each tick" (frame-skip 3, rewards accumulate
  *              between decisions, contiguous [actions|observations|rewards|dones]), "What the agent
  *              sees and does" (43x31 tile grid, 15-dim player state stacked 4 frames, 4 checkpoint
@@ -19,7 +20,8 @@
  *              order, high-water-mark progress, time penalty) and Version 2 (+100 finish).
  *   [PLAYTRAIN] "PlayTrain: An Efficient RL Framework for LLM-Generated Adaptable JavaScript Games":
  *              Table 4 (terminated / truncated at 2000), Table 8 (clip 0.2, value 0.5, entropy 0.01),
- *              App. B (frame stack, grayscale observation knobs).
+ *              App. B (frame stack, grayscale observation knobs), Figure 8C and Table 9 (double
+ *              buffering: one env group steps while the other's inference runs).
  *
  * The pages never fix the environment's mechanics; every constant and step of the tick below is a
  * reading, stated where it is used.
@@ -31,6 +33,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---------------------------------------------------------------------------------------------- */
@@ -808,5 +811,87 @@ int oracle_vtrace(const float *rewards, const float *values, const float *dones,
             pg_adv[k] = rho_pg * ((double)rewards[k] + g * vs_next - (double)values[k]);
         }
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------- */
+/* Stand-in policy inference, the work one env group's decision needs while the other group steps  */
+/* ([PLAYTRAIN] Figure 8C and Table 9: double buffering; App. C.3).                                 */
+/* The network's shape follows [MARIO] s.8 (PufferLib 5.0's default policy): a bias-free linear      */
+/* encoder from the observation to 128 numbers, and one decoder matrix from those to the logits plus */
+/* the value. Its recurrent layers between the two are left out of the stand-in. [MARIO] s.6 gives  */
+/* the heads: logits, one per action, sampled through a softmax, and the value.                     */
+/* Readings: the encoder reads the observation and its weights rounded to bfloat16 (round to nearest */
+/* even), the products summed exactly (float64 here); the decoder is float32 weights on the encoder's */
+/* output (float64 here); the sample is the Gumbel-max form of softmax sampling (Gumbel 1954; the    */
+/* "Gumbel-max trick"): a = argmax_j (logit_j + g_j), g_j = -ln(-ln u_j), lowest j on a tie, with    */
+/* u_j = (2 (x_j >> 41) + 1) / 2^24 and x_j = mix64(seed + GOLDEN_GAMMA (16 (t 2^24 + n) + j + 1)),   */
+/* the SplitMix64 output for global env n, decision t, logit j.                                      */
+/* ---------------------------------------------------------------------------------------------- */
+#define POLICY_HIDDEN 128
+#define POLICY_ACTIONS 12
+#define POLICY_OUT (POLICY_ACTIONS + 1)
+
+/* Round a float32 to the nearest bfloat16 (ties to even), returned as a float32 (finite inputs). */
+static float to_bf16(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    uint32_t lsb = (b >> 16) & 1u;
+    b = (b + 0x7FFFu + lsb) & 0xFFFF0000u;
+    float r;
+    memcpy(&r, &b, 4);
+    return r;
+}
+
+/* The uniform draw u_j in (0, 1) and its Gumbel variate, for the tests. */
+double oracle_policy_gumbel(uint64_t seed, int64_t t, int64_t n, int32_t j, double *u_out)
+{
+    uint64_t key = (uint64_t)t * ((uint64_t)1 << 24) + (uint64_t)n;
+    uint64_t x = mix64(seed + GOLDEN_GAMMA * (16 * key + (uint64_t)j + 1));
+    double u = (double)(2 * (x >> 41) + 1) / 16777216.0;
+    if (u_out) *u_out = u;
+    return -log(-log(u));
+}
+
+/* obs float32 [n][stride] (the first OBS_TILES of each row); enc_w float32 [128][OBS_TILES];
+ * dec_w float32 [13][128] (rows 0..11 the logits, row 12 the value). Writes out float64 [n][13]
+ * (logits then value), the sampled actions and log pi(a) = logit_a - logsumexp(logits). */
+int oracle_policy_forward(const float *obs, int64_t n, int64_t stride, const float *enc_w, const float *dec_w,
+                          uint64_t seed, int64_t t, int64_t env_offset, double *out, int32_t *actions,
+                          double *logp)
+{
+    if (n < 0 || stride < OBS_TILES || t < 0 || env_offset < 0) return -1;
+    double hidden[POLICY_HIDDEN], xq[OBS_TILES];
+    double *wq = malloc(sizeof(double) * POLICY_HIDDEN * OBS_TILES);   /* the rounded encoder weights */
+    if (!wq) return -1;
+    for (size_t i = 0; i < (size_t)POLICY_HIDDEN * OBS_TILES; ++i) wq[i] = (double)to_bf16(enc_w[i]);
+    for (int64_t e = 0; e < n; ++e) {
+        const float *x = obs + (size_t)e * stride;
+        for (int k = 0; k < OBS_TILES; ++k) xq[k] = (double)to_bf16(x[k]);
+        for (int h = 0; h < POLICY_HIDDEN; ++h) {
+            double s = 0.0;
+            for (int k = 0; k < OBS_TILES; ++k) s += xq[k] * wq[(size_t)h * OBS_TILES + k];
+            hidden[h] = s;
+        }
+        double *o = out + (size_t)e * POLICY_OUT;
+        for (int j = 0; j < POLICY_OUT; ++j) {
+            double s = 0.0;
+            for (int h = 0; h < POLICY_HIDDEN; ++h) s += hidden[h] * (double)dec_w[j * POLICY_HIDDEN + h];
+            o[j] = s;
+        }
+        int best = 0;
+        double best_score = 0.0, mx = o[0];
+        for (int j = 0; j < POLICY_ACTIONS; ++j) {
+            double score = o[j] + oracle_policy_gumbel(seed, t, env_offset + e, j, NULL);
+            if (j == 0 || score > best_score) { best = j; best_score = score; }
+            if (o[j] > mx) mx = o[j];
+        }
+        double z = 0.0;
+        for (int j = 0; j < POLICY_ACTIONS; ++j) z += exp(o[j] - mx);
+        actions[e] = best;
+        logp[e] = o[best] - (mx + log(z));
+    }
+    free(wq);
     return 0;
 }
