@@ -190,6 +190,9 @@ int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
 int rl_env_get_step_counter(const rl_env* env, int64_t* counter);
 int rl_env_set_step_counter(rl_env* env, int64_t counter);
 
+/* Copy of the configuration the env batch was created with. */
+int rl_env_get_config(const rl_env* env, rl_env_config* out);
+
 /* Free the host handle (the state buffer stays the caller's). NULL is ignored. */
 void rl_env_destroy(rl_env* env);
 
@@ -277,6 +280,73 @@ int rl_ppo_loss_grad(const float* logits, const int32_t* actions, const float* o
                      const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
                      float ent_coef, float* out, float* dlogits, float* dvalues, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* ---- Stand-in policy inference and the double-buffered rollout ---------------------------------- */
+
+/* The inference a decision needs, standing in for the trainer's policy: the shape of PufferLib 5.0's
+ * default policy ("Teaching Mario to speedrun", s.8: a bias-free linear encoder from the observation to
+ * 128 numbers, one decoder matrix to the logits plus the value; its recurrent layers are left out) and
+ * the heads of s.6 (12 logits sampled through a softmax, and the value). Weights are seeded stand-ins:
+ * nothing here is trained. */
+#define RL_POLICY_HIDDEN 128
+#define RL_POLICY_ACTIONS 12
+#define RL_ROLLOUT_MAX_GROUPS 8
+
+/* Bytes of the packed weights rl_policy_pack writes (bfloat16 encoder padded to 1408 columns, float32
+ * decoder). */
+int rl_policy_weights_bytes(size_t* bytes);
+
+/* Pack float32 weights into the caller's device buffer `packed` (256-byte aligned,
+ * rl_policy_weights_bytes bytes), on `stream`:
+ *   enc_w  device f32[128][1397]: hidden h = sum_k enc_w[h][k] obs[k] (rounded to bfloat16, nearest even);
+ *   dec_w  device f32[13][128]: rows 0..11 the action logits, row 12 the value. */
+int rl_policy_pack(const float* enc_w, const float* dec_w, void* packed, void* stream);
+
+/* Inference for envs env_offset .. env_offset + n - 1 (global indices, < 2^24) at decision t >= 0:
+ *   hidden = bf16(obs[e]) . bf16(enc_w)^T summed in float32 on the matrix cores; out = hidden . dec_w^T;
+ *   actions[e] = argmax_j (out[j] + g_j) over the 12 logits, lowest j on a tie, with the Gumbel variate
+ *   g_j = -ln(-ln u_j), u_j = (2 (x_j >> 41) + 1) / 2^24, x_j = SplitMix64 output
+ *   mix64(seed + 0x9E3779B97F4A7C15 (16 (t 2^24 + env_offset + e) + j + 1)) (the Gumbel-max form of
+ *   sampling from softmax(logits));
+ *   logp[e] = out[a] - logsumexp(out[0..11]);  values[e] = out[12].
+ *   obs device f32[n][obs_stride] (tile observations, obs_stride >= 1397); actions device int32[n];
+ *   logp, values device f32[n]. n = 0 does nothing. */
+int rl_policy_forward(const void* packed, const float* obs, int64_t n, int64_t obs_stride, uint64_t seed, int64_t t,
+                      int64_t env_offset, int32_t* actions, float* logp, float* values, void* stream);
+
+/* One env group of a rollout: decision t of the group's n envs (the env's num_envs) reads and writes
+ *   actions + t*row, logp + t*row, values + t*row, rewards + t*row, dones + t*row   (n elements each),
+ *   obs + t*obs_row                                                            (n x obs_stride floats),
+ * so two groups can own the two halves of one [T][N] rollout (row = N, obs_row = N * obs_stride, the
+ * second group's pointers offset by its first env). obs0 holds the observations decision 0 reads
+ * ([n][obs_stride], e.g. the reset's). env_offset is the global index of the group's first env (it keys
+ * the action draws). */
+typedef struct rl_rollout_group {
+    rl_env* env;
+    const float* obs0;
+    float* obs;
+    int32_t* actions;
+    float* logp;
+    float* values;
+    float* rewards;
+    float* dones;
+    int64_t row;
+    int64_t obs_row;
+    int64_t env_offset;
+    void* stream;
+} rl_rollout_group;
+
+/* Rollout decisions t0 .. t0 + steps - 1 of every group ("PlayTrain", Figure 8C and Table 9, double
+ * buffering). Per decision and per group, in group order, it enqueues on the group's stream the
+ * inference on the group's previous observations (obs0 at t = 0, else obs + (t-1)*obs_row), whose draws
+ * are keyed by the envs' decision counter, and then rl_env_step on the actions just written. One group
+ * is the single-buffered rollout; with two groups on two streams one group's step runs while the
+ * other's inference runs. With `alternate` the groups also take turns at the inference: group g's
+ * inference of a decision waits for group g-1's (group 0's waits for the last group's of the decision
+ * before), which keeps them out of phase. Every group's env must use tile observations and stand at the
+ * same decision counter. Results equal the single-buffered rollout's for the same envs. */
+int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups, int32_t num_groups, int32_t t0,
+               int32_t steps, int32_t alternate);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* rl_last_error(void);

@@ -39,6 +39,17 @@ class EnvConfig(ctypes.Structure):
                 ("respawn_mode", ctypes.c_int32), ("respawn_seed", ctypes.c_uint64)]
 
 
+POLICY_HIDDEN, POLICY_ACTIONS = 128, 12
+ROLLOUT_MAX_GROUPS = 8
+
+
+class RolloutGroup(ctypes.Structure):
+    _fields_ = [("env", ctypes.c_void_p), ("obs0", ctypes.c_void_p), ("obs", ctypes.c_void_p),
+                ("actions", ctypes.c_void_p), ("logp", ctypes.c_void_p), ("values", ctypes.c_void_p),
+                ("rewards", ctypes.c_void_p), ("dones", ctypes.c_void_p), ("row", ctypes.c_int64),
+                ("obs_row", ctypes.c_int64), ("env_offset", ctypes.c_int64), ("stream", ctypes.c_void_p)]
+
+
 # (name, restype, argtypes) of every symbol include/rl.h declares.
 _P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _CFG = ctypes.POINTER(EnvConfig)
@@ -56,6 +67,7 @@ SIGNATURES = [
     ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
     ("rl_env_get_step_counter", ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
     ("rl_env_set_step_counter", ctypes.c_int, [_P, _I64]),
+    ("rl_env_get_config", ctypes.c_int, [_P, _CFG]),
     ("rl_env_destroy", None, [_P]),
     ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
     ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -65,6 +77,10 @@ SIGNATURES = [
                                    _P, _SZ, _P]),
     ("rl_ppo_loss_grad", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32,
                                         _P, _P, _P, _P, _SZ, _P]),
+    ("rl_policy_weights_bytes", ctypes.c_int, [ctypes.POINTER(_SZ)]),
+    ("rl_policy_pack", ctypes.c_int, [_P, _P, _P, _P]),
+    ("rl_policy_forward", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_uint64, _I64, _I64, _P, _P, _P, _P]),
+    ("rl_rollout", ctypes.c_int, [_P, ctypes.c_uint64, ctypes.POINTER(RolloutGroup), _I32, _I32, _I32, _I32]),
     ("rl_last_error", ctypes.c_char_p, []),
 ]
 
@@ -331,3 +347,76 @@ def ppo_loss_grad(logits, actions, old_logp, adv, ret, new_values, perm, minibat
                                  dptr(out, torch.float32, "out"), dptr(dlogits, torch.float32, "dlogits"),
                                  dptr(dvalues, torch.float32, "dvalues"), dptr(ws), ws.numel(), stream_ptr(stream)))
     return out, dlogits, dvalues
+
+
+def _rows_view(t, dtype, what, inner):
+    """Device address and dim-0 stride (elements) of a [T][...] view whose inner `inner` elements per
+    row are contiguous."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype:
+        raise TypeError(f"{what} must be a {dtype} device tensor")
+    flat_inner = t[0].numel() if t.dim() > 1 else 1
+    if flat_inner != inner or not t[0].is_contiguous():
+        raise ValueError(f"{what}: each decision's {inner} elements must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0)
+
+
+class Policy:
+    """Packed stand-in policy weights on the device (rl_policy_pack): the encoder float32 [128][1397]
+    (stored as bfloat16) and the decoder float32 [13][128] (12 logits, then the value)."""
+
+    def __init__(self, enc_w, dec_w, seed=0, device="cuda", stream=None):
+        L = lib()
+        nb = ctypes.c_size_t()
+        check(L.rl_policy_weights_bytes(ctypes.byref(nb)))
+        self.device = torch.device(device)
+        self.seed = int(seed) & ((1 << 64) - 1)
+        self.packed = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+        self._enc = _dev(enc_w, torch.float32, self.device).reshape(POLICY_HIDDEN, OBS_TILES_SIZE).contiguous()
+        self._dec = _dev(dec_w, torch.float32, self.device).reshape(POLICY_ACTIONS + 1, POLICY_HIDDEN).contiguous()
+        check(L.rl_policy_pack(dptr(self._enc), dptr(self._dec), dptr(self.packed), stream_ptr(stream)))
+
+    def forward(self, obs, t, env_offset=0, actions=None, logp=None, values=None, stream=None):
+        """rl_policy_forward on obs float32 [n][stride]; returns (actions int32, logp, values float32 [n])."""
+        if obs.dim() != 2 or obs.stride(1) != 1:
+            raise ValueError("obs must be [n][stride] with contiguous rows")
+        n = obs.shape[0]
+        if actions is None:
+            actions = torch.empty(n, dtype=torch.int32, device=self.device)
+        if logp is None:
+            logp = torch.empty(n, dtype=torch.float32, device=self.device)
+        if values is None:
+            values = torch.empty(n, dtype=torch.float32, device=self.device)
+        if obs.dtype != torch.float32 or not obs.is_cuda:
+            raise TypeError("obs must be a float32 device tensor")
+        check(lib().rl_policy_forward(dptr(self.packed), ctypes.c_void_p(obs.data_ptr()), n, obs.stride(0),
+                                      self.seed, int(t), int(env_offset), dptr(actions, torch.int32, "actions"),
+                                      dptr(logp, torch.float32, "logp"), dptr(values, torch.float32, "values"),
+                                      stream_ptr(stream)))
+        return actions, logp, values
+
+
+def rollout_group(env, obs0, obs, actions, logp, values, rewards, dones, env_offset=0, stream=None):
+    """An rl_rollout_group over [T][n...] views (each decision's block contiguous; dim 0 may stride over
+    a wider [T][N] rollout)."""
+    n, d = env.num_envs, env.obs_stride
+    g = RolloutGroup()
+    g.env = env._handle
+    g.obs0 = None if obs0 is None else dptr(obs0, torch.float32, "obs0")
+    g.obs, g.obs_row = _rows_view(obs, torch.float32, "obs", n * d)
+    g.actions, g.row = _rows_view(actions, torch.int32, "actions", n)
+    for name, t in (("logp", logp), ("values", values), ("rewards", rewards), ("dones", dones)):
+        addr, row = _rows_view(t, torch.float32, name, n)
+        if row != g.row:
+            raise ValueError(f"{name} must have the same decision stride as actions")
+        setattr(g, name, addr)
+    g.env_offset = int(env_offset)
+    g.stream = stream_ptr(stream)
+    g._keep = (obs0, obs, actions, logp, values, rewards, dones)
+    return g
+
+
+def rollout(policy, groups, t0, steps, alternate=True):
+    """rl_rollout: decisions t0 .. t0 + steps - 1 of every group (see rollout_group)."""
+    arr = (RolloutGroup * len(groups))(*groups)
+    check(lib().rl_rollout(dptr(policy.packed), policy.seed, arr, len(groups), int(t0), int(steps),
+                           1 if alternate else 0))

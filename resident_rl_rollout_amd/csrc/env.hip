@@ -1334,6 +1334,13 @@ int rl_env_read_state(const rl_env* e, int32_t* out, void* stream)
     return rl::check_launch("read_state");
 }
 
+int rl_env_get_config(const rl_env* e, rl_env_config* out)
+{
+    if (!e || !out) return rl::fail(RL_EINVAL, "env and out must be non-NULL");
+    *out = e->cfg;
+    return RL_OK;
+}
+
 int rl_env_get_step_counter(const rl_env* e, int64_t* counter)
 {
     if (!e || !counter) return rl::fail(RL_EINVAL, "env and counter must be non-NULL");

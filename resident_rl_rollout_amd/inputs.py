@@ -187,6 +187,16 @@ def make_values(seed: int, t: int, n: int):
             rng.standard_normal(n, dtype=np.float32))
 
 
+def make_policy_weights(seed: int, enc_std: float = 0.01):
+    """Seeded stand-in weights of the inference: encoder f32[128][1397] ~ N(0, enc_std^2) (observation
+    norms are about 100, so hidden units come out about N(0, 1)) and decoder f32[13][128] ~ N(0, 1/128)
+    (logits and value about N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    enc = (rng.standard_normal((128, 1397)) * enc_std).astype(np.float32)
+    dec = (rng.standard_normal((13, 128)) / np.sqrt(128.0)).astype(np.float32)
+    return enc, dec
+
+
 # The five workloads, by what they are. Sizes only; the generators above draw their contents.
 WORKLOADS = {
     "tiny": dict(n=64, t=128, maps=1, map_h=32, map_w=128, map_seed0=1, action_seed=2, value_seed=3),

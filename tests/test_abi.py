@@ -19,7 +19,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("rl_env_create", "rl_env_reset", "rl_env_step", "rl_env_destroy", "rl_gae", "rl_ppo_loss",
-                     "rl_last_error"):
+                     "rl_policy_forward", "rl_rollout", "rl_last_error"):
         assert required in names
 
 
@@ -118,7 +118,24 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_ppo_loss_grad(*g, 100, 12, 10, 0.2, 0.5, 0.01, fake, ctypes.c_void_p(4100), fake, fake, 1 << 20,
                                 None) == -2
     assert lib.rl_ppo_loss_grad(*g, 100, 12, 30, 0.2, 0.5, 0.01, fake, fake, fake, fake, 1 << 20, None) == -1
-    need = ctypes.c_size_t()
+    # the stand-in policy and the rollout driver
+    assert lib.rl_policy_weights_bytes(ctypes.byref(need := ctypes.c_size_t())) == 0
+    assert need.value == 128 * 1408 * 2 + 13 * 128 * 4
+    assert lib.rl_policy_pack(None, fake, fake, None) == -1
+    assert lib.rl_policy_pack(fake, fake, ctypes.c_void_p(4096 + 16), None) == -2
+    assert lib.rl_policy_forward(None, fake, 10, 1397, 0, 0, 0, fake, fake, fake, None) == -1
+    assert lib.rl_policy_forward(fake, fake, 10, 1396, 0, 0, 0, fake, fake, fake, None) == -1
+    assert lib.rl_policy_forward(fake, fake, 10, 1397, 0, -1, 0, fake, fake, fake, None) == -1
+    assert lib.rl_policy_forward(fake, fake, 10, 1397, 0, 0, (1 << 24) - 5, fake, fake, fake, None) == -1
+    assert lib.rl_policy_forward(fake, None, 10, 1397, 0, 0, 0, fake, fake, fake, None) == -1
+    assert lib.rl_policy_forward(fake, fake, 0, 1397, 0, 0, 0, None, None, None, None) == 0   # n = 0: nothing
+    assert lib.rl_policy_forward(fake, ctypes.c_void_p(4098), 10, 1397, 0, 0, 0, fake, fake, fake, None) == -2
+    grp = (binding.RolloutGroup * 2)()
+    assert lib.rl_rollout(fake, 0, grp, 0, 0, 1, 1) == -1
+    assert lib.rl_rollout(fake, 0, grp, 9, 0, 1, 1) == -1
+    assert lib.rl_rollout(fake, 0, grp, 1, 0, 1, 1) == -1          # no env
+    assert lib.rl_rollout(fake, 0, grp, 1, -1, 1, 1) == -1
+    assert lib.rl_env_get_config(None, None) == -1
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
     assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128
 
