@@ -14,7 +14,7 @@ independent). GAE and loss GB/s come
 from separate repetitions after a read-only cache flush (their own HBM efficiency); their times inside the
 rollout, which also absorb the write-back of the rollout's last observations, are reported beside them.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload rollout|pixels]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload rollout|pixels|infer]
 """
 from __future__ import annotations
 
@@ -48,6 +48,12 @@ PIX_BYTES_PER_ENV_STEP = 4 * 84 * 84 + (4 + 20 + 8) + (20 + 8 + 4 + 4) + 4 * 8  
 GAE_BYTES_PER_ELEM = 5 * 4                            # r, v, d in; adv, ret out (statistics only: normalised in the loss)
 VTRACE_BYTES_PER_ELEM = 6 * 4                        # r, v, d, log rho in; vs, pg advantage out
 GRAD_BYTES_PER_SAMPLE = 12 * 4 + 4                   # the gradient row and the value gradient, written
+# The stand-in inference per env: the observation row read; the action, its log-probability and the value
+# written. Per launch also the packed weights once (bfloat16 encoder 128 x 1408, float32 decoder 13 x 128);
+# blocks re-read them from L2, which HBM does not see.
+POLICY_BYTES_PER_ENV = 1397 * 4 + 3 * 4               # 5600
+POLICY_WEIGHT_BYTES = 128 * 1408 * 2 + 13 * 128 * 4   # 367104
+POLICY_SEED = 31
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
                          "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
 
@@ -64,7 +70,9 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy, whose rocprofv3 FETCH_SIZE / WRITE_SIZE "
                         "scale the counters of the other kernels")
-    p.add_argument("--workload", choices=("rollout", "pixels"), default="rollout",
+    p.add_argument("--schedule", choices=("double", "alternate", "single"), default="double",
+                   help="infer workload: the schedule whose throughput is `value` (all three are measured)")
+    p.add_argument("--workload", choices=("rollout", "pixels", "infer"), default="rollout",
                    help="rollout: the tile-observation full rollout (the default bench line); pixels: 16384 envs "
                         "x 128 steps rendering 4 x 84 x 84 u8 frames, then GAE")
     p.add_argument("--reward", choices=("checkpoints", "waypoints"), default="checkpoints",
@@ -396,15 +404,194 @@ def main_pixels(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_infer(ms, enc, dec, pi, n_sample):
+    """The oracle as it stands, single-threaded, on the first n_sample envs of the inference workload:
+    per decision the stand-in inference on the env's observations, then the env step on its actions;
+    the bootstrap inference, GAE over the inferred values with normalisation, and the loss over the
+    sample's batch. Returns env-steps/s of the whole path."""
+    import oracle
+    n = n_sample
+    t0 = time.perf_counter()
+    env = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, **_env_kw())
+    env.reset()
+    obs = env.obs_tiles()
+    rew = np.empty((HORIZON, n), np.float32)
+    dn = np.empty((HORIZON, n), np.float32)
+    val = np.empty((HORIZON, n), np.float32)
+    act = np.empty((HORIZON, n), np.int32)
+    logp = np.empty((HORIZON, n), np.float32)
+    for t in range(HORIZON):
+        out, act[t], logp[t] = oracle.policy_forward(obs, enc, dec, POLICY_SEED, t)
+        val[t] = out[:, 12]
+        rew[t], dn[t] = env.step(act[t])
+        env.obs_tiles(obs)
+    out, _, _ = oracle.policy_forward(obs, enc, dec, POLICY_SEED, HORIZON)
+    adv, ret = oracle.gae(rew, val, dn, out[:, 12].astype(np.float32), float(np.float32(GAMMA)),
+                          float(np.float32(LAMBDA)))
+    na, _, _ = oracle.normalize(adv)
+    b = HORIZON * n
+    sel = (np.arange(HORIZON)[:, None] * N_ENVS + np.arange(n)[None, :]).reshape(-1)
+    perm = np.random.default_rng(5).permutation(b).astype(np.int32)
+    oracle.ppo_loss(pi.new_logits[sel], act.reshape(-1), logp.reshape(-1), na.reshape(-1), ret.reshape(-1),
+                    pi.new_values[sel], perm, b // MINIBATCHES)
+    dt = time.perf_counter() - t0
+    return b / dt, dt
+
+
+def main_infer(args):
+    """Rollouts with the stand-in inference in the loop: per decision the inference on the last
+    observations and the env step on its actions (rl_rollout), then a bootstrap inference, GAE over the
+    inferred values and the loss with the rollout's actions and log-probabilities. Three schedules of the
+    same work: single-buffered (one group of 65536 envs), double-buffered (two groups of 32768 on two
+    streams), and double-buffered with the groups taking turns at the inference."""
+    from resident_rl_rollout_amd import inputs
+
+    n, T = N_ENVS, HORIZON
+    ms = inputs.make_mapset(range(100, 100 + N_MAPS), MAP_H, MAP_W)
+    enc, dec = inputs.make_policy_weights(POLICY_SEED)
+    b = T * n
+    pi = inputs.make_policy_inputs(20, b)
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_s = min(args.cpu_envs, n)
+        rate, dt = cpu_baseline_infer(ms, enc, dec, pi, n_s)
+        cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} of the 65536 envs x 128 decisions (stand-in inference + env step + tile obs), "
+                         f"bootstrap inference, GAE + normalisation over [128][{n_s}], loss over the sample's "
+                         f"{T * n_s} samples in 16 minibatches; {dt:.1f} s single-threaded"}
+
+    import torch
+
+    from resident_rl_rollout_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+    pol = binding.Policy(enc, dec, seed=POLICY_SEED, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    obs = torch.empty((T, n, 1397), **f32)
+    actions = torch.empty((T, n), dtype=torch.int32, device=dev)
+    logp, values, rewards, dones = (torch.empty((T, n), **f32) for _ in range(4))
+    obs0 = torch.empty((n, 1397), **f32)
+    last_values = torch.empty(n, **f32)
+    boot_act = torch.empty(n, dtype=torch.int32, device=dev)
+    boot_logp = torch.empty(n, **f32)
+    adv = torch.empty((T, n), **f32)
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    loss_out = torch.empty((MINIBATCHES, 4), **f32)
+    logits, new_v = (torch.from_numpy(x).to(dev) for x in (pi.new_logits, pi.new_values))
+    mb_index = torch.from_numpy(inputs.minibatch_index(pi.perm, b // MINIBATCHES)).to(dev)
+    main_stream = torch.cuda.current_stream()
+
+    def schedule(groups, alternate):
+        per = n // groups
+        envs = [binding.Env(ms.maps, ms.ckpts, ms.spawns, per, frame_skip=3, time_limit=2000, device=dev)
+                for _ in range(groups)]
+        for g, e in enumerate(envs):
+            e.reset(obs0[g * per:(g + 1) * per])
+        streams = [torch.cuda.Stream(device=dev) for _ in range(groups)]
+        torch.cuda.synchronize()
+
+        def groups_from(start):
+            out = []
+            for g, e in enumerate(envs):
+                sl = slice(g * per, (g + 1) * per)
+                out.append(binding.rollout_group(e, start[sl], obs[:, sl], actions[:, sl], logp[:, sl], values[:, sl],
+                                                 rewards[:, sl], dones[:, sl], env_offset=g * per, stream=streams[g]))
+            return out
+        first, later = groups_from(obs0), groups_from(obs[T - 1])
+        state = {"k": 0}
+
+        def rollout():
+            grp = first if state["k"] == 0 else later
+            for s_ in streams:                 # the previous loss has read the buffers this rollout rewrites
+                s_.wait_stream(main_stream)
+            binding.rollout(pol, grp, 0, T, alternate=alternate)
+            for g, s_ in enumerate(streams):   # the bootstrap value of each group, on its own stream
+                sl = slice(g * per, (g + 1) * per)
+                pol.forward(obs[T - 1, sl], t=envs[g].step_counter, env_offset=g * per, actions=boot_act[sl],
+                            logp=boot_logp[sl], values=last_values[sl], stream=s_)
+            for s_ in streams:
+                main_stream.wait_stream(s_)
+            binding.gae(rewards, values, dones, last_values, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret,
+                        adv_stats=stats)
+            binding.ppo_loss(logits, actions.view(-1), logp.view(-1), adv.view(-1), ret.view(-1), new_v, None,
+                             b // MINIBATCHES, adv_stats=stats, out=loss_out, mb_index=mb_index)
+            state["k"] += 1
+
+        for _ in range(args.warmup):
+            rollout()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            rollout()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for e in envs:
+            e.close()
+        return {"value": args.steps * T * n / wall, "ms_per_step": wall / args.steps * 1e3}
+
+    results = {"single": schedule(1, False), "double": schedule(2, False), "alternate": schedule(2, True)}
+
+    # the inference kernel alone over a resident observation block, after a read-only cache flush
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush.zero_()
+    iso = []
+    for rep in range(args.iso_reps):
+        flush.sum()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pol.forward(obs[T // 2], t=rep, actions=boot_act, logp=boot_logp, values=last_values)
+        z.record()
+        torch.cuda.synchronize()
+        iso.append(a.elapsed_time(z))
+    del flush
+    pol_s = float(np.median(iso)) * 1e-3
+    launch_bytes = n * POLICY_BYTES_PER_ENV + POLICY_WEIGHT_BYTES
+    achieved = launch_bytes / pol_s / 1e9
+    chosen = results[args.schedule]
+    out = {
+        "metric": "env-steps/s of the whole rollout with the stand-in inference in the loop",
+        "value": chosen["value"],
+        "unit": "env-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": chosen["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i32+f32 env, bf16 x bf16 -> f32 encoder",
+        "data": "synthetic",
+        "config": {"workload": "inference rollout: 65536 envs x 128 decisions on 64 seeded 256x1024 maps; per "
+                               "decision a stand-in policy (seeded encoder 1397 -> 128, decoder -> 12 logits + "
+                               "value, Gumbel-max sampling) then the env step; bootstrap inference, GAE, loss in "
+                               "16 minibatches",
+                   "schedule": args.schedule, "num_envs": n, "horizon": T, "minibatches": MINIBATCHES},
+        "schedules": {k: {"value": v["value"], "ms_per_step": v["ms_per_step"],
+                          "vs_single": v["value"] / results["single"]["value"]} for k, v in results.items()},
+        "roofline": {"kernel": "stand-in inference (rl_policy_forward: k_policy_forward) at 65536 envs", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("policy_forward"), "bytes_per_launch": launch_bytes,
+                     "avg_launch_us": pol_s * 1e6},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.cpu_envs is None:
-        args.cpu_envs = 512 if args.workload == "pixels" else 16384
+        args.cpu_envs = {"pixels": 512, "infer": 256}.get(args.workload, 16384)
     if args.workload == "pixels":
         return main_pixels(args)
+    if args.workload == "infer":
+        return main_infer(args)
     from resident_rl_rollout_amd import inputs
 
     # ---- seeded inputs (host) ----

@@ -26,21 +26,25 @@ constexpr int kHidden = 128;
 constexpr int kActions = 12;
 constexpr int kOut = kActions + 1;
 constexpr int kRows = 64;                // envs per block
+constexpr int kThreads = kRows * 4;      // a wave per 16 rows for the loads; waves own 32 x 64 output tiles
+constexpr int kKsUnroll = 4;             // k-steps of a chunk whose fragments are read ahead
 constexpr int kKC = 128;                 // k elements per staged chunk
 constexpr int kChunks = kK / kKC;        // 11
 constexpr int kPitch = kKC + 8;          // LDS row pitch of a staged chunk, bfloat16 elements (272 bytes)
 constexpr int kHPitch = kHidden + 4;     // LDS row pitch of the hidden activations, floats
 constexpr size_t kEncBytes = sizeof(uint16_t) * kHidden * kK;   // 360,448
 constexpr size_t kDecBytes = sizeof(float) * kOut * kHidden;    // 6,656
-constexpr int kStageBytes = (kRows + kHidden) * kPitch * 2;     // 52,224
-constexpr int kEpilogueBytes = (kRows * kHPitch + kOut * kHidden) * 4;   // 40,448
+constexpr int kStageBytes = (kRows + kHidden) * kPitch * 2;     // 52,224 at 64 rows
+constexpr int kEpilogueBytes = (kRows * kHPitch + kOut * kHidden) * 4;   // 40,448 at 64 rows
+constexpr int kLdsBytes = kStageBytes > kEpilogueBytes ? kStageBytes : kEpilogueBytes;
 constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
 
 static_assert(kK % kKC == 0 && kK >= kObs, "chunks cover the padded encoder rows");
-static_assert(kEpilogueBytes <= kStageBytes, "the epilogue reuses the staging LDS");
+static_assert(kRows % 32 == 0 && (kHidden * kKC / 8) % kThreads == 0, "tiles and weight segments divide");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_bits(float x)
@@ -89,9 +93,9 @@ struct PolicyArgs {
 // chunk's loads are in flight while the current one multiplies. The epilogue parks the 64 x 128 hidden
 // values in LDS, applies the decoder (four threads per env, each a quarter of the hidden units in a fixed
 // order, combined by two exchanges) and draws the action.
-__global__ __launch_bounds__(256) void k_policy_forward(PolicyArgs p)
+__global__ __launch_bounds__(kThreads) void k_policy_forward(PolicyArgs p)
 {
-    __shared__ __align__(16) uint8_t lds[kStageBytes];
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
     uint16_t* As = reinterpret_cast<uint16_t*>(lds);   // [64][kPitch]
     uint16_t* Bs = As + kRows * kPitch;                 // [128][kPitch]
     const int t = threadIdx.x, l = t & 63;
@@ -100,44 +104,47 @@ __global__ __launch_bounds__(256) void k_policy_forward(PolicyArgs p)
     const int rh = w >> 1, ch = w & 1;
 
     float ra[16][2];   // observation rows 16 w + i, elements k0 + 2 l and k0 + 2 l + 1
-    uint4 rb[8];       // 16-byte segments t + 256 i of the weight chunk (column s >> 4, segment s & 15)
-    const float* rows[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) rows[i] = p.obs + min(e0 + w * 16 + i, p.n - 1) * p.stride;
+    constexpr int kSeg = kHidden * kKC / 8 / kThreads;   // 16-byte weight segments per thread and chunk
+    u32x4 rb[kSeg];    // segments t + kThreads i of the weight chunk (column s >> 4, segment s & 15)
+    // the wave's 16 rows (clamped to the last env) start at row0 + i * stride, i <= last
+    const float* row0 = p.obs + min(e0 + w * 16, p.n - 1) * p.stride;
+    const int last = (int)min<int64_t>(15, p.n - 1 - min(e0 + w * 16, p.n - 1));
 
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
         const int k0 = c * kKC;
         const int k = k0 + 2 * l;
         if (k0 + kKC <= kObs) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                ra[i][0] = rows[i][k];
-                ra[i][1] = rows[i][k + 1];
+                const float* r = row0 + (int64_t)min(i, last) * p.stride;
+                ra[i][0] = r[k];
+                ra[i][1] = r[k + 1];
             }
         } else {   // the last chunk: elements past the observation are zero
             const int ka = min(k, kObs - 1), kb = min(k + 1, kObs - 1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float a = rows[i][ka], b = rows[i][kb];
+                const float* r = row0 + (int64_t)min(i, last) * p.stride;
+                const float a = r[ka], b = r[kb];
                 ra[i][0] = k < kObs ? a : 0.0f;
                 ra[i][1] = k + 1 < kObs ? b : 0.0f;
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int s = i * 256 + t;
-            rb[i] = *reinterpret_cast<const uint4*>(p.enc + (size_t)(s >> 4) * kK + k0 + (s & 15) * 8);
+        for (int i = 0; i < kSeg; ++i) {
+            const int s = i * kThreads + t;
+            rb[i] = *reinterpret_cast<const u32x4*>(p.enc + (size_t)(s >> 4) * kK + k0 + (s & 15) * 8);
         }
     };
-    auto store_chunk = [&]() {
+    auto store_chunk = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             *reinterpret_cast<uint32_t*>(As + (w * 16 + i) * kPitch + 2 * l) =
                 bf16_bits(ra[i][0]) | (bf16_bits(ra[i][1]) << 16);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int s = i * 256 + t;
-            *reinterpret_cast<uint4*>(Bs + (s >> 4) * kPitch + (s & 15) * 8) = rb[i];
+        for (int i = 0; i < kSeg; ++i) {
+            const int s = i * kThreads + t;
+            *reinterpret_cast<u32x4*>(Bs + (s >> 4) * kPitch + (s & 15) * 8) = rb[i];
         }
     };
 
@@ -153,11 +160,11 @@ __global__ __launch_bounds__(256) void k_policy_forward(PolicyArgs p)
         const uint16_t* pa = As + (rh * 32 + (l & 31)) * kPitch + 8 * (l >> 5);
         const uint16_t* pb0 = Bs + (ch * 64 + (l & 31)) * kPitch + 8 * (l >> 5);
         const uint16_t* pb1 = pb0 + 32 * kPitch;
-#pragma unroll
+#pragma unroll kKsUnroll
         for (int ks = 0; ks < kKC / 16; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pa + ks * 16));
-            const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb0 + ks * 16));
-            const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb1 + ks * 16));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pa + ks * 16));
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pb0 + ks * 16));
+            const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pb1 + ks * 16));
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
         }
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(256) void k_policy_forward(PolicyArgs p)
         Hs[row * kHPitch + ch * 64 + (l & 31)] = acc0[r];
         Hs[row * kHPitch + ch * 64 + 32 + (l & 31)] = acc1[r];
     }
-    for (int i = t; i < kOut * kHidden; i += 256) Ds[i] = p.dec[i];
+    for (int i = t; i < kOut * kHidden; i += kThreads) Ds[i] = p.dec[i];
     __syncthreads();
 
     const int e = t >> 2, q = t & 3;
@@ -297,7 +304,7 @@ int rl_policy_forward(const void* packed, const float* obs, int64_t n, int64_t o
     p.actions = actions;
     p.logp = logp;
     p.values = values;
-    hipLaunchKernelGGL(k_policy_forward, dim3((unsigned)((n + kRows - 1) / kRows)), dim3(256), 0,
+    hipLaunchKernelGGL(k_policy_forward, dim3((unsigned)((n + kRows - 1) / kRows)), dim3(kThreads), 0,
                        rl::as_stream(stream), p);
     return rl::check_launch("policy_forward");
 }
