@@ -484,6 +484,9 @@ def main_infer(args):
     logits, new_v = (torch.from_numpy(x).to(dev) for x in (pi.new_logits, pi.new_values))
     mb_index = torch.from_numpy(inputs.minibatch_index(pi.perm, b // MINIBATCHES)).to(dev)
     main_stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
 
     def schedule(groups, alternate):
         per = n // groups

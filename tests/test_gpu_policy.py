@@ -69,6 +69,25 @@ def test_forward_matches_oracle_on_random_observations(gpu_lib, n, stride, offse
                  f"n={n} stride={stride} offset={offset}")
 
 
+def test_wide_launches_equal_narrow_ones_and_the_oracle(gpu_lib):
+    # 65536 envs and more take 128-env blocks, smaller launches 64-env blocks: per-env results are the same
+    n = 65536 + 77
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    obs = torch.randint(0, 4, (n, OBS), generator=gen, device="cuda").float()
+    obs[:, 1333:] = torch.randn((n, OBS - 1333), generator=gen, device="cuda") * 20
+    enc, dec = inputs.make_policy_weights(12)
+    pol = binding.Policy(enc, dec, seed=8)
+    a, lp, v = pol.forward(obs, t=5)
+    parts = [pol.forward(obs[lo:hi], t=5, env_offset=lo) for lo, hi in ((0, 40000), (40000, n))]
+    for got, want in zip((a, lp, v), (torch.cat([p_[k] for p_ in parts]) for k in range(3))):
+        assert torch.equal(got, want)
+    # against the oracle: the first two blocks, the ragged last block, and single rows in between
+    segments = [(0, 130), (n - 200, n)] + [(int(r), int(r) + 1) for r in np.random.default_rng(0).choice(n - 200, 40)]
+    for lo, hi in segments:
+        check_policy(obs[lo:hi].cpu().numpy(), enc, dec, 8, 5, lo, a[lo:hi].cpu().numpy(), lp[lo:hi].cpu().numpy(),
+                     v[lo:hi].cpu().numpy(), f"rows {lo}..{hi}")
+
+
 def test_forward_reads_exactly_the_observation_row(gpu_lib):
     # a padded stride with poison past element 1397 and a last row at the very end of its allocation
     n, stride = 130, 1400
