@@ -123,7 +123,8 @@ int rl_env_reset(rl_env* env, const uint8_t* mask, void* obs, void* stream);
 
 /* The waypoint path of every map, for RL_REWARD_WAYPOINTS ("boesch.dev DDNet RL post", Reward Engineering,
  * Version 2: progress along a path traced through the map, e.g. by rl_waypoint_path). Copies
- *   waypoints  device int32[M][max_waypoints][2] (column, row) of the path's tiles, in order, and
+ *   waypoints  device int32[M][max_waypoints][2] (column, row) of the path's tiles, in order (tiles of
+ *              the map: 0 <= column < map_w, 0 <= row < map_h, where the distances are exact), and
  *   lens       device int32[M] path length of each map (values outside 1 .. max_waypoints are clamped)
  * into the state buffer on `stream`; the inputs may be freed once the stream has passed this call. Must
  * be called before the first rl_env_step of a waypoint-reward env (the step fails otherwise); RL_EINVAL

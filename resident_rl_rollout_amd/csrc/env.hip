@@ -346,7 +346,9 @@ struct Decision {
 // the high-water index and the kWpAhead after it (the lowest index on a tie); moving the high-water index
 // forward pays kUnitsWaypoint per waypoint; a distance d = floor(sqrt(d2)) beyond the grace zone costs
 // (d - kWpGrace) >> kWpPenaltyShift units. The candidates are loaded unconditionally (indices clamped to
-// the path's end) so that the loads issue together; d2 is exact in int64, d is needed only past the zone.
+// the path's end) so that the loads issue together. Squared distances are exact in float64: positions
+// and waypoint centres lie below 2^25 sub-units, so d2 < 2^51 (full-rate float64 instead of 64-bit
+// integer multiplies); d = floor(sqrt(d2)) is checked against d2 exactly, and needed only past the zone.
 __device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_t x, int32_t y, int32_t& path)
 {
     const int32_t len = clampi(d.wplen[m], 1, d.kw);
@@ -355,14 +357,14 @@ __device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_
     int2 w[kWpAhead + 1];
 #pragma unroll
     for (int j = 0; j <= kWpAhead; ++j) w[j] = row[min(path + j, len - 1)];
-    const int64_t cx = (int64_t)x + kHalfBox, cy = (int64_t)y + kHalfBox;
+    const double cx = (double)(x + kHalfBox), cy = (double)(y + kHalfBox);
     int32_t best = path;
-    int64_t best_d2 = 0;
+    double best_d2 = 0.0;
 #pragma unroll
     for (int j = 0; j <= kWpAhead; ++j) {
-        const int64_t dx = cx - ((int64_t)w[j].x * kTile + kTile / 2);
-        const int64_t dy = cy - ((int64_t)w[j].y * kTile + kTile / 2);
-        const int64_t d2 = dx * dx + dy * dy;
+        const double dx = cx - (double)(w[j].x * kTile + kTile / 2);
+        const double dy = cy - (double)(w[j].y * kTile + kTile / 2);
+        const double d2 = fma(dx, dx, dy * dy);
         if (j == 0 || (path + j < len && d2 < best_d2)) {
             best_d2 = d2;
             best = path + j;
@@ -373,11 +375,11 @@ __device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_
         units += (best - path) * kUnitsWaypoint;
         path = best;
     }
-    if (best_d2 >= (int64_t)(kWpGrace + 1) * (kWpGrace + 1)) {
-        int64_t r = (int64_t)sqrt((double)best_d2);   // then corrected to the exact integer floor
-        while (r * r > best_d2) --r;
-        while ((r + 1) * (r + 1) <= best_d2) ++r;
-        units -= (int32_t)((r - kWpGrace) >> kWpPenaltyShift);
+    if (best_d2 >= (double)((kWpGrace + 1) * (kWpGrace + 1))) {
+        double r = floor(sqrt(best_d2));   // then checked to be the exact integer floor
+        while (r * r > best_d2) r -= 1.0;
+        while ((r + 1.0) * (r + 1.0) <= best_d2) r += 1.0;
+        units -= (int32_t)(((int64_t)r - kWpGrace) >> kWpPenaltyShift);
     }
     return units;
 }
@@ -828,7 +830,7 @@ __device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int l
 }
 
 template <int E, int MODE>
-__global__ __launch_bounds__(256) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
                                                     int head_new)
