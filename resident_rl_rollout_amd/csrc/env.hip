@@ -829,62 +829,59 @@ __device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int l
     }
 }
 
+// Phase A for env e (< ne) of the group starting at n0: every physics-independent load first, then the
+// decision; the 64 non-window observation values go to tail[e] and the window's top-left offset to wbase[e].
 template <int E, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
-                                                    float* __restrict__ rewards, float* __restrict__ dones,
-                                                    float* __restrict__ obs, int64_t stride, int head_prev,
-                                                    int head_new)
+__device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const int32_t* __restrict__ actions,
+                                           float* __restrict__ rewards, float* __restrict__ dones, int head_prev,
+                                           int head_new, float (*tail)[kTail], int64_t* wbase)
 {
-    static_assert(E % 4 == 0 && E <= 64, "whole envs per wave; one lane per env in phase A");
-    __shared__ uint32_t wwin[E][kWinDwords + 1];
-    __shared__ float tail[E][kTail];
-    __shared__ int64_t wbase[E];
-    const int n0 = blockIdx.x * E;
-    const int ne = min(E, d.n - n0);
-
-    if ((int)threadIdx.x < ne) {
-        const int e = threadIdx.x;
-        const int n = n0 + e;
-        const int m = n % d.m;
-        const int32_t a = actions[n];
-        const SlotWords cur = load_slot(d, head_prev, n);
-        const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
-        const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
-        const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
-        const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
-        const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
-        const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, rewards, dones, head_new);
-        float* t = tail[e];
-        put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
-        if (s.done) {
+    const int n = n0 + e;
+    const int m = n % d.m;
+    const int32_t a = actions[n];
+    const SlotWords cur = load_slot(d, head_prev, n);
+    const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
+    const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
+    const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
+    const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
+    const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
+    const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, rewards, dones, head_new);
+    float* t = tail[e];
+    put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
+    if (s.done) {
 #pragma unroll
-            for (int f = 1; f < kStack; ++f)
+        for (int f = 1; f < kStack; ++f)
 #pragma unroll
-                for (int dim = 0; dim < kFrameDims; ++dim) t[f * kFrameDims + dim] = t[dim];
-        } else {
-            put_frame(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
-            put_frame(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
-            put_frame(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
-        }
-        float* ck = t + kStack * kFrameDims;
-        if (s.next < d.k) {
-            const int32_t* p = d.ckpt + ((int64_t)m * d.k + s.next) * 2;
-            ck[0] = (float)(p[0] * kTile + kTile / 2 - (s.x + kHalfBox)) * 0x1p-8f;
-            ck[1] = (float)(p[1] * kTile + kTile / 2 - (s.y + kHalfBox)) * 0x1p-8f;
-        } else {
-            ck[0] = 0.0f;
-            ck[1] = 0.0f;
-        }
-        ck[2] = (float)s.next;
-        ck[3] = (float)s.best_x * 0x1p-8f;
-        const int pcol = clampi((s.x + kHalfBox) >> 8, 0, d.w - 1);
-        const int prow = clampi((s.y + kHalfBox) >> 8, 0, d.h - 1);
-        wbase[e] = tile_ptr(d, m, prow - kWinCy, pcol - kWinCx) - d.map;
+            for (int dim = 0; dim < kFrameDims; ++dim) t[f * kFrameDims + dim] = t[dim];
+    } else {
+        put_frame(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
+        put_frame(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
+        put_frame(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
     }
-    __syncthreads();
+    float* ck = t + kStack * kFrameDims;
+    if (s.next < d.k) {
+        const int32_t* p = d.ckpt + ((int64_t)m * d.k + s.next) * 2;
+        ck[0] = (float)(p[0] * kTile + kTile / 2 - (s.x + kHalfBox)) * 0x1p-8f;
+        ck[1] = (float)(p[1] * kTile + kTile / 2 - (s.y + kHalfBox)) * 0x1p-8f;
+    } else {
+        ck[0] = 0.0f;
+        ck[1] = 0.0f;
+    }
+    ck[2] = (float)s.next;
+    ck[3] = (float)s.best_x * 0x1p-8f;
+    const int pcol = clampi((s.x + kHalfBox) >> 8, 0, d.w - 1);
+    const int prow = clampi((s.y + kHalfBox) >> 8, 0, d.h - 1);
+    wbase[e] = tile_ptr(d, m, prow - kWinCy, pcol - kWinCx) - d.map;
+}
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+// Phase B for the group starting at n0 (ne envs), by four waves: wave w owns envs w, w + 4, ... It first
+// reads its envs' windows from the padded map into wwin (loads and stores share one in-order completion
+// counter, so every load goes before the first store), then writes each env's observation row.
+template <int E>
+__device__ __forceinline__ void write_group(const EnvDev& d, int n0, int ne, int wave, int lane,
+                                            uint32_t (*wwin)[kWinDwords + 1], const float (*tail)[kTail],
+                                            const int64_t* wbase, float* __restrict__ obs, int64_t stride)
+{
     constexpr int EW = E / 4;                 // envs per wave
     constexpr int EB = EW <= 6 ? EW : 4;      // windows in registers at once
     static_assert(EW % EB == 0, "whole batches");
@@ -905,6 +902,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     for (int e = wave; e < ne; e += 4) write_row(wwin[e], tail[e], obs + (int64_t)(n0 + e) * stride, lane);
+}
+
+template <int E, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+                                                    float* __restrict__ rewards, float* __restrict__ dones,
+                                                    float* __restrict__ obs, int64_t stride, int head_prev,
+                                                    int head_new)
+{
+    static_assert(E % 4 == 0 && E <= 64, "whole envs per wave; one lane per env in phase A");
+    __shared__ uint32_t wwin[E][kWinDwords + 1];
+    __shared__ float tail[E][kTail];
+    __shared__ int64_t wbase[E];
+    const int n0 = blockIdx.x * E;
+    const int ne = min(E, d.n - n0);
+    if ((int)threadIdx.x < ne)
+        decide_env<E, MODE>(d, n0, threadIdx.x, actions, rewards, dones, head_prev, head_new, tail, wbase);
+    __syncthreads();
+    write_group<E>(d, n0, ne, threadIdx.x >> 6, threadIdx.x & 63, wwin, tail, wbase, obs, stride);
 }
 
 // ------------------------------------------------------------------------------------------------
