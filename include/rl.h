@@ -342,7 +342,10 @@ typedef struct rl_rollout_group {
  * inference on the group's previous observations (obs0 at t = 0, else obs + (t-1)*obs_row), whose draws
  * are keyed by the envs' decision counter, and then rl_env_step on the actions just written. One group
  * is the single-buffered rollout; with two groups on two streams one group's step runs while the
- * other's inference runs. With `alternate` the groups also take turns at the inference: group g's
+ * other's inference runs. The buffers must hold rows t0 .. t0 + steps - 1 (the library does not know
+ * their length); every check (NULL buffers, 4-byte alignment, row lengths, env offsets, matching decision
+ * counters) runs before anything is enqueued. With `alternate` the groups also take turns at the
+ * inference: group g's
  * inference of a decision waits for group g-1's (group 0's waits for the last group's of the decision
  * before), which keeps them out of phase. Every group's env must use tile observations and stand at the
  * same decision counter. Results equal the single-buffered rollout's for the same envs. */

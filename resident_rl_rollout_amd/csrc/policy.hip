@@ -337,6 +337,9 @@ int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups
         const int64_t n = cfg[g].num_envs;
         if (!x.actions || !x.logp || !x.values || !x.obs || !x.rewards || !x.dones || (t0 == 0 && !x.obs0))
             return rl::fail(RL_EINVAL, "group %d: a buffer is NULL", g);
+        const void* ptrs[] = {x.obs0, x.obs, x.actions, x.logp, x.values, x.rewards, x.dones};
+        for (const void* q : ptrs)
+            if (q && !rl::aligned(q, 4)) return rl::fail(RL_EALIGN, "group %d: a buffer is not 4-byte aligned", g);
         if (x.row < n || x.obs_row < n * cfg[g].obs_stride)
             return rl::fail(RL_EINVAL, "group %d: row %lld / obs_row %lld shorter than one decision's data", g,
                             (long long)x.row, (long long)x.obs_row);

@@ -208,6 +208,23 @@ def test_double_buffered_equals_single_buffered(gpu_lib, groups, alternate):
         assert torch.equal(one[k], many[k]), f"{groups} groups, alternate={alternate}: {k} differs"
 
 
+def test_double_buffered_at_the_bench_size(gpu_lib):
+    # 65536 envs on the bench's map set for 3 decisions: the single-buffered rollout takes the 128-env
+    # inference blocks, the two 32768-env groups the 64-env blocks; every buffer must agree bit for bit
+    ms = inputs.make_mapset(range(100, 164), 256, 1024)
+    enc, dec = inputs.make_policy_weights(31)
+    pol = binding.Policy(enc, dec, seed=31)
+    one = _run(pol, ms, 65536, 3, 1, False, time_limit=2000)
+    two = _run(pol, ms, 65536, 3, 2, False, time_limit=2000)
+    for k in one:
+        assert torch.equal(one[k], two[k]), k
+    # the first decision's inference against the oracle on the first and last 128 envs
+    for lo in (0, 65536 - 128):
+        sl = slice(lo, lo + 128)
+        check_policy(one["obs0"][sl].cpu().numpy(), enc, dec, 31, 0, lo, one["actions"][0, sl].cpu().numpy(),
+                     one["logp"][0, sl].cpu().numpy(), one["values"][0, sl].cpu().numpy(), f"envs {lo}..")
+
+
 def test_rollout_resumes_across_calls(gpu_lib):
     ms = _mapset()
     n, t = 192, 9
@@ -236,6 +253,11 @@ def test_rollout_rejects_mismatched_groups(gpu_lib):
                                b["dones"][:, i * 64:(i + 1) * 64], env_offset=64 * i) for i, e in enumerate((e1, e2))]
     with pytest.raises(binding.RLError, match="decision counter"):
         binding.rollout(pol, g, 0, 1)
+    bad = binding.rollout_group(e1, obs0[:64], b["obs"][:, :64], b["actions"][:, :64], b["logp"][:, :64],
+                                b["values"][:, :64], b["rewards"][:, :64], b["dones"][:, :64])
+    bad.logp = bad.logp + 2                                   # misaligned: refused before anything is enqueued
+    with pytest.raises(binding.RLError, match="4-byte aligned"):
+        binding.rollout(pol, [bad], 0, 1)
     pix = binding.Env(ms.maps, ms.ckpts, ms.spawns, 64, obs_mode=binding.OBS_PIXELS, sprites=inputs.make_sprites())
     gp = binding.RolloutGroup()
     gp.env = pix._handle
