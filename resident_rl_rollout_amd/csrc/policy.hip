@@ -91,8 +91,8 @@ struct PolicyArgs {
 // [ROWS x 1408] x [1408 x 128] runs on v_mfma_f32_32x32x16_bf16: wave w owns rows 32 (w >> 1) .. +32 and
 // columns 64 (w & 1) .. +64 (two 32 x 32 tiles). The observation and weight chunks of 128 k are staged in
 // LDS as bfloat16; the next chunk's loads are in flight while the current one multiplies. The epilogue
-// parks the ROWS x 128 hidden values in LDS, applies the decoder (four threads per env, each a quarter of
-// the hidden units in a fixed order, combined by two exchanges) and draws the action.
+// parks the ROWS x 128 hidden values in LDS, applies the decoder (four threads per env, each a contiguous
+// quarter of the hidden units in order, combined by two exchanges) and draws the action.
 // Measured at 65536 envs with 128 rows: 87-94 us. Without the observation loads the kernel still takes
 // 63 us and without the weight loads 88 us: it is bound by the latency of its chunk pipeline (one chunk
 // of loads in flight per block, two barriers per chunk), not by HBM; 64-k chunks (twice the steps) run
@@ -190,15 +190,23 @@ __global__ __launch_bounds__(ROWS * 4) void k_policy_forward(PolicyArgs p)
     for (int i = t; i < kOut * kHidden; i += kThreads) Ds[i] = p.dec[i];
     __syncthreads();
 
+    // thread (e, q) sums hidden units 32 q .. 32 q + 31 of env e in order, four at a time (16-byte LDS reads)
     const int e = t >> 2, q = t & 3;
     float o[kOut];
 #pragma unroll
     for (int j = 0; j < kOut; ++j) o[j] = 0.0f;
-    for (int hh = 0; hh < kHidden / 4; ++hh) {
-        const int h = 4 * hh + q;
-        const float x = Hs[e * kHPitch + h];
+    const float4* hx = reinterpret_cast<const float4*>(Hs + e * kHPitch + 32 * q);
+#pragma unroll 2
+    for (int i = 0; i < 8; ++i) {
+        const float4 x = hx[i];
 #pragma unroll
-        for (int j = 0; j < kOut; ++j) o[j] = fmaf(x, Ds[j * kHidden + h], o[j]);
+        for (int j = 0; j < kOut; ++j) {
+            const float4 wj = reinterpret_cast<const float4*>(Ds + j * kHidden + 32 * q)[i];
+            o[j] = fmaf(x.x, wj.x, o[j]);
+            o[j] = fmaf(x.y, wj.y, o[j]);
+            o[j] = fmaf(x.z, wj.z, o[j]);
+            o[j] = fmaf(x.w, wj.w, o[j]);
+        }
     }
     // the four quarters: (p0 + p1) + (p2 + p3), the same bits in all four lanes
 #pragma unroll
