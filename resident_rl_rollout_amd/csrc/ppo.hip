@@ -167,7 +167,7 @@ __device__ __forceinline__ void load_sample(const LossArgs& p, int64_t i, Sample
 // with GRAD and `write` also the sample's gradient row and value gradient.
 template <int AC, bool GRAD>
 __device__ __forceinline__ void terms_of(const LossArgs& p, int64_t i, bool write, const SampleIn<AC>& s, float mean,
-                                         float scale, float* pg, float* v, float* h)
+                                         float scale, float* pg, float* v, float* h, float* gz_out = nullptr)
 {
     const int A = AC > 0 ? AC : p.A;
     int a = s.a;
@@ -200,7 +200,10 @@ __device__ __forceinline__ void terms_of(const LossArgs& p, int64_t i, bool writ
                 const float pj = ex[j] * r.inv_s;
                 gz[j] = c_pg * ((j == a ? 1.0f : 0.0f) - pj) + c_h * pj * ((s.z[j] - r.mx) - r.mean_u);
             }
-            if constexpr (AC % 4 == 0) {
+            if (gz_out) {   // the caller stores the row
+#pragma unroll
+                for (int j = 0; j < AC; ++j) gz_out[j] = gz[j];
+            } else if constexpr (AC % 4 == 0) {
 #pragma unroll
                 for (int j = 0; j < AC / 4; ++j)
                     reinterpret_cast<float4*>(g)[j] = make_float4(gz[4 * j], gz[4 * j + 1], gz[4 * j + 2], gz[4 * j + 3]);
@@ -294,7 +297,39 @@ __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t
             const int64_t i = i0 + (int64_t)u * THREADS;
             const bool valid = i < hi;
             float pg, v, h;
-            terms_of<AC, GRAD>(p, min(i, hi - 1), valid, s[u], mean, scale, &pg, &v, &h);
+            if constexpr (GRAD && AC == 12) {
+                // the wave's 64 samples are consecutive: when all are in the chunk, its 64 gradient rows
+                // (3 KB, contiguous) go out as three 1 KB stores, each lane's 16 bytes gathered from the
+                // lanes that own them; else every lane stores its own row
+                float gz[12];
+                terms_of<AC, GRAD>(p, min(i, hi - 1), valid, s[u], mean, scale, &pg, &v, &h, gz);
+                const int L = t & 63;
+                const int64_t base = i - L;
+                if (base + 63 < hi) {
+                    float4* dst = reinterpret_cast<float4*>(p.dlogits + base * 12);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        // float 256 j + 4 L + c of the block is element 4 ((j + L) mod 3) + c of sample
+                        // (256 j + 4 L + c) / 12
+                        const int sel = (j + L) % 3;
+                        float out[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int src = (256 * j + 4 * L + c) / 12;
+                            const float v0 = __shfl(gz[c], src, 64), v1 = __shfl(gz[c + 4], src, 64),
+                                        v2 = __shfl(gz[c + 8], src, 64);
+                            out[c] = sel == 0 ? v0 : (sel == 1 ? v1 : v2);
+                        }
+                        dst[64 * j + L] = make_float4(out[0], out[1], out[2], out[3]);
+                    }
+                } else if (valid) {
+                    float4* g4 = reinterpret_cast<float4*>(p.dlogits + i * 12);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) g4[j] = make_float4(gz[4 * j], gz[4 * j + 1], gz[4 * j + 2], gz[4 * j + 3]);
+                }
+            } else {
+                terms_of<AC, GRAD>(p, min(i, hi - 1), valid, s[u], mean, scale, &pg, &v, &h);
+            }
             float* slot = acc + (mbi[u] * 3) * THREADS + t;
             slot[0] += valid ? pg : 0.0f;
             slot[THREADS] += valid ? v : 0.0f;
