@@ -590,7 +590,7 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.cpu_envs is None:
-        args.cpu_envs = {"pixels": 512, "infer": 256}.get(args.workload, 16384)
+        args.cpu_envs = {"pixels": 2048, "infer": 1024}.get(args.workload, 32768)   # 10-15 s single-threaded
     if args.workload == "pixels":
         return main_pixels(args)
     if args.workload == "infer":
