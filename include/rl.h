@@ -217,6 +217,17 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
            int32_t T, int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize,
            double* adv_stats, void* ws, size_t ws_bytes, void* stream);
 
+/* rl_gae over N columns of wider [T][ld] arrays (ld >= N elements between rows; last_values stays f32[N]
+ * contiguous): rewards, values, dones, adv and ret address element [t][n] at t * ld + n, and elements
+ * outside the N columns are neither read nor written. This is the per-minibatch form ("Teaching Mario
+ * to speedrun", s.8: PufferLib 5.0 computes advantages per minibatch from fresh values): a minibatch of
+ * envs n0 .. n0 + N - 1 of a [T][ld] rollout passes its column pointers (base + n0) and its fresh values
+ * in the same layout, and normalize = 1 / 2 use that minibatch's own statistics. rl_gae is this call with
+ * ld = N; the same kernel runs for the same T and N, so the results are the same bits. */
+int rl_gae_strided(const float* rewards, const float* values, const float* dones, const float* last_values,
+                   int32_t T, int32_t N, int64_t ld, float gamma, float lambda, float* adv, float* ret,
+                   int32_t normalize, double* adv_stats, void* ws, size_t ws_bytes, void* stream);
+
 /* V-trace over a [T][N] rollout: the IMPALA off-policy targets and policy-gradient advantages (PlayTrain
  * App. C.3 takes V-trace from torchbeast for its IMPALA trainer; "Teaching Mario to speedrun" s.8 names it
  * beside GAE for per-minibatch advantages). Restated from the published definition (Espeholt et al. 2018,
@@ -232,6 +243,12 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
 int rl_vtrace(const float* rewards, const float* values, const float* dones, const float* last_values,
               const float* log_rhos, int32_t T, int32_t N, float gamma, float lambda, float rho_bar, float c_bar,
               float pg_rho_bar, float* vs, float* pg_adv, void* stream);
+
+/* rl_vtrace over N columns of [T][ld] arrays (rewards, values, dones, log_rhos, vs, pg_adv), as for
+ * rl_gae_strided; rl_vtrace is this call with ld = N. */
+int rl_vtrace_strided(const float* rewards, const float* values, const float* dones, const float* last_values,
+                      const float* log_rhos, int32_t T, int32_t N, int64_t ld, float gamma, float lambda,
+                      float rho_bar, float c_bar, float pg_rho_bar, float* vs, float* pg_adv, void* stream);
 
 /* Workspace bytes rl_ppo_loss needs for B samples in minibatches of mb. */
 int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);

@@ -72,6 +72,9 @@ SIGNATURES = [
     ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
     ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
     ("rl_vtrace", ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _F32, _P, _P, _P]),
+    ("rl_gae_strided", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I64, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    ("rl_vtrace_strided", ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I64, _F32, _F32, _F32, _F32, _F32, _P, _P,
+                                         _P]),
     ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
     ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P,
                                    _P, _SZ, _P]),
@@ -266,9 +269,23 @@ def gae_workspace_bytes(t: int, n: int) -> int:
     return b.value
 
 
+def _rows(x, what, ld=None):
+    """Address and row stride of a [T][N] float32 device view whose rows are contiguous; every such
+    argument of one call must share the row stride."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.float32 or x.dim() != 2:
+        raise TypeError(f"{what} must be a 2-D float32 device tensor")
+    if x.stride(1) != 1 or (x.shape[0] > 1 and x.stride(0) < x.shape[1]):
+        raise ValueError(f"{what}: rows must be contiguous")
+    stride = x.stride(0) if x.shape[0] > 1 else (ld if ld is not None else x.shape[1])
+    if ld is not None and stride != ld:
+        raise ValueError(f"{what}: row stride {stride} differs from the other arrays' {ld}")
+    return ctypes.c_void_p(x.data_ptr()), stride
+
+
 def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, ret=None, adv_stats=None,
         ws=None, stream=None):
-    """rl_gae over [T][N] float32 device tensors; returns (adv, ret, adv_stats)."""
+    """rl_gae over [T][N] float32 device tensors; returns (adv, ret, adv_stats). The [T][N] arguments may be
+    column ranges of wider arrays (rows contiguous, one shared row stride): then rl_gae_strided runs."""
     t, n = rewards.shape
     dev = rewards.device
     adv = torch.empty((t, n), dtype=torch.float32, device=dev) if adv is None else adv
@@ -277,12 +294,12 @@ def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, 
         adv_stats = torch.zeros(3, dtype=torch.float64, device=dev)
     if normalize and ws is None:
         ws = workspace("gae", gae_workspace_bytes(t, n), dev)
-    check(lib().rl_gae(dptr(rewards, torch.float32, "rewards"), dptr(values, torch.float32, "values"),
-                       dptr(dones, torch.float32, "dones"), dptr(last_values, torch.float32, "last_values"),
-                       t, n, float(gamma), float(lam), dptr(adv, torch.float32, "adv"),
-                       dptr(ret, torch.float32, "ret"), int(normalize),
-                       dptr(adv_stats, torch.float64, "adv_stats"), dptr(ws), 0 if ws is None else ws.numel(),
-                       stream_ptr(stream)))
+    r_p, ld = _rows(rewards, "rewards")
+    ptrs = [r_p] + [_rows(x, name, ld)[0] for x, name in ((values, "values"), (dones, "dones"))]
+    out = [_rows(x, name, ld)[0] for x, name in ((adv, "adv"), (ret, "ret"))]
+    check(lib().rl_gae_strided(*ptrs, dptr(last_values, torch.float32, "last_values"), t, n, ld, float(gamma),
+                               float(lam), *out, int(normalize), dptr(adv_stats, torch.float64, "adv_stats"),
+                               dptr(ws), 0 if ws is None else ws.numel(), stream_ptr(stream)))
     return adv, ret, adv_stats
 
 
@@ -290,13 +307,14 @@ def vtrace(rewards, values, dones, last_values, log_rhos, gamma, lam=1.0, rho_ba
            vs=None, pg_adv=None, stream=None):
     """rl_vtrace over [T][N]; returns (vs, pg_adv)."""
     t, n = rewards.shape
-    vs = torch.empty_like(rewards) if vs is None else vs
-    pg_adv = torch.empty_like(rewards) if pg_adv is None else pg_adv
-    check(lib().rl_vtrace(dptr(rewards, torch.float32, "rewards"), dptr(values, torch.float32, "values"),
-                          dptr(dones, torch.float32, "dones"), dptr(last_values, torch.float32, "last_values"),
-                          dptr(log_rhos, torch.float32, "log_rhos"), t, n, float(gamma), float(lam), float(rho_bar),
-                          float(c_bar), float(pg_rho_bar), dptr(vs, torch.float32, "vs"),
-                          dptr(pg_adv, torch.float32, "pg_adv"), stream_ptr(stream)))
+    vs = torch.empty((t, n), dtype=torch.float32, device=rewards.device) if vs is None else vs
+    pg_adv = torch.empty((t, n), dtype=torch.float32, device=rewards.device) if pg_adv is None else pg_adv
+    r_p, ld = _rows(rewards, "rewards")
+    ins = [r_p] + [_rows(x, name, ld)[0] for x, name in ((values, "values"), (dones, "dones"))]
+    check(lib().rl_vtrace_strided(*ins, dptr(last_values, torch.float32, "last_values"),
+                                  _rows(log_rhos, "log_rhos", ld)[0], t, n, ld, float(gamma), float(lam),
+                                  float(rho_bar), float(c_bar), float(pg_rho_bar), _rows(vs, "vs", ld)[0],
+                                  _rows(pg_adv, "pg_adv", ld)[0], stream_ptr(stream)))
     return vs, pg_adv
 
 

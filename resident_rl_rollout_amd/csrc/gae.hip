@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void k_stats_finalize(const double* __restrict
 template <int E, int LMAX, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__ rew, const float* __restrict__ val,
                                                      const float* __restrict__ done, const float* __restrict__ vlast,
-                                                     int T, int N, int L, float gamma, float gl,
+                                                     int T, int N, int64_t ld, int L, float gamma, float gl,
                                                      float* __restrict__ adv, float* __restrict__ ret,
                                                      int want_stats, StatsOut so)
 {
@@ -101,12 +101,12 @@ __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__
     float delta[LMAX], cf[LMAX], vv[LMAX];
 #pragma unroll
     for (int j = 0; j < LMAX; ++j) {
-        const int64_t idx = (int64_t)min(t0 + j, T - 1) * N + nn;
+        const int64_t idx = (int64_t)min(t0 + j, T - 1) * ld + nn;
         vv[j] = val[idx];
         delta[j] = rew[idx];
         cf[j] = 1.0f - done[idx];
     }
-    const float v_after = val[(int64_t)min(t0 + len, T - 1) * N + nn];
+    const float v_after = val[(int64_t)min(t0 + len, T - 1) * ld + nn];
     const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
 
     float b = 0.0f, c = 1.0f;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__
     for (int j = LMAX - 1; j >= 0; --j) {
         if (j < len) {
             a = delta[j] + cf[j] * a;
-            const int64_t idx = (int64_t)(t0 + j) * N + n;
+            const int64_t idx = (int64_t)(t0 + j) * ld + n;
             adv[idx] = a;
             ret[idx] = a + vv[j];
             s1 += (double)a;
@@ -146,15 +146,16 @@ __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__
 // One lane per env walking t = T-1 .. 0: the fallback for horizons longer than the chunked kernels hold.
 __global__ __launch_bounds__(256) void k_gae_seq(const float* __restrict__ rew, const float* __restrict__ val,
                                                  const float* __restrict__ done, const float* __restrict__ vlast,
-                                                 int T, int N, float gamma, float gl, float* __restrict__ adv,
-                                                 float* __restrict__ ret, int want_stats, StatsOut so)
+                                                 int T, int N, int64_t ld, float gamma, float gl,
+                                                 float* __restrict__ adv, float* __restrict__ ret, int want_stats,
+                                                 StatsOut so)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     double s1 = 0.0, s2 = 0.0;
     if (n < N) {
         float a = 0.0f, vn = vlast[n];
         for (int t = T - 1; t >= 0; --t) {
-            const int64_t idx = (int64_t)t * N + n;
+            const int64_t idx = (int64_t)t * ld + n;
             const float v = val[idx];
             const float nd = 1.0f - done[idx];
             const float delta = rew[idx] + gamma * vn * nd - v;
@@ -188,6 +189,19 @@ __global__ __launch_bounds__(256) void k_normalize(float* __restrict__ adv, int6
         adv[i] = (adv[i] - mean) * scale;
 }
 
+// The same over a [T][N] block of rows ld elements apart (normalize = 1 on a column range).
+__global__ __launch_bounds__(256) void k_normalize_rows(float* __restrict__ adv, int T, int N, int64_t ld,
+                                                        const double* __restrict__ stats)
+{
+    const float mean = (float)stats[1];
+    const float scale = (float)(1.0 / (stats[2] + kNormEps));
+    const int64_t count = (int64_t)T * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
+        float* a = adv + (i / N) * ld + i % N;
+        *a = (*a - mean) * scale;
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // V-trace targets and policy-gradient advantages (the IMPALA off-policy correction that PlayTrain's
 // IMPALA trainer takes from torchbeast, App. C.3; "Teaching Mario to speedrun" s.8 names it beside GAE),
@@ -208,8 +222,9 @@ struct VtraceCoef {
 template <int E, int LMAX, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restrict__ rew, const float* __restrict__ val,
                                                         const float* __restrict__ done, const float* __restrict__ vlast,
-                                                        const float* __restrict__ lrho, int T, int N, int L,
-                                                        VtraceCoef k, float* __restrict__ vs, float* __restrict__ pg)
+                                                        const float* __restrict__ lrho, int T, int N, int64_t ld,
+                                                        int L, VtraceCoef k, float* __restrict__ vs,
+                                                        float* __restrict__ pg)
 {
     constexpr int C = BLOCK / E;
     __shared__ float sb[C][E];
@@ -225,13 +240,13 @@ __global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restric
     float td[LMAX], ratio[LMAX], nd[LMAX], vv[LMAX];
 #pragma unroll
     for (int j = 0; j < LMAX; ++j) {
-        const int64_t idx = (int64_t)min(t0 + j, T - 1) * N + nn;
+        const int64_t idx = (int64_t)min(t0 + j, T - 1) * ld + nn;
         vv[j] = val[idx];
         td[j] = rew[idx];
         nd[j] = 1.0f - done[idx];
         ratio[j] = lrho[idx];
     }
-    const float v_after = val[(int64_t)min(t0 + len, T - 1) * N + nn];
+    const float v_after = val[(int64_t)min(t0 + len, T - 1) * ld + nn];
     const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
 
     float b = 0.0f, c = 1.0f;
@@ -259,7 +274,7 @@ __global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restric
     for (int j = LMAX - 1; j >= 0; --j) {
         if (j < len) {
             const float g = k.gamma * nd[j];
-            const int64_t idx = (int64_t)(t0 + j) * N + n;
+            const int64_t idx = (int64_t)(t0 + j) * ld + n;
             pg[idx] = fminf(k.pg_rho_bar, ratio[j]) * (td[j] + g * a);
             a = fminf(k.rho_bar, ratio[j]) * td[j] + g * k.lambda * fminf(k.c_bar, ratio[j]) * a;
             vs[idx] = a + vv[j];
@@ -270,14 +285,14 @@ __global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restric
 // One lane per env walking t = T-1 .. 0: V-trace for horizons longer than the chunked kernels hold.
 __global__ __launch_bounds__(256) void k_vtrace_seq(const float* __restrict__ rew, const float* __restrict__ val,
                                                     const float* __restrict__ done, const float* __restrict__ vlast,
-                                                    const float* __restrict__ lrho, int T, int N, VtraceCoef k,
-                                                    float* __restrict__ vs, float* __restrict__ pg)
+                                                    const float* __restrict__ lrho, int T, int N, int64_t ld,
+                                                    VtraceCoef k, float* __restrict__ vs, float* __restrict__ pg)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
     float a = 0.0f, vn = vlast[n];
     for (int t = T - 1; t >= 0; --t) {
-        const int64_t idx = (int64_t)t * N + n;
+        const int64_t idx = (int64_t)t * ld + n;
         const float v = val[idx];
         const float g = k.gamma * (1.0f - done[idx]);
         const float ratio = expf(lrho[idx]);
@@ -328,12 +343,13 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes)
     return RL_OK;
 }
 
-int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values, int32_t T,
-           int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize, double* adv_stats,
-           void* ws, size_t ws_bytes, void* stream)
+int rl_gae_strided(const float* rewards, const float* values, const float* dones, const float* last_values,
+                   int32_t T, int32_t N, int64_t ld, float gamma, float lambda, float* adv, float* ret,
+                   int32_t normalize, double* adv_stats, void* ws, size_t ws_bytes, void* stream)
 {
     if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
-    if ((int64_t)T * N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "T*N too large");
+    if (ld < N) return rl::fail(RL_EINVAL, "row stride %lld < N %d", (long long)ld, N);
+    if ((T - 1) * ld + N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "(T-1)*ld + N too large");
     if (!rewards || !values || !dones || !last_values || !adv || !ret)
         return rl::fail(RL_EINVAL, "rewards, values, dones, last_values, adv and ret must be non-NULL");
     if (normalize < 0 || normalize > 2) return rl::fail(RL_EINVAL, "normalize %d outside {0, 1, 2}", normalize);
@@ -341,7 +357,6 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     const void* ptrs[] = {rewards, values, dones, last_values, adv, ret};
     for (const void* p : ptrs)
         if (!rl::aligned(p, 4)) return rl::fail(RL_EALIGN, "a float array is not 4-byte aligned");
-    if (normalize == 1 && !rl::aligned(adv, 16)) return rl::fail(RL_EALIGN, "adv must be 16-byte aligned to normalize");
     size_t need = 0;
     rl_gae_workspace_bytes(T, N, &need);
     if (normalize != 0) {
@@ -357,28 +372,28 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     const dim3 grid(blocks_of(k, N)), block(256);
     switch (k) {
     case GaeKernel::C32x8_16:
-        hipLaunchKernelGGL((k_gae_chunked<32, 16, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<32, 16, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N, ld,
                            (T + 7) / 8, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_8:
-        hipLaunchKernelGGL((k_gae_chunked<16, 8, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 8, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N, ld,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_32:
-        hipLaunchKernelGGL((k_gae_chunked<16, 32, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 32, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N, ld,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C16x16_64:
-        hipLaunchKernelGGL((k_gae_chunked<16, 64, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N,
+        hipLaunchKernelGGL((k_gae_chunked<16, 64, 256>), grid, block, 0, st, rewards, values, dones, last_values, T, N, ld,
                            (T + 15) / 16, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::C256x4_32:
         hipLaunchKernelGGL((k_gae_chunked<256, 32, 1024>), grid, dim3(1024), 0, st, rewards, values, dones,
-                           last_values, T, N, (T + 3) / 4, gamma, gl, adv, ret, want, so);
+                           last_values, T, N, ld, (T + 3) / 4, gamma, gl, adv, ret, want, so);
         break;
     case GaeKernel::Seq:
-        hipLaunchKernelGGL(k_gae_seq, grid, block, 0, st, rewards, values, dones, last_values, T, N, gamma, gl, adv,
-                           ret, want, so);
+        hipLaunchKernelGGL(k_gae_seq, grid, block, 0, st, rewards, values, dones, last_values, T, N, ld, gamma, gl,
+                           adv, ret, want, so);
         break;
     }
     if (int rc = rl::check_launch("gae_scan")) return rc;
@@ -389,19 +404,33 @@ int rl_gae(const float* rewards, const float* values, const float* dones, const 
     }
     if (normalize == 1) {
         const int64_t count = (int64_t)T * N;
-        const int nb = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 8192);
-        hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, st, adv, count, adv_stats);
+        if (ld == N && rl::aligned(adv, 16)) {   // one contiguous block: float4 passes
+            const int nb = (int)std::min<int64_t>((count / 4 + 255) / 256 + 1, 8192);
+            hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, st, adv, count, adv_stats);
+        } else {
+            const int nb = (int)std::min<int64_t>((count + 255) / 256, 8192);
+            hipLaunchKernelGGL(k_normalize_rows, dim3(nb), dim3(256), 0, st, adv, T, N, ld, adv_stats);
+        }
         if (int rc = rl::check_launch("adv_normalize")) return rc;
     }
     return RL_OK;
 }
 
-int rl_vtrace(const float* rewards, const float* values, const float* dones, const float* last_values,
-              const float* log_rhos, int32_t T, int32_t N, float gamma, float lambda, float rho_bar, float c_bar,
-              float pg_rho_bar, float* vs, float* pg_adv, void* stream)
+int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values, int32_t T,
+           int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize, double* adv_stats,
+           void* ws, size_t ws_bytes, void* stream)
+{
+    return rl_gae_strided(rewards, values, dones, last_values, T, N, N, gamma, lambda, adv, ret, normalize, adv_stats,
+                          ws, ws_bytes, stream);
+}
+
+int rl_vtrace_strided(const float* rewards, const float* values, const float* dones, const float* last_values,
+                      const float* log_rhos, int32_t T, int32_t N, int64_t ld, float gamma, float lambda,
+                      float rho_bar, float c_bar, float pg_rho_bar, float* vs, float* pg_adv, void* stream)
 {
     if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
-    if ((int64_t)T * N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "T*N too large");
+    if (ld < N) return rl::fail(RL_EINVAL, "row stride %lld < N %d", (long long)ld, N);
+    if ((T - 1) * ld + N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "(T-1)*ld + N too large");
     if (!rewards || !values || !dones || !last_values || !log_rhos || !vs || !pg_adv)
         return rl::fail(RL_EINVAL, "rewards, values, dones, last_values, log_rhos, vs and pg_adv must be non-NULL");
     if (!(rho_bar >= 0.0f) || !(c_bar >= 0.0f) || !(pg_rho_bar >= 0.0f))
@@ -413,22 +442,30 @@ int rl_vtrace(const float* rewards, const float* values, const float* dones, con
     const VtraceCoef k{gamma, lambda, rho_bar, c_bar, pg_rho_bar};
     if (T <= 128 && (N + 127) / 128 >= 256) {
         hipLaunchKernelGGL((k_vtrace_chunked<128, 16, 1024>), dim3((N + 127) / 128), dim3(1024), 0, st, rewards, values,
-                           dones, last_values, log_rhos, T, N, (T + 7) / 8, k, vs, pg_adv);
+                           dones, last_values, log_rhos, T, N, ld, (T + 7) / 8, k, vs, pg_adv);
     } else if (T <= 128) {
         hipLaunchKernelGGL((k_vtrace_chunked<16, 8, 256>), dim3((N + 15) / 16), dim3(256), 0, st, rewards, values,
-                           dones, last_values, log_rhos, T, N, (T + 15) / 16, k, vs, pg_adv);
+                           dones, last_values, log_rhos, T, N, ld, (T + 15) / 16, k, vs, pg_adv);
     } else if (T <= 256) {
         hipLaunchKernelGGL((k_vtrace_chunked<16, 16, 256>), dim3((N + 15) / 16), dim3(256), 0, st, rewards, values,
-                           dones, last_values, log_rhos, T, N, (T + 15) / 16, k, vs, pg_adv);
+                           dones, last_values, log_rhos, T, N, ld, (T + 15) / 16, k, vs, pg_adv);
     } else if (T <= 512) {
         // four per-step arrays of 32 steps would not fit the register file: 32 chunks of up to 16 steps
         hipLaunchKernelGGL((k_vtrace_chunked<8, 16, 256>), dim3((N + 7) / 8), dim3(256), 0, st, rewards, values,
-                           dones, last_values, log_rhos, T, N, (T + 31) / 32, k, vs, pg_adv);
+                           dones, last_values, log_rhos, T, N, ld, (T + 31) / 32, k, vs, pg_adv);
     } else {
         hipLaunchKernelGGL(k_vtrace_seq, dim3((N + 255) / 256), dim3(256), 0, st, rewards, values, dones, last_values,
-                           log_rhos, T, N, k, vs, pg_adv);
+                           log_rhos, T, N, ld, k, vs, pg_adv);
     }
     return rl::check_launch("vtrace");
+}
+
+int rl_vtrace(const float* rewards, const float* values, const float* dones, const float* last_values,
+              const float* log_rhos, int32_t T, int32_t N, float gamma, float lambda, float rho_bar, float c_bar,
+              float pg_rho_bar, float* vs, float* pg_adv, void* stream)
+{
+    return rl_vtrace_strided(rewards, values, dones, last_values, log_rhos, T, N, N, gamma, lambda, rho_bar, c_bar,
+                             pg_rho_bar, vs, pg_adv, stream);
 }
 
 }  // extern "C"

@@ -136,6 +136,11 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_rollout(fake, 0, grp, 1, 0, 1, 1) == -1          # no env
     assert lib.rl_rollout(fake, 0, grp, 1, -1, 1, 1) == -1
     assert lib.rl_env_get_config(None, None) == -1
+    # strided GAE / V-trace: a row stride below the width
+    assert lib.rl_gae_strided(fake, fake, fake, fake, 4, 64, 63, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
+    assert "row stride" in lib.rl_last_error().decode()
+    assert lib.rl_vtrace_strided(fake, fake, fake, fake, fake, 4, 64, 10, 0.99, 1.0, 1.0, 1.0, 1.0, fake, fake,
+                                 None) == -1
     assert lib.rl_policy_forward(fake, fake, 10, 1397, 0, 0, 0, ctypes.c_void_p(4098), fake, fake, None) == -2
     assert lib.rl_ppo_loss_workspace_bytes(100, 10, ctypes.byref(need)) == 0 and need.value > 8
     assert lib.rl_gae_workspace_bytes(128, 2048, ctypes.byref(need)) == 0 and need.value >= 16 * 128
