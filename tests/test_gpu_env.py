@@ -144,6 +144,14 @@ def test_pixels_small(gpu_lib):
     _run_and_check(pe, inputs.make_actions(31, 40, 256), "pixels")
 
 
+def test_pixels_ragged_batch_and_padded_stride(gpu_lib):
+    # 257 envs (a partial wave in the physics kernel) and rows of 28228 bytes (not a 16-byte multiple)
+    ms = inputs.make_mapset(range(110, 113), 256, 1024)
+    sprites = inputs.make_sprites(31)
+    pe = PairedEnvs(ms, 257, obs_mode=binding.OBS_PIXELS, sprites=sprites, obs_stride=28228)
+    _run_and_check(pe, inputs.make_actions(33, 30, 257), "pixels n=257 stride 28228", obs_every=5)
+
+
 def test_pixels_workload_full_size(gpu_lib):
     ms = inputs.make_mapset(range(100, 164), 256, 1024)
     sprites = inputs.make_sprites(30)
