@@ -19,7 +19,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-NF = 18            # canonical state fields per env
+NF = 24            # canonical state fields per env
 RESPAWN_BUF = 64   # outcomes in each map's respawn buffer
 STACK = 4
 FRAME_DIMS = 15
@@ -27,7 +27,7 @@ OBS_TILES = 31 * 43 + STACK * FRAME_DIMS + 4   # 1397
 PIX = 84
 STATE_FIELDS = ("x", "y", "vx", "vy", "facing", "freeze_ticks", "hook_ticks", "hook_held", "jump_held",
                 "grounded", "wall_left", "wall_right", "tick", "next_ckpt", "best_x", "last_action", "path",
-                "from_start")
+                "from_start", "hook_phase", "hook_x", "hook_y", "hook_vx", "hook_vy", "hook_flight")
 
 
 def build() -> str:
@@ -42,7 +42,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("num_envs", "env_offset", "num_maps", "map_h", "map_w", "num_ckpts", "frame_skip",
-                 "time_limit", "reward_mode", "max_waypoints", "respawn_mode")]
+                 "time_limit", "reward_mode", "max_waypoints", "respawn_mode", "hook_mode")]
 
 
 def _load():
@@ -57,7 +57,7 @@ def _load():
     cfgp = ctypes.POINTER(_Cfg)
     lib.oracle_env_reset.argtypes = [cfgp, p, p, p, p]
     lib.oracle_env_step.argtypes = [cfgp, p, p, p, p, p, p, p, p, p, p, ctypes.c_uint64, i64, p,
-                                    p, p, p, p, p]
+                                    p, p, p, p, p, p]
     lib.oracle_bfs_path.argtypes = [p, i32, i32, i32, i32, i32, i32, p, i32, p, p]
     lib.oracle_respawn_draw.argtypes = [ctypes.c_uint64, i64, i32, i32]
     lib.oracle_respawn_draw.restype = ctypes.c_uint64
@@ -88,12 +88,12 @@ def _c(a, dtype):
 
 
 class OracleEnv:
-    """A batch of envs held in numpy arrays: canonical state int32[N][16] and the frame stack
+    """A batch of envs held in numpy arrays: canonical state int32[N][NF] and the frame stack
     f32[N][4][15] (newest first)."""
 
     def __init__(self, maps, ckpts, spawns, num_envs, frame_skip=3, time_limit=2000, sprites=None,
                  env_offset=0, reward_mode=0, waypoints=None, wp_lens=None, respawn_mode=0, ckpt_spawns=None,
-                 respawn_seed=0):
+                 respawn_seed=0, hook_mode=0):
         self.maps = _c(maps, np.uint8)
         self.ckpts = _c(ckpts, np.int32).reshape(self.maps.shape[0], -1, 2)
         self.spawns = _c(spawns, np.int32).reshape(self.maps.shape[0], 2)
@@ -108,7 +108,7 @@ class OracleEnv:
             self.waypoints = self.wp_lens = None
             kw = 0
         self.cfg = _Cfg(num_envs, env_offset, m, h, w, self.ckpts.shape[1], frame_skip, time_limit, reward_mode, kw,
-                        respawn_mode)
+                        respawn_mode, hook_mode)
         # adaptive respawn: each map's outcome ring, fill, write position and frontier; the decision counter
         self.ckpt_spawns = None if ckpt_spawns is None else _c(ckpt_spawns, np.int32).reshape(m, -1, 2)
         assert respawn_mode == 0 or (self.ckpt_spawns is not None and self.ckpts.shape[1] >= 1)
@@ -129,17 +129,22 @@ class OracleEnv:
         self._lib.oracle_env_reset(ctypes.byref(self.cfg), _ptr(self.spawns), _ptr(mask),
                                    _ptr(self.state), _ptr(self.stack))
 
-    def step(self, actions):
-        """Advance every env one decision; returns (rewards f32[N], dones f32[N])."""
+    def step(self, actions, aim=None):
+        """Advance every env one decision; returns (rewards f32[N], dones f32[N]). aim: hook mode's aim of
+        every env, int32[N] packing dx (low 16 bits) and dy (high 16 bits), or None for no aim."""
         actions = _c(actions, np.int32)
         assert actions.shape == (self.n,)
+        if aim is not None:
+            aim = _c(aim, np.int32)
+            assert aim.shape == (self.n,)
         rew = np.empty(self.n, np.float32)
         done = np.empty(self.n, np.float32)
         self._lib.oracle_env_step(ctypes.byref(self.cfg), _ptr(self.maps), _ptr(self.ckpts),
                                   _ptr(self.spawns), _ptr(self.waypoints), _ptr(self.wp_lens),
                                   _ptr(self.ckpt_spawns), _ptr(self.ring), _ptr(self.fill), _ptr(self.head),
                                   _ptr(self.frontier), self.respawn_seed, self.counter, _ptr(self.ended),
-                                  _ptr(actions), _ptr(self.state), _ptr(self.stack), _ptr(rew), _ptr(done))
+                                  _ptr(actions), _ptr(aim), _ptr(self.state), _ptr(self.stack), _ptr(rew),
+                                  _ptr(done))
         self.counter += 1
         return rew, done
 

@@ -60,6 +60,15 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 /* Adaptive checkpoint respawn ([DDNET] "Checkpoint Respawning"; readings): */
 #define RESPAWN_BUF 64           /* the rolling buffer of episode outcomes, per map */
 #define RESPAWN_START_U32 858993459u  /* a draw below this (20% of 2^32) starts from the beginning */
+/* Grapple hook with a continuous aim ([DDNET] "What the agent sees and does": a hook button and an aim
+ * angle with a magnitude). The page gives no hook mechanics; the flight, attachment and pull below, and
+ * these constants, are readings: */
+#define HOOK_SPEED 256      /* tip speed along the aim, sub-units per tick (one tile, so no tile row or
+                               column is stepped over) */
+#define HOOK_FLIGHT 10      /* ticks of flight before the tip is lost: a reach of 10 tiles */
+#define HOOK_ACCEL 24       /* pull of an attached hook toward its tip, sub/tick^2 (twice gravity) */
+#define HOOK_MAX_V 160      /* bound on each velocity component while attached (the fall-speed limit) */
+enum { HOOK_IDLE = 0, HOOK_FLYING = 1, HOOK_ATTACHED = 2 };
 #define WIN_W 43            /* tile window: 43 columns ... */
 #define WIN_H 31            /* ... by 31 rows */
 #define WIN_CX 21           /* the player's tile sits at window column 21, row 15 */
@@ -72,7 +81,8 @@ enum { AIR = 0, SOLID = 1, PLATFORM = 2, FREEZE = 3 };
 /* Canonical state layout: int32[N][NF] in this field order. */
 enum {
     F_X, F_Y, F_VX, F_VY, F_FACING, F_FREEZE, F_HOOK_TICKS, F_HOOK_HELD, F_JUMP_HELD, F_GROUNDED,
-    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, F_PATH, F_FROM_START, NF
+    F_WALL_L, F_WALL_R, F_TICK, F_NEXT, F_BEST_X, F_LAST_ACTION, F_PATH, F_FROM_START,
+    F_HOOK_PHASE, F_HOOK_X, F_HOOK_Y, F_HOOK_VX, F_HOOK_VY, F_HOOK_FLIGHT, NF
 };
 
 typedef struct {
@@ -83,11 +93,14 @@ typedef struct {
     int32_t reward_mode;    /* 0: checkpoint rewards (Version 1); 1: waypoint path (Version 2) */
     int32_t max_waypoints;  /* row length of the waypoint table (reward_mode 1) */
     int32_t respawn_mode;   /* 0: every episode starts at the spawn; 1: adaptive checkpoint respawn */
+    int32_t hook_mode;      /* 0: the hook button is only state; 1: grapple hook aimed by the aim input */
 } oracle_cfg;
 
 typedef struct {
     int32_t x, y, vx, vy, facing, freeze, hook_ticks, hook_held, jump_held, grounded;
     int32_t wall_l, wall_r, tick, next, best_x, last_action, path, from_start;
+    int32_t hook_phase, hook_x, hook_y, hook_vx, hook_vy, hook_flight;   /* hook mode: tip (absolute
+                                           sub-units), its velocity while flying, ticks flown */
 } env_t;
 
 /* Adaptive respawn state of every map: the ring of the last RESPAWN_BUF episode outcomes (checkpoints
@@ -116,6 +129,8 @@ static void load_env(const int32_t *s, env_t *e)
     e->wall_l = s[F_WALL_L]; e->wall_r = s[F_WALL_R]; e->tick = s[F_TICK]; e->next = s[F_NEXT];
     e->best_x = s[F_BEST_X]; e->last_action = s[F_LAST_ACTION]; e->path = s[F_PATH];
     e->from_start = s[F_FROM_START];
+    e->hook_phase = s[F_HOOK_PHASE]; e->hook_x = s[F_HOOK_X]; e->hook_y = s[F_HOOK_Y];
+    e->hook_vx = s[F_HOOK_VX]; e->hook_vy = s[F_HOOK_VY]; e->hook_flight = s[F_HOOK_FLIGHT];
 }
 
 static void store_env(const env_t *e, int32_t *s)
@@ -126,6 +141,8 @@ static void store_env(const env_t *e, int32_t *s)
     s[F_WALL_L] = e->wall_l; s[F_WALL_R] = e->wall_r; s[F_TICK] = e->tick; s[F_NEXT] = e->next;
     s[F_BEST_X] = e->best_x; s[F_LAST_ACTION] = e->last_action; s[F_PATH] = e->path;
     s[F_FROM_START] = e->from_start;
+    s[F_HOOK_PHASE] = e->hook_phase; s[F_HOOK_X] = e->hook_x; s[F_HOOK_Y] = e->hook_y;
+    s[F_HOOK_VX] = e->hook_vx; s[F_HOOK_VY] = e->hook_vy; s[F_HOOK_FLIGHT] = e->hook_flight;
 }
 
 /* Mathematical floor of a / b for b > 0 (C's '/' truncates toward zero). */
@@ -248,8 +265,9 @@ static void spawn_at(const oracle_cfg *c, const int32_t *spawns, const respawn_t
 }
 
 /* The 15-dim frame of a state ("What the agent sees and does": position, velocity, hook state,
- * freeze status). Sub-unit quantities are scaled by 2^-8 (tile units), the tick by 2^-11. */
-static void make_frame(const env_t *e, float *f)
+ * freeze status). Sub-unit quantities are scaled by 2^-8 (tile units), the tick by 2^-11. In hook mode
+ * dimension 9 is the hook's phase (idle 0, flying 1, attached 2) instead of the ticks it was held. */
+static void make_frame(const oracle_cfg *c, const env_t *e, float *f)
 {
     f[0] = (float)e->x * 0x1p-8f;
     f[1] = (float)e->y * 0x1p-8f;
@@ -260,7 +278,7 @@ static void make_frame(const env_t *e, float *f)
     f[6] = e->freeze > 0 ? 1.0f : 0.0f;
     f[7] = (float)e->freeze;
     f[8] = (float)e->hook_held;
-    f[9] = (float)e->hook_ticks;
+    f[9] = c->hook_mode ? (float)e->hook_phase : (float)e->hook_ticks;
     f[10] = (float)e->jump_held;
     f[11] = (float)e->wall_l;
     f[12] = (float)e->wall_r;
@@ -316,7 +334,8 @@ static int32_t approach(int32_t v, int32_t target, int32_t acc)
 
 /* One physics tick (all integer). Adds the tick's reward units to *units; returns 1 on the finish. */
 static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckpts, const path_t *pt,
-                        int m, env_t *e, int dir, int jump, int hook, int32_t *units)
+                        int m, env_t *e, int dir, int jump, int hook, int32_t aim_dx, int32_t aim_dy,
+                        int32_t *units)
 {
     /* 1. a frozen player's input is ignored */
     if (e->freeze > 0) { dir = 0; jump = 0; hook = 0; }
@@ -330,6 +349,48 @@ static int physics_tick(const oracle_cfg *c, const uint8_t *maps, const int32_t 
     if (jump && e->grounded) e->vy = -JUMP_V;
     e->vy = e->vy + GRAVITY;
     if (e->vy > MAX_FALL) e->vy = MAX_FALL;
+
+    /* 4h. the grapple hook (hook mode; readings). Letting go retracts it at once. Pressing it while it
+     * is idle and was not held on the previous tick, with a non-zero aim (dx, dy), fires the tip from
+     * the box centre with velocity HOOK_SPEED * (dx, dy) / floor(|(dx, dy)|), each component truncated
+     * toward zero. A flying tip moves once a tick; it attaches where it lands if that tile blocks
+     * movement (outside the map included), and is lost after HOOK_FLIGHT ticks in the air. An attached
+     * hook adds HOOK_ACCEL * e / floor(|e|) (truncated toward zero) to the velocity, e the offset from
+     * the box centre to the tip, and bounds each component by HOOK_MAX_V. */
+    if (c->hook_mode) {
+        if (!hook) {
+            e->hook_phase = HOOK_IDLE;
+        } else if (e->hook_phase == HOOK_IDLE && !e->hook_held && (aim_dx != 0 || aim_dy != 0)) {
+            int64_t len = isqrt64((int64_t)aim_dx * aim_dx + (int64_t)aim_dy * aim_dy);
+            e->hook_vx = (int32_t)((int64_t)aim_dx * HOOK_SPEED / len);
+            e->hook_vy = (int32_t)((int64_t)aim_dy * HOOK_SPEED / len);
+            e->hook_x = e->x + BOX / 2;
+            e->hook_y = e->y + BOX / 2;
+            e->hook_flight = 0;
+            e->hook_phase = HOOK_FLYING;
+        }
+        if (e->hook_phase == HOOK_FLYING) {
+            e->hook_x += e->hook_vx;
+            e->hook_y += e->hook_vy;
+            e->hook_flight += 1;
+            if (blocks(tile_at(c, maps, m, floordiv(e->hook_y, TILE), floordiv(e->hook_x, TILE))))
+                e->hook_phase = HOOK_ATTACHED;
+            else if (e->hook_flight >= HOOK_FLIGHT)
+                e->hook_phase = HOOK_IDLE;
+        }
+        if (e->hook_phase == HOOK_ATTACHED) {
+            int64_t ex = (int64_t)e->hook_x - (e->x + BOX / 2), ey = (int64_t)e->hook_y - (e->y + BOX / 2);
+            int64_t dist = isqrt64(ex * ex + ey * ey);
+            if (dist > 0) {
+                e->vx += (int32_t)(ex * HOOK_ACCEL / dist);
+                e->vy += (int32_t)(ey * HOOK_ACCEL / dist);
+            }
+            if (e->vx > HOOK_MAX_V) e->vx = HOOK_MAX_V;
+            if (e->vx < -HOOK_MAX_V) e->vx = -HOOK_MAX_V;
+            if (e->vy > HOOK_MAX_V) e->vy = HOOK_MAX_V;
+            if (e->vy < -HOOK_MAX_V) e->vy = -HOOK_MAX_V;
+        }
+    }
 
     /* 5. move along x against the rows the box covers before the y move */
     {
@@ -418,7 +479,7 @@ int oracle_env_reset(const oracle_cfg *c, const int32_t *spawns, const uint8_t *
         spawn_env(spawns, map_of(c, n), &e);
         store_env(&e, state + (size_t)n * NF);
         float f[FRAME_DIMS];
-        make_frame(&e, f);
+        make_frame(c, &e, f);
         for (int k = 0; k < STACK; ++k)
             memcpy(stack + ((size_t)n * STACK + k) * FRAME_DIMS, f, sizeof f);
     }
@@ -434,7 +495,8 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
                     const int32_t *spawns, const int32_t *waypoints, const int32_t *wp_lens,
                     const int32_t *ckpt_spawns, int32_t *ring, int32_t *fill, int32_t *head, int32_t *frontier,
                     uint64_t seed, int64_t counter, int32_t *ended,
-                    const int32_t *actions, int32_t *state, float *stack, float *rewards, float *dones)
+                    const int32_t *actions, const int32_t *aim, int32_t *state, float *stack, float *rewards,
+                    float *dones)
 {
     const path_t pt = {waypoints, wp_lens};
     const respawn_t rs = {ckpt_spawns, ring, fill, head, frontier, seed, counter};
@@ -445,11 +507,14 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
         int32_t a = actions[n];
         if (a < 0 || a >= 12) a = 0;                   /* out-of-range actions act as no-op */
         int dir = a / 4, jump = (a >> 1) & 1, hook = a & 1;
+        /* hook mode's aim: dx in the low 16 bits, dy in the high 16 bits, both signed (NULL: no aim) */
+        int32_t aim_dx = aim ? (int16_t)(aim[n] & 0xffff) : 0;
+        int32_t aim_dy = aim ? (int16_t)((uint32_t)aim[n] >> 16) : 0;
 
         int32_t units = 0;
         int terminated = 0, truncated = 0;
         for (int i = 0; i < c->frame_skip && !terminated && !truncated; ++i) {
-            terminated = physics_tick(c, maps, ckpts, &pt, m, &e, dir, jump, hook, &units);
+            terminated = physics_tick(c, maps, ckpts, &pt, m, &e, dir, jump, hook, aim_dx, aim_dy, &units);
             if (e.tick >= c->time_limit) truncated = 1;
         }
         e.last_action = a;
@@ -465,11 +530,11 @@ int oracle_env_step(const oracle_cfg *c, const uint8_t *maps, const int32_t *ckp
             int32_t k = c->respawn_mode == 1 ? respawn_choice(c, &rs, m, c->env_offset + n) : 0;
             spawn_at(c, spawns, &rs, m, k, &e);
             float f[FRAME_DIMS];
-            make_frame(&e, f);
+            make_frame(c, &e, f);
             for (int k = 0; k < STACK; ++k) memcpy(st + k * FRAME_DIMS, f, sizeof f);
         } else {
             memmove(st + FRAME_DIMS, st, (STACK - 1) * FRAME_DIMS * sizeof(float));
-            make_frame(&e, st);
+            make_frame(c, &e, st);
         }
         store_env(&e, state + (size_t)n * NF);
     }

@@ -180,6 +180,29 @@ def minibatch_index(perm: np.ndarray, mb: int) -> np.ndarray:
     return idx
 
 
+def pack_aim(dx, dy) -> np.ndarray:
+    """Hook mode's aim per env as int32: dx in the low 16 bits, dy in the high 16 bits (both int16)."""
+    dx = np.asarray(dx, np.int64)
+    dy = np.asarray(dy, np.int64)
+    assert ((dx >= -32768) & (dx <= 32767) & (dy >= -32768) & (dy <= 32767)).all()
+    return ((dx & 0xFFFF) | ((dy & 0xFFFF) << 16)).astype(np.uint32).view(np.int32)
+
+
+def make_aims(seed: int, steps: int, n: int, zero_frac: float = 0.05) -> np.ndarray:
+    """Synthetic continuous aims, int32[steps][n] packed by pack_aim: angle uniform over the circle,
+    magnitude uniform in [64, 4096] sub-units (a quarter tile to 16 tiles), rounded to integers; a
+    fraction zero_frac of them exactly (0, 0)."""
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(0.0, 2.0 * np.pi, (steps, n))
+    mag = rng.uniform(64.0, 4096.0, (steps, n))
+    dx = np.rint(mag * np.cos(ang)).astype(np.int64)
+    dy = np.rint(mag * np.sin(ang)).astype(np.int64)
+    zero = rng.random((steps, n)) < zero_frac
+    dx[zero] = 0
+    dy[zero] = 0
+    return pack_aim(dx, dy)
+
+
 def make_values(seed: int, t: int, n: int):
     """Stand-in value head outputs: values f32[T][N] and bootstrap values f32[N], both ~ N(0,1)."""
     rng = np.random.default_rng(seed)
