@@ -57,8 +57,9 @@ enum {
 enum { RL_OBS_TILES = 0, RL_OBS_PIXELS = 1 };
 enum { RL_REWARD_CHECKPOINTS = 0, RL_REWARD_WAYPOINTS = 1 };
 enum { RL_RESPAWN_OFF = 0, RL_RESPAWN_ADAPTIVE = 1 };
+enum { RL_HOOK_OFF = 0, RL_HOOK_GRAPPLE = 1 };
 
-#define RL_STATE_FIELDS 18      /* canonical state fields per env, see rl_env_read_state */
+#define RL_STATE_FIELDS 24      /* canonical state fields per env, see rl_env_read_state */
 #define RL_RESPAWN_BUF 64       /* episode outcomes kept per map for the adaptive respawn */
 #define RL_OBS_TILES_SIZE 1397  /* f32 elements: 31*43 window + 4*15 frames + 4 checkpoint dims */
 #define RL_OBS_PIXELS_SIZE 28224 /* u8 elements: 4 frames of 84*84 */
@@ -82,6 +83,8 @@ typedef struct rl_env_config {
     int32_t max_waypoints; /* waypoints per map path, 1 .. 2^20, with RL_REWARD_WAYPOINTS (else ignored) */
     int32_t respawn_mode;  /* RL_RESPAWN_OFF or RL_RESPAWN_ADAPTIVE (1 .. 1024 checkpoints; see rl_env_step) */
     uint64_t respawn_seed; /* seed of the adaptive respawn's draws */
+    int32_t hook_mode;     /* RL_HOOK_OFF (the hook button is state only) or RL_HOOK_GRAPPLE (a grapple hook
+                              aimed by rl_env_step_aim's aims; see there) */
 } rl_env_config;
 
 typedef struct rl_env rl_env;   /* opaque host handle */
@@ -180,10 +183,28 @@ int rl_waypoint_path(const uint8_t* map, int32_t h, int32_t w, int32_t c0, int32
 int rl_env_step(rl_env* env, const int32_t* actions, void* obs, float* rewards, float* dones,
                 void* stream);
 
+/* rl_env_step with a continuous aim per env, for RL_HOOK_GRAPPLE ("boesch.dev DDNet RL post", What the
+ * agent sees and does: a hook button and an aim given as an angle and a magnitude). aim is device
+ * int32[N], (dx & 0xffff) | (dy << 16) with dx, dy int16: the aim as a vector in sub-units (its polar form
+ * is the angle and the magnitude); NULL means no aim (the hook never fires); non-NULL with RL_HOOK_OFF is
+ * RL_EINVAL. The post gives no hook mechanics; this library's reading, a step of every tick after gravity:
+ * releasing the hook retracts it; pressing it while it is idle and was not held on the previous tick,
+ * with a non-zero aim, fires the tip from the box centre with velocity 256 (dx, dy) / floor(|(dx, dy)|)
+ * per tick (each component truncated toward zero); a flying tip moves once a tick and attaches where it
+ * lands if that tile is solid, a platform or outside the map, and is lost after 10 ticks of flight; an
+ * attached hook adds 24 e / floor(|e|) (truncated) to the velocity, e the offset from the box centre to
+ * the tip, then bounds each velocity component to [-160, 160]. A frozen player's hook input is 0. In hook
+ * mode frame dimension 9 of the observation is the hook's phase (0 idle, 1 flying, 2 attached) instead
+ * of the ticks the button has been held. */
+int rl_env_step_aim(rl_env* env, const int32_t* actions, const int32_t* aim, void* obs, float* rewards,
+                    float* dones, void* stream);
+
 /* Decode the state of every env into device int32[N][RL_STATE_FIELDS] with fields in the order
  * x, y, vx, vy, facing (+1/-1), freeze_ticks, hook_ticks, hook_held, jump_held, grounded, wall_left,
  * wall_right, tick, next_ckpt, best_x, last_action, path (the waypoint high-water index; 0 with
- * checkpoint rewards), from_start (1 if the episode began at the spawn). */
+ * checkpoint rewards), from_start (1 if the episode began at the spawn), then the grapple hook's phase
+ * (0 idle, 1 flying, 2 attached), tip x, tip y, flight velocity x, y and ticks flown (all 0 without
+ * RL_HOOK_GRAPPLE). */
 int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
 
 /* The decision counter, whose value mod 4 selects the frame ring's newest slot. Saving the state
@@ -364,8 +385,8 @@ typedef struct rl_rollout_group {
  * counters) runs before anything is enqueued. With `alternate` the groups also take turns at the
  * inference: group g's
  * inference of a decision waits for group g-1's (group 0's waits for the last group's of the decision
- * before), which keeps them out of phase. Every group's env must use tile observations and stand at the
- * same decision counter. Results equal the single-buffered rollout's for the same envs. */
+ * before), which keeps them out of phase. Every group's env must use tile observations, no grapple hook
+ * (the stand-in inference gives no aims) and stand at the same decision counter. Results equal the single-buffered rollout's for the same envs. */
 int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups, int32_t num_groups, int32_t t0,
                int32_t steps, int32_t alternate);
 

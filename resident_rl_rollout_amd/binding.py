@@ -17,9 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librl.so")
 
 OBS_TILES, OBS_PIXELS = 0, 1
-STATE_FIELDS = 18
+STATE_FIELDS = 24
 REWARD_CHECKPOINTS, REWARD_WAYPOINTS = 0, 1
 RESPAWN_OFF, RESPAWN_ADAPTIVE = 0, 1
+HOOK_OFF, HOOK_GRAPPLE = 0, 1
 RESPAWN_BUF = 64
 OBS_TILES_SIZE = 1397
 OBS_PIXELS_SIZE = 28224
@@ -36,7 +37,7 @@ class EnvConfig(ctypes.Structure):
                 ("map_w", ctypes.c_int32), ("num_ckpts", ctypes.c_int32), ("frame_skip", ctypes.c_int32),
                 ("time_limit", ctypes.c_int32), ("obs_mode", ctypes.c_int32), ("obs_stride", ctypes.c_int64),
                 ("reward_mode", ctypes.c_int32), ("max_waypoints", ctypes.c_int32),
-                ("respawn_mode", ctypes.c_int32), ("respawn_seed", ctypes.c_uint64)]
+                ("respawn_mode", ctypes.c_int32), ("respawn_seed", ctypes.c_uint64), ("hook_mode", ctypes.c_int32)]
 
 
 POLICY_HIDDEN, POLICY_ACTIONS = 128, 12
@@ -64,6 +65,7 @@ SIGNATURES = [
     ("rl_env_read_respawn", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     ("rl_waypoint_path", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_I32)]),
     ("rl_env_step", ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    ("rl_env_step_aim", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
     ("rl_env_get_step_counter", ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
     ("rl_env_set_step_counter", ctypes.c_int, [_P, _I64]),
@@ -153,9 +155,10 @@ class Env:
 
     def __init__(self, maps, ckpts, spawns, num_envs, *, frame_skip=3, time_limit=2000, obs_mode=OBS_TILES,
                  sprites=None, obs_stride=None, device="cuda", stream=None, reward_mode=REWARD_CHECKPOINTS,
-                 waypoints=None, wp_lens=None, respawn_mode=RESPAWN_OFF, ckpt_spawns=None, respawn_seed=0):
+                 waypoints=None, wp_lens=None, respawn_mode=RESPAWN_OFF, ckpt_spawns=None, respawn_seed=0,
+                 hook_mode=HOOK_OFF):
         """reward_mode REWARD_WAYPOINTS needs waypoints int32[M][KW][2] and wp_lens int32[M] (copied to the
-        device and set on the env after creation)."""
+        device and set on the env after creation). hook_mode HOOK_GRAPPLE takes aims in step()."""
         L = lib()
         self.device = torch.device(device)
         self.maps = _dev(maps, torch.uint8, self.device)
@@ -172,7 +175,7 @@ class Env:
             wpt = _dev(waypoints, torch.int32, self.device).reshape(m, -1, 2)
             kw = wpt.shape[1]
         self.cfg = EnvConfig(num_envs, m, h, w, ck.shape[1], frame_skip, time_limit, obs_mode, self.obs_stride,
-                             reward_mode, kw, respawn_mode, int(respawn_seed) & (2 ** 64 - 1))
+                             reward_mode, kw, respawn_mode, int(respawn_seed) & (2 ** 64 - 1), hook_mode)
         nbytes = ctypes.c_size_t()
         check(L.rl_env_state_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
         self.state = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
@@ -202,10 +205,17 @@ class Env:
         check(lib().rl_env_reset(self._handle, dptr(mask, torch.uint8, "mask"), dptr(obs, self.obs_dtype, "obs"),
                                  stream_ptr(stream)))
 
-    def step(self, actions, obs, rewards, dones, stream=None):
-        check(lib().rl_env_step(self._handle, dptr(actions, torch.int32, "actions"),
-                                dptr(obs, self.obs_dtype, "obs"), dptr(rewards, torch.float32, "rewards"),
-                                dptr(dones, torch.float32, "dones"), stream_ptr(stream)))
+    def step(self, actions, obs, rewards, dones, stream=None, aim=None):
+        """rl_env_step, or rl_env_step_aim when aim (device int32[N], dx | dy << 16) is given."""
+        if aim is None:
+            check(lib().rl_env_step(self._handle, dptr(actions, torch.int32, "actions"),
+                                    dptr(obs, self.obs_dtype, "obs"), dptr(rewards, torch.float32, "rewards"),
+                                    dptr(dones, torch.float32, "dones"), stream_ptr(stream)))
+        else:
+            check(lib().rl_env_step_aim(self._handle, dptr(actions, torch.int32, "actions"),
+                                        dptr(aim, torch.int32, "aim"), dptr(obs, self.obs_dtype, "obs"),
+                                        dptr(rewards, torch.float32, "rewards"), dptr(dones, torch.float32, "dones"),
+                                        stream_ptr(stream)))
 
     def read_state(self, stream=None):
         out = torch.empty((self.num_envs, STATE_FIELDS), dtype=torch.int32, device=self.device)

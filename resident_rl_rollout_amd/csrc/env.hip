@@ -14,9 +14,10 @@
 //   slots  int32[4][5][Np]  ring of the last 4 frames; slot s, word w of env n at (s*5 + w)*Np + n.
 //                           Words: x, y, (vx & 0xffff) | vy << 16, flags / counters, tick. The newest
 //                           slot is the current state; the decision counter mod 4 names it.
-//   extra  int32[5][Np]     next checkpoint index, best x, waypoint high-water index, began-at-spawn flag,
+//   extra  int32[8][Np]     next checkpoint index, best x, waypoint high-water index, began-at-spawn flag,
 //                           the step's ended outcome (checkpoints passed, bit 30 = began at the spawn;
-//                           -1 when the env did not end; written in respawn mode only).
+//                           -1 when the env did not end; written in respawn mode only), and in hook mode
+//                           the hook tip's x, y and flight velocity ((vx & 0xffff) | vy << 16).
 //   map    u8[M][H+32][Wp]  the maps with a 16-row / 32-column solid border, Wp = round_up(W+64, 64),
 //                           so that every read of the step and observation kernels stays inside.
 //   ckpt   int32[M][K][2], spawn int32[M][2], sprites u8[16][8][8].
@@ -25,6 +26,7 @@
 //   rhist int32[M][K+1]                                    (adaptive respawn only; empty otherwise)
 // Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
 
+#include <type_traits>
 #include <vector>
 
 #include "rl_internal.hpp"
@@ -54,9 +56,18 @@ constexpr int kRespawnBuf = RL_RESPAWN_BUF;          // outcomes kept per map
 constexpr uint32_t kRespawnStartU32 = 858993459u;    // a draw below this (20% of 2^32) restarts at the spawn
 constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;  // SplitMix64's increment
 constexpr int kMaxRespawnCkpts = 1024;
-// the step kernels' variants: bit 0 = the waypoint-path reward, bit 1 = the adaptive respawn
+// grapple hook aimed by a continuous aim ("boesch.dev DDNet RL post", What the agent sees and does: a hook
+// button and an aim; the mechanics are readings): tip speed one tile a tick along the aim, 10 ticks of
+// flight, a pull of twice gravity toward the tip, velocity components bounded by 160 while attached
+constexpr int kHookSpeed = 256;
+constexpr int kHookFlight = 10;
+constexpr int kHookAccel = 24;
+constexpr int kHookMaxV = 160;
+// the step kernels' variants: bit 0 = the waypoint-path reward, bit 1 = the adaptive respawn, bit 2 = the
+// grapple hook
 constexpr int kModeWaypoints = 1;
 constexpr int kModeRespawn = 2;
+constexpr int kModeHook = 4;
 
 constexpr int kWinW = 43;
 constexpr int kWinH = 31;
@@ -84,9 +95,12 @@ constexpr uint32_t kJumpHeldBit = 1u << 2;
 constexpr uint32_t kHookHeldBit = 1u << 3;
 constexpr uint32_t kWallLBit = 1u << 4;
 constexpr uint32_t kWallRBit = 1u << 5;
-constexpr int kFreezeShift = 8;   // 5 bits, 0..30
-constexpr int kHookShift = 16;    // 8 bits, 0..255
-constexpr int kActionShift = 24;  // 4 bits, 0..11
+constexpr int kHookPhaseShift = 6;    // 2 bits, hook mode: idle 0, flying 1, attached 2
+constexpr int kFreezeShift = 8;       // 5 bits, 0..30
+constexpr int kHookShift = 16;        // 8 bits, 0..255: ticks the hook button has been held
+constexpr int kActionShift = 24;      // 4 bits, 0..11
+constexpr int kHookFlightShift = 28;  // 4 bits, hook mode: ticks the tip has flown
+constexpr int kExtraRows = 8;
 
 struct Layout {
     size_t slots, extra, map, ckpt, spawn, sprites, waypoints, wplens, spots, ring, rmeta, rhist, total;
@@ -106,9 +120,11 @@ struct EnvDev {
     int32_t* ring;          // [M][kRespawnBuf] buffered outcomes
     int32_t* rmeta;         // [M][4] fill, head, frontier, -
     int32_t* rhist;         // [M][k + 1] counts of the buffered outcomes
+    const int32_t* aim;     // [N] this step's aims (hook mode; NULL: no aim)
     uint64_t seed;          // respawn draws
     int64_t counter;        // the decision counter of this step
     int32_t n, m, h, w, k, fs, time_limit, kw;
+    int32_t hook;           // hook mode: frame dimension 9 is the hook's phase
     int64_t np, hp, wp;
 };
 
@@ -143,6 +159,8 @@ int validate_cfg(const rl_env_config* c)
     if (c->respawn_mode == RL_RESPAWN_ADAPTIVE && (c->num_ckpts < 1 || c->num_ckpts > kMaxRespawnCkpts))
         return rl::fail(RL_EINVAL, "the adaptive respawn needs 1 .. %d checkpoints, got %d", kMaxRespawnCkpts,
                         c->num_ckpts);
+    if (c->hook_mode != RL_HOOK_OFF && c->hook_mode != RL_HOOK_GRAPPLE)
+        return rl::fail(RL_EINVAL, "hook_mode %d is neither off (0) nor grapple (1)", c->hook_mode);
     return RL_OK;
 }
 
@@ -155,8 +173,8 @@ Layout layout_of(const rl_env_config* c)
     size_t off = 0;
     l.slots = off;
     off = rl::round_up(off + sizeof(int32_t) * kStack * kSlotWords * l.np, 256);
-    l.extra = off;   // next checkpoint, best x, path index, from-start flag, the step's ended outcome
-    off = rl::round_up(off + sizeof(int32_t) * 5 * l.np, 256);
+    l.extra = off;   // next checkpoint, best x, path index, from-start flag, the step's ended outcome, hook
+    off = rl::round_up(off + sizeof(int32_t) * kExtraRows * l.np, 256);
     l.map = off;
     off = rl::round_up(off + (size_t)c->num_maps * l.hp * l.wp, 256);
     l.ckpt = off;
@@ -206,9 +224,10 @@ __device__ __forceinline__ const uint8_t* tile_ptr(const EnvDev& d, int m, int r
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Observation value of frame dimension `dim` from a slot's five words (all conversions exact).
+// Observation value of frame dimension `dim` from a slot's five words (all conversions exact). In hook
+// mode dimension 9 is the hook's phase instead of the ticks the button has been held.
 __device__ __forceinline__ float frame_dim(int dim, int32_t x, int32_t y, int32_t vxy, uint32_t misc,
-                                           int32_t tick)
+                                           int32_t tick, bool hook)
 {
     switch (dim) {
     case 0: return (float)x * 0x1p-8f;
@@ -220,7 +239,7 @@ __device__ __forceinline__ float frame_dim(int dim, int32_t x, int32_t y, int32_
     case 6: return ((misc >> kFreezeShift) & 31u) ? 1.0f : 0.0f;
     case 7: return (float)((misc >> kFreezeShift) & 31u);
     case 8: return (misc & kHookHeldBit) ? 1.0f : 0.0f;
-    case 9: return (float)((misc >> kHookShift) & 255u);
+    case 9: return hook ? (float)((misc >> kHookPhaseShift) & 3u) : (float)((misc >> kHookShift) & 255u);
     case 10: return (misc & kJumpHeldBit) ? 1.0f : 0.0f;
     case 11: return (misc & kWallLBit) ? 1.0f : 0.0f;
     case 12: return (misc & kWallRBit) ? 1.0f : 0.0f;
@@ -271,6 +290,9 @@ __device__ __forceinline__ void write_spawn(const EnvDev& d, int n)
     d.extra[d.np + n] = x;
     d.extra[2 * d.np + n] = 0;
     d.extra[3 * d.np + n] = 1;
+    d.extra[5 * d.np + n] = 0;
+    d.extra[6 * d.np + n] = 0;
+    d.extra[7 * d.np + n] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_reset(EnvDev d, const uint8_t* __restrict__ mask)
@@ -301,6 +323,60 @@ struct Neighbourhood {
     }
 };
 
+// Hook mode: a hook can push either velocity component to 160 a tick, so 5 ticks reach up to 800
+// sub-units (3.2 tiles) in any direction; every probe then lies inside rows r0-4 .. r0+4 and columns
+// c0-4 .. c0+4. Bit (row - rb) * 9 + (col - cb) of 81, in two words.
+struct WideNeighbourhood {
+    uint64_t solid[2], freeze[2];
+    int rb, cb;
+    __device__ __forceinline__ static uint32_t bit(const uint64_t (&w)[2], int i)
+    {
+        return (uint32_t)((i < 64 ? w[0] >> i : w[1] >> (i - 64)) & 1u);
+    }
+    __device__ __forceinline__ uint32_t s(int row, int col) const { return bit(solid, (row - rb) * 9 + (col - cb)); }
+    __device__ __forceinline__ uint32_t f(int row, int col) const { return bit(freeze, (row - rb) * 9 + (col - cb)); }
+};
+
+__device__ __forceinline__ WideNeighbourhood load_wide_neighbourhood(const EnvDev& d, int m, int32_t x, int32_t y)
+{
+    WideNeighbourhood nb;
+    nb.rb = clampi(y >> 8, 0, d.h - 1) - 4;
+    nb.cb = clampi(x >> 8, 0, d.w - 1) - 4;
+    uint64_t s[2] = {0, 0}, f[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        uint64_t row[2];
+        __builtin_memcpy(row, tile_ptr(d, m, nb.rb + i, nb.cb), 16);   // 9 of the 16 bytes are used
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const uint32_t t = (uint32_t)((j < 8 ? row[0] >> (8 * j) : row[1]) & 0xffu);
+            const int b = i * 9 + j;
+            const uint64_t sb = (uint64_t)(t == kSolid || t == kPlatform), fb = (uint64_t)(t == kFreeze);
+            if (b < 64) {
+                s[0] |= sb << b;
+                f[0] |= fb << b;
+            } else {
+                s[1] |= sb << (b - 64);
+                f[1] |= fb << (b - 64);
+            }
+        }
+    }
+    nb.solid[0] = s[0];
+    nb.solid[1] = s[1];
+    nb.freeze[0] = f[0];
+    nb.freeze[1] = f[1];
+    return nb;
+}
+
+// floor(sqrt(v)) for an integer-valued v in [0, 2^53): the rounded square root, then checked exactly.
+__device__ __forceinline__ double floor_sqrt(double v)
+{
+    double r = floor(sqrt(v));
+    while (r * r > v) r -= 1.0;
+    while ((r + 1.0) * (r + 1.0) <= v) r += 1.0;
+    return r;
+}
+
 __device__ __forceinline__ Neighbourhood load_neighbourhood(const EnvDev& d, int m, int32_t x, int32_t y)
 {
     Neighbourhood nb;
@@ -329,6 +405,21 @@ __device__ __forceinline__ Neighbourhood load_neighbourhood(const EnvDev& d, int
 struct SlotWords {
     int32_t x, y, vxy, misc, tick;
 };
+
+// Hook mode's inputs of a decision: the tip (x, y), its flight velocity ((vx & 0xffff) | vy << 16) and the
+// decision's aim ((dx & 0xffff) | dy << 16).
+struct HookIn {
+    int32_t x, y, v, aim;
+};
+
+template <int MODE>
+__device__ __forceinline__ HookIn load_hook(const EnvDev& d, int n)
+{
+    if constexpr ((MODE & kModeHook) != 0)
+        return HookIn{d.extra[5 * d.np + n], d.extra[6 * d.np + n], d.extra[7 * d.np + n], d.aim ? d.aim[n] : 0};
+    else
+        return HookIn{0, 0, 0, 0};
+}
 
 __device__ __forceinline__ SlotWords load_slot(const EnvDev& d, int s, int n)
 {
@@ -376,10 +467,7 @@ __device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_
         path = best;
     }
     if (best_d2 >= (double)((kWpGrace + 1) * (kWpGrace + 1))) {
-        double r = floor(sqrt(best_d2));   // then checked to be the exact integer floor
-        while (r * r > best_d2) r -= 1.0;
-        while ((r + 1.0) * (r + 1.0) <= best_d2) r += 1.0;
-        units -= (int32_t)(((int64_t)r - kWpGrace) >> kWpPenaltyShift);
+        units -= (int32_t)(((int64_t)floor_sqrt(best_d2) - kWpGrace) >> kWpPenaltyShift);
     }
     return units;
 }
@@ -435,6 +523,7 @@ __device__ int32_t respawn_choice(const EnvDev& d, int m, int n)
 
 // Start a new episode of env n on map m at checkpoint k in all four ring slots and the extras: the spawn
 // for k = 0, else checkpoint k - 1's standing spot with k checkpoints passed. Returns its decision.
+template <bool HOOK>
 __device__ __forceinline__ Decision spawn_at(const EnvDev& d, int n, int m, int32_t k)
 {
     int32_t x = d.spawn[2 * m], y = d.spawn[2 * m + 1];
@@ -455,6 +544,11 @@ __device__ __forceinline__ Decision spawn_at(const EnvDev& d, int n, int m, int3
     d.extra[d.np + n] = x;
     d.extra[2 * d.np + n] = 0;
     d.extra[3 * d.np + n] = k == 0 ? 1 : 0;
+    if constexpr (HOOK) {
+        d.extra[5 * d.np + n] = 0;
+        d.extra[6 * d.np + n] = 0;
+        d.extra[7 * d.np + n] = 0;
+    }
     return Decision{x, y, 0, misc, 0, k, x, true};
 }
 
@@ -528,9 +622,10 @@ __global__ __launch_bounds__(256) void k_zero(int32_t* __restrict__ p, int64_t c
 
 template <int MODE>
 __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a, const SlotWords& cur, int32_t next,
-                                               int32_t best_x, int32_t path, int32_t from_start,
+                                               int32_t best_x, int32_t path, int32_t from_start, const HookIn& hk,
                                                float* __restrict__ rewards, float* __restrict__ dones, int head_new)
 {
+    constexpr bool kHook = (MODE & kModeHook) != 0;
     const int m = n % d.m;
     int32_t x = cur.x;
     int32_t y = cur.y;
@@ -547,8 +642,17 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     int32_t hook_ticks = (int32_t)((misc >> kHookShift) & 255u);
     uint32_t wall_l = (misc & kWallLBit) ? 1u : 0u, wall_r = (misc & kWallRBit) ? 1u : 0u;
     uint32_t jump_held = (misc & kJumpHeldBit) ? 1u : 0u, hook_held = (misc & kHookHeldBit) ? 1u : 0u;
+    int32_t phase = kHook ? (int32_t)((misc >> kHookPhaseShift) & 3u) : 0;
+    int32_t flight = kHook ? (int32_t)((misc >> kHookFlightShift) & 15u) : 0;
+    int32_t hx = hk.x, hy = hk.y;
+    int32_t hvx = (int16_t)(hk.v & 0xffff), hvy = hk.v >> 16;
+    const int32_t adx = (int16_t)(hk.aim & 0xffff), ady = hk.aim >> 16;
 
-    const Neighbourhood nb = load_neighbourhood(d, m, x, y);
+    std::conditional_t<kHook, WideNeighbourhood, Neighbourhood> nb;
+    if constexpr (kHook)
+        nb = load_wide_neighbourhood(d, m, x, y);
+    else
+        nb = load_neighbourhood(d, m, x, y);
     const int32_t* ck = d.ckpt + (int64_t)m * d.k * 2;
     int32_t ck_col = next < d.k ? ck[2 * next] : 0;
 
@@ -572,6 +676,46 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         // 3-4. jump from the ground, gravity, terminal fall speed
         if (jump && grounded) vy = -kJumpV;
         vy = min(vy + kGravity, kMaxFall);
+        // 4h. the grapple hook: letting go retracts it; a new press with a non-zero aim fires the tip from
+        // the box centre at kHookSpeed along the aim (each component truncated toward zero after dividing by
+        // the aim's floored length); a flying tip moves once a tick and attaches in the first tile it lands
+        // in that blocks movement (the border included), or is lost after kHookFlight ticks; an attached
+        // hook adds kHookAccel toward the tip (same rounding) and bounds each velocity component.
+        if constexpr (kHook) {
+            if (!hook) {
+                phase = 0;
+            } else if (phase == 0 && !hook_held && (adx | ady) != 0) {
+                const int32_t len = (int32_t)floor_sqrt((double)adx * adx + (double)ady * ady);
+                hvx = adx * kHookSpeed / len;
+                hvy = ady * kHookSpeed / len;
+                hx = x + kHalfBox;
+                hy = y + kHalfBox;
+                flight = 0;
+                phase = 1;
+            }
+            if (phase == 1) {
+                hx += hvx;
+                hy += hvy;
+                flight += 1;
+                // the tip never gets past the first border tile, which holds it; the clamp only matters for
+                // a spawn placed outside the map
+                const int row = clampi(hy >> 8, -kPadY, d.h + kPadY - 1);
+                const int col = clampi(hx >> 8, -kPadX, d.w + kPadX - 1);
+                const uint32_t t = *tile_ptr(d, m, row, col);
+                if (t == kSolid || t == kPlatform) phase = 2;
+                else if (flight >= kHookFlight) phase = 0;
+            }
+            if (phase == 2) {
+                const int32_t ex = hx - (x + kHalfBox), ey = hy - (y + kHalfBox);
+                const int32_t dist = (int32_t)floor_sqrt((double)ex * ex + (double)ey * ey);
+                if (dist > 0) {
+                    vx += ex * kHookAccel / dist;
+                    vy += ey * kHookAccel / dist;
+                }
+                vx = clampi(vx, -kHookMaxV, kHookMaxV);
+                vy = clampi(vy, -kHookMaxV, kHookMaxV);
+            }
+        }
         // 5. x move against the rows of the box before the y move
         {
             int32_t nx = x + vx;
@@ -643,14 +787,16 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
             d.extra[4 * d.np + n] = next | (from_start ? (1 << 30) : 0);   // the ended episode's outcome
             k = respawn_choice(d, m, n);
         }
-        return spawn_at(d, n, m, k);
+        return spawn_at<kHook>(d, n, m, k);
     }
     if constexpr ((MODE & kModeRespawn) != 0) d.extra[4 * d.np + n] = -1;
     const uint32_t new_misc = (facing > 0 ? kFacingRight : 0u) | (grounded ? kGroundedBit : 0u) |
                               (jump_held ? kJumpHeldBit : 0u) | (hook_held ? kHookHeldBit : 0u) |
                               (wall_l ? kWallLBit : 0u) | (wall_r ? kWallRBit : 0u) |
                               ((uint32_t)freeze << kFreezeShift) | ((uint32_t)hook_ticks << kHookShift) |
-                              ((uint32_t)a << kActionShift);
+                              ((uint32_t)a << kActionShift) |
+                              (kHook ? ((uint32_t)phase << kHookPhaseShift) | ((uint32_t)flight << kHookFlightShift)
+                                     : 0u);
     slot_word(d, head_new, 0, n) = x;
     slot_word(d, head_new, 1, n) = y;
     slot_word(d, head_new, 2, n) = (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16));
@@ -659,6 +805,11 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     d.extra[n] = next;
     d.extra[d.np + n] = best_x;
     if constexpr ((MODE & kModeWaypoints) != 0) d.extra[2 * d.np + n] = path;
+    if constexpr (kHook) {
+        d.extra[5 * d.np + n] = hx;
+        d.extra[6 * d.np + n] = hy;
+        d.extra[7 * d.np + n] = (int32_t)(((uint32_t)hvx & 0xffffu) | ((uint32_t)hvy << 16));
+    }
     return Decision{x, y, (int32_t)(((uint32_t)vx & 0xffffu) | ((uint32_t)vy << 16)), (int32_t)new_misc, tick,
                     next, best_x, false};
 }
@@ -674,7 +825,8 @@ __global__ __launch_bounds__(64) void k_step(EnvDev d, const int32_t* __restrict
     if (n >= d.n) return;
     env_decide<MODE>(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n],
                      (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0,
-                     (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1, rewards, dones, head_new);
+                     (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1, load_hook<MODE>(d, n), rewards, dones,
+                     head_new);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -710,7 +862,7 @@ __global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__
                 const int f = t / kFrameDims, dim = t - f * kFrameDims;
                 const int s = (head - f) & 3;
                 v = frame_dim(dim, slot_word(d, s, 0, n), slot_word(d, s, 1, n), slot_word(d, s, 2, n),
-                              (uint32_t)slot_word(d, s, 3, n), slot_word(d, s, 4, n));
+                              (uint32_t)slot_word(d, s, 3, n), slot_word(d, s, 4, n), d.hook != 0);
             } else {
                 const int q = t - kStack * kFrameDims;
                 const int32_t next = d.extra[n];
@@ -758,10 +910,11 @@ constexpr int kWinDwords = kWinH * kRowDwords;    // 341 per env
 constexpr int kWinPerLane = (kWinDwords + 63) / 64;   // 6
 constexpr int kStepTilesEnvs = 16;                // envs per block of the fused tile kernel
 
+template <bool HOOK>
 __device__ __forceinline__ void put_frame(float* t, int32_t x, int32_t y, int32_t vxy, uint32_t misc, int32_t tick)
 {
 #pragma unroll
-    for (int dim = 0; dim < kFrameDims; ++dim) t[dim] = frame_dim(dim, x, y, vxy, misc, tick);
+    for (int dim = 0; dim < kFrameDims; ++dim) t[dim] = frame_dim(dim, x, y, vxy, misc, tick, HOOK);
 }
 
 // Observation element k (< 1397) from a staged window and the staged frame / checkpoint values.
@@ -845,18 +998,20 @@ __device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const
     const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
     const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
     const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
-    const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, rewards, dones, head_new);
+    const HookIn hk = load_hook<MODE>(d, n);
+    const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, hk, rewards, dones, head_new);
+    constexpr bool kHook = (MODE & kModeHook) != 0;
     float* t = tail[e];
-    put_frame(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
+    put_frame<kHook>(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
     if (s.done) {
 #pragma unroll
         for (int f = 1; f < kStack; ++f)
 #pragma unroll
             for (int dim = 0; dim < kFrameDims; ++dim) t[f * kFrameDims + dim] = t[dim];
     } else {
-        put_frame(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
-        put_frame(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
-        put_frame(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
+        put_frame<kHook>(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
+        put_frame<kHook>(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
+        put_frame<kHook>(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
     }
     float* ck = t + kStack * kFrameDims;
     if (s.next < d.k) {
@@ -905,7 +1060,7 @@ __device__ __forceinline__ void write_group(const EnvDev& d, int n0, int ne, int
 }
 
 template <int E, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MODE & kModeHook) ? 3 : 4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
                                                     int head_new)
@@ -1027,6 +1182,13 @@ __global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restric
     o[16] = d.extra[2 * d.np + n];
     o[17] = d.extra[3 * d.np + n];
     o[15] = (int32_t)((misc >> kActionShift) & 15u);
+    const int32_t hv = d.extra[7 * d.np + n];
+    o[18] = (int32_t)((misc >> kHookPhaseShift) & 3u);
+    o[19] = d.extra[5 * d.np + n];
+    o[20] = d.extra[6 * d.np + n];
+    o[21] = (int16_t)(hv & 0xffff);
+    o[22] = hv >> 16;
+    o[23] = (int32_t)((misc >> kHookFlightShift) & 15u);
 }
 
 }  // namespace
@@ -1067,6 +1229,8 @@ EnvDev dev_of(const rl_env* e)
     d.k = e->cfg.num_ckpts;
     d.fs = e->cfg.frame_skip;
     d.time_limit = e->cfg.time_limit;
+    d.hook = e->cfg.hook_mode == RL_HOOK_GRAPPLE ? 1 : 0;
+    d.aim = nullptr;
     d.np = e->lay.np;
     d.hp = e->lay.hp;
     d.wp = e->lay.wp;
@@ -1205,40 +1369,58 @@ int rl_env_reset(rl_env* e, const uint8_t* mask, void* obs, void* stream)
     return RL_OK;
 }
 
-int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, float* dones, void* stream)
+int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void* obs, float* rewards, float* dones,
+                    void* stream)
 {
     if (!e) return rl::fail(RL_EINVAL, "env is NULL");
     if (!actions || !rewards || !dones) return rl::fail(RL_EINVAL, "actions, rewards and dones must be non-NULL");
-    if (!rl::aligned(actions, 4) || !rl::aligned(rewards, 4) || !rl::aligned(dones, 4))
-        return rl::fail(RL_EALIGN, "actions / rewards / dones are not 4-byte aligned");
+    if (!rl::aligned(actions, 4) || !rl::aligned(rewards, 4) || !rl::aligned(dones, 4) || !rl::aligned(aim, 4))
+        return rl::fail(RL_EALIGN, "actions / aim / rewards / dones are not 4-byte aligned");
+    const bool hk = e->cfg.hook_mode == RL_HOOK_GRAPPLE;
+    if (aim && !hk) return rl::fail(RL_EINVAL, "aims given to an env without the grapple hook");
     if (int rc = check_obs_ptr(e, obs)) return rc;
     const bool wp = e->cfg.reward_mode == RL_REWARD_WAYPOINTS;
     const bool rs = e->cfg.respawn_mode == RL_RESPAWN_ADAPTIVE;
     if (wp && !e->waypoints_set) return rl::fail(RL_EINVAL, "waypoint rewards need rl_env_set_waypoints first");
     if (rs && !e->spots_set) return rl::fail(RL_EINVAL, "the adaptive respawn needs rl_env_set_respawn_spots first");
     hipStream_t st = rl::as_stream(stream);
-    const EnvDev d = dev_of(e);
+    EnvDev d = dev_of(e);
+    d.aim = aim;
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
-    const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0);
+    const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0) | (hk ? kModeHook : 0);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
         const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs), block(256);
         float* o = static_cast<float*>(obs);
         const int64_t os = e->cfg.obs_stride;
+#define RL_STEP_TILES(M) \
+    hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, M>), grid, block, 0, st, d, actions, rewards, dones, o, os, \
+                       head_prev, head_new)
         switch (mode) {
-        case 0: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 0>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
-        case 1: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 1>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
-        case 2: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 2>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
-        default: hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, 3>), grid, block, 0, st, d, actions, rewards, dones, o, os, head_prev, head_new); break;
+        case 0: RL_STEP_TILES(0); break;
+        case 1: RL_STEP_TILES(1); break;
+        case 2: RL_STEP_TILES(2); break;
+        case 3: RL_STEP_TILES(3); break;
+        case 4: RL_STEP_TILES(4); break;
+        case 5: RL_STEP_TILES(5); break;
+        case 6: RL_STEP_TILES(6); break;
+        default: RL_STEP_TILES(7); break;
         }
+#undef RL_STEP_TILES
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
     } else {
         const dim3 grid((d.n + 63) / 64), block(64);
+#define RL_STEP(M) hipLaunchKernelGGL(k_step<M>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new)
         switch (mode) {
-        case 0: hipLaunchKernelGGL(k_step<0>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
-        case 1: hipLaunchKernelGGL(k_step<1>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
-        case 2: hipLaunchKernelGGL(k_step<2>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
-        default: hipLaunchKernelGGL(k_step<3>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new); break;
+        case 0: RL_STEP(0); break;
+        case 1: RL_STEP(1); break;
+        case 2: RL_STEP(2); break;
+        case 3: RL_STEP(3); break;
+        case 4: RL_STEP(4); break;
+        case 5: RL_STEP(5); break;
+        case 6: RL_STEP(6); break;
+        default: RL_STEP(7); break;
         }
+#undef RL_STEP
         if (int rc = rl::check_launch("env_step")) return rc;
     }
     if (rs) {
@@ -1248,6 +1430,11 @@ int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, fl
     e->counter += 1;
     if (e->cfg.obs_mode == RL_OBS_TILES) return RL_OK;
     return launch_obs(e, obs, st, head_new);
+}
+
+int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, float* dones, void* stream)
+{
+    return rl_env_step_aim(e, actions, nullptr, obs, rewards, dones, stream);
 }
 
 int rl_env_set_respawn_spots(rl_env* e, const int32_t* ckpt_spawns, void* stream)

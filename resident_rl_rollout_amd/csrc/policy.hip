@@ -342,6 +342,8 @@ int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups
         const rl_rollout_group& x = groups[g];
         if (int rc = rl_env_get_config(x.env, &cfg[g])) return rc;
         if (cfg[g].obs_mode != RL_OBS_TILES) return rl::fail(RL_EINVAL, "group %d: the inference reads tile observations", g);
+        if (cfg[g].hook_mode != RL_HOOK_OFF)
+            return rl::fail(RL_EINVAL, "group %d: the stand-in inference gives no aims for the grapple hook", g);
         const int64_t n = cfg[g].num_envs;
         if (!x.actions || !x.logp || !x.values || !x.obs || !x.rewards || !x.dones || (t0 == 0 && !x.obs0))
             return rl::fail(RL_EINVAL, "group %d: a buffer is NULL", g);

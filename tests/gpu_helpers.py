@@ -98,16 +98,16 @@ class PairedEnvs:
 
     def __init__(self, ms: inputs.MapSet, n, *, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_TILES,
                  sprites=None, obs_stride=None, reward_mode=0, waypoints=None, wp_lens=None, respawn_mode=0,
-                 respawn_seed=0):
+                 respawn_seed=0, hook_mode=0):
         spots = ms.ckpt_spawns if respawn_mode else None
         self.gpu = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip, time_limit=time_limit,
                                obs_mode=obs_mode, sprites=sprites, obs_stride=obs_stride, reward_mode=reward_mode,
                                waypoints=waypoints, wp_lens=wp_lens, respawn_mode=respawn_mode, ckpt_spawns=spots,
-                               respawn_seed=respawn_seed)
+                               respawn_seed=respawn_seed, hook_mode=hook_mode)
         self.ora = oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=frame_skip,
                                     time_limit=time_limit, sprites=sprites, reward_mode=reward_mode,
                                     waypoints=waypoints, wp_lens=wp_lens, respawn_mode=respawn_mode,
-                                    ckpt_spawns=spots, respawn_seed=respawn_seed)
+                                    ckpt_spawns=spots, respawn_seed=respawn_seed, hook_mode=hook_mode)
         self.ora.reset()
         self.n = n
         self.obs_mode = obs_mode
@@ -125,10 +125,11 @@ class PairedEnvs:
         size = binding.OBS_TILES_SIZE if self.obs_mode == binding.OBS_TILES else binding.OBS_PIXELS_SIZE
         return self.obs[:, :size].cpu().numpy()
 
-    def step(self, actions_np):
+    def step(self, actions_np, aim_np=None):
         a = torch.from_numpy(np.ascontiguousarray(actions_np, np.int32)).cuda()
-        self.gpu.step(a, self.obs, self.rew, self.done)
-        r, d = self.ora.step(actions_np)
+        aim = None if aim_np is None else torch.from_numpy(np.ascontiguousarray(aim_np, np.int32)).cuda()
+        self.gpu.step(a, self.obs, self.rew, self.done, aim=aim)
+        r, d = self.ora.step(actions_np, aim_np)
         return r, d
 
     def check_state(self, what):

@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(**kw):
     base = dict(num_envs=64, num_maps=1, map_h=32, map_w=128, num_ckpts=7, frame_skip=3, time_limit=2000,
-                obs_mode=0, obs_stride=1397, reward_mode=0, max_waypoints=0, respawn_mode=0, respawn_seed=0)
+                obs_mode=0, obs_stride=1397, reward_mode=0, max_waypoints=0, respawn_mode=0, respawn_seed=0,
+                hook_mode=0)
     base.update(kw)
     return binding.EnvConfig(*[base[k] for k, _ in binding.EnvConfig._fields_])
 
@@ -46,7 +47,8 @@ def _cfg(**kw):
     (dict(reward_mode=1, max_waypoints=0), -1, "max_waypoints"),
     (dict(reward_mode=1, max_waypoints=(1 << 20) + 1), -1, "max_waypoints"),
     (dict(respawn_mode=2), -1, "respawn_mode"), (dict(respawn_mode=1, num_ckpts=0), -1, "checkpoints"),
-    (dict(respawn_mode=1, num_ckpts=1025), -1, "checkpoints"),
+    (dict(respawn_mode=1, num_ckpts=1025), -1, "checkpoints"), (dict(hook_mode=2), -1, "hook_mode"),
+    (dict(hook_mode=-1), -1, "hook_mode"),
 ])
 def test_config_validation(kw, code, msg):
     lib = binding.lib()
@@ -81,6 +83,7 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.rl_env_create(ctypes.byref(_cfg(obs_mode=1, obs_stride=28224)), fake, fake, fake, None, fake, 1 << 30,
                              None, ctypes.byref(out)) == -1
     assert lib.rl_env_step(None, fake, fake, fake, fake, None) == -1
+    assert lib.rl_env_step_aim(None, fake, fake, fake, fake, fake, None) == -1
     assert lib.rl_env_set_waypoints(None, fake, fake, None) == -1
     assert lib.rl_env_set_respawn_spots(None, fake, None) == -1
     assert lib.rl_env_read_respawn(None, fake, fake, fake, fake, None) == -1

@@ -1,0 +1,114 @@
+"""GPU parity of the grapple hook (hook mode, rl_env_step_aim) against the oracle: bit-exact state (the
+hook's phase, tip, flight velocity and ticks flown included), observations, rewards and dones, with the
+same seeded maps, actions and aims on both sides."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from resident_rl_rollout_amd import binding, inputs
+from tests.gpu_helpers import PairedEnvs, waypoint_table
+
+pytestmark = pytest.mark.gpu
+F = {name: i for i, name in enumerate(oracle.STATE_FIELDS)}
+
+
+def hook_inputs(seed, steps, n, p_hook=0.7):
+    """Actions with the hook bit set with probability p_hook (so presses, holds and releases all occur)
+    and aims mostly upward (70% in the upper half-plane), magnitudes 64 .. 4096, 5% zero."""
+    rng = np.random.default_rng(seed)
+    acts = (4 * rng.integers(0, 3, (steps, n)) + 2 * rng.integers(0, 2, (steps, n))
+            + (rng.random((steps, n)) < p_hook)).astype(np.int32)
+    aims = inputs.make_aims(seed + 1, steps, n)
+    up = rng.random((steps, n)) < 0.7
+    dy = (aims.astype(np.int64) >> 16)
+    dx = ((aims.astype(np.int64) & 0xFFFF) ^ 0x8000) - 0x8000
+    dy = np.where(up, -np.abs(dy), dy)
+    return acts, inputs.pack_aim(dx, dy)
+
+
+def run(pe, acts, aims, what, obs_every=1, obs_envs=None):
+    pe.check_obs(f"{what} reset")
+    phases = np.zeros(3, np.int64)
+    vmax = 0
+    for s in range(len(acts)):
+        r, d = pe.step(acts[s], None if aims is None else aims[s])
+        pe.check_step(r, d, f"{what} step {s}")
+        pe.check_state(f"{what} step {s}")
+        if obs_every and (s % obs_every == 0 or s == len(acts) - 1):
+            pe.check_obs(f"{what} step {s}", obs_envs)
+        phases += np.bincount(pe.ora.state[:, F["hook_phase"]], minlength=3)
+        vmax = max(vmax, int(np.abs(pe.ora.state[:, [F["vx"], F["vy"]]]).max()))
+    return phases, vmax
+
+
+def test_tiny_workload_with_the_hook(gpu_lib):
+    ms = inputs.make_mapset([1], 32, 128)
+    pe = PairedEnvs(ms, 64, hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(2, 128, 64)
+    phases, _ = run(pe, acts, aims, "tiny hook")
+    assert phases[1] > 0 and phases[2] > 0        # tips flew and held
+
+
+@pytest.mark.parametrize("fs", [1, 3, 5])
+def test_hook_frame_skip_and_fast_swings(fs, gpu_lib):
+    # frame-skip 5 with hook speeds up to 160 a tick spans the widest neighbourhood a decision can probe
+    ms = inputs.make_mapset([4, 5, 6], 48, 96)
+    pe = PairedEnvs(ms, 300, frame_skip=fs, time_limit=400, hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(10 + fs, 120, 300, p_hook=0.85)
+    phases, vmax = run(pe, acts, aims, f"hook fs={fs}", obs_every=9)
+    assert phases[2] > 0 and vmax > 100
+
+
+def test_hook_workload_full_size(gpu_lib):
+    ms = inputs.make_mapset(range(100, 164), 256, 1024)
+    pe = PairedEnvs(ms, 65536, hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(3, 12, 65536)
+    rng = np.random.default_rng(0)
+    envs = np.concatenate([np.arange(64), rng.choice(65536, 448, replace=False), np.arange(65536 - 64, 65536)])
+    pe.check_obs("hook full reset", envs)
+    for s in range(len(acts)):
+        r, d = pe.step(acts[s], aims[s])
+        pe.check_step(r, d, f"hook full step {s}")
+        if s in (0, 5, len(acts) - 1):
+            pe.check_state(f"hook full step {s}")
+            pe.check_obs(f"hook full step {s}", envs)
+    assert (pe.ora.state[:, F["hook_phase"]] == 2).sum() > 1000
+
+
+def test_hook_with_pixels(gpu_lib):
+    ms = inputs.make_mapset(range(100, 104), 256, 1024)
+    pe = PairedEnvs(ms, 256, obs_mode=binding.OBS_PIXELS, sprites=inputs.make_sprites(30),
+                    hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(4, 40, 256)
+    run(pe, acts, aims, "hook pixels", obs_every=4)
+
+
+def test_hook_with_waypoints_and_respawn(gpu_lib):
+    ms = inputs.make_mapset([7, 8, 9], 32, 40)
+    wpt, lens = waypoint_table(ms)
+    pe = PairedEnvs(ms, 300, time_limit=30, reward_mode=binding.REWARD_WAYPOINTS, waypoints=wpt, wp_lens=lens,
+                    respawn_mode=binding.RESPAWN_ADAPTIVE, respawn_seed=77, hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(5, 150, 300)
+    phases, _ = run(pe, acts, aims, "hook + waypoints + respawn", obs_every=5)
+    assert phases[2] > 0
+
+
+def test_hook_mode_without_aims_never_fires(gpu_lib):
+    ms = inputs.make_mapset([1], 32, 128)
+    pe = PairedEnvs(ms, 128, hook_mode=binding.HOOK_GRAPPLE)
+    acts, _ = hook_inputs(6, 40, 128)
+    phases, _ = run(pe, acts, None, "hook without aims", obs_every=10)
+    assert phases[1] == 0 and phases[2] == 0
+
+
+def test_aims_need_hook_mode(gpu_lib):
+    ms = inputs.make_mapset([1], 32, 128)
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, 8)
+    obs = env.new_obs()
+    r = torch.empty(8, dtype=torch.float32, device="cuda")
+    a = torch.zeros(8, dtype=torch.int32, device="cuda")
+    with pytest.raises(binding.RLError, match="grapple"):
+        env.step(a, obs, r, r.clone(), aim=torch.zeros(8, dtype=torch.int32, device="cuda"))
+    with pytest.raises(binding.RLError, match="hook_mode"):
+        binding.Env(ms.maps, ms.ckpts, ms.spawns, 8, hook_mode=2)
