@@ -40,6 +40,7 @@ GAMMA, LAMBDA = 0.99, 0.95
 ENV_BYTES_PER_ENV_STEP = 1397 * 4 + 4 + 20 + 40 + 8 + 20 + 8 + 4 + 4    # 5696
 ENV_BYTES_WAYPOINTS = 4 + 4   # the path index, read and written (the 0.5 MB waypoint table stays in cache)
 ENV_BYTES_RESPAWN = 4 + 4 + 4  # the from-start flag read, the step's outcome written and read back by the append
+ENV_BYTES_HOOK = 4 + 12 + 12   # the aim read; the hook's tip x, y and flight velocity read and written
 # The pixel step per env (two kernels): the physics reads the action, the current slot and the extras and
 # writes the new slot, the extras, the reward and the done; the render reads (x, y) of the four stacked
 # slots and writes the 4 x 84 x 84 frame bytes.
@@ -80,6 +81,8 @@ def parse():
                         "path (progress along each map's BFS tile path, grace-zone distance penalty)")
     p.add_argument("--respawn", choices=("off", "adaptive"), default="off",
                    help="adaptive checkpoint respawn (each map's outcome buffer, top-quarter restarts, frontier cap)")
+    p.add_argument("--hook", choices=("off", "grapple"), default="off",
+                   help="grapple hook aimed by seeded continuous aims (rl_env_step_aim)")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
     return p.parse_args()
@@ -139,7 +142,12 @@ RESPAWN_SEED = 2024
 
 def _env_kw():
     return {k: _SHARED[k] for k in ("reward_mode", "waypoints", "wp_lens", "respawn_mode", "ckpt_spawns",
-                                    "respawn_seed") if k in _SHARED}
+                                    "respawn_seed", "hook_mode") if k in _SHARED}
+
+
+def _aim(t, lo, hi):
+    aims = _SHARED.get("aims")
+    return None if aims is None else aims[t, lo:hi]
 
 
 def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
@@ -155,7 +163,7 @@ def cpu_baseline(ms, policy_actions, values, last_values, pi, n_sample):
     rew = np.empty((HORIZON, n), np.float32)
     dn = np.empty((HORIZON, n), np.float32)
     for t in range(HORIZON):
-        rew[t], dn[t] = env.step(policy_actions[t, :n])
+        rew[t], dn[t] = env.step(policy_actions[t, :n], _aim(t, 0, n))
         env.obs_tiles(obs)
     adv, ret = oracle.gae(rew, values[:, :n], dn, last_values[:n], float(np.float32(GAMMA)),
                           float(np.float32(LAMBDA)))
@@ -186,7 +194,7 @@ def _env_shard(lo_hi):
     rew = np.empty((HORIZON, n), np.float32)
     dn = np.empty((HORIZON, n), np.float32)
     for t in range(HORIZON):
-        rew[t], dn[t] = env.step(g["actions"][t, lo:hi])
+        rew[t], dn[t] = env.step(g["actions"][t, lo:hi], _aim(t, lo, hi))
         env.obs_tiles(obs)
     adv, ret = oracle.gae(rew, g["values"][:, lo:hi], dn, g["last_values"][lo:hi], float(np.float32(GAMMA)),
                           float(np.float32(LAMBDA)))
@@ -603,6 +611,8 @@ def main():
     pi = inputs.make_policy_inputs(20, b)
     values, last_values = inputs.make_values(21, HORIZON, N_ENVS)
     policy_actions = pi.actions.reshape(HORIZON, N_ENVS)
+    hook = args.hook == "grapple"
+    aims = inputs.make_aims(22, HORIZON, N_ENVS) if hook else None
 
     # The CPU legs run before this process first touches the GPU: the all-core leg forks workers, and a
     # process whose GPU runtime is initialised must not fork them.
@@ -615,6 +625,8 @@ def main():
             _SHARED.update(reward_mode=1, waypoints=table, wp_lens=lens)
         if respawn:
             _SHARED.update(respawn_mode=1, ckpt_spawns=ms.ckpt_spawns, respawn_seed=RESPAWN_SEED)
+        if hook:
+            _SHARED.update(hook_mode=1, aims=aims)
         n_s = min(args.cpu_envs, N_ENVS)
         rate, dt = cpu_baseline(ms, policy_actions, values, last_values, pi, n_s)
         cpu = {"value": rate, "unit": "env-steps/s", "cores": 1, "kind": "oracle",
@@ -642,7 +654,10 @@ def main():
         wp_kw = dict(reward_mode=binding.REWARD_WAYPOINTS, waypoints=table, wp_lens=lens)
     if respawn:
         wp_kw.update(respawn_mode=binding.RESPAWN_ADAPTIVE, ckpt_spawns=ms.ckpt_spawns, respawn_seed=RESPAWN_SEED)
+    if hook:
+        wp_kw.update(hook_mode=binding.HOOK_GRAPPLE)
     env = binding.Env(ms.maps, ms.ckpts, ms.spawns, N_ENVS, frame_skip=3, time_limit=2000, device=dev, **wp_kw)
+    aims_d = torch.from_numpy(aims).to(dev) if hook else None
     # rollout buffer: one allocation of [actions T*N | obs T*N*1397 | rewards T*N | dones T*N]
     a_bytes = HORIZON * N_ENVS * 4
     o_bytes = HORIZON * N_ENVS * 1397 * 4
@@ -678,7 +693,7 @@ def main():
         if ev is not None:
             ev["env"][0].record()
         for t in range(HORIZON):
-            env.step(actions[t], obs[t], rewards[t], dones[t])
+            env.step(actions[t], obs[t], rewards[t], dones[t], aim=None if aims_d is None else aims_d[t])
         if ev is not None:
             ev["env"][1].record()
             ev["gae"][0].record()
@@ -748,7 +763,9 @@ def main():
     value = env_steps / wall
 
     env_launch_bytes = N_ENVS * (ENV_BYTES_PER_ENV_STEP + (ENV_BYTES_WAYPOINTS if waypoints else 0)
-                                 + (ENV_BYTES_RESPAWN if respawn else 0))
+                                 + (ENV_BYTES_RESPAWN if respawn else 0) + (ENV_BYTES_HOOK if hook else 0))
+    env_key = ("env_step+obs_gather" + ("+waypoints" if waypoints else "") + ("+respawn" if respawn else "")
+               + ("+hook" if hook else ""))
     env_avg_s = float(env_ms.mean()) * 1e-3
     achieved = env_launch_bytes / env_avg_s / 1e9
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
@@ -783,13 +800,14 @@ def main():
                                "tile obs (31x43 + 4x15 + 4) into a resident rollout buffer, GAE + whole-batch "
                                "normalisation, PPO loss over 16 shuffled minibatches of 524288"
                                + (", waypoint-path reward" if waypoints else "")
-                               + (", adaptive checkpoint respawn" if respawn else ""),
+                               + (", adaptive checkpoint respawn" if respawn else "")
+                               + (", grapple hook with seeded continuous aims" if hook else ""),
                    "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES,
                    "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss",
-                   "reward": args.reward, "respawn": args.respawn},
+                   "reward": args.reward, "respawn": args.respawn, "hook": args.hook},
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": load_traffic("env_step+obs_gather"),
+                     "traffic": load_traffic(env_key),
                      "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
         "env_step_us": float(env_ms.mean()) * 1e3,
         "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
