@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP path's binding, on a GPU machine; the test fails loudly when the library is missing."""
+    """The HIP path's binding where a GPU is present; the test fails loudly when the library is missing."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
