@@ -56,7 +56,7 @@ POLICY_BYTES_PER_ENV = 1397 * 4 + 3 * 4               # 5600
 POLICY_WEIGHT_BYTES = 128 * 1408 * 2 + 13 * 128 * 4   # 367104
 POLICY_SEED = 31
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
-                         "perm": 12 * 4 + 6 * 4}        # ... and the permutation entry instead of the id
+                         "perm": 12 * 4 + 6 * 4 + 2 + 2}  # ... the permutation entry, its minibatch id written and read
 
 
 def parse():
@@ -84,7 +84,8 @@ def parse():
     p.add_argument("--hook", choices=("off", "grapple"), default="off",
                    help="grapple hook aimed by seeded continuous aims (rl_env_step_aim)")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
-                   help="minibatches as per-sample minibatch ids read in storage order, or as a gather by perm")
+                   help="minibatches as per-sample minibatch ids read in storage order, or given by a permutation "
+                        "(turned into the same ids on the device, then the same pass)")
     return p.parse_args()
 
 

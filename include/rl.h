@@ -293,7 +293,10 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   contents); calls sharing it must not overlap. The per-sample terms are float32 (exponentials and
  *   logarithms from the hardware's base-2 instructions, about 1 ulp each) and are reduced through float64
  *   partials in a fixed order (identical results from run to run). With mb_index every input is read
- *   once, in storage order; with perm every read is a gather. */
+ *   once, in storage order. With perm and at most 64 minibatches the perm is first turned into each
+ *   sample's minibatch number (in the workspace) and the samples are then read the same way; with more
+ *   minibatches every read is a gather. perm entries outside [0, B) are clamped into it (a permutation
+ *   has none). */
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
                 const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
                 const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,

@@ -6,8 +6,12 @@
 // Two ways to visit the samples, both ending in per-block float64 partials that a finalise kernel (one
 // block per minibatch) reduces in block order; no floating-point atomics, so results are identical from
 // run to run.
-//   Gather (perm or contiguous): grid (blocks per minibatch, minibatches); thread k of minibatch m reads
-//   sample perm[m*mb + k]. Shuffled indices make every per-sample read a random access.
+//   Gather (contiguous, or perm with more than 64 minibatches): grid (blocks per minibatch, minibatches);
+//   thread k of minibatch m reads sample perm[m*mb + k]. Shuffled indices make every per-sample read a
+//   random access.
+//   perm with at most 64 minibatches is first turned into each sample's minibatch number (one scatter of
+//   2 bytes per sample into the workspace), then takes the stream pass below: the same sets, summed in
+//   storage order instead of perm order.
 //   Stream (mb_index): each minibatch's scalars are means over its set of samples, so one pass over the
 //   batch in storage order serves all minibatches at once: every read is coalesced and each sample is
 //   read exactly once. Each thread adds its samples' terms into its own per-minibatch slots in LDS
@@ -245,7 +249,8 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     double s_pg = 0.0, s_v = 0.0, s_h = 0.0;
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < p.mb; k += step) {
-        const int64_t i = p.perm ? (int64_t)p.perm[base + k] : base + k;
+        // entries outside [0, B) (never in a permutation) are clamped so that every read stays in bounds
+        const int64_t i = p.perm ? min(max((int64_t)p.perm[base + k], (int64_t)0), p.B - 1) : base + k;
         float pg, v, h;
         sample_terms<AC, GRAD>(p, i, mean, scale, &pg, &v, &h);
         s_pg += (double)pg;
@@ -388,6 +393,18 @@ __global__ __launch_bounds__(256) void k_ppo_finalize(const double* __restrict__
     }
 }
 
+// Each sample's minibatch number from a permutation: ids[perm[m*mb + k]] = m. Grid (blocks per minibatch,
+// minibatches), so the minibatch is the block's. Entries outside [0, B) are clamped into it, so every write
+// stays in the array (a permutation writes each entry exactly once).
+__global__ __launch_bounds__(256) void k_perm_to_index(const int32_t* __restrict__ perm, int64_t B, int64_t mb,
+                                                       uint16_t* __restrict__ ids)
+{
+    const int64_t base = (int64_t)blockIdx.y * mb;
+    const uint16_t m = (uint16_t)blockIdx.y;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < mb; k += (int64_t)gridDim.x * blockDim.x)
+        ids[min(max((int64_t)perm[base + k], (int64_t)0), B - 1)] = m;
+}
+
 int blocks_per_mb(int64_t mb)
 {
     const int64_t per_block = 256 * kSamplesPerThread;
@@ -398,6 +415,13 @@ constexpr int kStreamMaxMinibatches = 64;
 // Every stream variant holds 48 KB of LDS per block, so a CU keeps 3 blocks and 768 blocks are one
 // resident round on 256 CUs: no tail round of partly filled CUs.
 constexpr int kStreamBlocks = 768;
+
+// Bytes of the per-block partials at the front of the workspace (rounded up to 256, where the minibatch
+// numbers of a converted perm follow).
+size_t partial_bytes(int64_t num_mb, size_t blocks)
+{
+    return rl::round_up(sizeof(double) * 3 * (size_t)num_mb * blocks, 256);
+}
 
 // Stream-mode grid: blocks of `chunk` samples, at most kStreamBlocks of them.
 int stream_blocks(int64_t B, int64_t* chunk)
@@ -419,7 +443,9 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     const int64_t num_mb = B / mb;
     int64_t chunk = 0;
     const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, &chunk) : 0);
-    *bytes = sizeof(double) * 3 * (size_t)num_mb * blocks;
+    *bytes = partial_bytes(num_mb, blocks);
+    // with at most 64 minibatches, room for the minibatch numbers a perm is turned into
+    if (num_mb <= kStreamMaxMinibatches) *bytes += sizeof(uint16_t) * (size_t)B;
     return RL_OK;
 }
 
@@ -509,6 +535,18 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
     p.inv_mb = (float)(1.0 / (double)mb);
     p.dv_coef = (float)(2.0 * (double)vf_coef / (double)mb);
     hipStream_t st = rl::as_stream(stream);
+    if (perm && num_mb <= kStreamMaxMinibatches) {
+        // the perm's sets as minibatch numbers behind the partials, then the stream pass
+        int64_t c = 0;
+        const size_t blocks = (size_t)std::max(blocks_per_mb(mb), stream_blocks(B, &c));
+        uint16_t* ids = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks));
+        hipLaunchKernelGGL(k_perm_to_index, dim3((unsigned)blocks_per_mb(mb), (unsigned)num_mb), dim3(256), 0, st,
+                           perm, B, (int64_t)mb, ids);
+        if (int rc = rl::check_launch("ppo_loss perm")) return rc;
+        mb_index = ids;
+        p.mb_index = ids;
+        p.perm = nullptr;
+    }
     int64_t chunk = 0;
     const int nblk = mb_index ? stream_blocks(B, &chunk) : blocks_per_mb(mb);
     if (dlogits) launch_loss<true>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
