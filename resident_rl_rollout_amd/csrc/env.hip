@@ -26,7 +26,6 @@
 //   rhist int32[M][K+1]                                    (adaptive respawn only; empty otherwise)
 // Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
 
-#include <type_traits>
 #include <vector>
 
 #include "rl_internal.hpp"
@@ -323,51 +322,6 @@ struct Neighbourhood {
     }
 };
 
-// Hook mode: a hook can push either velocity component to 160 a tick, so 5 ticks reach up to 800
-// sub-units (3.2 tiles) in any direction; every probe then lies inside rows r0-4 .. r0+4 and columns
-// c0-4 .. c0+4. Bit (row - rb) * 9 + (col - cb) of 81, in two words.
-struct WideNeighbourhood {
-    uint64_t solid[2], freeze[2];
-    int rb, cb;
-    __device__ __forceinline__ static uint32_t bit(const uint64_t (&w)[2], int i)
-    {
-        return (uint32_t)((i < 64 ? w[0] >> i : w[1] >> (i - 64)) & 1u);
-    }
-    __device__ __forceinline__ uint32_t s(int row, int col) const { return bit(solid, (row - rb) * 9 + (col - cb)); }
-    __device__ __forceinline__ uint32_t f(int row, int col) const { return bit(freeze, (row - rb) * 9 + (col - cb)); }
-};
-
-__device__ __forceinline__ WideNeighbourhood load_wide_neighbourhood(const EnvDev& d, int m, int32_t x, int32_t y)
-{
-    WideNeighbourhood nb;
-    nb.rb = clampi(y >> 8, 0, d.h - 1) - 4;
-    nb.cb = clampi(x >> 8, 0, d.w - 1) - 4;
-    uint64_t s[2] = {0, 0}, f[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        uint64_t row[2];
-        __builtin_memcpy(row, tile_ptr(d, m, nb.rb + i, nb.cb), 16);   // 9 of the 16 bytes are used
-#pragma unroll
-        for (int j = 0; j < 9; ++j) {
-            const uint32_t t = (uint32_t)((j < 8 ? row[0] >> (8 * j) : row[1]) & 0xffu);
-            const int b = i * 9 + j;
-            const uint64_t sb = (uint64_t)(t == kSolid || t == kPlatform), fb = (uint64_t)(t == kFreeze);
-            if (b < 64) {
-                s[0] |= sb << b;
-                f[0] |= fb << b;
-            } else {
-                s[1] |= sb << (b - 64);
-                f[1] |= fb << (b - 64);
-            }
-        }
-    }
-    nb.solid[0] = s[0];
-    nb.solid[1] = s[1];
-    nb.freeze[0] = f[0];
-    nb.freeze[1] = f[1];
-    return nb;
-}
-
 // floor(sqrt(v)) for an integer-valued v in [0, 2^53): the rounded square root, then checked exactly.
 __device__ __forceinline__ double floor_sqrt(double v)
 {
@@ -648,11 +602,29 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     int32_t hvx = (int16_t)(hk.v & 0xffff), hvy = hk.v >> 16;
     const int32_t adx = (int16_t)(hk.aim & 0xffff), ady = hk.aim >> 16;
 
-    std::conditional_t<kHook, WideNeighbourhood, Neighbourhood> nb;
-    if constexpr (kHook)
-        nb = load_wide_neighbourhood(d, m, x, y);
-    else
-        nb = load_neighbourhood(d, m, x, y);
+    const Neighbourhood nb = load_neighbourhood(d, m, x, y);
+    // A hook can push either velocity component to 160 a tick, so in hook mode a decision's probes can
+    // leave the 8x8 neighbourhood (by up to 4 tiles in any direction over 5 ticks). Those probes read the
+    // tile from the padded map instead (cached; rare, as they need a fast swing), clamped into the border,
+    // which is solid like everything outside the map.
+    const auto tile_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
+        return *tile_ptr(d, m, clampi(row, -kPadY, d.h + kPadY - 1), clampi(col, -kPadX, d.w + kPadX - 1));
+    };
+    const auto solid_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (kHook) {
+            if ((unsigned)(row - nb.rb) >= 8u || (unsigned)(col - nb.cb) >= 8u) {
+                const uint32_t t = tile_at(row, col);
+                return (t == kSolid || t == kPlatform) ? 1u : 0u;
+            }
+        }
+        return nb.s(row, col);
+    };
+    const auto freeze_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (kHook) {
+            if ((unsigned)(row - nb.rb) >= 8u || (unsigned)(col - nb.cb) >= 8u) return tile_at(row, col) == kFreeze ? 1u : 0u;
+        }
+        return nb.f(row, col);
+    };
     const int32_t* ck = d.ckpt + (int64_t)m * d.k * 2;
     int32_t ck_col = next < d.k ? ck[2 * next] : 0;
 
@@ -699,9 +671,7 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
                 flight += 1;
                 // the tip never gets past the first border tile, which holds it; the clamp only matters for
                 // a spawn placed outside the map
-                const int row = clampi(hy >> 8, -kPadY, d.h + kPadY - 1);
-                const int col = clampi(hx >> 8, -kPadX, d.w + kPadX - 1);
-                const uint32_t t = *tile_ptr(d, m, row, col);
+                const uint32_t t = tile_at(hy >> 8, hx >> 8);
                 if (t == kSolid || t == kPlatform) phase = 2;
                 else if (flight >= kHookFlight) phase = 0;
             }
@@ -722,10 +692,10 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
             const int r0 = y >> 8, r1 = (y + kBox - 1) >> 8;
             if (vx > 0) {
                 const int col = (nx + kBox - 1) >> 8;
-                if (nb.s(r0, col) | nb.s(r1, col)) { nx = col * kTile - kBox; vx = 0; }
+                if (solid_at(r0, col) | solid_at(r1, col)) { nx = col * kTile - kBox; vx = 0; }
             } else if (vx < 0) {
                 const int col = nx >> 8;
-                if (nb.s(r0, col) | nb.s(r1, col)) { nx = (col + 1) * kTile; vx = 0; }
+                if (solid_at(r0, col) | solid_at(r1, col)) { nx = (col + 1) * kTile; vx = 0; }
             }
             x = nx;
         }
@@ -735,10 +705,10 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
             const int c0 = x >> 8, c1 = (x + kBox - 1) >> 8;
             if (vy > 0) {
                 const int row = (ny + kBox - 1) >> 8;
-                if (nb.s(row, c0) | nb.s(row, c1)) { ny = row * kTile - kBox; vy = 0; }
+                if (solid_at(row, c0) | solid_at(row, c1)) { ny = row * kTile - kBox; vy = 0; }
             } else if (vy < 0) {
                 const int row = ny >> 8;
-                if (nb.s(row, c0) | nb.s(row, c1)) { ny = (row + 1) * kTile; vy = 0; }
+                if (solid_at(row, c0) | solid_at(row, c1)) { ny = (row + 1) * kTile; vy = 0; }
             }
             y = ny;
         }
@@ -747,11 +717,11 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
             const int c0 = x >> 8, c1 = (x + kBox - 1) >> 8;
             const int r0 = y >> 8, r1 = (y + kBox - 1) >> 8;
             const int below = (y + kBox) >> 8;
-            grounded = nb.s(below, c0) | nb.s(below, c1);
+            grounded = solid_at(below, c0) | solid_at(below, c1);
             const int cl = (x - 1) >> 8, cr = (x + kBox) >> 8;
-            wall_l = nb.s(r0, cl) | nb.s(r1, cl);
-            wall_r = nb.s(r0, cr) | nb.s(r1, cr);
-            const uint32_t touching = nb.f(r0, c0) | nb.f(r0, c1) | nb.f(r1, c0) | nb.f(r1, c1);
+            wall_l = solid_at(r0, cl) | solid_at(r1, cl);
+            wall_r = solid_at(r0, cr) | solid_at(r1, cr);
+            const uint32_t touching = freeze_at(r0, c0) | freeze_at(r0, c1) | freeze_at(r1, c0) | freeze_at(r1, c1);
             freeze = touching ? kFreezeTicks : (freeze > 0 ? freeze - 1 : 0);
         }
         // 9. hook and jump state
@@ -993,8 +963,13 @@ __device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const
     const int m = n % d.m;
     const int32_t a = actions[n];
     const SlotWords cur = load_slot(d, head_prev, n);
-    const SlotWords old1 = load_slot(d, (head_prev - 1) & 3, n);
-    const SlotWords old2 = load_slot(d, (head_prev - 2) & 3, n);
+    // the two older slots are only written out; in hook mode they are loaded after the decision, whose
+    // state the hook enlarges, to keep the registers within four waves a SIMD
+    SlotWords old1{}, old2{};
+    if constexpr ((MODE & kModeHook) == 0) {
+        old1 = load_slot(d, (head_prev - 1) & 3, n);
+        old2 = load_slot(d, (head_prev - 2) & 3, n);
+    }
     const int32_t next0 = d.extra[n], best0 = d.extra[d.np + n];
     const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
     const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
@@ -1009,6 +984,10 @@ __device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const
 #pragma unroll
             for (int dim = 0; dim < kFrameDims; ++dim) t[f * kFrameDims + dim] = t[dim];
     } else {
+        if constexpr (kHook) {
+            old1 = load_slot(d, (head_prev - 1) & 3, n);
+            old2 = load_slot(d, (head_prev - 2) & 3, n);
+        }
         put_frame<kHook>(t + kFrameDims, cur.x, cur.y, cur.vxy, (uint32_t)cur.misc, cur.tick);
         put_frame<kHook>(t + 2 * kFrameDims, old1.x, old1.y, old1.vxy, (uint32_t)old1.misc, old1.tick);
         put_frame<kHook>(t + 3 * kFrameDims, old2.x, old2.y, old2.vxy, (uint32_t)old2.misc, old2.tick);
@@ -1060,7 +1039,7 @@ __device__ __forceinline__ void write_group(const EnvDev& d, int n0, int ne, int
 }
 
 template <int E, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((MODE & kModeHook) ? 3 : 4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
                                                     float* __restrict__ obs, int64_t stride, int head_prev,
                                                     int head_new)

@@ -28,36 +28,49 @@ def hook_inputs(seed, steps, n, p_hook=0.7):
 
 
 def run(pe, acts, aims, what, obs_every=1, obs_envs=None):
+    """Steps both sides, checking everything; returns the phase counts, the largest speed, and how far past
+    the 8x8 collision neighbourhood (3 rows up, 2 columns left of the starting box) a decision probed."""
     pe.check_obs(f"{what} reset")
     phases = np.zeros(3, np.int64)
     vmax = 0
+    beyond = 0
     for s in range(len(acts)):
+        x0, y0 = pe.ora.state[:, F["x"]].copy(), pe.ora.state[:, F["y"]].copy()
         r, d = pe.step(acts[s], None if aims is None else aims[s])
+        x1, y1 = pe.ora.state[:, F["x"]], pe.ora.state[:, F["y"]]
+        live = d == 0
+        left = (x0 >> 8) - ((x1 - 1) >> 8) - 2          # wall probe columns past c0 - 2
+        up = (y0 >> 8) - (y1 >> 8) - 3                  # ceiling probe rows past r0 - 3
+        if live.any():
+            beyond = max(beyond, int(np.maximum(left, up)[live].max()))
         pe.check_step(r, d, f"{what} step {s}")
         pe.check_state(f"{what} step {s}")
         if obs_every and (s % obs_every == 0 or s == len(acts) - 1):
             pe.check_obs(f"{what} step {s}", obs_envs)
         phases += np.bincount(pe.ora.state[:, F["hook_phase"]], minlength=3)
         vmax = max(vmax, int(np.abs(pe.ora.state[:, [F["vx"], F["vy"]]]).max()))
-    return phases, vmax
+    return phases, vmax, beyond
 
 
 def test_tiny_workload_with_the_hook(gpu_lib):
     ms = inputs.make_mapset([1], 32, 128)
     pe = PairedEnvs(ms, 64, hook_mode=binding.HOOK_GRAPPLE)
     acts, aims = hook_inputs(2, 128, 64)
-    phases, _ = run(pe, acts, aims, "tiny hook")
+    phases, _, _ = run(pe, acts, aims, "tiny hook")
     assert phases[1] > 0 and phases[2] > 0        # tips flew and held
 
 
 @pytest.mark.parametrize("fs", [1, 3, 5])
 def test_hook_frame_skip_and_fast_swings(fs, gpu_lib):
-    # frame-skip 5 with hook speeds up to 160 a tick spans the widest neighbourhood a decision can probe
+    # frame-skip 5 with hook speeds up to 160 a tick takes collision probes past the 8x8 neighbourhood
+    # (read from the map instead)
     ms = inputs.make_mapset([4, 5, 6], 48, 96)
     pe = PairedEnvs(ms, 300, frame_skip=fs, time_limit=400, hook_mode=binding.HOOK_GRAPPLE)
     acts, aims = hook_inputs(10 + fs, 120, 300, p_hook=0.85)
-    phases, vmax = run(pe, acts, aims, f"hook fs={fs}", obs_every=9)
+    phases, vmax, beyond = run(pe, acts, aims, f"hook fs={fs}", obs_every=9)
     assert phases[2] > 0 and vmax > 100
+    if fs == 5:
+        assert beyond > 0
 
 
 def test_hook_workload_full_size(gpu_lib):
@@ -90,7 +103,7 @@ def test_hook_with_waypoints_and_respawn(gpu_lib):
     pe = PairedEnvs(ms, 300, time_limit=30, reward_mode=binding.REWARD_WAYPOINTS, waypoints=wpt, wp_lens=lens,
                     respawn_mode=binding.RESPAWN_ADAPTIVE, respawn_seed=77, hook_mode=binding.HOOK_GRAPPLE)
     acts, aims = hook_inputs(5, 150, 300)
-    phases, _ = run(pe, acts, aims, "hook + waypoints + respawn", obs_every=5)
+    phases, _, _ = run(pe, acts, aims, "hook + waypoints + respawn", obs_every=5)
     assert phases[2] > 0
 
 
@@ -98,7 +111,7 @@ def test_hook_mode_without_aims_never_fires(gpu_lib):
     ms = inputs.make_mapset([1], 32, 128)
     pe = PairedEnvs(ms, 128, hook_mode=binding.HOOK_GRAPPLE)
     acts, _ = hook_inputs(6, 40, 128)
-    phases, _ = run(pe, acts, None, "hook without aims", obs_every=10)
+    phases, _, _ = run(pe, acts, None, "hook without aims", obs_every=10)
     assert phases[1] == 0 and phases[2] == 0
 
 
