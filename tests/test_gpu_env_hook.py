@@ -1,6 +1,8 @@
 """GPU parity of the grapple hook (hook mode, rl_env_step_aim) against the oracle: bit-exact state (the
 hook's phase, tip, flight velocity and ticks flown included), observations, rewards and dones, with the
 same seeded maps, actions and aims on both sides."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -125,3 +127,10 @@ def test_aims_need_hook_mode(gpu_lib):
         env.step(a, obs, r, r.clone(), aim=torch.zeros(8, dtype=torch.int32, device="cuda"))
     with pytest.raises(binding.RLError, match="hook_mode"):
         binding.Env(ms.maps, ms.ckpts, ms.spawns, 8, hook_mode=2)
+    # a misaligned aim array is refused before anything is enqueued
+    hk = binding.Env(ms.maps, ms.ckpts, ms.spawns, 8, hook_mode=binding.HOOK_GRAPPLE)
+    aim = torch.zeros(9, dtype=torch.int32, device="cuda")
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    rc = binding.lib().rl_env_step_aim(hk._handle, P(a), ctypes.c_void_p(aim.data_ptr() + 2), P(obs), P(r), P(r),
+                                       None)
+    assert rc == -2 and "aligned" in binding.lib().rl_last_error().decode()
