@@ -1110,7 +1110,11 @@ __global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restric
     const int lo_b = max(bx0 - wx, 0), hi_b = min(bx1 - wx, 3);
     const uint32_t boxmask =
         lo_b <= hi_b ? (0xffffffffu >> (8 * (3 - hi_b))) & (0xffffffffu << (8 * lo_b)) : 0u;
-    for (int py = rl; py < kPix; py += 3) {
+    // 28 passes for every lane (84 rows in steps of 3 from its row offset): a fixed count, unrolled, so
+    // that the LDS reads of several passes are in flight together
+#pragma unroll
+    for (int i = 0; i < kPix / 3; ++i) {
+        const int py = rl + 3 * i;
         const int wy = cam_y + py;
         const int sy = wy & 7;
         const uint8_t* trow = tiles + ((wy >> 3) - ty0) * kCamTileStride + tc;
