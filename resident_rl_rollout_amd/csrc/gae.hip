@@ -96,15 +96,17 @@ __global__ __launch_bounds__(BLOCK) void k_gae_chunked(const float* __restrict__
     const int len = valid ? max(0, min(L, T - t0)) : 0;
 
     // Loads are unconditional (indices clamped into the arrays) so that all of a thread's loads issue
-    // back to back; only the arithmetic and the stores are predicated on the chunk's length.
+    // back to back; only the arithmetic and the stores are predicated on the chunk's length. Each input
+    // element is read once, so the loads carry the non-temporal hint (they need not displace cached
+    // lines).
     const int nn = min(n, N - 1);
     float delta[LMAX], cf[LMAX], vv[LMAX];
 #pragma unroll
     for (int j = 0; j < LMAX; ++j) {
         const int64_t idx = (int64_t)min(t0 + j, T - 1) * ld + nn;
-        vv[j] = val[idx];
-        delta[j] = rew[idx];
-        cf[j] = 1.0f - done[idx];
+        vv[j] = __builtin_nontemporal_load(val + idx);
+        delta[j] = __builtin_nontemporal_load(rew + idx);
+        cf[j] = 1.0f - __builtin_nontemporal_load(done + idx);
     }
     const float v_after = val[(int64_t)min(t0 + len, T - 1) * ld + nn];
     const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
@@ -241,10 +243,10 @@ __global__ __launch_bounds__(BLOCK) void k_vtrace_chunked(const float* __restric
 #pragma unroll
     for (int j = 0; j < LMAX; ++j) {
         const int64_t idx = (int64_t)min(t0 + j, T - 1) * ld + nn;
-        vv[j] = val[idx];
-        td[j] = rew[idx];
-        nd[j] = 1.0f - done[idx];
-        ratio[j] = lrho[idx];
+        vv[j] = __builtin_nontemporal_load(val + idx);   // read once: non-temporal, as in the GAE scan
+        td[j] = __builtin_nontemporal_load(rew + idx);
+        nd[j] = 1.0f - __builtin_nontemporal_load(done + idx);
+        ratio[j] = __builtin_nontemporal_load(lrho + idx);
     }
     const float v_after = val[(int64_t)min(t0 + len, T - 1) * ld + nn];
     const float vnext_tail = (t0 + len < T) ? v_after : vlast[nn];
