@@ -28,26 +28,35 @@ struct StatsOut {
     double* partials;     // [grid][2]: sum A, sum A^2 of each block
 };
 
-// Sum of a double across the block (256 threads), the same fixed order on every run.
-__device__ __forceinline__ double block_sum(double v, double* lds)
+// Sums of two doubles across the block at once, each in the same fixed order on every run (a wave's
+// butterfly, then the waves in order), with one barrier. The LDS array must not have been used earlier in
+// the kernel.
+__device__ __forceinline__ void block_sum2(double& a, double& b, double* lds)
 {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    const int w = threadIdx.x >> 6;
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+    }
+    const int w = threadIdx.x >> 6, nw = (int)(blockDim.x >> 6);
+    if ((threadIdx.x & 63) == 0) {
+        lds[w] = a;
+        lds[16 + w] = b;
+    }
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) lds[w] = v;
-    __syncthreads();
-    double s = 0.0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += lds[i];
-    return s;
+    a = 0.0;
+    b = 0.0;
+    for (int i = 0; i < nw; ++i) {
+        a += lds[i];
+        b += lds[16 + i];
+    }
 }
 
 // Publish this block's (sum A, sum A^2).
 __device__ void publish_stats(double s1, double s2, const StatsOut& so)
 {
     __shared__ double lds[32];
-    s1 = block_sum(s1, lds);
-    s2 = block_sum(s2, lds + 16);
+    block_sum2(s1, s2, lds);
     if (threadIdx.x == 0) {
         so.partials[2 * blockIdx.x] = s1;
         so.partials[2 * blockIdx.x + 1] = s2;
@@ -58,14 +67,13 @@ __device__ void publish_stats(double s1, double s2, const StatsOut& so)
 __global__ __launch_bounds__(256) void k_stats_finalize(const double* __restrict__ partials, int blocks, double count,
                                                         double* __restrict__ stats)
 {
-    __shared__ double lds[8];
+    __shared__ double lds[32];
     double a = 0.0, b = 0.0;
     for (int i = threadIdx.x; i < blocks; i += blockDim.x) {
         a += partials[2 * i];
         b += partials[2 * i + 1];
     }
-    a = block_sum(a, lds);
-    b = block_sum(b, lds + 4);
+    block_sum2(a, b, lds);
     if (threadIdx.x == 0) {
         const double mean = a / count;
         double var = b / count - mean * mean;
