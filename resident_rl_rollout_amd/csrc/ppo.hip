@@ -59,16 +59,32 @@ struct LossArgs {
     float dv_coef;      // 2 vf / M
 };
 
-__device__ __forceinline__ double block_sum(double v, double* lds)
+// Sums of three doubles across a block of at most 4 waves, each in the same fixed order on every run (a
+// wave's butterfly, then the waves in order), with one barrier. The LDS array (12 doubles) must not have
+// been used earlier in the kernel.
+__device__ __forceinline__ void block_sum3(double& a, double& b, double& c, double* lds)
 {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+        c += __shfl_xor(c, off, 64);
+    }
+    const int w = threadIdx.x >> 6, nw = (int)(blockDim.x >> 6);
+    if ((threadIdx.x & 63) == 0) {
+        lds[w] = a;
+        lds[4 + w] = b;
+        lds[8 + w] = c;
+    }
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s = 0.0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += lds[i];
-    return s;
+    a = 0.0;
+    b = 0.0;
+    c = 0.0;
+    for (int i = 0; i < nw; ++i) {
+        a += lds[i];
+        b += lds[4 + i];
+        c += lds[8 + i];
+    }
 }
 
 // The logits row of a sample in registers (AC = compile-time action count).
@@ -257,9 +273,7 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
         s_v += (double)v;
         s_h += (double)h;
     }
-    s_pg = block_sum(s_pg, lds);
-    s_v = block_sum(s_v, lds + 4);
-    s_h = block_sum(s_h, lds + 8);
+    block_sum3(s_pg, s_v, s_h, lds);
     if (threadIdx.x == 0) {
         double* part = p.partials + ((int64_t)m * gridDim.x + blockIdx.x) * 3;
         part[0] = s_pg;
@@ -380,9 +394,7 @@ __global__ __launch_bounds__(256) void k_ppo_finalize(const double* __restrict__
         b += part[1];
         c += part[2];
     }
-    a = block_sum(a, lds);
-    b = block_sum(b, lds + 4);
-    c = block_sum(c, lds + 8);
+    block_sum3(a, b, c, lds);
     if (threadIdx.x == 0) {
         const double inv = 1.0 / (double)mb;
         const double pg = a * inv, v = b * inv, h = c * inv;
