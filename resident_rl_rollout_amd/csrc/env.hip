@@ -63,10 +63,11 @@ constexpr int kHookFlight = 10;
 constexpr int kHookAccel = 24;
 constexpr int kHookMaxV = 160;
 // the step kernels' variants: bit 0 = the waypoint-path reward, bit 1 = the adaptive respawn, bit 2 = the
-// grapple hook
+// grapple hook, bit 3 (with bit 2) = a frame skip above 3, where a hooked box can leave the 8x8 neighbourhood
 constexpr int kModeWaypoints = 1;
 constexpr int kModeRespawn = 2;
 constexpr int kModeHook = 4;
+constexpr int kModeHookFar = 8;
 
 constexpr int kWinW = 43;
 constexpr int kWinH = 31;
@@ -603,15 +604,17 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     const int32_t adx = (int16_t)(hk.aim & 0xffff), ady = hk.aim >> 16;
 
     const Neighbourhood nb = load_neighbourhood(d, m, x, y);
-    // A hook can push either velocity component to 160 a tick, so in hook mode a decision's probes can
-    // leave the 8x8 neighbourhood (by up to 4 tiles in any direction over 5 ticks). Those probes read the
-    // tile from the padded map instead (cached; rare, as they need a fast swing), clamped into the border,
-    // which is solid like everything outside the map.
+    // A hook can push either velocity component to 160 a tick. Over at most 3 ticks the box (192 wide) then
+    // moves at most 480 sub-units, less than two tiles, and every probe stays in rows r0-2..r0+3 and
+    // columns c0-2..c0+3, inside the neighbourhood. With 4 or 5 ticks a probe can leave it (by up to 4 tiles
+    // in any direction), so the kModeHookFar variants read such a tile from the padded map instead (cached;
+    // rare, as it needs a fast swing), clamped into the border, which is solid like everything outside.
+    constexpr bool kFar = (MODE & kModeHookFar) != 0;
     const auto tile_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
         return *tile_ptr(d, m, clampi(row, -kPadY, d.h + kPadY - 1), clampi(col, -kPadX, d.w + kPadX - 1));
     };
     const auto solid_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
-        if constexpr (kHook) {
+        if constexpr (kFar) {
             if ((unsigned)(row - nb.rb) >= 8u || (unsigned)(col - nb.cb) >= 8u) {
                 const uint32_t t = tile_at(row, col);
                 return (t == kSolid || t == kPlatform) ? 1u : 0u;
@@ -620,7 +623,7 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         return nb.s(row, col);
     };
     const auto freeze_at = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
-        if constexpr (kHook) {
+        if constexpr (kFar) {
             if ((unsigned)(row - nb.rb) >= 8u || (unsigned)(col - nb.cb) >= 8u) return tile_at(row, col) == kFreeze ? 1u : 0u;
         }
         return nb.f(row, col);
@@ -1370,7 +1373,8 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
     EnvDev d = dev_of(e);
     d.aim = aim;
     const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
-    const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0) | (hk ? kModeHook : 0);
+    const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0) | (hk ? kModeHook : 0) |
+                     (hk && e->cfg.frame_skip > 3 ? kModeHookFar : 0);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
         const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs), block(256);
         float* o = static_cast<float*>(obs);
@@ -1386,7 +1390,11 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
         case 4: RL_STEP_TILES(4); break;
         case 5: RL_STEP_TILES(5); break;
         case 6: RL_STEP_TILES(6); break;
-        default: RL_STEP_TILES(7); break;
+        case 7: RL_STEP_TILES(7); break;
+        case 12: RL_STEP_TILES(12); break;
+        case 13: RL_STEP_TILES(13); break;
+        case 14: RL_STEP_TILES(14); break;
+        default: RL_STEP_TILES(15); break;
         }
 #undef RL_STEP_TILES
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
@@ -1401,7 +1409,11 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
         case 4: RL_STEP(4); break;
         case 5: RL_STEP(5); break;
         case 6: RL_STEP(6); break;
-        default: RL_STEP(7); break;
+        case 7: RL_STEP(7); break;
+        case 12: RL_STEP(12); break;
+        case 13: RL_STEP(13); break;
+        case 14: RL_STEP(14); break;
+        default: RL_STEP(15); break;
         }
 #undef RL_STEP
         if (int rc = rl::check_launch("env_step")) return rc;

@@ -62,15 +62,18 @@ def test_tiny_workload_with_the_hook(gpu_lib):
     assert phases[1] > 0 and phases[2] > 0        # tips flew and held
 
 
-@pytest.mark.parametrize("fs", [1, 3, 5])
+@pytest.mark.parametrize("fs", [1, 3, 4, 5])
 def test_hook_frame_skip_and_fast_swings(fs, gpu_lib):
-    # frame-skip 5 with hook speeds up to 160 a tick takes collision probes past the 8x8 neighbourhood
-    # (read from the map instead)
+    # up to 3 ticks at hook speeds (at most 160 a tick) keep every collision probe inside the 8x8
+    # neighbourhood, which those launches rely on; frame-skip 4 and 5 take probes past it (read from the
+    # map instead)
     ms = inputs.make_mapset([4, 5, 6], 48, 96)
     pe = PairedEnvs(ms, 300, frame_skip=fs, time_limit=400, hook_mode=binding.HOOK_GRAPPLE)
     acts, aims = hook_inputs(10 + fs, 120, 300, p_hook=0.85)
     phases, vmax, beyond = run(pe, acts, aims, f"hook fs={fs}", obs_every=9)
     assert phases[2] > 0 and vmax > 100
+    if fs <= 3:
+        assert beyond <= 0
     if fs == 5:
         assert beyond > 0
 
