@@ -137,3 +137,22 @@ def test_aims_need_hook_mode(gpu_lib):
     rc = binding.lib().rl_env_step_aim(hk._handle, P(a), ctypes.c_void_p(aim.data_ptr() + 2), P(obs), P(r), P(r),
                                        None)
     assert rc == -2 and "aligned" in binding.lib().rl_last_error().decode()
+
+
+def test_masked_reset_while_hooks_fly_and_hold(gpu_lib):
+    # a masked reset puts every third env back at its spawn with the hook idle and the tip cleared, while the
+    # other envs' tips keep flying or holding; the run then continues on both sides
+    ms = inputs.make_mapset([7, 8], 32, 128)
+    pe = PairedEnvs(ms, 333, hook_mode=binding.HOOK_GRAPPLE)
+    acts, aims = hook_inputs(31, 40, 333, p_hook=0.85)
+    run(pe, acts[:14], aims[:14], "hook before the reset", obs_every=0)
+    phase = pe.ora.state[:, F["hook_phase"]]
+    mask = (np.arange(333) % 3 == 0).astype(np.uint8)
+    assert (phase[mask == 1] != 0).any() and (phase[mask == 0] != 0).any()
+    pe.gpu.reset(pe.obs, mask=torch.from_numpy(mask).cuda())
+    pe.ora.reset(mask)
+    pe.check_state("hook masked reset")
+    pe.check_obs("hook masked reset")
+    assert (pe.ora.state[mask == 1][:, F["hook_phase"]] == 0).all()
+    phases, _, _ = run(pe, acts[14:], aims[14:], "hook after the reset", obs_every=5)
+    assert phases[1] > 0 and phases[2] > 0
