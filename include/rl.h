@@ -109,7 +109,10 @@ int rl_step_layout(const rl_env_config* cfg, size_t offsets[4], size_t* block_by
  *   maps     device u8[M][H][W], row 0 at the top; cells outside the map read as solid.
  *   ckpts    device int32[M][K][2] (column, row) of each map's checkpoints, in the order they must be
  *            passed; may be NULL when K = 0.
- *   spawns   device int32[M][2] (x, y) spawn position of each map in sub-units.
+ *   spawns   device int32[M][2] (x, y) spawn position of each map in sub-units. The box placed there
+ *            must lie inside the map: a step's collision tests read the tiles around the box's starting
+ *            tile, which covers every move from a box inside the map; from a box outside it the
+ *            physics is unspecified (memory accesses stay inside the state buffer).
  *   sprites  device u8[16][8][8] grayscale patterns (pattern = tile code & 15); required for pixel mode,
  *            ignored (may be NULL) for tiles.
  *   state    device buffer of rl_env_state_bytes() bytes, 256-byte aligned, owned by the caller for the
@@ -135,8 +138,8 @@ int rl_env_reset(rl_env* env, const uint8_t* mask, void* obs, void* stream);
 int rl_env_set_waypoints(rl_env* env, const int32_t* waypoints, const int32_t* lens, void* stream);
 
 /* Standing spots for the adaptive respawn (RL_RESPAWN_ADAPTIVE): copies ckpt_spawns, device
- * int32[M][K][2] = (x, y) in sub-units where an episode restarted at checkpoint k + 1 begins, into the
- * state buffer on `stream` (the input may be freed once the stream has passed this call). Must be called
+ * int32[M][K][2] = (x, y) in sub-units where an episode restarted at checkpoint k + 1 begins (inside the
+ * map, as for rl_env_create's spawns), into the state buffer on `stream` (the input may be freed once the stream has passed this call). Must be called
  * before the first rl_env_step of such an env (the step fails otherwise); RL_EINVAL otherwise. */
 int rl_env_set_respawn_spots(rl_env* env, const int32_t* ckpt_spawns, void* stream);
 
