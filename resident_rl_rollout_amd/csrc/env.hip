@@ -388,21 +388,29 @@ struct Decision {
     bool done;
 };
 
+// The candidates of a tick: the waypoints at the high-water index (clamped to the path's end) and the
+// kWpAhead after it, loaded unconditionally with indices clamped to the end so that the loads issue together.
+__device__ __forceinline__ void wp_candidates(const EnvDev& d, int m, int32_t path, int2* w)
+{
+    const int32_t len = clampi(d.wplen[m], 1, d.kw);
+    const int32_t p0 = min(path, len - 1);
+    const int2* row = reinterpret_cast<const int2*>(d.wpt) + (int64_t)m * d.kw;
+#pragma unroll
+    for (int j = 0; j <= kWpAhead; ++j) w[j] = row[min(p0 + j, len - 1)];
+}
+
 // Reward mode 1's progress and distance terms of one tick: the waypoint nearest to the box centre among
 // the high-water index and the kWpAhead after it (the lowest index on a tie); moving the high-water index
 // forward pays kUnitsWaypoint per waypoint; a distance d = floor(sqrt(d2)) beyond the grace zone costs
-// (d - kWpGrace) >> kWpPenaltyShift units. The candidates are loaded unconditionally (indices clamped to
-// the path's end) so that the loads issue together. Squared distances are exact in float64: positions
-// and waypoint centres lie below 2^25 sub-units, so d2 < 2^51 (full-rate float64 instead of 64-bit
-// integer multiplies); d = floor(sqrt(d2)) is checked against d2 exactly, and needed only past the zone.
-__device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_t x, int32_t y, int32_t& path)
+// (d - kWpGrace) >> kWpPenaltyShift units. w holds the candidates, from wp_candidates. Squared distances
+// are exact in float64: positions and waypoint centres lie below 2^25 sub-units, so d2 < 2^51 (full-rate
+// float64 instead of 64-bit integer multiplies); d = floor(sqrt(d2)) is checked against d2 exactly, and
+// needed only past the zone.
+__device__ __forceinline__ int32_t waypoint_units(const EnvDev& d, int m, int32_t x, int32_t y, int32_t& path,
+                                                  const int2* w)
 {
     const int32_t len = clampi(d.wplen[m], 1, d.kw);
     if (path > len - 1) path = len - 1;
-    const int2* row = reinterpret_cast<const int2*>(d.wpt) + (int64_t)m * d.kw;
-    int2 w[kWpAhead + 1];
-#pragma unroll
-    for (int j = 0; j <= kWpAhead; ++j) w[j] = row[min(path + j, len - 1)];
     const double cx = (double)(x + kHalfBox), cy = (double)(y + kHalfBox);
     int32_t best = path;
     double best_d2 = 0.0;
@@ -638,6 +646,10 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
     int32_t units = 0;
     bool terminated = false, truncated = false;
     for (int i = 0; i < d.fs && !terminated && !truncated; ++i) {
+        // the tick's waypoint candidates depend only on the index the previous tick left, so they are
+        // loaded first and the tick's physics runs while they arrive
+        int2 wc[kWpAhead + 1];
+        if constexpr ((MODE & kModeWaypoints) != 0) wp_candidates(d, m, path, wc);
         // 1. a frozen player's input is ignored
         const bool frozen = freeze > 0;
         const int sign = frozen ? 0 : (dir == 1 ? -1 : (dir == 2 ? 1 : 0));
@@ -733,7 +745,7 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         jump_held = (uint32_t)jump;
         // 10. progress: past the high-water mark of x (mode 0), or along the waypoint path (mode 1); best x
         // is kept in both (it is an observation dim)
-        if constexpr ((MODE & kModeWaypoints) != 0) units += waypoint_units(d, m, x, y, path);
+        if constexpr ((MODE & kModeWaypoints) != 0) units += waypoint_units(d, m, x, y, path, wc);
         if (x > best_x) {
             if constexpr ((MODE & kModeWaypoints) == 0) units += x - best_x;
             best_x = x;
