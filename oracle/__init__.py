@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the tests, the smoke check and the b
 import this package. It shares no code with the HIP path and never imports it.
 
 ``build()`` compiles ``oracle.c`` with gcc (-O2, no floating-point contraction) into ``liboracle.so``
-next to it; the wrappers build it on first use when it is missing.
+next to it; the wrappers build it on first use when it is missing. The environment variable
+``RL_ORACLE_LIB`` names another build of the same source to load instead (the tests' sanitizer and
+planted-mistake builds); it is loaded as it is, never rebuilt.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra"]
 _lib = None
 
 NF = 24            # canonical state fields per env
@@ -33,8 +36,7 @@ STATE_FIELDS = ("x", "y", "vx", "vy", "facing", "freeze_ticks", "hook_ticks", "h
 def build() -> str:
     """Compile the oracle into liboracle.so (always recompiles)."""
     tmp = _LIB_PATH + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
-                           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+    subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -49,9 +51,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    override = os.environ.get("RL_ORACLE_LIB")
+    if override:
+        lib = ctypes.CDLL(override)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     p = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     cfgp = ctypes.POINTER(_Cfg)

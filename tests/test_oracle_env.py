@@ -66,6 +66,24 @@ def test_flat_walk_velocity_ramp_and_progress_reward():
     assert e.state[0, F["best_x"]] == x0 + ramp(14) + 40 + 32 + 24 + 16 + 8
 
 
+def test_ceiling_bump_snaps_below_the_tile():
+    # A solid row 10 right above the standing box (rows 11 .. 11.99, y = 2880). The jump's first tick gives
+    # vy = -120 + 12 = -108 and ny = 2772, whose top row 10 is solid: the box snaps to the ceiling's
+    # underside, y = 11 * 256 = 2816, and vy = 0. It then falls under gravity, vy = 12, 24, 36:
+    # y = 2828, 2852, and 2888 would reach row 12, so the box lands at 2880 with vy = 0 on the fourth tick.
+    m = flat_map()
+    m[10, :] = 1
+    e = make_env(m, fs=1)
+    ys, vys = [], []
+    for a in [JUMP, NOOP, NOOP, NOOP, NOOP]:
+        e.step([a])
+        ys.append(int(e.state[0, F["y"]]))
+        vys.append(int(e.state[0, F["vy"]]))
+    assert ys == [2816, 2828, 2852, 2880, 2880]
+    assert vys == [0, 12, 24, 0, 0]
+    assert e.state[0, F["grounded"]] == 1
+
+
 def test_jump_apex_and_period():
     e = make_env(flat_map(), fs=1)
     y0 = 12 * 256 - 192

@@ -131,3 +131,14 @@ def test_normalize_epsilon_is_added_to_std():
     out, mean, std = oracle.normalize(np.full(17, 3.0), eps=1e-8)
     assert std == 0.0 and mean == 3.0
     np.testing.assert_array_equal(out, np.zeros(17))
+
+
+def test_normalize_epsilon_placement_at_small_std():
+    # A = [a, -a]: mean 0 and population std a, so (A - mean) / (std + eps) = +-a / (a + eps). At a = 1e-4
+    # and eps = 1e-8 that is +-1 / (1 + 1e-4) = +-0.99990001; the other common placement,
+    # (A - mean) / sqrt(std^2 + eps), would give +-1e-4 / sqrt(2e-8) = +-0.7071, so this case tells them apart.
+    a = 1e-4
+    out, mean, std = oracle.normalize(np.array([a, -a]), eps=1e-8)
+    assert mean == 0.0 and std == a
+    np.testing.assert_allclose(out, [1.0 / (1.0 + 1e-4), -1.0 / (1.0 + 1e-4)], rtol=1e-14)
+    assert abs(out[0] - a / math.sqrt(a * a + 1e-8)) > 0.25

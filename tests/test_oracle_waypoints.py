@@ -143,3 +143,29 @@ def test_version_one_is_unchanged_by_the_path_field():
     e1.reset()
     r = e1.step([RIGHT])[0][0]
     assert r == (8 - 1) / 1024 and e1.state[0, F["path"]] == 0
+
+
+def test_shortened_table_clamps_the_high_water_index():
+    # Walking right along the floor path (1,11) .. (16,11) at single ticks: x = 424 + 48 (t - 6) from tick 6,
+    # so after 30 ticks x = 1576 and the box centre x + 96 = 1672 has passed the midpoints 512, 768, 1024,
+    # 1280 and 1536: the high-water index is 5 and the ticks paid 5 x 0.25. The table is then cut to its
+    # first waypoint (the length a later rl_env_set_waypoints may give). The index past the new end is
+    # clamped to the last waypoint, 0, whose centre is (384, 2944); the next tick (no input: vx 48 -> 40,
+    # x = 1616) puts the centre at (1712, 2976): d = floor(sqrt(1328^2 + 32^2)) = 1328, past the grace zone
+    # by 304, so the tick costs 304 >> 4 = 19 units and pays no progress.
+    m = flat_map()
+    path = oracle.bfs_path(m, (1, 11), (16, 11))
+    e = v2_env(m, path)
+    rews = [e.step([RIGHT])[0][0] for _ in range(30)]
+    assert sum(rews) == 5 * 0.25 and e.state[0, F["x"]] == 1576 and e.state[0, F["path"]] == 5
+    e.wp_lens[0] = 1
+    rew, done = e.step([NOOP])
+    assert e.state[0, F["x"]] == 1616 and e.state[0, F["y"]] == 2880
+    assert rew[0] == -19 / 1024 and done[0] == 0
+    assert e.state[0, F["path"]] == 0
+    # lengthening the table again resumes the search at the clamped index: waypoints 0 .. 8 are in reach,
+    # and after the next tick (vx 40 -> 32, x = 1648) the nearest to the centre (1744, 2976) is waypoint 5
+    # (centre 1664): 5 waypoints of progress, 5 x 0.25
+    e.wp_lens[0] = len(path)
+    rew, _ = e.step([NOOP])
+    assert e.state[0, F["x"]] == 1648 and rew[0] == 5 * 0.25 and e.state[0, F["path"]] == 5
