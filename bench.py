@@ -83,6 +83,8 @@ def parse():
                    help="adaptive checkpoint respawn (each map's outcome buffer, top-quarter restarts, frontier cap)")
     p.add_argument("--hook", choices=("off", "grapple"), default="off",
                    help="grapple hook aimed by seeded continuous aims (rl_env_step_aim)")
+    p.add_argument("--no-pixels", action="store_true",
+                   help="skip the short run of the pixel workload reported beside the default line")
     p.add_argument("--loss-mode", choices=("stream", "perm"), default="stream",
                    help="minibatches as per-sample minibatch ids read in storage order, or given by a permutation "
                         "(turned into the same ids on the device, then the same pass)")
@@ -249,6 +251,180 @@ def calibration_copy(torch, dev):
     del src, dst
 
 
+def pixel_rollouts(torch, binding, dev, ms, sprites, policy_actions, values, last_values, steps, warmup):
+    """The pixel workload on the GPU: 16384 envs x 128 steps rendering 4 x 84 x 84 u8 frames into a resident
+    rollout buffer, then GAE with whole-batch statistics; `warmup` untimed and `steps` timed rollouts.
+    Returns the whole-job rate, the per-launch env step times and the step's roofline."""
+    n = PIX_ENVS
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_PIXELS,
+                      sprites=sprites, device=dev)
+    # rollout buffer: one allocation of [actions T*N | obs T*N*28224 (u8) | rewards T*N | dones T*N]
+    a_bytes = HORIZON * n * 4
+    o_bytes = HORIZON * n * 4 * 84 * 84
+    offs = [0, a_bytes, a_bytes + o_bytes, a_bytes + o_bytes + a_bytes]
+    buf = torch.empty(offs[3] + a_bytes, dtype=torch.uint8, device=dev)
+    actions = buf[offs[0]:offs[1]].view(torch.int32).view(HORIZON, n)
+    obs = buf[offs[1]:offs[2]].view(HORIZON, n, 4 * 84 * 84)
+    rewards = buf[offs[2]:offs[3]].view(torch.float32).view(HORIZON, n)
+    dones = buf[offs[3]:].view(torch.float32).view(HORIZON, n)
+    actions.copy_(torch.from_numpy(policy_actions))
+    values_d = torch.from_numpy(values).to(dev)
+    last_d = torch.from_numpy(last_values).to(dev)
+    adv = torch.empty((HORIZON, n), dtype=torch.float32, device=dev)
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    env.reset(obs[0])
+    torch.cuda.synchronize()
+
+    def rollout(ev=None):
+        # one event pair around the 128 back-to-back env launches: events between launches would add
+        # their own barrier and timestamp packets to every step
+        if ev is not None:
+            ev["env"][0].record()
+        for t in range(HORIZON):
+            env.step(actions[t], obs[t], rewards[t], dones[t])
+        if ev is not None:
+            ev["env"][1].record()
+            ev["gae"][0].record()
+        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
+        if ev is not None:
+            ev["gae"][1].record()
+
+    for _ in range(warmup):
+        rollout()
+    torch.cuda.synchronize()
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    events = [{"env": mk(), "gae": mk()} for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        rollout(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    env.close()
+    del buf
+
+    env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
+    gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
+    env_avg_s = float(env_ms.mean()) * 1e-3
+    launch_bytes = n * PIX_BYTES_PER_ENV_STEP
+    achieved = launch_bytes / env_avg_s / 1e9
+    return {
+        "workload": "pixel rollout: 16384 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, 4 x 84 x 84 u8 "
+                    "frames from 16 seeded 8x8 sprites into a resident rollout buffer, then GAE with whole-batch "
+                    "statistics",
+        "value": steps * HORIZON * n / wall,
+        "ms_per_step": wall / steps * 1e3,
+        "steps": steps,
+        "roofline": {"kernel": "env_step + pixel render (one rl_env_step: k_step, k_obs_pixels)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("env_step+pixels"), "bytes_per_launch": launch_bytes,
+                     "avg_launch_us": env_avg_s * 1e6},
+        "env_launch_us": launch_stats(env_ms),
+        "gae_us_in_rollout": float(gae_ms.mean()) * 1e3,
+    }
+
+
+def launch_stats(per_launch_ms):
+    """Mean, median and min over the timed rollouts of the average launch time (each rollout's loop of 128
+    launches over 128), in microseconds."""
+    a = np.asarray(per_launch_ms) * 1e3
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
+            "rollouts": int(a.size)}
+
+
+def cpu_info():
+    """The host's CPU model and core counts (the oracle legs' machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable, "oracle_workers": CPU_WORKERS}
+
+
+def hbm_ceiling(torch, dev, store_bytes, reps=9):
+    """Same-run ceilings of plain HBM traffic with torch's own kernels, medians of `reps` timed launches:
+    stores of `store_bytes` (the observation bytes of one env step) into successive slices of a 4 GiB
+    buffer (so that no slice is still cached when it is written again), a 1 GiB device-to-device copy
+    (read + write bytes counted), and a 1 GiB read (a sum)."""
+    slab = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    n = store_bytes // 4
+    nslices = (1 << 30) // n
+    src, dst = slab[:1 << 28], slab[1 << 28:2 << 28]
+    slab.zero_()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) * 1e-3
+
+    store = [timed(lambda i=i: slab[(i % nslices) * n:(i % nslices + 1) * n].fill_(1.0)) for i in range(reps + 1)][1:]
+    copy = [timed(lambda: dst.copy_(src)) for _ in range(reps + 1)][1:]
+    read = [timed(lambda: src.sum()) for _ in range(reps + 1)][1:]
+    del slab
+    torch.cuda.empty_cache()
+    gbs = lambda nbytes, ts: nbytes / float(np.median(ts)) / 1e9
+    return {"store_GB/s": gbs(n * 4, store), "store_bytes": n * 4, "copy_GB/s": gbs(2 * (1 << 30), copy),
+            "read_GB/s": gbs(1 << 30, read), "kernels": "torch fill_, copy_, sum", "reps": reps,
+            "peak_GB/s": HBM_PEAK_GBS}
+
+
+def config2_record(torch, binding, inputs, dev, reps):
+    """The GAE+PPO workload (N = 2048, T = 128, 32 minibatches of 8192): rl_gae with statistics, and the loss
+    normalised inline from the permutation and from minibatch numbers; medians of `reps` back-to-back
+    launches. 5.2 MB + 18.9 MB stay in the caches: latency-bound, not an HBM test."""
+    t, n, mb = 128, 2048, 8192
+    b = t * n
+    gi = inputs.make_gae_inputs(10, t, n)
+    pi = inputs.make_policy_inputs(10, b)
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    r, v, dn, vl = d(gi.rewards), d(gi.values), d(gi.dones), d(gi.last_values)
+    logits, acts, old, nv, perm = d(pi.new_logits), d(pi.actions), d(pi.old_logp), d(pi.new_values), d(pi.perm)
+    idx = d(inputs.minibatch_index(pi.perm, mb))
+    adv = torch.empty((t, n), dtype=torch.float32, device=dev)
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    out = torch.empty((b // mb, 4), dtype=torch.float32, device=dev)
+    calls = {
+        "gae": lambda: binding.gae(r, v, dn, vl, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats),
+        "loss_perm": lambda: binding.ppo_loss(logits, acts, old, adv.view(-1), ret.view(-1), nv, perm, mb,
+                                              adv_stats=stats, out=out),
+        "loss_stream": lambda: binding.ppo_loss(logits, acts, old, adv.view(-1), ret.view(-1), nv, None, mb,
+                                                adv_stats=stats, out=out, mb_index=idx),
+    }
+    res = {"workload": "GAE+PPO: N=2048, T=128, minibatch 8192 (32 minibatches), perm seeded; cache-resident, "
+                       "latency-bound (not an HBM test)"}
+    nbytes = {"gae": b * GAE_BYTES_PER_ELEM + n * 4, "loss_perm": b * LOSS_BYTES_PER_SAMPLE["perm"],
+              "loss_stream": b * LOSS_BYTES_PER_SAMPLE["stream"]}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            z.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(z) * 1e-3)
+        med = float(np.median(ts))
+        res[name] = {"us": med * 1e6, "min_us": float(np.min(ts)) * 1e6, "GB/s": nbytes[name] / med / 1e9}
+    return res
+
+
 def cpu_baseline_pixels(ms, sprites, policy_actions, values, last_values, n):
     """The oracle, single-threaded, on the first n envs of the pixel workload: 128 steps with pixel
     observations, then GAE by its definition with normalisation. Returns env-steps/s."""
@@ -332,83 +508,30 @@ def main_pixels(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.lib()
-    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=3, time_limit=2000, obs_mode=binding.OBS_PIXELS,
-                      sprites=sprites, device=dev)
-    # rollout buffer: one allocation of [actions T*N | obs T*N*28224 (u8) | rewards T*N | dones T*N]
-    a_bytes = HORIZON * n * 4
-    o_bytes = HORIZON * n * 4 * 84 * 84
-    offs = [0, a_bytes, a_bytes + o_bytes, a_bytes + o_bytes + a_bytes]
-    buf = torch.empty(offs[3] + a_bytes, dtype=torch.uint8, device=dev)
-    actions = buf[offs[0]:offs[1]].view(torch.int32).view(HORIZON, n)
-    obs = buf[offs[1]:offs[2]].view(HORIZON, n, 4 * 84 * 84)
-    rewards = buf[offs[2]:offs[3]].view(torch.float32).view(HORIZON, n)
-    dones = buf[offs[3]:].view(torch.float32).view(HORIZON, n)
-    actions.copy_(torch.from_numpy(policy_actions))
-    values_d = torch.from_numpy(values).to(dev)
-    last_d = torch.from_numpy(last_values).to(dev)
-    adv = torch.empty((HORIZON, n), dtype=torch.float32, device=dev)
-    ret = torch.empty_like(adv)
-    stats = torch.zeros(3, dtype=torch.float64, device=dev)
-    env.reset(obs[0])
-    torch.cuda.synchronize()
     if args.calibrate_copy:
         calibration_copy(torch, dev)
-
-    def rollout(ev=None):
-        # one event pair around the 128 back-to-back env launches: events between launches would add
-        # their own barrier and timestamp packets to every step
-        if ev is not None:
-            ev["env"][0].record()
-        for t in range(HORIZON):
-            env.step(actions[t], obs[t], rewards[t], dones[t])
-        if ev is not None:
-            ev["env"][1].record()
-            ev["gae"][0].record()
-        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
-        if ev is not None:
-            ev["gae"][1].record()
-
-    for _ in range(args.warmup):
-        rollout()
-    torch.cuda.synchronize()
-    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    events = [{"env": mk(), "gae": mk()} for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        rollout(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-
-    env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
-    gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
-    env_avg_s = float(env_ms.mean()) * 1e-3
-    launch_bytes = n * PIX_BYTES_PER_ENV_STEP
-    achieved = launch_bytes / env_avg_s / 1e9
+    rec = pixel_rollouts(torch, binding, dev, ms, sprites, policy_actions, values, last_values, args.steps,
+                         args.warmup)
     out = {
         "metric": "env-steps/s incl. 84x84 u8 pixel obs write at 16384 envs",
-        "value": args.steps * HORIZON * n / wall,
+        "value": rec["value"],
         "unit": "env-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i32+u8+f32",
         "data": "synthetic",
-        "config": {"workload": "pixel rollout: 16384 envs x 128 steps on 64 seeded 256x1024 maps, frame-skip 3, "
-                               "4 x 84 x 84 u8 frames from 16 seeded 8x8 sprites into a resident rollout buffer, "
-                               "then GAE with whole-batch statistics",
-                   "num_envs": n, "horizon": HORIZON},
-        "roofline": {"kernel": "env_step + pixel render (one rl_env_step: k_step, k_obs_pixels)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": load_traffic("env_step+pixels"), "bytes_per_launch": launch_bytes,
-                     "avg_launch_us": env_avg_s * 1e6},
-        "gae_us_in_rollout": float(gae_ms.mean()) * 1e3,
+        "config": {"workload": rec["workload"], "num_envs": n, "horizon": HORIZON},
+        "roofline": rec["roofline"],
+        "env_launch_us": rec["env_launch_us"],
+        "gae_us_in_rollout": rec["gae_us_in_rollout"],
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
+        "host": cpu_info(),
     }
     print(json.dumps(out), flush=True)
 
@@ -729,9 +852,9 @@ def main():
     # 256 MB to be written back during the next kernel).
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     flush.zero_()
-    iso = {"gae": [], "scan": [], "loss": [], "grad": [], "vtrace": []}
+    iso = {"gae": [], "scan": [], "loss": [], "perm": [], "grad": [], "vtrace": []}
     for rep in range(args.iso_reps):
-        for which in ("gae", "scan", "loss", "grad", "vtrace"):
+        for which in ("gae", "scan", "loss", "perm", "grad", "vtrace"):
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -746,16 +869,33 @@ def main():
                 binding.ppo_loss_grad(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None,
                                       mb, adv_stats=stats, out=loss_out, dlogits=dlogits, dvalues=dvalues,
                                       mb_index=mb_index)
-            elif args.loss_mode == "stream":
-                binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
-                                 adv_stats=stats, out=loss_out, mb_index=mb_index)
-            else:
+            elif which == "perm" or args.loss_mode == "perm":   # the boundary's permutation input
                 binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, perm, mb,
                                  adv_stats=stats, out=loss_out)
+            else:
+                binding.ppo_loss(logits, actions.view(-1), old_logp, adv.view(-1), ret.view(-1), new_v, None, mb,
+                                 adv_stats=stats, out=loss_out, mb_index=mb_index)
             z.record()
             torch.cuda.synchronize()
             iso[which].append(a.elapsed_time(z))
     del flush
+
+    # one more loop of 128 env launches, each between its own event pair: the spread of single launches
+    # (the packets of 256 events add about 2 us to each launch, so these read high against the loop's mean)
+    per_launch = []
+    for t in range(HORIZON):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        env.step(actions[t], obs[t], rewards[t], dones[t], aim=None if aims_d is None else aims_d[t])
+        z.record()
+        per_launch.append((a, z))
+    torch.cuda.synchronize()
+    per_launch_us = np.array([a.elapsed_time(z) * 1e3 for a, z in per_launch])
+    env.close()
+    del buf, obs, actions, rewards, dones   # the rollout buffer (47 GB): the ceiling and the pixel run follow
+    torch.cuda.empty_cache()
+    ceiling = hbm_ceiling(torch, dev, N_ENVS * 1397 * 4)
+    cfg2 = config2_record(torch, binding, inputs, dev, args.iso_reps)
 
     env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
     gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
@@ -772,6 +912,9 @@ def main():
     gae_bytes = b * GAE_BYTES_PER_ELEM + N_ENVS * 4
     loss_bytes = b * LOSS_BYTES_PER_SAMPLE[args.loss_mode]
     gae_s, loss_s = float(np.median(iso["gae"])) * 1e-3, float(np.median(iso["loss"])) * 1e-3
+    perm_s = float(np.median(iso["perm"])) * 1e-3
+    perm_bytes = b * LOSS_BYTES_PER_SAMPLE["perm"]
+    stream_s = loss_s if args.loss_mode == "stream" else None
     scan_s = float(np.median(iso["scan"])) * 1e-3
     grad_s = float(np.median(iso["grad"])) * 1e-3
     vt_s = float(np.median(iso["vtrace"])) * 1e-3
@@ -809,14 +952,24 @@ def main():
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic(env_key),
-                     "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6},
+                     "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6,
+                     "frac_of_store_ceiling": achieved / ceiling["store_GB/s"],
+                     "frac_of_copy_ceiling": achieved / ceiling["copy_GB/s"]},
+        "hbm_ceiling": ceiling,
         "env_step_us": float(env_ms.mean()) * 1e3,
+        "env_launch_us": launch_stats(env_ms),
+        "env_launch_us_one_event_pair_each": {"median": float(np.median(per_launch_us)),
+                                              "min": float(per_launch_us.min()), "max": float(per_launch_us.max()),
+                                              "launches": int(per_launch_us.size)},
         "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
                 "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_us": scan_s * 1e6, "scan_GB/s": scan_gbs,
                 "scan_frac": scan_gbs / HBM_PEAK_GBS, "scan_traffic": load_traffic("gae_scan")},
         "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
                  "us_in_rollout": float(loss_ms.mean()) * 1e3,
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
+        "loss_perm": {"us": perm_s * 1e6, "GB/s": perm_bytes / perm_s / 1e9,
+                      "frac": perm_bytes / perm_s / 1e9 / HBM_PEAK_GBS, "bytes": perm_bytes,
+                      "vs_minibatch_numbers": None if stream_s is None else perm_s / stream_s},
         "loss_grad": {"us": grad_s * 1e6, "GB/s": grad_gbs, "frac": grad_gbs / HBM_PEAK_GBS, "bytes": grad_bytes,
                       "traffic": load_traffic("ppo_loss_grad")},
         "vtrace": {"us": vt_s * 1e6, "GB/s": vt_gbs, "frac": vt_gbs / HBM_PEAK_GBS, "bytes": vt_bytes,
@@ -826,7 +979,14 @@ def main():
         "loss_check": loss_out[0].tolist(),
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
+        "host": cpu_info(),
+        "gae_ppo_n2048": cfg2,
     }
+    if not args.no_pixels:   # the pixel workload's own rate beside the headline (a short run of it)
+        pix_actions = inputs.make_actions(22, HORIZON, PIX_ENVS)
+        pix_values, pix_last = inputs.make_values(23, HORIZON, PIX_ENVS)
+        out["pixels_n16384"] = pixel_rollouts(torch, binding, dev, ms, inputs.make_sprites(30), pix_actions,
+                                              pix_values, pix_last, 3, 1)
     print(json.dumps(out), flush=True)
 
 

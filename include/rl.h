@@ -294,9 +294,11 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   [0, A) (other values act as action 0); old_logp, adv, ret, new_values device f32[B].
  *   B % mb must be 0. ws: device workspace of rl_ppo_loss_workspace_bytes(B, mb) bytes, 8-byte aligned (any
  *   contents); calls sharing it must not overlap. The per-sample terms are float32 (exponentials and
- *   logarithms from the hardware's base-2 instructions, about 1 ulp each) and are reduced through float64
- *   partials in a fixed order (identical results from run to run). With mb_index every input is read
- *   once, in storage order. With perm and at most 64 minibatches the perm is first turned into each
+ *   logarithms from the hardware's base-2 instructions, about 1 ulp each) and are reduced in a fixed order
+ *   (identical results from run to run): with mb_index (and perm converted to it) each thread first adds
+ *   at most 256 of its samples into float32 sums per minibatch (a rounding error of at most 256 * 2^-24,
+ *   1.5e-5, of the summed magnitudes), which are then reduced in float64; the gather path adds every term in
+ *   float64. With mb_index every input is read once, in storage order. With perm and at most 64 minibatches the perm is first turned into each
  *   sample's minibatch number (in the workspace) and the samples are then read the same way; with more
  *   minibatches every read is a gather. perm entries outside [0, B) are clamped into it (a permutation
  *   has none). */
@@ -392,7 +394,11 @@ typedef struct rl_rollout_group {
  * inference: group g's
  * inference of a decision waits for group g-1's (group 0's waits for the last group's of the decision
  * before), which keeps them out of phase. Every group's env must use tile observations, no grapple hook
- * (the stand-in inference gives no aims) and stand at the same decision counter. Results equal the single-buffered rollout's for the same envs. */
+ * (the stand-in inference gives no aims) and stand at the same decision counter; env_offset must be a
+ * multiple of the group's num_maps (a group's env n plays map n mod num_maps, global env env_offset + n
+ * plays map (env_offset + n) mod num_maps); the adaptive respawn (whose outcome buffers and draws belong
+ * to one env batch) needs a single group at env_offset 0. RL_EINVAL otherwise. Under these conditions the
+ * results equal the single-buffered rollout's for the same envs. */
 int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups, int32_t num_groups, int32_t t0,
                int32_t steps, int32_t alternate);
 

@@ -139,10 +139,11 @@ def _dev(x, dtype, device):
 _workspaces: dict = {}
 
 
-def workspace(kind: str, nbytes: int, device) -> torch.Tensor:
-    """A device workspace per (kind, size, device), reused by every call of that kind (calls on one
-    stream never overlap)."""
-    key = (kind, int(nbytes), str(device))
+def workspace(kind: str, nbytes: int, device, stream=None) -> torch.Tensor:
+    """A device workspace per (kind, size, device, stream), reused by every call of that kind on that
+    stream: calls on one stream run in order, so they never overlap, while calls on two streams get two
+    workspaces."""
+    key = (kind, int(nbytes), str(device), stream_ptr(stream).value)
     ws = _workspaces.get(key)
     if ws is None:
         ws = torch.zeros(max(int(nbytes), 8), dtype=torch.uint8, device=device)
@@ -185,13 +186,22 @@ class Env:
                               dptr(self.spawns), dptr(self.sprites), dptr(self.state), nbytes.value,
                               stream_ptr(stream), ctypes.byref(self._handle)))
         if reward_mode == REWARD_WAYPOINTS:
-            self.waypoints = wpt
-            self.wp_lens = _dev(wp_lens, torch.int32, self.device).reshape(m)
-            check(L.rl_env_set_waypoints(self._handle, dptr(self.waypoints), dptr(self.wp_lens), stream_ptr(stream)))
+            self.set_waypoints(wpt, wp_lens, stream)
         self.respawn_mode = respawn_mode
         if respawn_mode == RESPAWN_ADAPTIVE:
             self.ckpt_spawns = _dev(ckpt_spawns, torch.int32, self.device).reshape(m, -1, 2)
             check(L.rl_env_set_respawn_spots(self._handle, dptr(self.ckpt_spawns), stream_ptr(stream)))
+
+    def set_waypoints(self, waypoints, wp_lens, stream=None):
+        """rl_env_set_waypoints: each map's path table int32[M][max_waypoints][2] (the width the env was
+        created with) and its lengths int32[M]; may be called again between steps."""
+        m = self.maps.shape[0]
+        wpt = _dev(waypoints, torch.int32, self.device).reshape(m, -1, 2)
+        if wpt.shape[1] != self.cfg.max_waypoints:
+            raise ValueError(f"waypoint table has {wpt.shape[1]} entries per map, the env {self.cfg.max_waypoints}")
+        self.waypoints = wpt
+        self.wp_lens = _dev(wp_lens, torch.int32, self.device).reshape(m)
+        check(lib().rl_env_set_waypoints(self._handle, dptr(self.waypoints), dptr(self.wp_lens), stream_ptr(stream)))
 
     @property
     def obs_dtype(self):
@@ -303,7 +313,7 @@ def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, 
     if normalize and adv_stats is None:
         adv_stats = torch.zeros(3, dtype=torch.float64, device=dev)
     if normalize and ws is None:
-        ws = workspace("gae", gae_workspace_bytes(t, n), dev)
+        ws = workspace("gae", gae_workspace_bytes(t, n), dev, stream)
     r_p, ld = _rows(rewards, "rewards")
     ptrs = [r_p] + [_rows(x, name, ld)[0] for x, name in ((values, "values"), (dones, "dones"))]
     out = [_rows(x, name, ld)[0] for x, name in ((adv, "adv"), (ret, "ret"))]
@@ -343,7 +353,7 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
     dev = logits.device
     out = torch.empty((b // minibatch, 4), dtype=torch.float32, device=dev) if out is None else out
     if ws is None:
-        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev)
+        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev, stream)
     check(lib().rl_ppo_loss(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
                             dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
                             dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),
@@ -365,7 +375,7 @@ def ppo_loss_grad(logits, actions, old_logp, adv, ret, new_values, perm, minibat
     dlogits = torch.empty((b, a), dtype=torch.float32, device=dev) if dlogits is None else dlogits
     dvalues = torch.empty(b, dtype=torch.float32, device=dev) if dvalues is None else dvalues
     if ws is None:
-        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev)
+        ws = workspace("ppo", ppo_loss_workspace_bytes(b, minibatch), dev, stream)
     check(lib().rl_ppo_loss_grad(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
                                  dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
                                  dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),

@@ -355,6 +355,15 @@ int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups
                             (long long)x.row, (long long)x.obs_row);
         if (x.env_offset < 0 || x.env_offset + n > ((int64_t)1 << 24))
             return rl::fail(RL_EINVAL, "group %d: envs outside [0, 2^24)", g);
+        // a group's env n plays map n mod M of its own batch; it is global env env_offset + n only when the
+        // offset is a multiple of M
+        if (x.env_offset % cfg[g].num_maps != 0)
+            return rl::fail(RL_EINVAL, "group %d: env_offset %lld is not a multiple of num_maps %d", g,
+                            (long long)x.env_offset, cfg[g].num_maps);
+        // the adaptive respawn keeps its outcome buffers and draw keys per env batch: split into groups (or
+        // offset), its restarts would differ from one batch's
+        if (cfg[g].respawn_mode != RL_RESPAWN_OFF && (num_groups > 1 || x.env_offset != 0))
+            return rl::fail(RL_EINVAL, "group %d: the adaptive respawn needs a single group at env_offset 0", g);
         int64_t c = 0;
         rl_env_get_step_counter(x.env, &c);
         if (g == 0) counter0 = c;

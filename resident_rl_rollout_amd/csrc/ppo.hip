@@ -307,7 +307,7 @@ __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t
         for (int u = 0; u < U; ++u) {
             const int64_t i = min(i0 + (int64_t)u * THREADS, hi - 1);
             load_sample<AC>(p, i, s[u]);
-            mbi[u] = min((int)p.mb_index[i], NB - 1);
+            mbi[u] = min((int)p.mb_index[i], p.num_mb - 1);   // past the last minibatch counts as the last
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -435,10 +435,20 @@ size_t partial_bytes(int64_t num_mb, size_t blocks)
     return rl::round_up(sizeof(double) * 3 * (size_t)num_mb * blocks, 256);
 }
 
-// Stream-mode grid: blocks of `chunk` samples, at most kStreamBlocks of them.
-int stream_blocks(int64_t B, int64_t* chunk)
+// Each thread adds at most this many samples into its float32 slots (the slot sums are then reduced in
+// float64), which bounds their rounding error at kSlotSamples * 2^-24 (1.5e-5) of the summed magnitudes
+// at any B.
+constexpr int64_t kSlotSamples = 256;
+
+// Threads per stream-mode block: the per-thread slots of 16 / 32 / 64 minibatches fill 48 KB of LDS.
+int stream_threads(int64_t num_mb) { return num_mb <= 16 ? 256 : (num_mb <= 32 ? 128 : 64); }
+
+// Stream-mode grid: blocks of `chunk` samples, kStreamBlocks of them (one resident round) unless a chunk
+// would give a thread more than kSlotSamples samples.
+int stream_blocks(int64_t B, int64_t num_mb, int64_t* chunk)
 {
-    const int64_t c = std::max<int64_t>(256, (B + kStreamBlocks - 1) / kStreamBlocks);
+    const int64_t c = std::min<int64_t>(std::max<int64_t>(256, (B + kStreamBlocks - 1) / kStreamBlocks),
+                                        stream_threads(num_mb) * kSlotSamples);
     *chunk = c;
     return (int)((B + c - 1) / c);
 }
@@ -454,7 +464,7 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
     const int64_t num_mb = B / mb;
     int64_t chunk = 0;
-    const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, &chunk) : 0);
+    const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, num_mb, &chunk) : 0);
     *bytes = partial_bytes(num_mb, blocks);
     // with at most 64 minibatches, room for the minibatch numbers a perm is turned into
     if (num_mb <= kStreamMaxMinibatches) *bytes += sizeof(uint16_t) * (size_t)B;
@@ -550,7 +560,7 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
     if (perm && num_mb <= kStreamMaxMinibatches) {
         // the perm's sets as minibatch numbers behind the partials, then the stream pass
         int64_t c = 0;
-        const size_t blocks = (size_t)std::max(blocks_per_mb(mb), stream_blocks(B, &c));
+        const size_t blocks = (size_t)std::max(blocks_per_mb(mb), stream_blocks(B, num_mb, &c));
         uint16_t* ids = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks));
         hipLaunchKernelGGL(k_perm_to_index, dim3((unsigned)blocks_per_mb(mb), (unsigned)num_mb), dim3(256), 0, st,
                            perm, B, (int64_t)mb, ids);
@@ -560,7 +570,7 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
         p.perm = nullptr;
     }
     int64_t chunk = 0;
-    const int nblk = mb_index ? stream_blocks(B, &chunk) : blocks_per_mb(mb);
+    const int nblk = mb_index ? stream_blocks(B, num_mb, &chunk) : blocks_per_mb(mb);
     if (dlogits) launch_loss<true>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
     else launch_loss<false>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
     if (int rc = rl::check_launch("ppo_loss")) return rc;

@@ -93,6 +93,61 @@ def waypoint_table(ms: inputs.MapSet):
     return table, np.array([len(p) for p in paths], np.int32)
 
 
+def poison(obs, rew, done, obs_mode, step):
+    """Fill a step's outputs with values no step writes, so that every element a parity check compares
+    must have been written by that step: NaN for float observations, rewards and dones; for u8 pixels
+    (where every byte value can occur) a byte that changes with the step, so a skipped store leaves the
+    previous step's poison, which differs. Padding past the observation is left alone (no step may write
+    it)."""
+    size = binding.OBS_TILES_SIZE if obs_mode == binding.OBS_TILES else binding.OBS_PIXELS_SIZE
+    if obs_mode == binding.OBS_TILES:
+        obs[..., :size].fill_(float("nan"))
+    else:
+        obs[..., :size].fill_((37 * step + 11) & 0xFF)
+    rew.fill_(float("nan"))
+    done.fill_(float("nan"))
+
+
+class SubsetPairs:
+    """One GPU env batch of n envs beside oracle batches of stated env ranges (env_offset keys each
+    range's maps and draws as global envs), for the full-size workloads the oracle cannot step whole."""
+
+    def __init__(self, gpu_env, ms, ranges, **oracle_kw):
+        self.gpu = gpu_env
+        self.ranges = ranges
+        self.oras = [oracle.OracleEnv(ms.maps, ms.ckpts, ms.spawns, hi - lo, env_offset=lo, **oracle_kw)
+                     for lo, hi in ranges]
+        for o in self.oras:
+            o.reset()
+        self.sel_np = np.concatenate([np.arange(lo, hi) for lo, hi in ranges])
+        self.sel = torch.from_numpy(self.sel_np).cuda()
+
+    def step(self, actions_np):
+        outs = [o.step(actions_np[lo:hi]) for o, (lo, hi) in zip(self.oras, self.ranges)]
+        return np.concatenate([r for r, _ in outs]), np.concatenate([d for _, d in outs])
+
+    def check_state(self, what):
+        got = self.gpu.read_state()[self.sel].cpu().numpy()
+        want = np.concatenate([o.state for o in self.oras])
+        if not np.array_equal(got, want):
+            e, f = np.argwhere(got != want)[0]
+            raise AssertionError(f"{what}: state of env {self.sel_np[e]} field {oracle.STATE_FIELDS[f]}: gpu "
+                                 f"{got[e]} oracle {want[e]}")
+
+    def check_obs(self, obs, what):
+        got = obs[self.sel].cpu().numpy()
+        if self.gpu.obs_mode == binding.OBS_TILES:
+            want = np.concatenate([o.obs_tiles() for o in self.oras])
+            got = got[:, :binding.OBS_TILES_SIZE]
+        else:
+            want = np.concatenate([o.obs_pixels().reshape(len(o.state), -1) for o in self.oras])
+            got = got[:, :binding.OBS_PIXELS_SIZE]
+        if not np.array_equal(got.view(np.uint8), want.view(np.uint8)):
+            bad = np.argwhere(got != want)
+            raise AssertionError(f"{what}: obs differ at {len(bad)} elements, first (row in the subset, element) "
+                                 f"{bad[:5].tolist()}")
+
+
 class PairedEnvs:
     """The same env batch on the GPU (through the C ABI) and in the oracle, stepped with the same actions."""
 
@@ -128,6 +183,8 @@ class PairedEnvs:
     def step(self, actions_np, aim_np=None):
         a = torch.from_numpy(np.ascontiguousarray(actions_np, np.int32)).cuda()
         aim = None if aim_np is None else torch.from_numpy(np.ascontiguousarray(aim_np, np.int32)).cuda()
+        self.steps = getattr(self, "steps", 0) + 1
+        poison(self.obs, self.rew, self.done, self.obs_mode, self.steps)
         self.gpu.step(a, self.obs, self.rew, self.done, aim=aim)
         r, d = self.ora.step(actions_np, aim_np)
         return r, d

@@ -95,3 +95,24 @@ def test_step_without_waypoints_is_rejected(gpu_lib):
     with pytest.raises(binding.RLError, match="rl_env_set_waypoints"):
         binding.check(binding.lib().rl_env_step(h, a.data_ptr(), obs.data_ptr(), r.data_ptr(), r.data_ptr(), None))
     binding.lib().rl_env_destroy(h)
+
+
+def test_shortened_table_mid_episode(gpu_lib):
+    # mostly rightward play until the high-water indexes are well along the paths, then a table cut below
+    # them through rl_env_set_waypoints (the index is clamped to the new last waypoint), then the full
+    # table again: bit-exact against the oracle given the same lengths at the same decisions
+    ms = inputs.make_mapset([7, 8, 9], 32, 40)
+    table, lens = waypoint_table(ms)
+    pe = PairedEnvs(ms, 300, reward_mode=binding.REWARD_WAYPOINTS, waypoints=table, wp_lens=lens.copy(),
+                    time_limit=10 ** 6)           # a copy: the oracle keeps its lengths array and reads it each step
+    acts = _rightward(11, 150, 300, p_right=0.9)
+    _run(pe, acts[:50], "before the cut", obs_every=10)
+    st = pe.gpu.read_state().cpu().numpy()
+    short = np.maximum(1, lens // 4).astype(np.int32)
+    assert (st[:, F["path"]] > short[np.arange(300) % 3] - 1).any()      # some indexes lie past the new end
+    pe.gpu.set_waypoints(table, short)
+    pe.ora.wp_lens[:] = short
+    _run(pe, acts[50:100], "shortened table", obs_every=10)
+    pe.gpu.set_waypoints(table, lens)
+    pe.ora.wp_lens[:] = lens
+    _run(pe, acts[100:], "full table again", obs_every=10)

@@ -118,3 +118,21 @@ def test_rejects_bad_arguments(gpu_lib):
     pi, adv, ret = _case(1, 100)
     with pytest.raises(binding.RLError, match="multiple"):
         _gpu(pi, adv, ret, 30)
+
+
+@pytest.mark.parametrize("b,mb", [(16384, 4096), (60000, 3000), (4000, 1000)])
+def test_minibatch_numbers_past_the_last_count_as_the_last(b, mb, gpu_lib):
+    # 4, 20 and 4 minibatches, fewer than the 16 / 32 / 64 per-thread slots of the stream pass: every
+    # sample of the last minibatch is renumbered to a value past it (up to 65535); the header reads those
+    # as the last minibatch, so the sets, and the oracle's scalars from the permutation, are unchanged
+    pi, adv, ret = _case(b + 3, b)
+    nmb = b // mb
+    idx = inputs.minibatch_index(pi.perm, mb)
+    rng = np.random.default_rng(b)
+    last = idx == nmb - 1
+    idx[last] = rng.integers(nmb - 1, 65536, int(last.sum())).astype(np.uint16)
+    assert (idx[last] >= nmb).any() and (idx[last] < 16).any()
+    out = binding.ppo_loss(_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret),
+                           _dev(pi.new_values), None, mb, mb_index=_dev(idx)).cpu().numpy()
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(out, ref, scale, f"B={b} mb={mb} renumbered last minibatch")
