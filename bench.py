@@ -351,11 +351,12 @@ def cpu_info():
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable, "oracle_workers": CPU_WORKERS}
 
 
-def hbm_ceiling(torch, dev, store_bytes, reps=9):
-    """Same-run ceilings of plain HBM traffic with torch's own kernels, medians of `reps` timed launches:
-    stores of `store_bytes` (the observation bytes of one env step) into successive slices of a 4 GiB
-    buffer (so that no slice is still cached when it is written again), a 1 GiB device-to-device copy
-    (read + write bytes counted), and a 1 GiB read (a sum)."""
+def hbm_ceiling(torch, binding, dev, store_bytes, row_chunk, reps=9):
+    """Same-run ceilings of plain HBM traffic, medians of `reps` timed launches: stores of `store_bytes`
+    (the observation bytes of one env step) into successive slices of a 4 GiB buffer (so that no slice is
+    still cached when it is written again) by torch's fill and by the library's store probe at two
+    granularities (4 KB per block, and `row_chunk` bytes per block: what one env-step block writes), a
+    1 GiB device-to-device copy (read + write bytes counted), and a 1 GiB sum (a reduction's read)."""
     slab = torch.empty(1 << 30, dtype=torch.float32, device=dev)
     n = store_bytes // 4
     nslices = (1 << 30) // n
@@ -372,14 +373,22 @@ def hbm_ceiling(torch, dev, store_bytes, reps=9):
         return a.elapsed_time(z) * 1e-3
 
     store = [timed(lambda i=i: slab[(i % nslices) * n:(i % nslices + 1) * n].fill_(1.0)) for i in range(reps + 1)][1:]
+    n16 = n // 4 * 4   # 16-byte multiple of the slice
+    chunks = {}
+    for name, chunk in (("4KB", 4096), ("env_block", row_chunk)):
+        chunks[name] = [timed(lambda i=i: binding.store_probe(slab[(i % nslices) * n:(i % nslices) * n + n16], chunk))
+                        for i in range(reps + 1)][1:]
     copy = [timed(lambda: dst.copy_(src)) for _ in range(reps + 1)][1:]
     read = [timed(lambda: src.sum()) for _ in range(reps + 1)][1:]
     del slab
     torch.cuda.empty_cache()
     gbs = lambda nbytes, ts: nbytes / float(np.median(ts)) / 1e9
-    return {"store_GB/s": gbs(n * 4, store), "store_bytes": n * 4, "copy_GB/s": gbs(2 * (1 << 30), copy),
-            "read_GB/s": gbs(1 << 30, read), "kernels": "torch fill_, copy_, sum", "reps": reps,
-            "peak_GB/s": HBM_PEAK_GBS}
+    return {"store_GB/s": gbs(n * 4, store), "store_bytes": n * 4,
+            "store_4KB_blocks_GB/s": gbs(n16 * 4, chunks["4KB"]),
+            "store_env_block_GB/s": gbs(n16 * 4, chunks["env_block"]), "env_block_bytes": row_chunk,
+            "copy_GB/s": gbs(2 * (1 << 30), copy), "sum_read_GB/s": gbs(1 << 30, read),
+            "kernels": "torch fill_ (store), rl_store_probe (store_4KB_blocks, store_env_block), torch copy_, torch sum",
+            "reps": reps, "peak_GB/s": HBM_PEAK_GBS}
 
 
 def config2_record(torch, binding, inputs, dev, reps):
@@ -396,10 +405,10 @@ def config2_record(torch, binding, inputs, dev, reps):
     idx = d(inputs.minibatch_index(pi.perm, mb))
     adv = torch.empty((t, n), dtype=torch.float32, device=dev)
     ret = torch.empty_like(adv)
-    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    stats = torch.zeros(binding.gae_stats_bytes(t, n) // 8, dtype=torch.float64, device=dev)   # deferred form
     out = torch.empty((b // mb, 4), dtype=torch.float32, device=dev)
     calls = {
-        "gae": lambda: binding.gae(r, v, dn, vl, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats),
+        "gae": lambda: binding.gae(r, v, dn, vl, GAMMA, LAMBDA, normalize=3, adv=adv, ret=ret, adv_stats=stats),
         "loss_perm": lambda: binding.ppo_loss(logits, acts, old, adv.view(-1), ret.view(-1), nv, perm, mb,
                                               adv_stats=stats, out=out),
         "loss_stream": lambda: binding.ppo_loss(logits, acts, old, adv.view(-1), ret.view(-1), nv, None, mb,
@@ -611,7 +620,7 @@ def main_infer(args):
     boot_logp = torch.empty(n, **f32)
     adv = torch.empty((T, n), **f32)
     ret = torch.empty_like(adv)
-    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    stats = torch.zeros(binding.gae_stats_bytes(T, n) // 8, dtype=torch.float64, device=dev)   # deferred form
     loss_out = torch.empty((MINIBATCHES, 4), **f32)
     logits, new_v = (torch.from_numpy(x).to(dev) for x in (pi.new_logits, pi.new_values))
     mb_index = torch.from_numpy(inputs.minibatch_index(pi.perm, b // MINIBATCHES)).to(dev)
@@ -650,7 +659,7 @@ def main_infer(args):
                             logp=boot_logp[sl], values=last_values[sl], stream=s_)
             for s_ in streams:
                 main_stream.wait_stream(s_)
-            binding.gae(rewards, values, dones, last_values, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret,
+            binding.gae(rewards, values, dones, last_values, GAMMA, LAMBDA, normalize=3, adv=adv, ret=ret,
                         adv_stats=stats)
             binding.ppo_loss(logits, actions.view(-1), logp.view(-1), adv.view(-1), ret.view(-1), new_v, None,
                              b // MINIBATCHES, adv_stats=stats, out=loss_out, mb_index=mb_index)
@@ -798,7 +807,7 @@ def main():
     values_d, last_d = t_(values), t_(last_values)
     adv = torch.empty((HORIZON, N_ENVS), dtype=torch.float32, device=dev)
     ret = torch.empty_like(adv)
-    stats = torch.zeros(3, dtype=torch.float64, device=dev)
+    stats = torch.zeros(binding.gae_stats_bytes(HORIZON, N_ENVS) // 8, dtype=torch.float64, device=dev)   # deferred
     loss_out = torch.empty((MINIBATCHES, 4), dtype=torch.float32, device=dev)
     dlogits = torch.empty((b, 12), dtype=torch.float32, device=dev)
     log_rhos = torch.from_numpy(inputs.make_log_rhos(24, HORIZON, N_ENVS)).to(dev)
@@ -821,7 +830,7 @@ def main():
         if ev is not None:
             ev["env"][1].record()
             ev["gae"][0].record()
-        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret, adv_stats=stats)
+        binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=3, adv=adv, ret=ret, adv_stats=stats)
         if ev is not None:
             ev["gae"][1].record()
             ev["loss"][0].record()
@@ -858,8 +867,8 @@ def main():
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            if which == "gae":
-                binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=2, adv=adv, ret=ret,
+            if which == "gae":   # scan + deferred statistics: what the rollout runs
+                binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=3, adv=adv, ret=ret,
                             adv_stats=stats)
             elif which == "scan":   # the scan kernel alone: no statistics, no second launch
                 binding.gae(rewards, values_d, dones, last_d, GAMMA, LAMBDA, normalize=0, adv=adv, ret=ret)
@@ -880,6 +889,25 @@ def main():
             iso[which].append(a.elapsed_time(z))
     del flush
 
+    # the same 128-launch env loop captured once in a HIP graph (torch's CUDAGraph) and replayed: the decision
+    # counter lives on the device, so each replay continues the episodes
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        for t in range(HORIZON):
+            env.step(actions[t], obs[t], rewards[t], dones[t], aim=None if aims_d is None else aims_d[t])
+    graph.replay()
+    torch.cuda.synchronize()
+    g_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, z in g_ev:
+        a.record()
+        graph.replay()
+        z.record()
+    torch.cuda.synchronize()
+    graph_ms = np.array([a.elapsed_time(z) for a, z in g_ev])
+    del graph
+
     # one more loop of 128 env launches, each between its own event pair: the spread of single launches
     # (the packets of 256 events add about 2 us to each launch, so these read high against the loop's mean)
     per_launch = []
@@ -894,7 +922,7 @@ def main():
     env.close()
     del buf, obs, actions, rewards, dones   # the rollout buffer (47 GB): the ceiling and the pixel run follow
     torch.cuda.empty_cache()
-    ceiling = hbm_ceiling(torch, dev, N_ENVS * 1397 * 4)
+    ceiling = hbm_ceiling(torch, binding, dev, N_ENVS * 1397 * 4, 16 * 1397 * 4)
     cfg2 = config2_record(torch, binding, inputs, dev, args.iso_reps)
 
     env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
@@ -947,17 +975,21 @@ def main():
                                + (", adaptive checkpoint respawn" if respawn else "")
                                + (", grapple hook with seeded continuous aims" if hook else ""),
                    "num_envs": N_ENVS, "horizon": HORIZON, "minibatches": MINIBATCHES,
-                   "loss_mode": args.loss_mode, "normalisation": "statistics in GAE, applied inside the loss",
+                   "loss_mode": args.loss_mode, "normalisation": "partial statistics in GAE (deferred), reduced and applied inside the loss",
                    "reward": args.reward, "respawn": args.respawn, "hook": args.hook},
         "roofline": {"kernel": "env_step+obs_gather (one rl_env_step)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic(env_key),
                      "bytes_per_launch": env_launch_bytes, "avg_launch_us": env_avg_s * 1e6,
                      "frac_of_store_ceiling": achieved / ceiling["store_GB/s"],
+                     "frac_of_env_block_store_ceiling": achieved / ceiling["store_env_block_GB/s"],
                      "frac_of_copy_ceiling": achieved / ceiling["copy_GB/s"]},
         "hbm_ceiling": ceiling,
         "env_step_us": float(env_ms.mean()) * 1e3,
         "env_launch_us": launch_stats(env_ms),
+        "env_loop_128_ms": {"uncaptured_mean": float(env_ms.mean()) * HORIZON,
+                            "captured_graph_median": float(np.median(graph_ms)),
+                            "captured_graph_min": float(graph_ms.min()), "replays": int(graph_ms.size)},
         "env_launch_us_one_event_pair_each": {"median": float(np.median(per_launch_us)),
                                               "min": float(per_launch_us.min()), "max": float(per_launch_us.max()),
                                               "launches": int(per_launch_us.size)},

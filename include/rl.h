@@ -210,10 +210,23 @@ int rl_env_step_aim(rl_env* env, const int32_t* actions, const int32_t* aim, voi
  * RL_HOOK_GRAPPLE). */
 int rl_env_read_state(const rl_env* env, int32_t* out, void* stream);
 
-/* The decision counter, whose value mod 4 selects the frame ring's newest slot. Saving the state
- * buffer together with this counter and restoring both resumes the envs exactly. */
+/* The decision counter, whose value mod 4 selects the frame ring's newest slot and which keys the adaptive
+ * respawn's draws. Its device copy lives in the state buffer and every step advances it there, so a stream
+ * capture of steps (a HIP graph) advances it on every replay. A step launched outside a capture, while the
+ * host's count is known to equal the device's (from creation, and from the first step after
+ * rl_env_set_step_counter, until a step is recorded into a graph), takes the host's count as an argument
+ * and needs no read of the device copy; a step recorded into a graph, and every step after one until the
+ * counter is set again, reads the device copy.
+ *   rl_env_get_step_counter: the decisions enqueued through rl_env_step / rl_env_step_aim on the host (not
+ *     advanced by graph replays; after replays, read the device value or set it).
+ *   rl_env_set_step_counter: sets the counter (host and device); the value is applied by the next step,
+ *     which must not be inside a stream capture (it returns RL_EINVAL there): set the counter, run one step
+ *     outside the capture, then capture. After copying a saved state buffer back in, set the counter to the
+ *     saved value (the device value read from the saved buffer), or the host's count goes on.
+ *   rl_env_read_step_counter: the device value into out (device int64, 8-byte aligned), on `stream`. */
 int rl_env_get_step_counter(const rl_env* env, int64_t* counter);
 int rl_env_set_step_counter(rl_env* env, int64_t counter);
+int rl_env_read_step_counter(const rl_env* env, int64_t* out, void* stream);
 
 /* Copy of the configuration the env batch was created with. */
 int rl_env_get_config(const rl_env* env, rl_env_config* out);
@@ -232,14 +245,29 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes);
  *   adv, ret                device f32[T][N] outputs (may not alias the inputs)
  *   normalize  0: no statistics; 1: compute the whole-batch mean and population std of A and overwrite
  *              adv with (A - mean) / (std + 1e-8); 2: compute the statistics only (adv stays raw) so that
- *              rl_ppo_loss can normalise on the fly. ret always uses the raw A.
- *   adv_stats  device f64[3] = {count, mean, std}, written when normalize != 0 (may be NULL for 0).
+ *              rl_ppo_loss can normalise on the fly; 3: deferred statistics: as 2, but adv_stats receives
+ *              the scan blocks' partial sums (and a header) instead of the finished values, and the
+ *              reduction that turns them into the mean and std is left to the consumer (rl_ppo_loss,
+ *              rl_ppo_loss_grad, rl_adv_stats_finish), which saves a kernel launch on the rollout path.
+ *              ret always uses the raw A.
+ *   adv_stats  device f64[3] = {count, mean, std} for normalize 1 and 2; for 3 a device buffer of
+ *              rl_gae_stats_bytes(T, N) bytes in the deferred form (first double negative); may be NULL
+ *              for 0. 8-byte aligned.
  *   ws         device workspace of rl_gae_workspace_bytes(T, N) bytes, 8-byte aligned (any contents; used
- *              when normalize != 0, may be NULL otherwise). Calls sharing a workspace must not overlap.
- * Statistics are reduced in a fixed order, so results are identical from run to run. */
+ *              when normalize is 1 or 2, may be NULL otherwise). Calls sharing a workspace must not overlap.
+ * Statistics are reduced in a fixed order, so results are identical from run to run, and the mean and std
+ * a consumer computes from the deferred form have the same bits as normalize = 2's. */
 int rl_gae(const float* rewards, const float* values, const float* dones, const float* last_values,
            int32_t T, int32_t N, float gamma, float lambda, float* adv, float* ret, int32_t normalize,
            double* adv_stats, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of adv_stats for rl_gae's deferred statistics (normalize = 3) over T x N. */
+int rl_gae_stats_bytes(int32_t T, int32_t N, size_t* bytes);
+
+/* The finished statistics {count, mean, population std} (device f64[3] out) of an adv_stats buffer that
+ * rl_gae wrote, in either form: copied when finished, reduced from the partial sums when deferred (the same
+ * bits as normalize = 2 gives). One small kernel on `stream`. */
+int rl_adv_stats_finish(const double* adv_stats, double* out, void* stream);
 
 /* rl_gae over N columns of wider [T][ld] arrays (ld >= N elements between rows; last_values stays f32[N]
  * contiguous): rewards, values, dones, adv and ret address element [t][n] at t * ld + n, and elements
@@ -288,7 +316,8 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   logp = logits[i][actions[i]] - logsumexp(logits[i]),  ratio = exp(logp - old_logp[i])
  *   pg = -min(ratio * A, clip(ratio, 1 - clip_eps, 1 + clip_eps) * A),  v = (new_values[i] - ret[i])^2,
  *   H = entropy of softmax(logits[i]),  with A = adv[i], or (adv[i] - mean) / (std + 1e-8) from
- *   adv_stats when adv_stats is not NULL.
+ *   adv_stats when adv_stats is not NULL (as rl_gae wrote it with normalize 2, or 3: the deferred partial
+ *   sums are then reduced inside the loss, to the same mean and std bits).
  *   out  device f32[B/mb][4] = {mean pg, mean v, mean H, mean pg + vf_coef * mean v - ent_coef * mean H}.
  *   logits device f32[B][A], A in 1..64 (16-byte aligned when A % 4 == 0); actions device int32[B] in
  *   [0, A) (other values act as action 0); old_logp, adv, ret, new_values device f32[B].
@@ -390,8 +419,9 @@ typedef struct rl_rollout_group {
  * is the single-buffered rollout; with two groups on two streams one group's step runs while the
  * other's inference runs. The buffers must hold rows t0 .. t0 + steps - 1 (the library does not know
  * their length); every check (NULL buffers, 4-byte alignment, row lengths, env offsets, matching decision
- * counters) runs before anything is enqueued. With `alternate` the groups also take turns at the
- * inference: group g's
+ * counters) runs before anything is enqueued. The draws of each decision are keyed on the host (the
+ * envs' host decision counter), so a captured rl_rollout replays the same draws: capture rl_env_step
+ * loops, not rl_rollout. With `alternate` the groups also take turns at the inference: group g's
  * inference of a decision waits for group g-1's (group 0's waits for the last group's of the decision
  * before), which keeps them out of phase. Every group's env must use tile observations, no grapple hook
  * (the stand-in inference gives no aims) and stand at the same decision counter; env_offset must be a
@@ -401,6 +431,15 @@ typedef struct rl_rollout_group {
  * results equal the single-buffered rollout's for the same envs. */
 int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups, int32_t num_groups, int32_t t0,
                int32_t steps, int32_t alternate);
+
+/* ---- Measurement ------------------------------------------------------------------------------- */
+
+/* A plain store kernel for the rooflines, not part of the rollout path: fills the device buffer `buf`
+ * (16-byte aligned, `bytes` bytes, a multiple of 16) with 16-byte stores, each block of 256 threads
+ * writing one contiguous chunk of `chunk` bytes (a multiple of 16; the last chunk may be shorter) and
+ * exiting. Its bandwidth, timed beside a kernel whose blocks write chunks of the same size, is the write
+ * ceiling for that granularity on the same device in the same run. */
+int rl_store_probe(void* buf, int64_t bytes, int64_t chunk, void* stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* rl_last_error(void);

@@ -69,9 +69,12 @@ SIGNATURES = [
     ("rl_env_read_state", ctypes.c_int, [_P, _P, _P]),
     ("rl_env_get_step_counter", ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
     ("rl_env_set_step_counter", ctypes.c_int, [_P, _I64]),
+    ("rl_env_read_step_counter", ctypes.c_int, [_P, _P, _P]),
     ("rl_env_get_config", ctypes.c_int, [_P, _CFG]),
     ("rl_env_destroy", None, [_P]),
     ("rl_gae_workspace_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
+    ("rl_gae_stats_bytes", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_SZ)]),
+    ("rl_adv_stats_finish", ctypes.c_int, [_P, _P, _P]),
     ("rl_gae", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
     ("rl_vtrace", ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _F32, _P, _P, _P]),
     ("rl_gae_strided", ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I64, _F32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -86,6 +89,7 @@ SIGNATURES = [
     ("rl_policy_pack", ctypes.c_int, [_P, _P, _P, _P]),
     ("rl_policy_forward", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_uint64, _I64, _I64, _P, _P, _P, _P]),
     ("rl_rollout", ctypes.c_int, [_P, ctypes.c_uint64, ctypes.POINTER(RolloutGroup), _I32, _I32, _I32, _I32]),
+    ("rl_store_probe", ctypes.c_int, [_P, _I64, _I64, _P]),
     ("rl_last_error", ctypes.c_char_p, []),
 ]
 
@@ -251,6 +255,12 @@ class Env:
     def step_counter(self, value: int):
         check(lib().rl_env_set_step_counter(self._handle, int(value)))
 
+    def read_step_counter(self, stream=None):
+        """The device decision counter (advanced by every step launch, graph replays included)."""
+        out = torch.empty(1, dtype=torch.int64, device=self.device)
+        check(lib().rl_env_read_step_counter(self._handle, dptr(out), stream_ptr(stream)))
+        return out
+
     def step_layout(self):
         offs = (ctypes.c_size_t * 4)()
         total = ctypes.c_size_t()
@@ -302,17 +312,34 @@ def _rows(x, what, ld=None):
     return ctypes.c_void_p(x.data_ptr()), stride
 
 
+def gae_stats_bytes(t: int, n: int) -> int:
+    b = ctypes.c_size_t()
+    check(lib().rl_gae_stats_bytes(t, n, ctypes.byref(b)))
+    return b.value
+
+
+def adv_stats_finish(adv_stats, out=None, stream=None):
+    """rl_adv_stats_finish: {count, mean, std} (float64[3] device tensor) of an adv_stats buffer in either
+    form."""
+    out = torch.empty(3, dtype=torch.float64, device=adv_stats.device) if out is None else out
+    check(lib().rl_adv_stats_finish(dptr(adv_stats, torch.float64, "adv_stats"), dptr(out, torch.float64, "out"),
+                                    stream_ptr(stream)))
+    return out
+
+
 def gae(rewards, values, dones, last_values, gamma, lam, normalize=0, adv=None, ret=None, adv_stats=None,
         ws=None, stream=None):
     """rl_gae over [T][N] float32 device tensors; returns (adv, ret, adv_stats). The [T][N] arguments may be
-    column ranges of wider arrays (rows contiguous, one shared row stride): then rl_gae_strided runs."""
+    column ranges of wider arrays (rows contiguous, one shared row stride): then rl_gae_strided runs. With
+    normalize = 3, adv_stats holds the deferred form (rl_gae_stats_bytes bytes)."""
     t, n = rewards.shape
     dev = rewards.device
     adv = torch.empty((t, n), dtype=torch.float32, device=dev) if adv is None else adv
     ret = torch.empty((t, n), dtype=torch.float32, device=dev) if ret is None else ret
     if normalize and adv_stats is None:
-        adv_stats = torch.zeros(3, dtype=torch.float64, device=dev)
-    if normalize and ws is None:
+        size = 3 if normalize != 3 else gae_stats_bytes(t, n) // 8
+        adv_stats = torch.zeros(size, dtype=torch.float64, device=dev)
+    if normalize in (1, 2) and ws is None:
         ws = workspace("gae", gae_workspace_bytes(t, n), dev, stream)
     r_p, ld = _rows(rewards, "rewards")
     ptrs = [r_p] + [_rows(x, name, ld)[0] for x, name in ((values, "values"), (dones, "dones"))]
@@ -458,3 +485,9 @@ def rollout(policy, groups, t0, steps, alternate=True):
     arr = (RolloutGroup * len(groups))(*groups)
     check(lib().rl_rollout(dptr(policy.packed), policy.seed, arr, len(groups), int(t0), int(steps),
                            1 if alternate else 0))
+
+
+def store_probe(buf, chunk, stream=None):
+    """rl_store_probe over a device tensor: 16-byte stores, one `chunk`-byte contiguous chunk per block."""
+    nbytes = buf.numel() * buf.element_size()
+    check(lib().rl_store_probe(dptr(buf), nbytes, int(chunk), stream_ptr(stream)))

@@ -24,6 +24,11 @@
 //   waypoints int32[M][Kw][2], wplens int32[M]            (waypoint reward only; empty otherwise)
 //   spots int32[M][K][2], ring int32[M][64], rmeta int32[M][4] (fill, head, frontier, spare),
 //   rhist int32[M][K+1]                                    (adaptive respawn only; empty otherwise)
+//   ctr    int64[Np / 16]   the decision counter, one copy per block of a step launch: block b of a step
+//                           uses word b (unless the launch carries the value) and writes it back plus one, so
+//                           the counter lives on the device (a captured graph of steps advances it on every
+//                           replay) with no atomics; every word holds the same value between launches, and
+//                           other kernels read word 0.
 // Structure-of-arrays keeps the lane-per-env state loads and stores coalesced.
 
 #include <vector>
@@ -103,7 +108,7 @@ constexpr int kHookFlightShift = 28;  // 4 bits, hook mode: ticks the tip has fl
 constexpr int kExtraRows = 8;
 
 struct Layout {
-    size_t slots, extra, map, ckpt, spawn, sprites, waypoints, wplens, spots, ring, rmeta, rhist, total;
+    size_t slots, ctr, extra, map, ckpt, spawn, sprites, waypoints, wplens, spots, ring, rmeta, rhist, total;
     int64_t np, hp, wp;
 };
 
@@ -122,10 +127,11 @@ struct EnvDev {
     int32_t* rhist;         // [M][k + 1] counts of the buffered outcomes
     const int32_t* aim;     // [N] this step's aims (hook mode; NULL: no aim)
     uint64_t seed;          // respawn draws
-    int64_t counter;        // the decision counter of this step
+    int64_t ovr;            // the counter taken from the launch instead of the device words (-1: read them)
     int32_t n, m, h, w, k, fs, time_limit, kw;
     int32_t hook;           // hook mode: frame dimension 9 is the hook's phase
     int64_t np, hp, wp;
+    int64_t* ctr;           // [Np / 16] the decision counter, a word per step block
 };
 
 int validate_cfg(const rl_env_config* c)
@@ -198,6 +204,8 @@ Layout layout_of(const rl_env_config* c)
     off = rl::round_up(off + sizeof(int32_t) * 4 * mm, 256);
     l.rhist = off;
     off = rl::round_up(off + sizeof(int32_t) * mm * ((size_t)c->num_ckpts + 1), 256);
+    l.ctr = off;   // one word per 16 envs covers the tile step's blocks (16 envs) and the pixel step's (64)
+    off = rl::round_up(off + sizeof(int64_t) * (size_t)(l.np / 16), 256);
     l.total = off;
     return l;
 }
@@ -210,6 +218,27 @@ __device__ __forceinline__ int32_t& slot_word(const EnvDev& d, int s, int w, int
 {
     return d.slots[((int64_t)s * kSlotWords + w) * d.np + n];
 }
+
+// The decision counter as a step launch's block b sees it: its own word when the counter is kept on the
+// device (DEV: a step recorded into a graph, or any step after one), else the launch's value.
+template <bool DEV>
+__device__ __forceinline__ int64_t step_counter(const EnvDev& d, int b) { return DEV ? d.ctr[b] : d.ovr; }
+
+// A step launch's last act. On the device every block advances its own word (so no block can see a word
+// another block of the launch has advanced); with the launch's value no block reads a word, and block 0
+// writes them all, so that a step recorded into a graph later finds them current.
+template <bool DEV>
+__device__ __forceinline__ void advance_counter(const EnvDev& d, int64_t c)
+{
+    if constexpr (DEV) {
+        if (threadIdx.x == 0) d.ctr[blockIdx.x] = c + 1;
+    } else if (blockIdx.x == 0) {
+        for (unsigned i = threadIdx.x; i < gridDim.x; i += blockDim.x) d.ctr[i] = c + 1;
+    }
+}
+
+// The counter as any other kernel sees it: the launch's value, else word 0 (which every step advances).
+__device__ __forceinline__ int64_t current_counter(const EnvDev& d) { return d.ovr >= 0 ? d.ovr : d.ctr[0]; }
 
 __device__ __forceinline__ const uint8_t* map_base(const EnvDev& d, int m)
 {
@@ -453,12 +482,12 @@ __device__ __forceinline__ uint64_t splitmix_output(uint64_t z)
 // draws are SplitMix64's first and second outputs from the state seed + 2 golden (counter 2^24 + n). The
 // top quarter of the buffer is read off its histogram: the max(1, fill / 4)-th largest outcome thr, the
 // cand outcomes >= thr, and the (pick + 1)-th largest of them.
-__device__ int32_t respawn_choice(const EnvDev& d, int m, int n)
+__device__ int32_t respawn_choice(const EnvDev& d, int m, int n, int64_t counter)
 {
     const int32_t* meta = d.rmeta + 4 * m;
     const int32_t fill = meta[0];
     if (fill == 0) return 0;
-    const uint64_t key = (uint64_t)d.counter * ((uint64_t)1 << 24) + (uint64_t)n;
+    const uint64_t key = (uint64_t)counter * ((uint64_t)1 << 24) + (uint64_t)n;
     const uint64_t state = d.seed + 2 * kGolden * key;
     if ((uint32_t)(splitmix_output(state + kGolden) >> 32) < kRespawnStartU32) return 0;
     const int32_t* hist = d.rhist + (int64_t)m * (d.k + 1);
@@ -586,8 +615,9 @@ __global__ __launch_bounds__(256) void k_zero(int32_t* __restrict__ p, int64_t c
 template <int MODE>
 __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a, const SlotWords& cur, int32_t next,
                                                int32_t best_x, int32_t path, int32_t from_start, const HookIn& hk,
-                                               float* __restrict__ rewards, float* __restrict__ dones, int head_new)
+                                               float* __restrict__ rewards, float* __restrict__ dones, int64_t counter)
 {
+    const int head_new = (int)((counter + 1) & 3);
     constexpr bool kHook = (MODE & kModeHook) != 0;
     const int m = n % d.m;
     int32_t x = cur.x;
@@ -770,7 +800,7 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
         int32_t k = 0;
         if constexpr ((MODE & kModeRespawn) != 0) {
             d.extra[4 * d.np + n] = next | (from_start ? (1 << 30) : 0);   // the ended episode's outcome
-            k = respawn_choice(d, m, n);
+            k = respawn_choice(d, m, n, counter);
         }
         return spawn_at<kHook>(d, n, m, k);
     }
@@ -801,25 +831,27 @@ __device__ __forceinline__ Decision env_decide(const EnvDev& d, int n, int32_t a
 
 // env_step alone (the pixel path renders in its own kernel): one lane per env, one-wave blocks so that a
 // small batch still spreads over every CU (the kernel is latency-bound: a few waves per CU at most).
-template <int MODE>
+template <int MODE, bool DEV>
 __global__ __launch_bounds__(64) void k_step(EnvDev d, const int32_t* __restrict__ actions,
-                                              float* __restrict__ rewards, float* __restrict__ dones,
-                                              int head_prev, int head_new)
+                                              float* __restrict__ rewards, float* __restrict__ dones)
 {
+    const int64_t c = step_counter<DEV>(d, blockIdx.x);
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= d.n) return;
-    env_decide<MODE>(d, n, actions[n], load_slot(d, head_prev, n), d.extra[n], d.extra[d.np + n],
+    if (n < d.n)
+        env_decide<MODE>(d, n, actions[n], load_slot(d, (int)(c & 3), n), d.extra[n], d.extra[d.np + n],
                      (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0,
-                     (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1, load_hook<MODE>(d, n), rewards, dones,
-                     head_new);
+                         (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1, load_hook<MODE>(d, n), rewards,
+                         dones, c);
+    advance_counter<DEV>(d, c);
 }
 
 // ------------------------------------------------------------------------------------------------
 // obs_gather, tile mode: one wave per env writes its 1397 floats as 22 fully coalesced 256-byte rows.
 // ------------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__ obs, int64_t stride, int head)
+__global__ __launch_bounds__(256) void k_obs_tiles(EnvDev d, float* __restrict__ obs, int64_t stride)
 {
+    const int head = (int)(current_counter(d) & 3);
     const int lane = threadIdx.x & 63;
     const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (n >= d.n) return;
@@ -971,9 +1003,10 @@ __device__ __forceinline__ void load_window(const EnvDev& d, int64_t base, int l
 // decision; the 64 non-window observation values go to tail[e] and the window's top-left offset to wbase[e].
 template <int E, int MODE>
 __device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const int32_t* __restrict__ actions,
-                                           float* __restrict__ rewards, float* __restrict__ dones, int head_prev,
-                                           int head_new, float (*tail)[kTail], int64_t* wbase)
+                                           float* __restrict__ rewards, float* __restrict__ dones, int64_t counter,
+                                           float (*tail)[kTail], int64_t* wbase)
 {
+    const int head_prev = (int)(counter & 3);
     const int n = n0 + e;
     const int m = n % d.m;
     const int32_t a = actions[n];
@@ -989,7 +1022,7 @@ __device__ __forceinline__ void decide_env(const EnvDev& d, int n0, int e, const
     const int32_t path0 = (MODE & kModeWaypoints) != 0 ? d.extra[2 * d.np + n] : 0;
     const int32_t start0 = (MODE & kModeRespawn) != 0 ? d.extra[3 * d.np + n] : 1;
     const HookIn hk = load_hook<MODE>(d, n);
-    const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, hk, rewards, dones, head_new);
+    const Decision s = env_decide<MODE>(d, n, a, cur, next0, best0, path0, start0, hk, rewards, dones, counter);
     constexpr bool kHook = (MODE & kModeHook) != 0;
     float* t = tail[e];
     put_frame<kHook>(t, s.x, s.y, s.vxy, (uint32_t)s.misc, s.tick);
@@ -1053,11 +1086,10 @@ __device__ __forceinline__ void write_group(const EnvDev& d, int n0, int ne, int
     for (int e = wave; e < ne; e += 4) write_row(wwin[e], tail[e], obs + (int64_t)(n0 + e) * stride, lane);
 }
 
-template <int E, int MODE>
+template <int E, int MODE, bool DEV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_step_tiles(EnvDev d, const int32_t* __restrict__ actions,
                                                     float* __restrict__ rewards, float* __restrict__ dones,
-                                                    float* __restrict__ obs, int64_t stride, int head_prev,
-                                                    int head_new)
+                                                    float* __restrict__ obs, int64_t stride)
 {
     static_assert(E % 4 == 0 && E <= 64, "whole envs per wave; one lane per env in phase A");
     __shared__ uint32_t wwin[E][kWinDwords + 1];
@@ -1065,10 +1097,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     __shared__ int64_t wbase[E];
     const int n0 = blockIdx.x * E;
     const int ne = min(E, d.n - n0);
-    if ((int)threadIdx.x < ne)
-        decide_env<E, MODE>(d, n0, threadIdx.x, actions, rewards, dones, head_prev, head_new, tail, wbase);
+    if ((int)threadIdx.x < ne) {
+        decide_env<E, MODE>(d, n0, threadIdx.x, actions, rewards, dones, step_counter<DEV>(d, blockIdx.x), tail,
+                            wbase);
+    } else if (!DEV && blockIdx.x == 0 && threadIdx.x >= 64) {
+        // the launch's value: waves 1-3 of block 0, idle while wave 0 decides, write every block's word
+        for (unsigned i = threadIdx.x - 64; i < gridDim.x; i += blockDim.x - 64) d.ctr[i] = d.ovr + 1;
+    }
     __syncthreads();
     write_group<E>(d, n0, ne, threadIdx.x >> 6, threadIdx.x & 63, wwin, tail, wbase, obs, stride);
+    // on the device each block advances its own word, last: a store earlier in the wave would hold up the
+    // waits of its window loads, which share the wave's one completion counter with the stores
+    if (DEV && threadIdx.x == 0) d.ctr[blockIdx.x] = step_counter<DEV>(d, blockIdx.x) + 1;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1085,7 +1125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 constexpr int kCamTiles = 12;      // tile rows / columns a camera row / column can touch (84 px span 11-12)
 constexpr int kCamTileStride = 16; // bytes per staged tile row
 
-__global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restrict__ obs, int64_t stride, int head)
+__global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restrict__ obs, int64_t stride)
 {
     __shared__ uint2 spr[16 * 8];                                  // sprite rows, 8 pixels each
     __shared__ uint32_t cam[4][kCamTiles * kCamTileStride / 4];    // each frame's camera tiles
@@ -1094,7 +1134,7 @@ __global__ __launch_bounds__(256) void k_obs_pixels(EnvDev d, uint8_t* __restric
     const int f = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int m = n % d.m;
-    const int s = (head - f) & 3;
+    const int s = (int)((current_counter(d) - f) & 3);   // the frame's ring slot
     const int32_t x = clampi(slot_word(d, s, 0, n), 0, d.w * kTile - 1);
     const int32_t y = clampi(slot_word(d, s, 1, n), 0, d.h * kTile - 1);
     const int cam_x = ((x + kHalfBox) >> 5) - kPix / 2;
@@ -1155,10 +1195,11 @@ __global__ __launch_bounds__(64) void k_read_respawn(EnvDev d, int32_t* __restri
 }
 
 // Decode the newest slot and the extras into the canonical int32[N][RL_STATE_FIELDS] state.
-__global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restrict__ out, int head)
+__global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restrict__ out)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= d.n) return;
+    const int head = (int)(current_counter(d) & 3);
     const int32_t vxy = slot_word(d, head, 2, n);
     const uint32_t misc = (uint32_t)slot_word(d, head, 3, n);
     int32_t* o = out + (int64_t)n * RL_STATE_FIELDS;
@@ -1189,13 +1230,18 @@ __global__ __launch_bounds__(256) void k_read_state(EnvDev d, int32_t* __restric
     o[23] = (int32_t)((misc >> kHookFlightShift) & 15u);
 }
 
+// The device decision counter into out.
+__global__ void k_read_counter(EnvDev d, int64_t* __restrict__ out) { *out = current_counter(d); }
+
 }  // namespace
 
 struct rl_env {
     rl_env_config cfg;
     Layout lay;
     uint8_t* base;
-    int64_t counter;
+    int64_t counter;    // decisions enqueued through the entry points (graph replays advance only the device's)
+    int64_t pending;    // a value set by rl_env_set_step_counter that no step has applied yet (-1: none)
+    bool synced;        // the device words hold `counter` (false from a captured step until a value is set)
     bool waypoints_set;
     bool spots_set;
 };
@@ -1219,7 +1265,8 @@ EnvDev dev_of(const rl_env* e)
     d.rmeta = reinterpret_cast<int32_t*>(e->base + e->lay.rmeta);
     d.rhist = reinterpret_cast<int32_t*>(e->base + e->lay.rhist);
     d.seed = e->cfg.respawn_seed;
-    d.counter = e->counter;
+    d.ctr = reinterpret_cast<int64_t*>(e->base + e->lay.ctr);
+    d.ovr = e->pending;
     d.n = e->cfg.num_envs;
     d.m = e->cfg.num_maps;
     d.h = e->cfg.map_h;
@@ -1235,15 +1282,32 @@ EnvDev dev_of(const rl_env* e)
     return d;
 }
 
-int launch_obs(const rl_env* e, void* obs, hipStream_t st, int head)
+// Whether work enqueued on st is being recorded into a graph.
+bool capturing(hipStream_t st)
 {
-    const EnvDev d = dev_of(e);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
+// The counter a launch hands its kernels in place of the device words: a value set on the host and not yet
+// applied, else the host's count while it equals the words and the launch is not recorded into a graph (a
+// replay must read the words, which earlier replays advanced). -1 makes the kernels read the words.
+int64_t launch_counter(const rl_env* e, bool cap)
+{
+    if (e->pending >= 0) return e->pending;
+    return e->synced && !cap ? e->counter : -1;
+}
+
+int launch_obs(const rl_env* e, void* obs, hipStream_t st)
+{
+    EnvDev d = dev_of(e);
+    d.ovr = launch_counter(e, capturing(st));
     if (e->cfg.obs_mode == RL_OBS_TILES) {
         hipLaunchKernelGGL(k_obs_tiles, dim3((d.n + 3) / 4), dim3(256), 0, st, d, static_cast<float*>(obs),
-                           e->cfg.obs_stride, head);
+                           e->cfg.obs_stride);
     } else {
         hipLaunchKernelGGL(k_obs_pixels, dim3(d.n), dim3(256), 0, st, d, static_cast<uint8_t*>(obs),
-                           e->cfg.obs_stride, head);
+                           e->cfg.obs_stride);
     }
     return rl::check_launch("obs_gather");
 }
@@ -1313,6 +1377,8 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
     e->lay = lay;
     e->base = static_cast<uint8_t*>(state);
     e->counter = 0;
+    e->pending = -1;
+    e->synced = true;
     e->waypoints_set = false;
     e->spots_set = false;
     hipStream_t st = rl::as_stream(stream);
@@ -1333,6 +1399,12 @@ int rl_env_create(const rl_env_config* cfg, const uint8_t* maps, const int32_t* 
     if (rc == RL_OK && he == hipSuccess && cfg->obs_mode == RL_OBS_PIXELS)
         he = hipMemcpyAsync(base + lay.sprites, sprites, 16 * 64, hipMemcpyDeviceToDevice, st);
     if (rc == RL_OK && he != hipSuccess) rc = rl::fail(RL_EHIP, "table copy: %s", hipGetErrorString(he));
+    if (rc == RL_OK) {   // the decision counter starts at 0
+        const int64_t words = (int64_t)(lay.total - lay.ctr) / 4;
+        hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)), dim3(256), 0, st,
+                           reinterpret_cast<int32_t*>(base + lay.ctr), words);
+        rc = rl::check_launch("counter");
+    }
     if (rc == RL_OK && cfg->respawn_mode == RL_RESPAWN_ADAPTIVE) {
         // ring, meta and histogram are contiguous: zero them together
         const int64_t words = (int64_t)(lay.total - lay.ring) / 4;
@@ -1363,7 +1435,7 @@ int rl_env_reset(rl_env* e, const uint8_t* mask, void* obs, void* stream)
     const EnvDev d = dev_of(e);
     hipLaunchKernelGGL(k_reset, dim3((d.n + 255) / 256), dim3(256), 0, st, d, mask);
     if (int rc = rl::check_launch("reset")) return rc;
-    if (obs) return launch_obs(e, obs, st, (int)(e->counter & 3));
+    if (obs) return launch_obs(e, obs, st);
     return RL_OK;
 }
 
@@ -1382,18 +1454,28 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
     if (wp && !e->waypoints_set) return rl::fail(RL_EINVAL, "waypoint rewards need rl_env_set_waypoints first");
     if (rs && !e->spots_set) return rl::fail(RL_EINVAL, "the adaptive respawn needs rl_env_set_respawn_spots first");
     hipStream_t st = rl::as_stream(stream);
+    const bool cap = capturing(st);
+    // a counter set on the host is applied by this launch; inside a capture it would be baked into the graph
+    // and reapplied on every replay
+    if (cap && e->pending >= 0)
+        return rl::fail(RL_EINVAL, "rl_env_set_step_counter was called since the last step: run a step outside the "
+                                   "capture first");
+    if (cap) e->synced = false;   // replays advance the device words unseen by the host
     EnvDev d = dev_of(e);
+    d.ovr = launch_counter(e, cap);
+    const bool dev = d.ovr < 0;   // the step kernels read the device words
     d.aim = aim;
-    const int head_prev = (int)(e->counter & 3), head_new = (int)((e->counter + 1) & 3);
     const int mode = (wp ? kModeWaypoints : 0) | (rs ? kModeRespawn : 0) | (hk ? kModeHook : 0) |
                      (hk && e->cfg.frame_skip > 3 ? kModeHookFar : 0);
     if (e->cfg.obs_mode == RL_OBS_TILES) {
         const dim3 grid((d.n + kStepTilesEnvs - 1) / kStepTilesEnvs), block(256);
         float* o = static_cast<float*>(obs);
         const int64_t os = e->cfg.obs_stride;
-#define RL_STEP_TILES(M) \
-    hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, M>), grid, block, 0, st, d, actions, rewards, dones, o, os, \
-                       head_prev, head_new)
+#define RL_STEP_TILES(M)                                                                                     \
+    if (dev) hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, M, true>), grid, block, 0, st, d, actions, rewards, \
+                                dones, o, os);                                                                \
+    else hipLaunchKernelGGL((k_step_tiles<kStepTilesEnvs, M, false>), grid, block, 0, st, d, actions, rewards,    \
+                            dones, o, os)
         switch (mode) {
         case 0: RL_STEP_TILES(0); break;
         case 1: RL_STEP_TILES(1); break;
@@ -1412,7 +1494,9 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
         if (int rc = rl::check_launch("env_step+obs_gather")) return rc;
     } else {
         const dim3 grid((d.n + 63) / 64), block(64);
-#define RL_STEP(M) hipLaunchKernelGGL(k_step<M>, grid, block, 0, st, d, actions, rewards, dones, head_prev, head_new)
+#define RL_STEP(M)                                                                                           \
+    if (dev) hipLaunchKernelGGL((k_step<M, true>), grid, block, 0, st, d, actions, rewards, dones);            \
+    else hipLaunchKernelGGL((k_step<M, false>), grid, block, 0, st, d, actions, rewards, dones)
         switch (mode) {
         case 0: RL_STEP(0); break;
         case 1: RL_STEP(1); break;
@@ -1435,8 +1519,10 @@ int rl_env_step_aim(rl_env* e, const int32_t* actions, const int32_t* aim, void*
         if (int rc = rl::check_launch("respawn_append")) return rc;
     }
     e->counter += 1;
+    e->pending = -1;        // the step's blocks wrote the counter (the applied value plus one)
+    e->synced = d.ovr >= 0;
     if (e->cfg.obs_mode == RL_OBS_TILES) return RL_OK;
-    return launch_obs(e, obs, st, head_new);
+    return launch_obs(e, obs, st);
 }
 
 int rl_env_step(rl_env* e, const int32_t* actions, void* obs, float* rewards, float* dones, void* stream)
@@ -1540,8 +1626,7 @@ int rl_env_read_state(const rl_env* e, int32_t* out, void* stream)
     if (!e || !out) return rl::fail(RL_EINVAL, "env and out must be non-NULL");
     if (!rl::aligned(out, 4)) return rl::fail(RL_EALIGN, "out is not 4-byte aligned");
     const EnvDev d = dev_of(e);
-    hipLaunchKernelGGL(k_read_state, dim3((d.n + 255) / 256), dim3(256), 0, rl::as_stream(stream), d, out,
-                       (int)(e->counter & 3));
+    hipLaunchKernelGGL(k_read_state, dim3((d.n + 255) / 256), dim3(256), 0, rl::as_stream(stream), d, out);
     return rl::check_launch("read_state");
 }
 
@@ -1564,7 +1649,16 @@ int rl_env_set_step_counter(rl_env* e, int64_t counter)
     if (!e) return rl::fail(RL_EINVAL, "env is NULL");
     if (counter < 0) return rl::fail(RL_EINVAL, "counter %lld < 0", (long long)counter);
     e->counter = counter;
+    e->pending = counter;
     return RL_OK;
+}
+
+int rl_env_read_step_counter(const rl_env* e, int64_t* out, void* stream)
+{
+    if (!e || !out) return rl::fail(RL_EINVAL, "env and out must be non-NULL");
+    if (!rl::aligned(out, 8)) return rl::fail(RL_EALIGN, "out is not 8-byte aligned");
+    hipLaunchKernelGGL(k_read_counter, dim3(1), dim3(1), 0, rl::as_stream(stream), dev_of(e), out);
+    return rl::check_launch("read_step_counter");
 }
 
 void rl_env_destroy(rl_env* e) { delete e; }

@@ -12,9 +12,11 @@
 // each row [t][n0 .. n0+E) is a coalesced segment.
 //
 // Statistics: per-thread float64 sums of A and A^2, a block reduction, per-block partials in the
-// workspace, then a one-block finalise kernel reduces the partials in block order (the kernel boundary
+// workspace, then a one-wave finalise kernel reduces the partials in block order (the kernel boundary
 // makes every block's partial visible; no device-wide fence or atomic per block). No floating-point
-// atomics: results are identical from run to run.
+// atomics: results are identical from run to run. With deferred statistics (normalize = 3) the partials go
+// to the caller's adv_stats instead and no finalise runs: the loss kernels reduce them, with the same
+// function and so the same bits, when they read the statistics.
 
 #include <algorithm>
 
@@ -26,6 +28,8 @@ constexpr double kNormEps = 1e-8;
 
 struct StatsOut {
     double* partials;     // [grid][2]: sum A, sum A^2 of each block
+    double* header;       // deferred statistics: {-(grid), count} written by block 0; NULL otherwise
+    double count;
 };
 
 // Sums of two doubles across the block at once, each in the same fixed order on every run (a wave's
@@ -60,27 +64,40 @@ __device__ void publish_stats(double s1, double s2, const StatsOut& so)
     if (threadIdx.x == 0) {
         so.partials[2 * blockIdx.x] = s1;
         so.partials[2 * blockIdx.x + 1] = s2;
+        if (so.header && blockIdx.x == 0) {
+            so.header[0] = -(double)gridDim.x;
+            so.header[1] = so.count;
+        }
     }
 }
 
-// One block: reduce the per-block partials in block order into {count, mean, population std}.
-__global__ __launch_bounds__(256) void k_stats_finalize(const double* __restrict__ partials, int blocks, double count,
-                                                        double* __restrict__ stats)
+// One wave: reduce the per-block partials in block order into {count, mean, population std}.
+__global__ __launch_bounds__(64) void k_stats_finalize(const double* __restrict__ partials, int blocks, double count,
+                                                       double* __restrict__ stats)
 {
-    __shared__ double lds[32];
-    double a = 0.0, b = 0.0;
-    for (int i = threadIdx.x; i < blocks; i += blockDim.x) {
-        a += partials[2 * i];
-        b += partials[2 * i + 1];
-    }
-    block_sum2(a, b, lds);
+    double mean, stdev;
+    rl::stats_from_partials(partials, blocks, count, mean, stdev);
     if (threadIdx.x == 0) {
-        const double mean = a / count;
-        double var = b / count - mean * mean;
-        var = var > 0.0 ? var : 0.0;
         stats[0] = count;
         stats[1] = mean;
-        stats[2] = sqrt(var);
+        stats[2] = stdev;
+    }
+}
+
+// The finished statistics of an adv_stats buffer in either form (finished, or deferred partials).
+__global__ __launch_bounds__(64) void k_stats_finish(const double* __restrict__ in, double* __restrict__ out)
+{
+    const double h = in[0];
+    if (h >= 0.0) {
+        if (threadIdx.x < 3) out[threadIdx.x] = in[threadIdx.x];
+        return;
+    }
+    double mean, stdev;
+    rl::stats_from_partials(in + rl::kDeferredHead, (int)(-h), in[1], mean, stdev);
+    if (threadIdx.x == 0) {
+        out[0] = in[1];
+        out[1] = mean;
+        out[2] = stdev;
     }
 }
 
@@ -353,6 +370,22 @@ int rl_gae_workspace_bytes(int32_t T, int32_t N, size_t* bytes)
     return RL_OK;
 }
 
+int rl_gae_stats_bytes(int32_t T, int32_t N, size_t* bytes)
+{
+    if (T < 1 || N < 1) return rl::fail(RL_EINVAL, "T %d and N %d must be >= 1", T, N);
+    if (!bytes) return rl::fail(RL_EINVAL, "bytes is NULL");
+    *bytes = sizeof(double) * (rl::kDeferredHead + 2 * (size_t)blocks_of(pick(T, N), N));
+    return RL_OK;
+}
+
+int rl_adv_stats_finish(const double* adv_stats, double* out, void* stream)
+{
+    if (!adv_stats || !out) return rl::fail(RL_EINVAL, "adv_stats and out must be non-NULL");
+    if (!rl::aligned(adv_stats, 8) || !rl::aligned(out, 8)) return rl::fail(RL_EALIGN, "adv_stats / out not 8-byte aligned");
+    hipLaunchKernelGGL(k_stats_finish, dim3(1), dim3(64), 0, rl::as_stream(stream), adv_stats, out);
+    return rl::check_launch("adv_stats_finish");
+}
+
 int rl_gae_strided(const float* rewards, const float* values, const float* dones, const float* last_values,
                    int32_t T, int32_t N, int64_t ld, float gamma, float lambda, float* adv, float* ret,
                    int32_t normalize, double* adv_stats, void* ws, size_t ws_bytes, void* stream)
@@ -362,21 +395,28 @@ int rl_gae_strided(const float* rewards, const float* values, const float* dones
     if ((T - 1) * ld + N > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "(T-1)*ld + N too large");
     if (!rewards || !values || !dones || !last_values || !adv || !ret)
         return rl::fail(RL_EINVAL, "rewards, values, dones, last_values, adv and ret must be non-NULL");
-    if (normalize < 0 || normalize > 2) return rl::fail(RL_EINVAL, "normalize %d outside {0, 1, 2}", normalize);
-    if (normalize != 0 && (!adv_stats || !ws)) return rl::fail(RL_EINVAL, "normalize needs adv_stats and ws");
+    if (normalize < 0 || normalize > 3) return rl::fail(RL_EINVAL, "normalize %d outside {0, 1, 2, 3}", normalize);
+    if (normalize != 0 && !adv_stats) return rl::fail(RL_EINVAL, "normalize %d needs adv_stats", normalize);
+    if ((normalize == 1 || normalize == 2) && !ws) return rl::fail(RL_EINVAL, "normalize %d needs ws", normalize);
     const void* ptrs[] = {rewards, values, dones, last_values, adv, ret};
     for (const void* p : ptrs)
         if (!rl::aligned(p, 4)) return rl::fail(RL_EALIGN, "a float array is not 4-byte aligned");
     size_t need = 0;
     rl_gae_workspace_bytes(T, N, &need);
-    if (normalize != 0) {
+    if (normalize == 1 || normalize == 2) {
         if (!rl::aligned(ws, 8) || !rl::aligned(adv_stats, 8)) return rl::fail(RL_EALIGN, "ws / adv_stats not 8-byte aligned");
         if (ws_bytes < need) return rl::fail(RL_ESIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
     }
+    if (normalize == 3 && !rl::aligned(adv_stats, 8)) return rl::fail(RL_EALIGN, "adv_stats not 8-byte aligned");
     hipStream_t st = rl::as_stream(stream);
     const float gl = gamma * lambda;
     StatsOut so{};
-    if (normalize != 0) so.partials = static_cast<double*>(ws);
+    so.count = (double)T * (double)N;
+    if (normalize == 1 || normalize == 2) so.partials = static_cast<double*>(ws);
+    if (normalize == 3) {   // the partials and their header into the caller's adv_stats; no finalise
+        so.partials = adv_stats + rl::kDeferredHead;
+        so.header = adv_stats;
+    }
     const int want = normalize != 0 ? 1 : 0;
     const GaeKernel k = pick(T, N);
     const dim3 grid(blocks_of(k, N)), block(256);
@@ -407,8 +447,8 @@ int rl_gae_strided(const float* rewards, const float* values, const float* dones
         break;
     }
     if (int rc = rl::check_launch("gae_scan")) return rc;
-    if (normalize != 0) {
-        hipLaunchKernelGGL(k_stats_finalize, dim3(1), dim3(256), 0, st, static_cast<const double*>(ws),
+    if (normalize == 1 || normalize == 2) {
+        hipLaunchKernelGGL(k_stats_finalize, dim3(1), dim3(64), 0, st, static_cast<const double*>(ws),
                            blocks_of(k, N), (double)T * (double)N, adv_stats);
         if (int rc = rl::check_launch("adv_stats")) return rc;
     }

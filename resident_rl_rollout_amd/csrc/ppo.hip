@@ -9,9 +9,12 @@
 //   Gather (contiguous, or perm with more than 64 minibatches): grid (blocks per minibatch, minibatches);
 //   thread k of minibatch m reads sample perm[m*mb + k]. Shuffled indices make every per-sample read a
 //   random access.
-//   perm with at most 64 minibatches is first turned into each sample's minibatch number (one scatter of
-//   2 bytes per sample into the workspace), then takes the stream pass below: the same sets, summed in
-//   storage order instead of perm order.
+//   perm with at most 64 minibatches is first turned into each sample's minibatch number (2 bytes per
+//   sample in the workspace), then takes the stream pass below: the same sets, summed in storage order
+//   instead of perm order. The conversion bins the permutation's entries by destination (16384 samples per
+//   bin) so that no write is a lone 2-byte scatter: per-block counts and their scan give every block a run
+//   in each bin's staging, each block sorts its entries by bin in LDS and writes them run by run, then one
+//   block per bin places its entries in LDS and writes the bin's minibatch numbers as one 32 KB piece.
 //   Stream (mb_index): each minibatch's scalars are means over its set of samples, so one pass over the
 //   batch in storage order serves all minibatches at once: every read is coalesced and each sample is
 //   read exactly once. Each thread adds its samples' terms into its own per-minibatch slots in LDS
@@ -58,6 +61,36 @@ struct LossArgs {
     float inv_mb;       // 1 / M
     float dv_coef;      // 2 vf / M
 };
+
+// The normalisation of the advantages from adv_stats, which holds either the finished statistics
+// {count, mean, std} or the scan blocks' deferred partial sums (rl_gae with normalize = 3, header
+// adv_stats[0] < 0). Deferred partials are reduced by wave 0 with rl::stats_from_partials, the function the
+// scan's own finalise uses, so mean and std have the same bits either way. Every thread calls it; the
+// block's barrier follows it, after which norm_read gives mean and the scale 1 / (std + eps).
+__device__ __forceinline__ void norm_reduce(const double* __restrict__ stats, double* nrm)
+{
+    if (stats && stats[0] < 0.0 && threadIdx.x < 64) {
+        double mean, stdev;
+        rl::stats_from_partials(stats + rl::kDeferredHead, (int)(-stats[0]), stats[1], mean, stdev);
+        if (threadIdx.x == 0) {
+            nrm[0] = mean;
+            nrm[1] = stdev;
+        }
+    }
+}
+
+__device__ __forceinline__ void norm_read(const double* __restrict__ stats, const double* nrm, float& mean, float& scale)
+{
+    mean = 0.0f;
+    scale = 1.0f;
+    if (stats) {
+        const bool deferred = stats[0] < 0.0;
+        const double mu = deferred ? nrm[0] : stats[1];
+        const double sd = deferred ? nrm[1] : stats[2];
+        mean = (float)mu;
+        scale = (float)(1.0 / (sd + kNormEps));
+    }
+}
 
 // Sums of three doubles across a block of at most 4 waves, each in the same fixed order on every run (a
 // wave's butterfly, then the waves in order), with one barrier. The LDS array (12 doubles) must not have
@@ -255,13 +288,13 @@ template <int AC, bool GRAD>
 __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
 {
     __shared__ double lds[12];
+    __shared__ double nrm[2];
     const int m = blockIdx.y;
     const int64_t base = (int64_t)m * p.mb;
-    float mean = 0.0f, scale = 1.0f;
-    if (p.stats) {
-        mean = (float)p.stats[1];
-        scale = (float)(1.0 / (p.stats[2] + kNormEps));
-    }
+    norm_reduce(p.stats, nrm);
+    __syncthreads();
+    float mean, scale;
+    norm_read(p.stats, nrm, mean, scale);
     double s_pg = 0.0, s_v = 0.0, s_h = 0.0;
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < p.mb; k += step) {
@@ -290,14 +323,13 @@ template <int AC, int NB, int THREADS, int U, bool GRAD>
 __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t chunk)
 {
     __shared__ float acc[NB * 3 * THREADS];
+    __shared__ double nrm[2];
     const int t = threadIdx.x;
     for (int j = t; j < NB * 3 * THREADS; j += THREADS) acc[j] = 0.0f;
+    norm_reduce(p.stats, nrm);
     __syncthreads();
-    float mean = 0.0f, scale = 1.0f;
-    if (p.stats) {
-        mean = (float)p.stats[1];
-        scale = (float)(1.0 / (p.stats[2] + kNormEps));
-    }
+    float mean, scale;
+    norm_read(p.stats, nrm, mean, scale);
     const int64_t lo = (int64_t)blockIdx.x * chunk;
     const int64_t hi = min(p.B, lo + chunk);
     for (int64_t i0 = lo + t; i0 < hi; i0 += (int64_t)THREADS * U) {
@@ -417,6 +449,230 @@ __global__ __launch_bounds__(256) void k_perm_to_index(const int32_t* __restrict
         ids[min(max((int64_t)perm[base + k], (int64_t)0), B - 1)] = m;
 }
 
+// Binned perm conversion: destinations in bins of kBinSamples samples, perm positions in blocks of
+// kBinPositions (32 a thread). Five launches, none with a global atomic:
+//   count   per position block, the number of its entries for each bin (an LDS histogram), block-major;
+//   scan    per bin, the exclusive sum of those counts over the position blocks (where each block's run
+//           of the bin's staging starts) and the bin's total, in two launches (group sums, then offsets);
+//   scatter per position block, its entries sorted by bin in LDS, then written in that order, so that
+//           consecutive lanes write consecutive words of a run;
+//   place   per bin, its staged entries placed in LDS by destination and written out as one piece.
+// A staged entry is the destination's offset in its bin (14 bits) and its minibatch (6 bits: the stream
+// pass takes at most 64). Batches of up to kMaxBins bins (2^24 samples) take this path, larger ones the
+// direct scatter above.
+constexpr int kBinShift = 14;
+constexpr int kBinSamples = 1 << kBinShift;
+constexpr int kBinPositions = 8192;
+constexpr int kMaxBins = 1024;
+constexpr int kScanRows = 16;        // position blocks a scan group takes
+
+// Block-wide exclusive sum over 256 threads of one value each (LDS `sh` of 4 words); returns the thread's
+// prefix and leaves the block total in *total.
+__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* sh, int32_t* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    int32_t before = 0;
+    for (int k = 0; k < w; ++k) before += sh[k];
+    *total = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return before + inc - v;
+}
+
+// Positions a thread of a binning block takes: all of them are loaded before the first LDS update.
+constexpr int kPermPerThread = kBinPositions / 256;
+
+// The binned path takes B <= 2^24 (kMaxBins bins), so positions, destinations and minibatch products fit
+// 32-bit integers. Positions past a block's end (the last block's) count into a spare bin, kMaxBins, so that
+// every LDS update is unconditional.
+__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ perm, int32_t B, int nbins,
+                                                    int32_t* __restrict__ counts)
+{
+    __shared__ int32_t hist[kMaxBins + 1];
+    const int t = threadIdx.x;
+    const int32_t lo = blockIdx.x * kBinPositions;
+    const int32_t hi = min(B, lo + kBinPositions);
+    // every load unconditional (at the last position when past it), so all are in flight at once
+    int32_t bin[kPermPerThread];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) bin[j] = perm[min(lo + t + 256 * j, hi - 1)];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j)
+        bin[j] = lo + t + 256 * j < hi ? min(max(bin[j], 0), B - 1) >> kBinShift : kMaxBins;
+    for (int b = t; b <= nbins; b += 256) hist[b] = 0;
+    if (t == 0) hist[kMaxBins] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) atomicAdd(&hist[bin[j]], 1);
+    __syncthreads();
+    int32_t* row = counts + (int64_t)blockIdx.x * nbins;
+    for (int b = t; b < nbins; b += 256) row[b] = hist[b];
+}
+
+// The scan in two launches of one-wave blocks (bins [64 * blockIdx.x, + 64), one per lane; position
+// blocks in groups of kScanRows, group blockIdx.y): the first sums each group's counts, the second adds the
+// sums of the groups before its own and writes its rows' running offsets. The matrices hold at most 2^21
+// words (kMaxBins bins, 2048 position blocks), so 32-bit indexes suffice. Every load is unconditional
+// (clamped into range) and only its use is masked, so a lane's loads are all in flight at once.
+__global__ __launch_bounds__(64) void k_perm_group_sums(const int32_t* __restrict__ counts, int nbins, int nblk,
+                                                        int32_t* __restrict__ gsum)
+{
+    const int bin = blockIdx.x * 64 + threadIdx.x;
+    const int cb = min(bin, nbins - 1);
+    const int k0 = blockIdx.y * kScanRows, k1 = min(nblk, k0 + kScanRows);
+    int32_t c[kScanRows];
+#pragma unroll
+    for (int u = 0; u < kScanRows; ++u) c[u] = counts[min(k0 + u, k1 - 1) * nbins + cb];
+    int32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < kScanRows; ++u) sum += k0 + u < k1 ? c[u] : 0;
+    if (bin < nbins) gsum[blockIdx.y * nbins + bin] = sum;
+}
+
+__global__ __launch_bounds__(64) void k_perm_offsets(const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ gsum, int nbins, int nblk,
+                                                     int32_t* __restrict__ offs, int32_t* __restrict__ fill)
+{
+    constexpr int U = 16;
+    const int bin = blockIdx.x * 64 + threadIdx.x;
+    const int cb = min(bin, nbins - 1);
+    const int g = blockIdx.y;
+    const int k0 = g * kScanRows, k1 = min(nblk, k0 + kScanRows);
+    int32_t c[kScanRows];
+#pragma unroll
+    for (int u = 0; u < kScanRows; ++u) c[u] = counts[min(k0 + u, k1 - 1) * nbins + cb];
+    int32_t run = 0;
+    for (int h = 0; h < g; h += U) {
+        int32_t q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) q[u] = gsum[min(h + u, g - 1) * nbins + cb];
+#pragma unroll
+        for (int u = 0; u < U; ++u) run += h + u < g ? q[u] : 0;
+    }
+    if (bin >= nbins) return;
+#pragma unroll
+    for (int u = 0; u < kScanRows; ++u)
+        if (k0 + u < k1) {
+            offs[(k0 + u) * nbins + bin] = run;
+            run += c[u];
+        }
+    if (k1 == nblk) fill[bin] = run;
+}
+
+__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ perm, int32_t B, int32_t mb,
+                                                      float inv_mb, int nbins, const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offs, uint32_t* __restrict__ staging)
+{
+    __shared__ int32_t cur[kMaxBins + 1];  // next LDS slot of each bin (and of the spare bin)
+    __shared__ int32_t delta[kMaxBins];    // staging index minus LDS slot, per bin
+    __shared__ uint32_t sorted[kBinPositions];
+    __shared__ int32_t sh[4];
+    constexpr int BPT = kMaxBins / 256;    // bins a thread scans
+    const int t = threadIdx.x;
+    const int32_t lo = blockIdx.x * kBinPositions;
+    const int32_t hi = min(B, lo + kBinPositions);
+    // the positions' entries first, so their loads overlap the run set-up below
+    uint32_t e[kPermPerThread];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) e[j] = (uint32_t)perm[min(lo + t + 256 * j, hi - 1)];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) {
+        const int32_t p = lo + t + 256 * j;
+        const int32_t d = min(max((int32_t)e[j], 0), B - 1);
+        // p / mb: the float quotient is within 2^-17 of the exact one (below 64 here), so one step corrects it
+        int32_t m = (int32_t)((float)p * inv_mb);
+        if (m * mb > p) --m;
+        else if ((m + 1) * mb <= p) ++m;
+        e[j] = p < hi ? (uint32_t)(d & (kBinSamples - 1)) | ((uint32_t)m << kBinShift) | ((uint32_t)(d >> kBinShift) << 20)
+                      : 0xffffffffu;
+    }
+    const int64_t row = (int64_t)blockIdx.x * nbins;
+    int32_t c[BPT], o[BPT];
+    int32_t own = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int64_t i = row + min(t * BPT + j, nbins - 1);   // unconditional loads, their use masked
+        c[j] = counts[i];
+        o[j] = offs[i];
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        if (t * BPT + j >= nbins) c[j] = 0;
+        own += c[j];
+    }
+    int32_t total;
+    int32_t start = block_exclusive_sum(own, sh, &total);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int b = t * BPT + j;
+        if (b < nbins) {
+            cur[b] = start;
+            delta[b] = b * kBinSamples + o[j] - start;
+        }
+        start += c[j];
+    }
+    if (t == 0) cur[kMaxBins] = total;    // the spare bin's slots follow the block's entries
+    __syncthreads();
+    int32_t slot[kPermPerThread];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) slot[j] = atomicAdd(&cur[e[j] == 0xffffffffu ? kMaxBins : e[j] >> 20], 1);
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) sorted[slot[j]] = e[j];
+    __syncthreads();
+    const int n = (int)(hi - lo);
+    // all of the thread's LDS reads first, then its stores
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) e[j] = sorted[min(t + 256 * j, n - 1)];
+    int32_t g[kPermPerThread];
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) g[j] = delta[e[j] >> 20] + t + 256 * j;
+#pragma unroll
+    for (int j = 0; j < kPermPerThread; ++j) {
+        const int b = (int)(e[j] >> 20);
+        // a run past the bin's capacity only when perm is not a permutation: such entries are dropped
+        if (t + 256 * j < n && g[j] - b * kBinSamples < kBinSamples) staging[g[j]] = e[j] & 0xfffffu;
+    }
+}
+
+// One block per bin: its staged entries placed in LDS (destinations no entry names read 0xffff, past every
+// minibatch, which the loss counts as the last; a permutation names every destination once), then the bin's
+// minibatch numbers written out with 16-byte stores.
+__global__ __launch_bounds__(512) void k_perm_place(const int32_t* __restrict__ fill,
+                                                    const uint32_t* __restrict__ staging, int64_t B,
+                                                    uint16_t* __restrict__ ids)
+{
+    constexpr int J = 8;
+    __shared__ uint4 win4[kBinSamples / 8];
+    uint16_t* win = reinterpret_cast<uint16_t*>(win4);
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    for (int q = t; q < kBinSamples / 8; q += 512) win4[q] = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+    const int32_t cnt = min(fill[b], kBinSamples);
+    __syncthreads();
+    const uint32_t* st = staging + (int64_t)b * kBinSamples;
+    for (int i0 = t; i0 < cnt; i0 += 512 * J) {
+        uint32_t v[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = st[min(i0 + 512 * j, cnt - 1)];   // unconditional, clamped
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (i0 + 512 * j < cnt) win[v[j] & (kBinSamples - 1)] = (uint16_t)(v[j] >> kBinShift);
+    }
+    __syncthreads();
+    const int64_t lo = (int64_t)b * kBinSamples;
+    const int n = (int)min((int64_t)kBinSamples, B - lo);
+    uint4* out4 = reinterpret_cast<uint4*>(ids + lo);     // lo is a multiple of 16384: 32 KB aligned
+    for (int q = t; q < n / 8; q += 512) out4[q] = win4[q];
+    for (int i = (n / 8) * 8 + t; i < n; i += 512) ids[lo + i] = win[i];
+}
+
 int blocks_per_mb(int64_t mb)
 {
     const int64_t per_block = 256 * kSamplesPerThread;
@@ -429,10 +685,27 @@ constexpr int kStreamMaxMinibatches = 64;
 constexpr int kStreamBlocks = 768;
 
 // Bytes of the per-block partials at the front of the workspace (rounded up to 256, where the minibatch
-// numbers of a converted perm follow).
+// numbers of a converted perm follow, then the bins' fill counters and staging runs).
 size_t partial_bytes(int64_t num_mb, size_t blocks)
 {
     return rl::round_up(sizeof(double) * 3 * (size_t)num_mb * blocks, 256);
+}
+
+int64_t perm_bins(int64_t B) { return (B + kBinSamples - 1) / kBinSamples; }
+int64_t perm_blocks(int64_t B) { return (B + kBinPositions - 1) / kBinPositions; }
+
+// Bytes behind the partials for a perm's conversion: minibatch numbers, and for a binned conversion the
+// counts and run offsets (position blocks x bins), the scan's group sums, the bins' totals and the staging
+// runs.
+size_t perm_bytes(int64_t B)
+{
+    size_t bytes = rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
+    const int64_t nb = perm_bins(B);
+    if (nb <= kMaxBins)
+        bytes += 2 * rl::round_up(sizeof(int32_t) * (size_t)(nb * perm_blocks(B)), 256) +
+                 rl::round_up(sizeof(int32_t) * (size_t)(nb * ((perm_blocks(B) + kScanRows - 1) / kScanRows)), 256) +
+                 rl::round_up(sizeof(int32_t) * (size_t)nb, 256) + sizeof(uint32_t) * (size_t)nb * kBinSamples;
+    return bytes;
 }
 
 // Each thread adds at most this many samples into its float32 slots (the slot sums are then reduced in
@@ -466,8 +739,8 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     int64_t chunk = 0;
     const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, num_mb, &chunk) : 0);
     *bytes = partial_bytes(num_mb, blocks);
-    // with at most 64 minibatches, room for the minibatch numbers a perm is turned into
-    if (num_mb <= kStreamMaxMinibatches) *bytes += sizeof(uint16_t) * (size_t)B;
+    // with at most 64 minibatches, room for turning a perm into minibatch numbers
+    if (num_mb <= kStreamMaxMinibatches) *bytes += perm_bytes(B);
     return RL_OK;
 }
 
@@ -561,9 +834,31 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
         // the perm's sets as minibatch numbers behind the partials, then the stream pass
         int64_t c = 0;
         const size_t blocks = (size_t)std::max(blocks_per_mb(mb), stream_blocks(B, num_mb, &c));
-        uint16_t* ids = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks));
-        hipLaunchKernelGGL(k_perm_to_index, dim3((unsigned)blocks_per_mb(mb), (unsigned)num_mb), dim3(256), 0, st,
-                           perm, B, (int64_t)mb, ids);
+        uint8_t* tail = static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks);
+        uint16_t* ids = reinterpret_cast<uint16_t*>(tail);
+        const int64_t nbins = perm_bins(B);
+        if (nbins <= kMaxBins) {
+            const int64_t nblk = perm_blocks(B);
+            const int64_t groups = (nblk + kScanRows - 1) / kScanRows;
+            const size_t mat = rl::round_up(sizeof(int32_t) * (size_t)(nbins * nblk), 256);
+            uint8_t* w = tail + rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
+            int32_t* counts = reinterpret_cast<int32_t*>(w);
+            int32_t* offs = reinterpret_cast<int32_t*>(w + mat);
+            int32_t* gsum = reinterpret_cast<int32_t*>(w + 2 * mat);
+            w += 2 * mat + rl::round_up(sizeof(int32_t) * (size_t)(nbins * groups), 256);
+            int32_t* fill = reinterpret_cast<int32_t*>(w);
+            uint32_t* staging = reinterpret_cast<uint32_t*>(w + rl::round_up(sizeof(int32_t) * (size_t)nbins, 256));
+            const dim3 sgrid((unsigned)((nbins + 63) / 64), (unsigned)groups);
+            hipLaunchKernelGGL(k_perm_count, dim3((unsigned)nblk), dim3(256), 0, st, perm, (int32_t)B, (int)nbins, counts);
+            hipLaunchKernelGGL(k_perm_group_sums, sgrid, dim3(64), 0, st, counts, (int)nbins, (int)nblk, gsum);
+            hipLaunchKernelGGL(k_perm_offsets, sgrid, dim3(64), 0, st, counts, gsum, (int)nbins, (int)nblk, offs, fill);
+            hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)nblk), dim3(256), 0, st, perm, (int32_t)B, (int32_t)mb,
+                               (float)(1.0 / (double)mb), (int)nbins, counts, offs, staging);
+            hipLaunchKernelGGL(k_perm_place, dim3((unsigned)nbins), dim3(512), 0, st, fill, staging, B, ids);
+        } else {
+            hipLaunchKernelGGL(k_perm_to_index, dim3((unsigned)blocks_per_mb(mb), (unsigned)num_mb), dim3(256), 0, st,
+                               perm, B, (int64_t)mb, ids);
+        }
         if (int rc = rl::check_launch("ppo_loss perm")) return rc;
         mb_index = ids;
         p.mb_index = ids;

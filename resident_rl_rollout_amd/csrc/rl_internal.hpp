@@ -45,4 +45,43 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 constexpr int kWave = 64;
 
+// Whole-batch advantage statistics from per-block partial sums (sum A, sum A^2 of each scan block, in
+// block order), reduced by one wave in the order of a 256-thread block: virtual thread v sums partials v,
+// v + 256, ... in turn, each group of 64 virtual threads is combined by a butterfly, and the four group
+// sums are added in order. Every kernel that reduces the partials uses this function, so the mean and
+// population standard deviation have the same bits wherever they are computed. Returns them in every lane.
+__device__ __forceinline__ void stats_from_partials(const double* __restrict__ partials, int blocks, double count,
+                                                    double& mean, double& stdev)
+{
+    const int lane = threadIdx.x & 63;
+    double a[4] = {0.0, 0.0, 0.0, 0.0}, b[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        for (int i = 64 * w + lane; i < blocks; i += 256) {
+            a[w] += partials[2 * i];
+            b[w] += partials[2 * i + 1];
+        }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            a[w] += __shfl_xor(a[w], off, 64);
+            b[w] += __shfl_xor(b[w], off, 64);
+        }
+    double sa = 0.0, sb = 0.0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        sa += a[w];
+        sb += b[w];
+    }
+    mean = sa / count;
+    double var = sb / count - mean * mean;
+    var = var > 0.0 ? var : 0.0;
+    stdev = sqrt(var);
+}
+
+// The deferred form of the statistics (rl_gae with normalize = 3): adv_stats[0] = -(number of partial
+// pairs), adv_stats[1] = count, adv_stats[2] unused, pairs from adv_stats + kDeferredHead.
+constexpr int kDeferredHead = 4;
+
 }  // namespace rl

@@ -91,7 +91,11 @@ def test_entry_points_reject_before_any_hip_call():
     # rl_gae: sizes, NULLs, enum, workspace
     assert lib.rl_gae(fake, fake, fake, fake, 0, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
     assert lib.rl_gae(None, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -1
-    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 3, fake, fake, 1 << 20, None) == -1
+    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 4, fake, fake, 1 << 20, None) == -1
+    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 3, None, None, 0, None) == -1
+    assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 2, fake, None, 0, None) == -1
+    assert lib.rl_adv_stats_finish(None, fake, None) == -1
+    assert lib.rl_adv_stats_finish(ctypes.c_void_p(4100), fake, None) == -2
     assert lib.rl_gae(fake, fake, fake, fake, 4, 5, 0.99, 0.95, fake, fake, 1, fake, fake, 8, None) == -3
     assert lib.rl_gae(fake, ctypes.c_void_p(4098), fake, fake, 4, 5, 0.99, 0.95, fake, fake, 0, None, None, 0, None) == -2
     # rl_vtrace: sizes, NULLs, clip thresholds, alignment
@@ -171,3 +175,21 @@ def test_waypoint_path_host_bfs_matches_the_oracle():
     g[1, 1] = 1
     with pytest.raises(binding.RLError, match="blocked"):
         binding.waypoint_path(g, (1, 1), (2, 2))
+
+
+def test_store_probe_rejects_bad_arguments():
+    lib = binding.lib()
+    buf = ctypes.c_void_p(4096)   # never dereferenced: every call below fails its checks first
+    assert lib.rl_store_probe(None, 64, 16, None) == -1
+    assert lib.rl_store_probe(ctypes.c_void_p(4100), 64, 16, None) == -2
+    assert lib.rl_store_probe(buf, 60, 16, None) == -1
+    assert lib.rl_store_probe(buf, 64, 24, None) == -1
+    assert lib.rl_store_probe(buf, 0, 16, None) == -1
+    assert "multiples of 16" in lib.rl_last_error().decode()
+
+
+def test_deferred_statistics_size():
+    # a header of 4 doubles, then (sum A, sum A^2) of every scan block: 256 blocks of 256 envs at 65536 x
+    # 128, 128 blocks of 16 envs at 2048 x 128, 1 block of 16 envs at one env
+    for t, n, blocks in ((128, 65536, 256), (128, 2048, 128), (1, 1, 1)):
+        assert binding.gae_stats_bytes(t, n) == 8 * (4 + 2 * blocks)

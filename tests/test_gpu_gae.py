@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from resident_rl_rollout_amd import binding, inputs
-from tests.gpu_helpers import assert_gae_close
+from tests.gpu_helpers import assert_gae_close, assert_loss_close
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +120,35 @@ def test_deterministic_stats(gpu_lib):
     a2, _, s2 = _run(gi, 1)
     np.testing.assert_array_equal(a1, a2)
     np.testing.assert_array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("t,n", [(128, 65536), (128, 2048), (37, 1000), (1500, 33), (1, 1)])
+def test_deferred_statistics_equal_the_finished_ones(t, n, gpu_lib):
+    # normalize = 3 leaves the scan blocks' partial sums in adv_stats; finishing them (here, and inside the
+    # loss) must give the very bits normalize = 2 gives, and the scan's outputs must not change
+    gi = inputs.make_gae_inputs(30 + t + n, t, n)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    args = (dev(gi.rewards), dev(gi.values), dev(gi.dones), dev(gi.last_values), G, LAM)
+    adv2, ret2, st2 = binding.gae(*args, normalize=2)
+    adv3, ret3, st3 = binding.gae(*args, normalize=3)
+    assert st3.numel() * 8 == binding.gae_stats_bytes(t, n) and float(st3[0]) < 0
+    torch.testing.assert_close(adv3, adv2, rtol=0, atol=0)
+    torch.testing.assert_close(ret3, ret2, rtol=0, atol=0)
+    np.testing.assert_array_equal(binding.adv_stats_finish(st3).cpu().numpy(), st2.cpu().numpy())
+    np.testing.assert_array_equal(binding.adv_stats_finish(st2).cpu().numpy(), st2.cpu().numpy())
+    b = t * n
+    mb = b // next(k for k in (16, 8, 4, 2, 1) if b % k == 0)
+    pi = inputs.make_policy_inputs(31 + t, b)
+    la = (dev(pi.new_logits), dev(pi.actions), dev(pi.old_logp), adv2.reshape(-1), ret2.reshape(-1),
+          dev(pi.new_values))
+    idx = dev(inputs.minibatch_index(pi.perm, mb))
+    for kw in (dict(perm=dev(pi.perm)), dict(perm=None, mb_index=idx), dict(perm=None)):
+        perm = kw.pop("perm")
+        o2 = binding.ppo_loss(*la, perm, mb, adv_stats=st2, **kw).cpu().numpy()
+        o3 = binding.ppo_loss(*la, perm, mb, adv_stats=st3, **kw).cpu().numpy()
+        np.testing.assert_array_equal(o3, o2)
+        g2 = binding.ppo_loss_grad(*la, perm, mb, adv_stats=st2, **kw)
+        g3 = binding.ppo_loss_grad(*la, perm, mb, adv_stats=st3, **kw)
+        for x2, x3 in zip(g2, g3):
+            torch.testing.assert_close(x3, x2, rtol=0, atol=0)
+    np.testing.assert_array_equal(binding.adv_stats_finish(st3).cpu().numpy(), st2.cpu().numpy())

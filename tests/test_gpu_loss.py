@@ -129,10 +129,46 @@ def test_minibatch_numbers_past_the_last_count_as_the_last(b, mb, gpu_lib):
     nmb = b // mb
     idx = inputs.minibatch_index(pi.perm, mb)
     rng = np.random.default_rng(b)
-    last = idx == nmb - 1
-    idx[last] = rng.integers(nmb - 1, 65536, int(last.sum())).astype(np.uint16)
-    assert (idx[last] >= nmb).any() and (idx[last] < 16).any()
+    slots = 16 if nmb <= 16 else (32 if nmb <= 32 else 64)
+    last = np.nonzero(idx == nmb - 1)[0]
+    half = last.size // 2
+    idx[last[:half]] = rng.integers(nmb, slots, half).astype(np.uint16)           # slots the pass never sums
+    idx[last[half:]] = rng.integers(slots, 65536, last.size - half).astype(np.uint16)   # past every slot
     out = binding.ppo_loss(_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret),
                            _dev(pi.new_values), None, mb, mb_index=_dev(idx)).cpu().numpy()
     ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
     assert_loss_close(out, ref, scale, f"B={b} mb={mb} renumbered last minibatch")
+
+
+@pytest.mark.parametrize("b,mb", [(49616, 3101), (1 << 20, 1 << 16), (262144, 4096), (5, 5), (16384 * 5 + 16, 10242)])
+def test_perm_conversion_equals_minibatch_numbers(b, mb, gpu_lib):
+    # the perm is turned into minibatch numbers on the device (binned by destination, 16384 per bin; these
+    # sizes give one bin, several, and ragged last bins); the scalars must equal, bit for bit, those of the
+    # same split given as minibatch numbers, and the oracle's within tolerance
+    pi, adv, ret = _case(b + 7, b)
+    args = (_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret), _dev(pi.new_values))
+    out_perm = binding.ppo_loss(*args, _dev(pi.perm), mb).cpu().numpy()
+    out_idx = binding.ppo_loss(*args, None, mb, mb_index=_dev(inputs.minibatch_index(pi.perm, mb))).cpu().numpy()
+    np.testing.assert_array_equal(out_perm, out_idx)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(out_perm, ref, scale, f"B={b} mb={mb} from perm")
+    _, dl_p, dv_p = binding.ppo_loss_grad(*args, _dev(pi.perm), mb)
+    _, dl_i, dv_i = binding.ppo_loss_grad(*args, None, mb, mb_index=_dev(inputs.minibatch_index(pi.perm, mb)))
+    torch.testing.assert_close(dl_p, dl_i, rtol=0, atol=0)
+    torch.testing.assert_close(dv_p, dv_i, rtol=0, atol=0)
+
+
+
+@pytest.mark.timeout(300)
+def test_perm_conversion_past_the_binned_sizes(gpu_lib):
+    # more than 1024 bins of 16384 samples: the perm takes the direct scatter; the scalars must still equal
+    # those of the same split given as minibatch numbers, and the oracle's within tolerance
+    b = (1 << 24) + (1 << 16)
+    mb = b // 8
+    pi, adv, ret = _case(91, b, a=4)
+    args = (_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret), _dev(pi.new_values))
+    out_perm = binding.ppo_loss(*args, _dev(pi.perm), mb).cpu().numpy()
+    out_idx = binding.ppo_loss(*args, None, mb, mb_index=_dev(inputs.minibatch_index(pi.perm, mb))).cpu().numpy()
+    np.testing.assert_array_equal(out_perm, out_idx)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
+    assert_loss_close(out_perm, ref, scale, f"B={b} mb={mb} from perm (direct scatter)")
