@@ -336,6 +336,22 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
                 const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
                 float ent_coef, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* rl_ppo_loss for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments and results (the same kernels, so the same
+ * bits) without ws / ws_bytes. Its workspace is a fixed 64 MiB array that the library holds on every device
+ * it runs on, from its load until the process ends; the call allocates and frees nothing. The first call
+ * on a device looks up that device's copy of the array (the device current at the call; `stream`, if not
+ * NULL, must belong to it, else RL_EINVAL). A call whose workspace (rl_ppo_loss_workspace_bytes, less the
+ * perm conversion's part when perm is NULL) exceeds 64 MiB returns RL_ESIZE and launches nothing: at
+ * 16 minibatches that admits a perm up to 2^23 samples; mb_index any size (its partials take at most
+ * 1.2 MB); contiguous minibatches while their partials (24 bytes per minibatch and block) fit. Every call on one device shares that device's array and keeps
+ * no state in it between calls (nothing in it must start at zero): calls that overlap on one device, on
+ * different streams or from different host threads without ordering, race on it. */
+int rl_ppo_loss_noalloc(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                        const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                        const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                        float ent_coef, float* out, void* stream);
+
 /* rl_ppo_loss plus, in the same pass, the gradient of each minibatch's total loss
  * L_m = mean pg + vf_coef * mean v - ent_coef * mean H with respect to the logits and the value of every
  * sample of m (the next step of the learn phase in "Teaching Mario to speedrun", s.6; the loss and its

@@ -83,6 +83,8 @@ SIGNATURES = [
     ("rl_ppo_loss_workspace_bytes", ctypes.c_int, [_I64, _I32, ctypes.POINTER(_SZ)]),
     ("rl_ppo_loss", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32, _P,
                                    _P, _SZ, _P]),
+    ("rl_ppo_loss_noalloc", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32,
+                                           _P, _P]),
     ("rl_ppo_loss_grad", ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _F32,
                                         _P, _P, _P, _P, _SZ, _P]),
     ("rl_policy_weights_bytes", ctypes.c_int, [ctypes.POINTER(_SZ)]),
@@ -388,6 +390,22 @@ def ppo_loss(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, c
                             dptr(adv_stats, torch.float64, "adv_stats"),
                             b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
                             dptr(out, torch.float32, "out"), dptr(ws), ws.numel(), stream_ptr(stream)))
+    return out
+
+
+def ppo_loss_noalloc(logits, actions, old_logp, adv, ret, new_values, perm, minibatch, clip_eps=0.2, vf_coef=0.5,
+                     ent_coef=0.01, adv_stats=None, out=None, stream=None, mb_index=None):
+    """rl_ppo_loss_noalloc: ppo_loss with the library's fixed device workspace instead of a workspace
+    argument (pass `out` to allocate nothing here either)."""
+    b, a = logits.shape
+    out = torch.empty((b // minibatch, 4), dtype=torch.float32, device=logits.device) if out is None else out
+    check(lib().rl_ppo_loss_noalloc(dptr(logits, torch.float32, "logits"), dptr(actions, torch.int32, "actions"),
+                                    dptr(old_logp, torch.float32, "old_logp"), dptr(adv, torch.float32, "adv"),
+                                    dptr(ret, torch.float32, "ret"), dptr(new_values, torch.float32, "new_values"),
+                                    dptr(perm, torch.int32, "perm"), dptr(mb_index, torch.uint16, "mb_index"),
+                                    dptr(adv_stats, torch.float64, "adv_stats"),
+                                    b, a, minibatch, float(clip_eps), float(vf_coef), float(ent_coef),
+                                    dptr(out, torch.float32, "out"), stream_ptr(stream)))
     return out
 
 

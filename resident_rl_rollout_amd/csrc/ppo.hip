@@ -31,6 +31,7 @@
 // normalised or not, are constants.
 
 #include <algorithm>
+#include <mutex>
 
 #include "rl_internal.hpp"
 
@@ -772,13 +773,23 @@ void launch_loss(const LossArgs& p, int64_t num_mb, int A, bool stream_mode, int
     }
 }
 
+// Workspace bytes one call needs: the partials, and the perm's conversion only when a perm is given
+// (rl_ppo_loss_workspace_bytes covers both).
+int call_workspace_bytes(int64_t B, int32_t mb, bool with_perm, size_t* bytes)
+{
+    if (int rc = rl_ppo_loss_workspace_bytes(B, mb, bytes)) return rc;
+    const int64_t num_mb = B / mb;
+    if (!with_perm && num_mb <= kStreamMaxMinibatches) *bytes -= perm_bytes(B);
+    return RL_OK;
+}
+
 int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
                   const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
                   const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
                   float ent_coef, float* out, float* dlogits, float* dvalues, void* ws, size_t ws_bytes, void* stream)
 {
     size_t need = 0;
-    if (int rc = rl_ppo_loss_workspace_bytes(B, mb, &need)) return rc;
+    if (int rc = call_workspace_bytes(B, mb, perm != nullptr, &need)) return rc;
     if (A < 1 || A > 64) return rl::fail(RL_EINVAL, "A %d outside [1, 64]", A);
     if (B * (int64_t)A > ((int64_t)1 << 40)) return rl::fail(RL_EINVAL, "B*A too large");
     if (!logits || !actions || !old_logp || !adv || !ret || !new_values || !out || !ws)
@@ -874,9 +885,63 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
     return rl::check_launch("ppo_finalize");
 }
 
+// The no-allocation loss's workspace: a fixed array that every device the library runs on holds from the
+// library's load until the process ends. Host code never uses the array's name as an address (on the host
+// it names a stand-in, not device memory): the first call on each device looks up that device's copy.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device with that device current.
+int scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return rl::fail(RL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return rl::fail(RL_EINVAL, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return rl::fail(RL_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RL_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int rl_ppo_loss_noalloc(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
+                        const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,
+                        const double* adv_stats, int64_t B, int32_t A, int32_t mb, float clip_eps, float vf_coef,
+                        float ent_coef, float* out, void* stream)
+{
+    size_t need = 0;
+    if (int rc = call_workspace_bytes(B, mb, perm != nullptr, &need)) return rc;
+    if (need > kScratchBytes)
+        return rl::fail(RL_ESIZE, "this loss needs %zu bytes of workspace, more than the %zu bytes of the fixed device "
+                                  "array of rl_ppo_loss_noalloc: call rl_ppo_loss with a workspace",
+                        need, kScratchBytes);
+    void* ws = nullptr;
+    if (int rc = scratch_on_current_device(&ws)) return rc;
+    if (stream) {   // the array's address is the current device's: the work must run there
+        int cur = -1;
+        hipDevice_t sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(rl::as_stream(stream), &sdev) != hipSuccess)
+            return rl::fail(RL_EHIP, "could not query the current device or the stream's device");
+        if (sdev != cur)
+            return rl::fail(RL_EINVAL, "stream belongs to device %d, the current device is %d", (int)sdev, cur);
+    }
+    return ppo_loss_impl(logits, actions, old_logp, adv, ret, new_values, perm, mb_index, adv_stats, B, A, mb, clip_eps,
+                         vf_coef, ent_coef, out, nullptr, nullptr, ws, kScratchBytes, stream);
+}
 
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv, const float* ret,
                 const float* new_values, const int32_t* perm, const uint16_t* mb_index, const double* adv_stats,
