@@ -354,9 +354,10 @@ def cpu_info():
 def hbm_ceiling(torch, binding, dev, store_bytes, row_chunk, reps=9):
     """Same-run ceilings of plain HBM traffic, medians of `reps` timed launches: stores of `store_bytes`
     (the observation bytes of one env step) into successive slices of a 4 GiB buffer (so that no slice is
-    still cached when it is written again) by torch's fill and by the library's store probe at two
-    granularities (4 KB per block, and `row_chunk` bytes per block: what one env-step block writes), a
-    1 GiB device-to-device copy (read + write bytes counted), and a 1 GiB sum (a reduction's read)."""
+    still cached when it is written again) by torch's fill and by the library's store probe at several
+    granularities (bytes one block writes before it exits: 4 KB, 16 KB, `row_chunk` = what one env-step
+    block writes, and four times that), a 1 GiB device-to-device copy (read + write bytes counted), a 1 GiB
+    sum (a reduction's read), and the library's read probe over 1 GiB at 4 KB, 64 KB and 1 MB per block."""
     slab = torch.empty(1 << 30, dtype=torch.float32, device=dev)
     n = store_bytes // 4
     nslices = (1 << 30) // n
@@ -375,11 +376,19 @@ def hbm_ceiling(torch, binding, dev, store_bytes, row_chunk, reps=9):
     store = [timed(lambda i=i: slab[(i % nslices) * n:(i % nslices + 1) * n].fill_(1.0)) for i in range(reps + 1)][1:]
     n16 = n // 4 * 4   # 16-byte multiple of the slice
     chunks = {}
-    for name, chunk in (("4KB", 4096), ("env_block", row_chunk)):
+    store_sizes = {"4KB": 4096, "16KB": 16384, "env_block": row_chunk, "4_env_blocks": 4 * row_chunk}
+    for name, chunk in store_sizes.items():
         chunks[name] = [timed(lambda i=i: binding.store_probe(slab[(i % nslices) * n:(i % nslices) * n + n16], chunk))
                         for i in range(reps + 1)][1:]
     copy = [timed(lambda: dst.copy_(src)) for _ in range(reps + 1)][1:]
     read = [timed(lambda: src.sum()) for _ in range(reps + 1)][1:]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    reads = {}
+    read_sizes = {"4KB": 4096, "64KB": 1 << 16, "1MB": 1 << 20}
+    for name, chunk in read_sizes.items():
+        # successive 1 GiB quarters of the 4 GiB buffer, so that no read finds its bytes cached
+        reads[name] = [timed(lambda i=i: binding.read_probe(slab[(i % 4) * (1 << 28):(i % 4 + 1) * (1 << 28)], chunk,
+                                                             sink)) for i in range(reps + 1)][1:]
     del slab
     torch.cuda.empty_cache()
     gbs = lambda nbytes, ts: nbytes / float(np.median(ts)) / 1e9
@@ -387,7 +396,11 @@ def hbm_ceiling(torch, binding, dev, store_bytes, row_chunk, reps=9):
             "store_4KB_blocks_GB/s": gbs(n16 * 4, chunks["4KB"]),
             "store_env_block_GB/s": gbs(n16 * 4, chunks["env_block"]), "env_block_bytes": row_chunk,
             "copy_GB/s": gbs(2 * (1 << 30), copy), "sum_read_GB/s": gbs(1 << 30, read),
-            "kernels": "torch fill_ (store), rl_store_probe (store_4KB_blocks, store_env_block), torch copy_, torch sum",
+            "read_4KB_blocks_GB/s": gbs(1 << 30, reads["4KB"]), "read_1MB_blocks_GB/s": gbs(1 << 30, reads["1MB"]),
+            "store_probe_sweep_GB/s": {f"{v}B": gbs(n16 * 4, chunks[k]) for k, v in store_sizes.items()},
+            "read_probe_sweep_GB/s": {f"{v}B": gbs(1 << 30, reads[k]) for k, v in read_sizes.items()},
+            "kernels": "torch fill_ (store), rl_store_probe (store_4KB_blocks, store_env_block), torch copy_, "
+                       "torch sum, rl_read_probe (read_4KB_blocks, read_1MB_blocks)",
             "reps": reps, "peak_GB/s": HBM_PEAK_GBS}
 
 
@@ -995,8 +1008,10 @@ def main():
                                               "launches": int(per_launch_us.size)},
         "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
                 "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_us": scan_s * 1e6, "scan_GB/s": scan_gbs,
-                "scan_frac": scan_gbs / HBM_PEAK_GBS, "scan_traffic": load_traffic("gae_scan")},
+                "scan_frac": scan_gbs / HBM_PEAK_GBS, "scan_frac_of_copy_ceiling": scan_gbs / ceiling["copy_GB/s"],
+                "scan_traffic": load_traffic("gae_scan")},
         "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
+                 "frac_of_read_ceiling": loss_gbs / ceiling["read_1MB_blocks_GB/s"],
                  "us_in_rollout": float(loss_ms.mean()) * 1e3,
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
         "loss_perm": {"us": perm_s * 1e6, "GB/s": perm_bytes / perm_s / 1e9,

@@ -457,6 +457,13 @@ int rl_rollout(const void* packed, uint64_t seed, const rl_rollout_group* groups
  * ceiling for that granularity on the same device in the same run. */
 int rl_store_probe(void* buf, int64_t bytes, int64_t chunk, void* stream);
 
+/* Plain loads for the same purpose: `bytes` (a multiple of 16) of `buf` (device, 16-byte aligned) read with
+ * 16-byte loads, one `chunk`-byte piece (a multiple of 16) per 256-thread block. Each block folds its words
+ * by XOR and writes *sink (device uint32) only if the fold equals 0x9E3779B9, which keeps the loads and
+ * never happens for a buffer of zeros. Timed beside a read-bound kernel, it is the read ceiling of that
+ * granularity in the same run. Errors: RL_EINVAL (NULL, sizes), RL_EALIGN. */
+int rl_read_probe(const void* buf, int64_t bytes, int64_t chunk, uint32_t* sink, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* rl_last_error(void);
 

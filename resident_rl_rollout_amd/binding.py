@@ -92,6 +92,7 @@ SIGNATURES = [
     ("rl_policy_forward", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_uint64, _I64, _I64, _P, _P, _P, _P]),
     ("rl_rollout", ctypes.c_int, [_P, ctypes.c_uint64, ctypes.POINTER(RolloutGroup), _I32, _I32, _I32, _I32]),
     ("rl_store_probe", ctypes.c_int, [_P, _I64, _I64, _P]),
+    ("rl_read_probe", ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     ("rl_last_error", ctypes.c_char_p, []),
 ]
 
@@ -503,6 +504,13 @@ def rollout(policy, groups, t0, steps, alternate=True):
     arr = (RolloutGroup * len(groups))(*groups)
     check(lib().rl_rollout(dptr(policy.packed), policy.seed, arr, len(groups), int(t0), int(steps),
                            1 if alternate else 0))
+
+
+def read_probe(buf, chunk, sink, stream=None):
+    """rl_read_probe over a device tensor: 16-byte loads, one `chunk`-byte contiguous chunk per block; `sink`
+    is a device uint32 / int32 tensor of at least one element."""
+    nbytes = buf.numel() * buf.element_size()
+    check(lib().rl_read_probe(dptr(buf), nbytes, int(chunk), dptr(sink), stream_ptr(stream)))
 
 
 def store_probe(buf, chunk, stream=None):

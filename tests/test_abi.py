@@ -188,6 +188,19 @@ def test_store_probe_rejects_bad_arguments():
     assert "multiples of 16" in lib.rl_last_error().decode()
 
 
+def test_read_probe_rejects_bad_arguments():
+    lib = binding.lib()
+    buf = ctypes.c_void_p(4096)   # never dereferenced: every call below fails its checks first
+    sink = ctypes.c_void_p(8192)
+    assert lib.rl_read_probe(None, 64, 16, sink, None) == -1
+    assert lib.rl_read_probe(buf, 64, 16, None, None) == -1
+    assert lib.rl_read_probe(ctypes.c_void_p(4100), 64, 16, sink, None) == -2
+    assert lib.rl_read_probe(buf, 64, 16, ctypes.c_void_p(8194), None) == -2
+    assert lib.rl_read_probe(buf, 60, 16, sink, None) == -1
+    assert lib.rl_read_probe(buf, 64, 24, sink, None) == -1
+    assert "multiples of 16" in lib.rl_last_error().decode()
+
+
 def test_deferred_statistics_size():
     # a header of 4 doubles, then (sum A, sum A^2) of every scan block: 256 blocks of 256 envs at 65536 x
     # 128, 128 blocks of 16 envs at 2048 x 128, 1 block of 16 envs at one env
