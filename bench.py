@@ -62,12 +62,12 @@ LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, ol
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10, help="timed rollouts")
-    p.add_argument("--warmup", type=int, default=2, help="untimed rollouts")
+    p.add_argument("--steps", type=int, default=20, help="timed rollouts")
+    p.add_argument("--warmup", type=int, default=5, help="untimed rollouts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-envs", type=int, default=None,
                    help="envs in the oracle's bounded sample (default 16384 for the rollout, 512 for pixels)")
-    p.add_argument("--iso-reps", type=int, default=7, help="isolated GAE / loss repetitions (median reported)")
+    p.add_argument("--iso-reps", type=int, default=20, help="isolated GAE / loss repetitions (median and min reported)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy, whose rocprofv3 FETCH_SIZE / WRITE_SIZE "
                         "scale the counters of the other kernels")
@@ -402,6 +402,75 @@ def hbm_ceiling(torch, binding, dev, store_bytes, row_chunk, reps=9):
             "kernels": "torch fill_ (store), rl_store_probe (store_4KB_blocks, store_env_block), torch copy_, "
                        "torch sum, rl_read_probe (read_4KB_blocks, read_1MB_blocks)",
             "reps": reps, "peak_GB/s": HBM_PEAK_GBS}
+
+
+def tiny_record(torch, binding, inputs, dev, steps, warmup):
+    """The tiny workload (N = 64, T = 128, one 32 x 128 map): rollouts of 128 env steps into a resident buffer,
+    then GAE with the deferred statistics. Launch-latency bound (64 envs fill one wave), so not an HBM test;
+    per-rollout event pairs, median and min."""
+    t, n = HORIZON, 64
+    ms1 = inputs.make_mapset([1], 32, 128)
+    env = binding.Env(ms1.maps, ms1.ckpts, ms1.spawns, n, frame_skip=3, time_limit=2000, device=dev)
+    acts = torch.from_numpy(np.ascontiguousarray(inputs.make_actions(2, t, n), np.int32)).to(dev)
+    values, last = inputs.make_values(3, t, n)
+    values_d, last_d = torch.from_numpy(values).to(dev), torch.from_numpy(last).to(dev)
+    obs = torch.empty((t, n, binding.OBS_TILES_SIZE), dtype=torch.float32, device=dev)
+    rew = torch.empty((t, n), dtype=torch.float32, device=dev)
+    dn = torch.empty_like(rew)
+    adv, ret = torch.empty_like(rew), torch.empty_like(rew)
+    stats = torch.zeros(binding.gae_stats_bytes(t, n) // 8, dtype=torch.float64, device=dev)
+    env.reset(obs[0])
+    times = []
+    for k in range(warmup + steps):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(t):
+            env.step(acts[i], obs[i], rew[i], dn[i])
+        binding.gae(rew, values_d, dn, last_d, GAMMA, LAMBDA, normalize=3, adv=adv, ret=ret, adv_stats=stats)
+        z.record()
+        torch.cuda.synchronize()
+        if k >= warmup:
+            times.append(a.elapsed_time(z))
+    env.close()
+    ms_ = np.array(times)
+    return {"workload": "tiny: 64 envs x 128 steps on one seeded 32x128 map (seed 1), actions (2), values (3), "
+                        "GAE with the deferred statistics; launch-latency bound, not an HBM test",
+            "value": t * n / (float(np.median(ms_)) * 1e-3), "unit": "env-steps/s",
+            "rollout_ms": {"median": float(np.median(ms_)), "min": float(ms_.min())},
+            "us_per_env_step_launch": float(np.median(ms_)) * 1e3 / t, "steps": steps, "warmup": warmup}
+
+
+def env_episodes_record(torch, binding, inputs, dev, ms):
+    """The env-step workload as its own run: 65536 envs on the 64 bench maps, 16 warm-up steps then 1334 timed
+    steps (two whole 667-decision episodes at the 2000-tick limit, so every env resets inside the timed span),
+    each writing its observations into one resident [N][1397] block. One event pair around the 1334 launches."""
+    warm, timed, n = 16, 1334, N_ENVS
+    env = binding.Env(ms.maps, ms.ckpts, ms.spawns, n, frame_skip=3, time_limit=2000, device=dev)
+    acts = torch.from_numpy(np.ascontiguousarray(inputs.make_actions(4, warm + timed, n), np.int32)).to(dev)
+    obs = torch.empty((n, binding.OBS_TILES_SIZE), dtype=torch.float32, device=dev)
+    rew = torch.empty((warm + timed, n), dtype=torch.float32, device=dev)
+    dn = torch.empty_like(rew)
+    env.reset(obs)
+    for i in range(warm):
+        env.step(acts[i], obs, rew[i], dn[i])
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(warm, warm + timed):
+        env.step(acts[i], obs, rew[i], dn[i])
+    z.record()
+    torch.cuda.synchronize()
+    ms_ = a.elapsed_time(z)
+    ends = int(dn[warm:].sum().item())
+    env.close()
+    per_s = ms_ * 1e-3 / timed
+    achieved = n * ENV_BYTES_PER_ENV_STEP / per_s / 1e9
+    return {"workload": "env step: 65536 envs on 64 seeded 256x1024 maps, actions (seed 4), frame-skip 3, 2000-tick "
+                        "limit, 16 warm-up + 1334 timed steps, obs f32[N][1397] rewritten each step",
+            "value": timed * n / (ms_ * 1e-3), "unit": "env-steps/s", "ms": ms_, "avg_launch_us": per_s * 1e6,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS},
+            "episode_ends_in_timed_span": ends}
 
 
 def config2_record(torch, binding, inputs, dev, reps):
@@ -937,6 +1006,8 @@ def main():
     torch.cuda.empty_cache()
     ceiling = hbm_ceiling(torch, binding, dev, N_ENVS * 1397 * 4, 16 * 1397 * 4)
     cfg2 = config2_record(torch, binding, inputs, dev, args.iso_reps)
+    cfg1 = tiny_record(torch, binding, inputs, dev, 20, 5)
+    cfg3 = env_episodes_record(torch, binding, inputs, dev, ms)
 
     env_ms = np.array([ev["env"][0].elapsed_time(ev["env"][1]) / HORIZON for ev in events])   # per launch
     gae_ms = np.array([ev["gae"][0].elapsed_time(ev["gae"][1]) for ev in events])
@@ -1006,15 +1077,18 @@ def main():
         "env_launch_us_one_event_pair_each": {"median": float(np.median(per_launch_us)),
                                               "min": float(per_launch_us.min()), "max": float(per_launch_us.max()),
                                               "launches": int(per_launch_us.size)},
-        "gae": {"us": gae_s * 1e6, "GB/s": gae_gbs, "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
-                "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_us": scan_s * 1e6, "scan_GB/s": scan_gbs,
+        "gae": {"us": gae_s * 1e6, "min_us": float(np.min(iso["gae"])) * 1e3, "GB/s": gae_gbs,
+                "frac": gae_gbs / HBM_PEAK_GBS, "bytes": gae_bytes,
+                "us_in_rollout": float(gae_ms.mean()) * 1e3, "scan_us": scan_s * 1e6,
+                "scan_min_us": float(np.min(iso["scan"])) * 1e3, "scan_GB/s": scan_gbs,
                 "scan_frac": scan_gbs / HBM_PEAK_GBS, "scan_frac_of_copy_ceiling": scan_gbs / ceiling["copy_GB/s"],
                 "scan_traffic": load_traffic("gae_scan")},
-        "loss": {"us": loss_s * 1e6, "GB/s": loss_gbs, "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
+        "loss": {"us": loss_s * 1e6, "min_us": float(np.min(iso["loss"])) * 1e3, "GB/s": loss_gbs,
+                 "frac": loss_gbs / HBM_PEAK_GBS, "bytes": loss_bytes,
                  "frac_of_read_ceiling": loss_gbs / ceiling["read_1MB_blocks_GB/s"],
                  "us_in_rollout": float(loss_ms.mean()) * 1e3,
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
-        "loss_perm": {"us": perm_s * 1e6, "GB/s": perm_bytes / perm_s / 1e9,
+        "loss_perm": {"us": perm_s * 1e6, "min_us": float(np.min(iso["perm"])) * 1e3, "GB/s": perm_bytes / perm_s / 1e9,
                       "frac": perm_bytes / perm_s / 1e9 / HBM_PEAK_GBS, "bytes": perm_bytes,
                       "vs_minibatch_numbers": None if stream_s is None else perm_s / stream_s},
         "loss_grad": {"us": grad_s * 1e6, "GB/s": grad_gbs, "frac": grad_gbs / HBM_PEAK_GBS, "bytes": grad_bytes,
@@ -1028,6 +1102,8 @@ def main():
         "cpu_baseline_all_cores": cpu_all,
         "host": cpu_info(),
         "gae_ppo_n2048": cfg2,
+        "tiny_n64": cfg1,
+        "env_n65536_1334_steps": cfg3,
     }
     if not args.no_pixels:   # the pixel workload's own rate beside the headline (a short run of it)
         pix_actions = inputs.make_actions(22, HORIZON, PIX_ENVS)
