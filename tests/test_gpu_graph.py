@@ -134,3 +134,56 @@ def test_counter_set_before_capture_is_refused_inside_it(gpu_lib):
     graph2.replay()
     torch.cuda.synchronize()
     assert int(env.read_step_counter()[0]) == 43
+
+
+def test_captured_learn_phase_replays_bit_for_bit(gpu_lib):
+    # GAE with the deferred statistics, the loss from a permutation (its binned conversion) and the loss
+    # gradient from minibatch numbers, recorded into one graph: no call may allocate, synchronise or leave
+    # a memset in the graph, so every replay must give the eager call's bits. Outputs are poisoned before
+    # each replay; eager work and a synchronisation run between the replays.
+    t, n = 64, 4096
+    b, mb = t * n, t * n // 16
+    gi = inputs.make_gae_inputs(61, t, n)
+    pi = inputs.make_policy_inputs(62, b)
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    r, v, dn, lv = d(gi.rewards), d(gi.values), d(gi.dones), d(gi.last_values)
+    logits, acts, old, nv, perm = d(pi.new_logits), d(pi.actions), d(pi.old_logp), d(pi.new_values), d(pi.perm)
+    idx = d(inputs.minibatch_index(pi.perm, mb))
+    adv = torch.empty((t, n), dtype=torch.float32, device="cuda")
+    ret = torch.empty_like(adv)
+    stats = torch.zeros(binding.gae_stats_bytes(t, n) // 8, dtype=torch.float64, device="cuda")
+    out = torch.empty((16, 4), dtype=torch.float32, device="cuda")
+    out_g = torch.empty_like(out)
+    dl = torch.empty((b, 12), dtype=torch.float32, device="cuda")
+    dv = torch.empty(b, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(binding.ppo_loss_workspace_bytes(b, mb), dtype=torch.uint8, device="cuda")
+
+    def learn():
+        binding.gae(r, v, dn, lv, 0.99, 0.95, normalize=3, adv=adv, ret=ret, adv_stats=stats)
+        binding.ppo_loss(logits, acts, old, adv.view(-1), ret.view(-1), nv, perm, mb, adv_stats=stats, out=out,
+                         ws=ws)
+        binding.ppo_loss_grad(logits, acts, old, adv.view(-1), ret.view(-1), nv, None, mb, adv_stats=stats,
+                              out=out_g, dlogits=dl, dvalues=dv, ws=ws, mb_index=idx)
+
+    learn()
+    torch.cuda.synchronize()
+    outs = (adv, ret, out, out_g, dl, dv)
+    want = [x.clone() for x in outs]
+    want_stats = stats.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        learn()
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        stats[:2].fill_(float("nan"))     # the header's spare doubles are never written
+        stats[4:].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, w in zip(("adv", "ret", "loss", "loss of the gradient call", "dlogits", "dvalues"), outs, want):
+            torch.testing.assert_close(x, w, rtol=0, atol=0, msg=f"replay {rep}: {name}")
+        torch.testing.assert_close(stats, want_stats, rtol=0, atol=0, msg=f"replay {rep}: statistics")
+        (torch.ones(1 << 20, device="cuda") * 3.0).sum().item()
