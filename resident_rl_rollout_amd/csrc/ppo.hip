@@ -236,9 +236,10 @@ __device__ __forceinline__ void terms_of(const LossArgs& p, int64_t i, bool writ
     const float ratio = exp_hw(logp - s.old_logp);
     float adv = s.adv;
     if (p.stats) adv = (adv - mean) * scale;
-    const float clipped = fminf(fmaxf(ratio, p.clip_lo), p.clip_hi);
+    // clip and minimum by comparisons, which pass a NaN ratio on (fminf / fmaxf would drop it)
+    const float clipped = ratio < p.clip_lo ? p.clip_lo : (ratio > p.clip_hi ? p.clip_hi : ratio);
     const float s1 = ratio * adv, s2 = clipped * adv;
-    *pg = -fminf(s1, s2);
+    *pg = -(s1 < s2 ? s1 : s2);
     const float dv = s.v - s.ret;
     *v = dv * dv;
     if constexpr (GRAD) {

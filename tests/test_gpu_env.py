@@ -48,6 +48,21 @@ def test_short_time_limit_and_finish_resets(gpu_lib):
     assert done_total > 0
 
 
+def test_time_limit_one_ends_every_decision(gpu_lib):
+    # every decision is one tick, truncated, and resets in place: all dones set every step, state and
+    # observations those of the oracle (the new episodes' first)
+    ms = inputs.make_mapset([4, 5, 6], 48, 96)
+    pe = PairedEnvs(ms, 301, time_limit=1)
+    acts = inputs.make_actions(12, 20, 301)
+    pe.check_obs("tl=1 reset")
+    for s, a in enumerate(acts):
+        r, d = pe.step(a)
+        pe.check_step(r, d, f"tl=1 step {s}")
+        assert (d == 1.0).all()
+        pe.check_state(f"tl=1 step {s}")
+        pe.check_obs(f"tl=1 step {s}")
+
+
 @pytest.mark.parametrize("fs", [1, 2, 5])
 def test_frame_skip_settings(fs, gpu_lib):
     ms = inputs.make_mapset([4, 5], 48, 96)

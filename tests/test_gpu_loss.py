@@ -172,3 +172,25 @@ def test_perm_conversion_past_the_binned_sizes(gpu_lib):
     np.testing.assert_array_equal(out_perm, out_idx)
     ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, pi.perm, mb)
     assert_loss_close(out_perm, ref, scale, f"B={b} mb={mb} from perm (direct scatter)")
+
+@pytest.mark.parametrize("mode", ["perm", "stream", "contiguous"])
+def test_nan_logits_spoil_only_their_minibatch(mode, gpu_lib):
+    # a NaN in one sample's logits makes its minibatch's policy, entropy and total terms NaN and leaves the
+    # value term and every other minibatch finite, as in the oracle (no crash, no spread across minibatches)
+    b, mb = 65536, 8192
+    pi, adv, ret = _case(77, b)
+    logits = pi.new_logits.copy()
+    s = int(pi.perm[3 * mb + 5]) if mode != "contiguous" else 3 * mb + 5    # a sample of minibatch 3
+    logits[s, 7] = np.nan
+    args = (_dev(logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret), _dev(pi.new_values))
+    if mode == "perm":
+        out = binding.ppo_loss(*args, _dev(pi.perm), mb).cpu().numpy()
+    elif mode == "stream":
+        out = binding.ppo_loss(*args, None, mb, mb_index=_dev(inputs.minibatch_index(pi.perm, mb))).cpu().numpy()
+    else:
+        out = binding.ppo_loss(*args, None, mb).cpu().numpy()
+    ref, _ = oracle.ppo_loss(logits, pi.actions, pi.old_logp, adv, ret, pi.new_values,
+                             None if mode == "contiguous" else pi.perm, mb)
+    assert np.isnan(out[3, [0, 2, 3]]).all() and np.isfinite(out[3, 1])
+    np.testing.assert_array_equal(np.isnan(out), np.isnan(ref))
+    assert np.isfinite(np.delete(out, 3, axis=0)).all()

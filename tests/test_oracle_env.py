@@ -194,6 +194,16 @@ def test_time_limit_truncates_on_tick_2000():
     assert e.state[0, F["tick"]] == 0
 
 
+def test_time_limit_one_ends_every_decision():
+    # a 1-tick limit: every decision runs one tick, is truncated and resets at the spawn; standing still
+    # earns only the time penalty, a rightward tick 8 sub-units of progress less it
+    e = make_env(flat_map(), fs=3, tl=1)
+    for a, units in ((NOOP, -1), (RIGHT, 8 - 1), (RIGHT, 8 - 1), (LEFT, -1)):
+        rew, done = e.step([a])
+        assert rew[0] == units / 1024 and done[0] == 1
+        assert e.state[0, F["tick"]] == 0 and e.state[0, F["x"]] == 256 and e.state[0, F["vx"]] == 0
+
+
 def test_out_of_range_actions_are_noops():
     m = inputs.make_map(5, 32, 64)[0]
     e1 = make_env(m, n=4, fs=3, spawn=(256, (32 - 8) * 256 - 192))
