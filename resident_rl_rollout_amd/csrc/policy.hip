@@ -160,8 +160,8 @@ __global__ __launch_bounds__(ROWS * 4) void k_policy_forward(PolicyArgs p)
     for (int c = 0; c < kChunks; ++c) {
         __syncthreads();   // the previous chunk's fragments have been read
         store_chunk();
+        if (c + 1 < kChunks) load_chunk(c + 1);   // the registers are free: in flight across the barrier
         __syncthreads();
-        if (c + 1 < kChunks) load_chunk(c + 1);
         // A fragment: row 32 rh + (l & 31), k 8 (l >> 5) .. +7 of each 16-step; B: column (l & 31) of
         // each tile, the same k
         const uint16_t* pa = As + (rh * 32 + (l & 31)) * kPitch + 8 * (l >> 5);
