@@ -206,3 +206,15 @@ def test_deferred_statistics_size():
     # 128, 128 blocks of 16 envs at 2048 x 128, 1 block of 16 envs at one env
     for t, n, blocks in ((128, 65536, 256), (128, 2048, 128), (1, 1, 1)):
         assert binding.gae_stats_bytes(t, n) == 8 * (4 + 2 * blocks)
+
+
+def test_noalloc_loss_refuses_before_any_device_call():
+    # the size checks of rl_ppo_loss_noalloc run before it looks up its device array, so they answer on a
+    # machine without a GPU; the pointers are never dereferenced
+    lib = binding.lib()
+    p = ctypes.c_void_p(4096)
+    args = lambda b, mb, perm: (p, p, p, p, p, p, perm, None, None, b, 12, mb, 0.2, 0.5, 0.01, p, None)
+    assert lib.rl_ppo_loss_noalloc(*args(1000, 300, None)) == -1                  # B not a multiple of mb
+    assert "multiple" in lib.rl_last_error().decode()
+    assert lib.rl_ppo_loss_noalloc(*args(1 << 24, 1 << 20, p)) == -3              # 112 MiB with a perm
+    assert "fixed device array" in lib.rl_last_error().decode()
