@@ -22,7 +22,7 @@ def _rollout(seed, t, n):
 
 @pytest.mark.parametrize("t,n,n0,w", [(128, 65536, 4096, 8192), (128, 4096, 1000, 333), (37, 1000, 13, 211),
                                       (600, 512, 100, 64), (1, 300, 7, 5)])
-@pytest.mark.parametrize("normalize", [0, 1, 2])
+@pytest.mark.parametrize("normalize", [0, 1, 2, 3])
 def test_gae_on_a_column_range(gpu_lib, t, n, n0, w, normalize):
     r, v, d, vl = _rollout(t + n + w, t, n)
     fresh = v.clone()
@@ -38,6 +38,11 @@ def test_gae_on_a_column_range(gpu_lib, t, n, n0, w, normalize):
     assert torch.equal(adv[:, sl], a2) and torch.equal(ret[:, sl], r2)
     if normalize:
         assert torch.equal(st, st2)
+    if normalize == 3:
+        # the deferred partial sums of a column range finish to the statistics normalize = 2 leaves
+        _, _, st_fin = binding.gae(r[:, sl].contiguous(), fresh[:, sl].contiguous(), d[:, sl].contiguous(),
+                                   vl[sl].contiguous(), G, L, normalize=2)
+        assert torch.equal(binding.adv_stats_finish(st), st_fin)
     others = torch.ones(n, dtype=torch.bool)
     others[sl] = False
     assert (adv[:, others.cuda()] == -7.0).all() and (ret[:, others.cuda()] == -7.0).all()
