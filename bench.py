@@ -56,7 +56,11 @@ POLICY_BYTES_PER_ENV = 1397 * 4 + 3 * 4               # 5600
 POLICY_WEIGHT_BYTES = 128 * 1408 * 2 + 13 * 128 * 4   # 367104
 POLICY_SEED = 31
 LOSS_BYTES_PER_SAMPLE = {"stream": 12 * 4 + 5 * 4 + 2,  # logits row; action, old logp, adv, ret, value; minibatch id
-                         "perm": 12 * 4 + 6 * 4 + 2 + 2}  # ... the permutation entry, its minibatch id written and read
+                         # up to 16 minibatches: the same without the id, + the permutation entry read, its
+                         # sorted entry written and read back (the stream blocks place their own numbers)
+                         "perm": 12 * 4 + 5 * 4 + 3 * 4,
+                         # 17 to 64: + the 2-byte minibatch id written (and read, as in "stream")
+                         "perm_placed": 12 * 4 + 5 * 4 + 2 + 3 * 4 + 2}
 
 
 def parse():
@@ -498,7 +502,7 @@ def config2_record(torch, binding, inputs, dev, reps):
     }
     res = {"workload": "GAE+PPO: N=2048, T=128, minibatch 8192 (32 minibatches), perm seeded; cache-resident, "
                        "latency-bound (not an HBM test)"}
-    nbytes = {"gae": b * GAE_BYTES_PER_ELEM + n * 4, "loss_perm": b * LOSS_BYTES_PER_SAMPLE["perm"],
+    nbytes = {"gae": b * GAE_BYTES_PER_ELEM + n * 4, "loss_perm": b * LOSS_BYTES_PER_SAMPLE["perm_placed"],
               "loss_stream": b * LOSS_BYTES_PER_SAMPLE["stream"]}
     for name, fn in calls.items():
         for _ in range(3):

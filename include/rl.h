@@ -327,9 +327,10 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes);
  *   (identical results from run to run): with mb_index (and perm converted to it) each thread first adds
  *   at most 256 of its samples into float32 sums per minibatch (a rounding error of at most 256 * 2^-24,
  *   1.5e-5, of the summed magnitudes), which are then reduced in float64; the gather path adds every term in
- *   float64. With mb_index every input is read once, in storage order. With perm and at most 64 minibatches the perm is first turned into each
- *   sample's minibatch number (in the workspace) and the samples are then read the same way; with more
- *   minibatches every read is a gather. perm entries outside [0, B) are clamped into it (a permutation
+ *   float64. With mb_index every input is read once, in storage order. With perm and at most 64 minibatches the perm is first sorted into bins by
+ *   destination (in the workspace), each sample's minibatch number is placed from them (in LDS up to 16
+ *   minibatches, else in the workspace) and the samples are then read the same way, with the same bits as
+ *   the equivalent mb_index; with more minibatches every read is a gather. perm entries outside [0, B) are clamped into it (a permutation
  *   has none). */
 int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_logp, const float* adv,
                 const float* ret, const float* new_values, const int32_t* perm, const uint16_t* mb_index,

@@ -9,12 +9,11 @@
 //   Gather (contiguous, or perm with more than 64 minibatches): grid (blocks per minibatch, minibatches);
 //   thread k of minibatch m reads sample perm[m*mb + k]. Shuffled indices make every per-sample read a
 //   random access.
-//   perm with at most 64 minibatches is first turned into each sample's minibatch number (2 bytes per
-//   sample in the workspace), then takes the stream pass below: the same sets, summed in storage order
-//   instead of perm order. The conversion bins the permutation's entries by destination (16384 samples per
-//   bin) so that no write is a lone 2-byte scatter: per-block counts and their scan give every block a run
-//   in each bin's staging, each block sorts its entries by bin in LDS and writes them run by run, then one
-//   block per bin places its entries in LDS and writes the bin's minibatch numbers as one 32 KB piece.
+//   perm with at most 64 minibatches is first sorted by destination into bins (one launch, each block
+//   sorting its positions in LDS), then takes the stream pass below: the same sets, summed in storage
+//   order instead of perm order. Up to 16 minibatches each stream block's chunk is one bin, whose entries
+//   the block places in LDS as 4-bit minibatch numbers before it streams; with more, one block per bin
+//   writes 2-byte numbers that the stream pass reads.
 //   Stream (mb_index): each minibatch's scalars are means over its set of samples, so one pass over the
 //   batch in storage order serves all minibatches at once: every read is coalesced and each sample is
 //   read exactly once. Each thread adds its samples' terms into its own per-minibatch slots in LDS
@@ -41,6 +40,14 @@ constexpr double kNormEps = 1e-8;
 constexpr int kSamplesPerThread = 8;
 constexpr int kMaxBlocksPerMb = 4096;
 
+// Where the perm conversion's sort left each bin's entries: staging row k (kSortPositions words) holds
+// position block k's entries sorted by bin, and starts row k (bins + 1 words) where each bin's run begins.
+struct PermRuns {
+    const int32_t* starts;
+    const uint32_t* staging;
+    int rows, bins;
+};
+
 struct LossArgs {
     const float* logits;
     const int32_t* actions;
@@ -61,6 +68,7 @@ struct LossArgs {
     float* dvalues;     // [B]
     float inv_mb;       // 1 / M
     float dv_coef;      // 2 vf / M
+    PermRuns runs;      // the sorted perm, for the stream pass that places its own chunk's numbers
 };
 
 // The normalisation of the advantages from adv_stats, which holds either the finished statistics
@@ -317,21 +325,257 @@ __global__ __launch_bounds__(256) void k_ppo_loss(LossArgs p)
     }
 }
 
+// Binned perm conversion. perm names, position by position, the sample that minibatch position / mb
+// takes; the stream pass wants the inverse, each sample's minibatch. The plain inverse,
+// ids[perm[p]] = p / mb, is a random 2-byte scatter (k_perm_to_index below, kept for batches past 2^24
+// samples). Binned instead, with destinations in bins of S consecutive samples:
+//   sort   one launch over blocks of kSortPositions positions (32 a thread). A block tags its entries
+//          with their destination's bin, counts them per bin in LDS, sorts them by bin in LDS and writes
+//          them back as one contiguous piece (its staging row), with the start of each bin's run in that
+//          row (its starts row: bins + 1 words, the last the row's entry count);
+//   place  bin b's entries are the runs [starts[k][b], starts[k][b + 1]) of the staging rows k, placed by
+//          destination in LDS. With at most 16 minibatches the stream pass's own blocks do this (block b's
+//          chunk is bin b; a 4-bit number per sample, 8 KB for the largest bin), so no minibatch number
+//          goes through memory; with 17 to 64, k_perm_place_runs writes 2-byte numbers for the stream
+//          kernels of 32 and 64 minibatches (bins of kBinCap samples).
+// No global atomics and no scan across blocks: every block's output has a fixed place. A staged entry is
+// the destination's offset in its bin (14 bits) and its minibatch (6 bits); inside the sort its bin
+// follows (bits 20 and up).
+constexpr int kSortPositions = 16384;
+constexpr int kSortThreads = 512;
+// Words from one staging row to the next: a bin's runs lie at about the same offset in every row, so rows
+// exactly 64 KB apart would send a consumer's reads to a few memory channels; 256 bytes more spread them.
+constexpr int kStagingStride = kSortPositions + 64;
+constexpr int kBinCap = 16384;            // samples a bin holds at most: offsets take 14 bits
+constexpr int kMaxBins = 1024;
+constexpr int kMapWords = kBinCap / 8;    // a bin's 4-bit minibatch numbers, 8 to a word
+
+// Block-wide exclusive sum over W waves of one value a thread (LDS `sh` of W words); returns the thread's
+// prefix and leaves the block total in *total.
+template <int W>
+__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* sh, int32_t* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int32_t s = sh[k];
+        before += k < w ? s : 0;
+        all += s;
+    }
+    *total = all;
+    __syncthreads();
+    return before + inc - v;
+}
+
+// x / d for 0 <= x < 2^25 and quotients below 2^12: the float quotient is then within one of the exact
+// one (two roundings of relative size 2^-24), and one step corrects it; q * d stays below 2^26.
+__device__ __forceinline__ int32_t small_quotient(int32_t x, int32_t d, float inv_d)
+{
+    int32_t q = (int32_t)((float)x * inv_d);
+    if (q * d > x) --q;
+    else if ((q + 1) * d <= x) ++q;
+    return q;
+}
+
+constexpr size_t kSortLdsBytes = sizeof(uint32_t) * kSortPositions + sizeof(int32_t) * (kMaxBins + 1 + kSortThreads / 64);
+
+// The sort. B <= 2^24, bins <= kMaxBins and S <= kBinCap (bins = ceil(B / S)), at most 64 minibatches.
+// Positions past the batch's end (the last block's) go to a spare bin, kMaxBins, so that every load and
+// every LDS update is unconditional; their sorted slots follow the block's entries and are not written.
+__global__ __launch_bounds__(kSortThreads) void k_perm_sort(const int32_t* __restrict__ perm, int32_t B, int32_t mb,
+                                                            float inv_mb, int32_t S, float inv_S, int bins,
+                                                            int32_t* __restrict__ starts,
+                                                            uint32_t* __restrict__ staging)
+{
+    constexpr int PPT = kSortPositions / kSortThreads;
+    constexpr int W = kSortThreads / 64;
+    constexpr int BPT = kMaxBins / kSortThreads;    // bins a thread scans
+    // LDS from the launch (kSortLdsBytes): the sorted entries, the bins' counts and then their first slots
+    // (+ the spare bin), the scan's wave sums
+    uint32_t* sorted = reinterpret_cast<uint32_t*>(rl::launch_lds());
+    int32_t* cur = reinterpret_cast<int32_t*>(sorted + kSortPositions);
+    int32_t* sh = cur + kMaxBins + 1;
+    const int t = threadIdx.x;
+    const int32_t lo = blockIdx.x * kSortPositions;
+    const int32_t hi = min(B, lo + kSortPositions);
+    uint32_t e[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) e[j] = (uint32_t)perm[min(lo + t + kSortThreads * j, hi - 1)];
+    for (int b = t; b <= kMaxBins; b += kSortThreads) cur[b] = 0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int32_t p = lo + t + kSortThreads * j;
+        const int32_t d = min(max((int32_t)e[j], 0), B - 1);   // a permutation has no entry outside [0, B)
+        const int32_t bin = small_quotient(d, S, inv_S);
+        const int32_t m = small_quotient(p, mb, inv_mb);
+        e[j] = p < hi ? (uint32_t)(d - bin * S) | ((uint32_t)m << 14) | ((uint32_t)bin << 20) : 0xffffffffu;
+    }
+    __syncthreads();
+    // counting gives each entry its rank among the block's entries of its bin (in whatever order the
+    // atomics land: a bin's entries are a set, their order within its run does not matter)
+    int32_t rank[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) rank[j] = atomicAdd(&cur[e[j] == 0xffffffffu ? kMaxBins : (int)(e[j] >> 20)], 1);
+    __syncthreads();
+    int32_t c[BPT];
+    int32_t own = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
+        c[q] = b < bins ? cur[b] : 0;
+        own += c[q];
+    }
+    int32_t total;
+    int32_t start = block_exclusive_sum<W>(own, sh, &total);
+    int32_t* row = starts + (int64_t)blockIdx.x * (bins + 1);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
+        if (b < bins) {
+            cur[b] = start;
+            row[b] = start;
+        }
+        start += c[q];
+    }
+    if (t == 0) {
+        cur[kMaxBins] = total;
+        row[bins] = total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) rank[j] += cur[e[j] == 0xffffffffu ? kMaxBins : (int)(e[j] >> 20)];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) sorted[rank[j]] = e[j] & 0xfffffu;
+    __syncthreads();
+    const int n = hi - lo;
+    uint32_t* out = staging + (int64_t)blockIdx.x * kStagingStride;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int i = t + kSortThreads * j;
+        if (i < n) out[i] = sorted[i];
+    }
+}
+
+// Calls put(offset, minibatch) for every staged entry of bin b (for a permutation, each offset of the bin
+// exactly once), from THREADS threads. A wave reads one run per load instruction, a lane an entry, so that
+// the loads coalesce (a shuffled perm's runs average S * kSortPositions / B entries, 32 at the bench's
+// sizes). Wave w takes rows w, w + W, ... 64 at a time: each lane loads one row's run bounds, then the wave
+// issues the loads of R runs (each clamped into its row; only their use is masked) before it places any.
+// Entries past a run's 64th (only where one position block sends many entries to one bin, as an
+// unshuffled perm does) take further passes of the wave.
+template <int THREADS, typename Put>
+__device__ __forceinline__ void for_bin_entries(const PermRuns& r, int b, Put put)
+{
+    constexpr int W = THREADS / 64;
+    constexpr int R = 32;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int k0 = w; k0 < r.rows; k0 += 64 * W) {
+        const int n = min(64, (r.rows - k0 + W - 1) / W);   // rows of this group: k0 + W * j, j < n
+        const int k = min(k0 + W * lane, r.rows - 1);
+        const int32_t* row = r.starts + (int64_t)k * (r.bins + 1) + b;
+        const int32_t beg = row[0];
+        const int32_t len = lane < n ? row[1] - beg : 0;
+        for (int j0 = 0; j0 < n; j0 += R) {
+            uint32_t v[R];
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int j = min(j0 + q, 63);
+                const int32_t bj = __builtin_amdgcn_readlane(beg, j), lj = __builtin_amdgcn_readlane(len, j);
+                const int64_t kj = min(k0 + W * j, r.rows - 1);
+                v[q] = r.staging[kj * kStagingStride + min(max(bj + min(lane, lj - 1), 0), kSortPositions - 1)];
+            }
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int j = min(j0 + q, 63);
+                const int32_t lj = __builtin_amdgcn_readlane(len, j);
+                if (j0 + q < n && lane < lj) put((int)(v[q] & (kBinCap - 1)), (int)((v[q] >> 14) & 63));
+            }
+        }
+        for (int j = 0; j < n; ++j) {
+            const int32_t bj = __builtin_amdgcn_readlane(beg, j), lj = __builtin_amdgcn_readlane(len, j);
+            const int64_t kj = k0 + W * j;
+            for (int i = 64 + lane; i < lj; i += 64) {
+                const uint32_t e = r.staging[kj * kStagingStride + min(bj + i, kSortPositions - 1)];
+                put((int)(e & (kBinCap - 1)), (int)((e >> 14) & 63));
+            }
+        }
+    }
+}
+
+// With 17 to 64 minibatches: one block per bin of kBinCap samples places the bin's entries in an LDS
+// window (destinations no entry names read 0xffff, past every minibatch, which the stream pass counts as
+// the last; a permutation names every destination once), then writes the bin's minibatch numbers as one
+// piece with 16-byte stores.
+__global__ __launch_bounds__(512) void k_perm_place_runs(PermRuns r, int64_t B, uint16_t* __restrict__ ids)
+{
+    __shared__ uint4 win4[kBinCap / 8];
+    uint16_t* win = reinterpret_cast<uint16_t*>(win4);
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    for (int q = t; q < kBinCap / 8; q += 512) win4[q] = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+    __syncthreads();
+    for_bin_entries<512>(r, b, [&](int off, int m) { win[off] = (uint16_t)m; });
+    __syncthreads();
+    const int64_t lo = (int64_t)b * kBinCap;
+    const int n = (int)min((int64_t)kBinCap, B - lo);
+    uint4* out4 = reinterpret_cast<uint4*>(ids + lo);     // lo is a multiple of 16384: 32 KB aligned
+    for (int q = t; q < n / 8; q += 512) out4[q] = win4[q];
+    for (int i = (n / 8) * 8 + t; i < n; i += 512) ids[lo + i] = win[i];
+}
+
 // Stream mode: block b visits samples [b*chunk, min(B, (b+1)*chunk)) in storage order. THREADS * NB * 3
 // floats of LDS hold each thread's private per-minibatch sums (slot (j*3 + s)*THREADS + thread). A
 // thread loads the inputs of its next U samples (indices clamped to the chunk, so the loads issue
 // together) before the arithmetic of the first; it still adds its samples in increasing index order.
-template <int AC, int NB, int THREADS, int U, bool GRAD>
+// The minibatch numbers come from mb_index, or (MAP) from the sorted perm: block b's chunk is then bin b of
+// the sort, whose entries the block first places in LDS as 4-bit numbers. Either way the samples, their
+// order and the slots are the same, so the two give the same bits.
+// LDS bytes of a stream block: the slots, then the 4-bit minibatch numbers (MAP) or two doubles.
+constexpr size_t stream_lds_bytes(int NB, int THREADS, bool MAP)
+{
+    return sizeof(float) * ((size_t)NB * 3 * THREADS + (MAP ? kMapWords : 4));
+}
+
+template <int AC, int NB, int THREADS, int U, bool GRAD, bool MAP = false>
 __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t chunk)
 {
-    __shared__ float acc[NB * 3 * THREADS];
-    __shared__ double nrm[2];
+    constexpr int kAcc = NB * 3 * THREADS;
+    static_assert(!MAP || NB <= 16, "4-bit minibatch numbers");
+    // the slots, then the chunk's minibatch numbers (MAP) or the normalisation's two doubles; with MAP the
+    // doubles pass through the last 16 bytes of the slots, which are cleared only after every thread has
+    // read them
+    float* lds = reinterpret_cast<float*>(rl::launch_lds());   // stream_lds_bytes(NB, THREADS, MAP)
+    float* acc = lds;
+    uint32_t* map = reinterpret_cast<uint32_t*>(lds + kAcc);
+    double* nrm = reinterpret_cast<double*>(MAP ? lds + kAcc - 4 : lds + kAcc);
     const int t = threadIdx.x;
-    for (int j = t; j < NB * 3 * THREADS; j += THREADS) acc[j] = 0.0f;
+    if constexpr (MAP) {
+        for (int j = t; j < kMapWords; j += THREADS) map[j] = 0xffffffffu;
+    } else {
+        for (int j = t; j < kAcc; j += THREADS) acc[j] = 0.0f;
+    }
     norm_reduce(p.stats, nrm);
     __syncthreads();
     float mean, scale;
     norm_read(p.stats, nrm, mean, scale);
+    if constexpr (MAP) {
+        // a number is set by clearing the bits it lacks: a destination no entry names keeps 15, the last
+        for_bin_entries<THREADS>(p.runs, blockIdx.x, [&](int off, int m) {
+            atomicAnd(&map[off >> 3], ~((uint32_t)(~m & 15) << ((off & 7) * 4)));
+        });
+        __syncthreads();
+        for (int j = t; j < kAcc; j += THREADS) acc[j] = 0.0f;
+        __syncthreads();
+    }
     const int64_t lo = (int64_t)blockIdx.x * chunk;
     const int64_t hi = min(p.B, lo + chunk);
     for (int64_t i0 = lo + t; i0 < hi; i0 += (int64_t)THREADS * U) {
@@ -341,7 +585,13 @@ __global__ __launch_bounds__(THREADS) void k_ppo_loss_stream(LossArgs p, int64_t
         for (int u = 0; u < U; ++u) {
             const int64_t i = min(i0 + (int64_t)u * THREADS, hi - 1);
             load_sample<AC>(p, i, s[u]);
-            mbi[u] = min((int)p.mb_index[i], p.num_mb - 1);   // past the last minibatch counts as the last
+            // past the last minibatch counts as the last
+            if constexpr (MAP) {
+                const int li = (int)(i - lo);
+                mbi[u] = min((int)((map[li >> 3] >> ((li & 7) * 4)) & 15u), p.num_mb - 1);
+            } else {
+                mbi[u] = min((int)p.mb_index[i], p.num_mb - 1);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -451,230 +701,6 @@ __global__ __launch_bounds__(256) void k_perm_to_index(const int32_t* __restrict
         ids[min(max((int64_t)perm[base + k], (int64_t)0), B - 1)] = m;
 }
 
-// Binned perm conversion: destinations in bins of kBinSamples samples, perm positions in blocks of
-// kBinPositions (32 a thread). Five launches, none with a global atomic:
-//   count   per position block, the number of its entries for each bin (an LDS histogram), block-major;
-//   scan    per bin, the exclusive sum of those counts over the position blocks (where each block's run
-//           of the bin's staging starts) and the bin's total, in two launches (group sums, then offsets);
-//   scatter per position block, its entries sorted by bin in LDS, then written in that order, so that
-//           consecutive lanes write consecutive words of a run;
-//   place   per bin, its staged entries placed in LDS by destination and written out as one piece.
-// A staged entry is the destination's offset in its bin (14 bits) and its minibatch (6 bits: the stream
-// pass takes at most 64). Batches of up to kMaxBins bins (2^24 samples) take this path, larger ones the
-// direct scatter above.
-constexpr int kBinShift = 14;
-constexpr int kBinSamples = 1 << kBinShift;
-constexpr int kBinPositions = 8192;
-constexpr int kMaxBins = 1024;
-constexpr int kScanRows = 16;        // position blocks a scan group takes
-
-// Block-wide exclusive sum over 256 threads of one value each (LDS `sh` of 4 words); returns the thread's
-// prefix and leaves the block total in *total.
-__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* sh, int32_t* total)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int32_t inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t o = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += o;
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    int32_t before = 0;
-    for (int k = 0; k < w; ++k) before += sh[k];
-    *total = sh[0] + sh[1] + sh[2] + sh[3];
-    __syncthreads();
-    return before + inc - v;
-}
-
-// Positions a thread of a binning block takes: all of them are loaded before the first LDS update.
-constexpr int kPermPerThread = kBinPositions / 256;
-
-// The binned path takes B <= 2^24 (kMaxBins bins), so positions, destinations and minibatch products fit
-// 32-bit integers. Positions past a block's end (the last block's) count into a spare bin, kMaxBins, so that
-// every LDS update is unconditional.
-__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ perm, int32_t B, int nbins,
-                                                    int32_t* __restrict__ counts)
-{
-    __shared__ int32_t hist[kMaxBins + 1];
-    const int t = threadIdx.x;
-    const int32_t lo = blockIdx.x * kBinPositions;
-    const int32_t hi = min(B, lo + kBinPositions);
-    // every load unconditional (at the last position when past it), so all are in flight at once
-    int32_t bin[kPermPerThread];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) bin[j] = perm[min(lo + t + 256 * j, hi - 1)];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j)
-        bin[j] = lo + t + 256 * j < hi ? min(max(bin[j], 0), B - 1) >> kBinShift : kMaxBins;
-    for (int b = t; b <= nbins; b += 256) hist[b] = 0;
-    if (t == 0) hist[kMaxBins] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) atomicAdd(&hist[bin[j]], 1);
-    __syncthreads();
-    int32_t* row = counts + (int64_t)blockIdx.x * nbins;
-    for (int b = t; b < nbins; b += 256) row[b] = hist[b];
-}
-
-// The scan in two launches of one-wave blocks (bins [64 * blockIdx.x, + 64), one per lane; position
-// blocks in groups of kScanRows, group blockIdx.y): the first sums each group's counts, the second adds the
-// sums of the groups before its own and writes its rows' running offsets. The matrices hold at most 2^21
-// words (kMaxBins bins, 2048 position blocks), so 32-bit indexes suffice. Every load is unconditional
-// (clamped into range) and only its use is masked, so a lane's loads are all in flight at once.
-__global__ __launch_bounds__(64) void k_perm_group_sums(const int32_t* __restrict__ counts, int nbins, int nblk,
-                                                        int32_t* __restrict__ gsum)
-{
-    const int bin = blockIdx.x * 64 + threadIdx.x;
-    const int cb = min(bin, nbins - 1);
-    const int k0 = blockIdx.y * kScanRows, k1 = min(nblk, k0 + kScanRows);
-    int32_t c[kScanRows];
-#pragma unroll
-    for (int u = 0; u < kScanRows; ++u) c[u] = counts[min(k0 + u, k1 - 1) * nbins + cb];
-    int32_t sum = 0;
-#pragma unroll
-    for (int u = 0; u < kScanRows; ++u) sum += k0 + u < k1 ? c[u] : 0;
-    if (bin < nbins) gsum[blockIdx.y * nbins + bin] = sum;
-}
-
-__global__ __launch_bounds__(64) void k_perm_offsets(const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ gsum, int nbins, int nblk,
-                                                     int32_t* __restrict__ offs, int32_t* __restrict__ fill)
-{
-    constexpr int U = 16;
-    const int bin = blockIdx.x * 64 + threadIdx.x;
-    const int cb = min(bin, nbins - 1);
-    const int g = blockIdx.y;
-    const int k0 = g * kScanRows, k1 = min(nblk, k0 + kScanRows);
-    int32_t c[kScanRows];
-#pragma unroll
-    for (int u = 0; u < kScanRows; ++u) c[u] = counts[min(k0 + u, k1 - 1) * nbins + cb];
-    int32_t run = 0;
-    for (int h = 0; h < g; h += U) {
-        int32_t q[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) q[u] = gsum[min(h + u, g - 1) * nbins + cb];
-#pragma unroll
-        for (int u = 0; u < U; ++u) run += h + u < g ? q[u] : 0;
-    }
-    if (bin >= nbins) return;
-#pragma unroll
-    for (int u = 0; u < kScanRows; ++u)
-        if (k0 + u < k1) {
-            offs[(k0 + u) * nbins + bin] = run;
-            run += c[u];
-        }
-    if (k1 == nblk) fill[bin] = run;
-}
-
-__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ perm, int32_t B, int32_t mb,
-                                                      float inv_mb, int nbins, const int32_t* __restrict__ counts,
-                                                      const int32_t* __restrict__ offs, uint32_t* __restrict__ staging)
-{
-    __shared__ int32_t cur[kMaxBins + 1];  // next LDS slot of each bin (and of the spare bin)
-    __shared__ int32_t delta[kMaxBins];    // staging index minus LDS slot, per bin
-    __shared__ uint32_t sorted[kBinPositions];
-    __shared__ int32_t sh[4];
-    constexpr int BPT = kMaxBins / 256;    // bins a thread scans
-    const int t = threadIdx.x;
-    const int32_t lo = blockIdx.x * kBinPositions;
-    const int32_t hi = min(B, lo + kBinPositions);
-    // the positions' entries first, so their loads overlap the run set-up below
-    uint32_t e[kPermPerThread];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) e[j] = (uint32_t)perm[min(lo + t + 256 * j, hi - 1)];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) {
-        const int32_t p = lo + t + 256 * j;
-        const int32_t d = min(max((int32_t)e[j], 0), B - 1);
-        // p / mb: the float quotient is within 2^-17 of the exact one (below 64 here), so one step corrects it
-        int32_t m = (int32_t)((float)p * inv_mb);
-        if (m * mb > p) --m;
-        else if ((m + 1) * mb <= p) ++m;
-        e[j] = p < hi ? (uint32_t)(d & (kBinSamples - 1)) | ((uint32_t)m << kBinShift) | ((uint32_t)(d >> kBinShift) << 20)
-                      : 0xffffffffu;
-    }
-    const int64_t row = (int64_t)blockIdx.x * nbins;
-    int32_t c[BPT], o[BPT];
-    int32_t own = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int64_t i = row + min(t * BPT + j, nbins - 1);   // unconditional loads, their use masked
-        c[j] = counts[i];
-        o[j] = offs[i];
-    }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        if (t * BPT + j >= nbins) c[j] = 0;
-        own += c[j];
-    }
-    int32_t total;
-    int32_t start = block_exclusive_sum(own, sh, &total);
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int b = t * BPT + j;
-        if (b < nbins) {
-            cur[b] = start;
-            delta[b] = b * kBinSamples + o[j] - start;
-        }
-        start += c[j];
-    }
-    if (t == 0) cur[kMaxBins] = total;    // the spare bin's slots follow the block's entries
-    __syncthreads();
-    int32_t slot[kPermPerThread];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) slot[j] = atomicAdd(&cur[e[j] == 0xffffffffu ? kMaxBins : e[j] >> 20], 1);
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) sorted[slot[j]] = e[j];
-    __syncthreads();
-    const int n = (int)(hi - lo);
-    // all of the thread's LDS reads first, then its stores
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) e[j] = sorted[min(t + 256 * j, n - 1)];
-    int32_t g[kPermPerThread];
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) g[j] = delta[e[j] >> 20] + t + 256 * j;
-#pragma unroll
-    for (int j = 0; j < kPermPerThread; ++j) {
-        const int b = (int)(e[j] >> 20);
-        // a run past the bin's capacity only when perm is not a permutation: such entries are dropped
-        if (t + 256 * j < n && g[j] - b * kBinSamples < kBinSamples) staging[g[j]] = e[j] & 0xfffffu;
-    }
-}
-
-// One block per bin: its staged entries placed in LDS (destinations no entry names read 0xffff, past every
-// minibatch, which the loss counts as the last; a permutation names every destination once), then the bin's
-// minibatch numbers written out with 16-byte stores.
-__global__ __launch_bounds__(512) void k_perm_place(const int32_t* __restrict__ fill,
-                                                    const uint32_t* __restrict__ staging, int64_t B,
-                                                    uint16_t* __restrict__ ids)
-{
-    constexpr int J = 8;
-    __shared__ uint4 win4[kBinSamples / 8];
-    uint16_t* win = reinterpret_cast<uint16_t*>(win4);
-    const int b = blockIdx.x;
-    const int t = threadIdx.x;
-    for (int q = t; q < kBinSamples / 8; q += 512) win4[q] = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
-    const int32_t cnt = min(fill[b], kBinSamples);
-    __syncthreads();
-    const uint32_t* st = staging + (int64_t)b * kBinSamples;
-    for (int i0 = t; i0 < cnt; i0 += 512 * J) {
-        uint32_t v[J];
-#pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = st[min(i0 + 512 * j, cnt - 1)];   // unconditional, clamped
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (i0 + 512 * j < cnt) win[v[j] & (kBinSamples - 1)] = (uint16_t)(v[j] >> kBinShift);
-    }
-    __syncthreads();
-    const int64_t lo = (int64_t)b * kBinSamples;
-    const int n = (int)min((int64_t)kBinSamples, B - lo);
-    uint4* out4 = reinterpret_cast<uint4*>(ids + lo);     // lo is a multiple of 16384: 32 KB aligned
-    for (int q = t; q < n / 8; q += 512) out4[q] = win4[q];
-    for (int i = (n / 8) * 8 + t; i < n; i += 512) ids[lo + i] = win[i];
-}
-
 int blocks_per_mb(int64_t mb)
 {
     const int64_t per_block = 256 * kSamplesPerThread;
@@ -682,32 +708,17 @@ int blocks_per_mb(int64_t mb)
 }
 
 constexpr int kStreamMaxMinibatches = 64;
-// Every stream variant holds 48 KB of LDS per block, so a CU keeps 3 blocks and 768 blocks are one
-// resident round on 256 CUs: no tail round of partly filled CUs.
+// The stream variants of 32 and 64 minibatches hold 48 KB of LDS per block, so a CU keeps 3 blocks and 768
+// blocks are one resident round on 256 CUs: no tail round of partly filled CUs. The 16-minibatch variant
+// (384 threads) holds 72 KB, with its chunk's 4-bit minibatch numbers 80 KB: 2 blocks a CU, 512 a round.
 constexpr int kStreamBlocks = 768;
+constexpr int kStreamBlocks16 = 512;
 
-// Bytes of the per-block partials at the front of the workspace (rounded up to 256, where the minibatch
-// numbers of a converted perm follow, then the bins' fill counters and staging runs).
+// Bytes of the per-block partials at the front of the workspace (rounded up to 256, where a perm's
+// conversion follows).
 size_t partial_bytes(int64_t num_mb, size_t blocks)
 {
     return rl::round_up(sizeof(double) * 3 * (size_t)num_mb * blocks, 256);
-}
-
-int64_t perm_bins(int64_t B) { return (B + kBinSamples - 1) / kBinSamples; }
-int64_t perm_blocks(int64_t B) { return (B + kBinPositions - 1) / kBinPositions; }
-
-// Bytes behind the partials for a perm's conversion: minibatch numbers, and for a binned conversion the
-// counts and run offsets (position blocks x bins), the scan's group sums, the bins' totals and the staging
-// runs.
-size_t perm_bytes(int64_t B)
-{
-    size_t bytes = rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
-    const int64_t nb = perm_bins(B);
-    if (nb <= kMaxBins)
-        bytes += 2 * rl::round_up(sizeof(int32_t) * (size_t)(nb * perm_blocks(B)), 256) +
-                 rl::round_up(sizeof(int32_t) * (size_t)(nb * ((perm_blocks(B) + kScanRows - 1) / kScanRows)), 256) +
-                 rl::round_up(sizeof(int32_t) * (size_t)nb, 256) + sizeof(uint32_t) * (size_t)nb * kBinSamples;
-    return bytes;
 }
 
 // Each thread adds at most this many samples into its float32 slots (the slot sums are then reduced in
@@ -715,17 +726,63 @@ size_t perm_bytes(int64_t B)
 // at any B.
 constexpr int64_t kSlotSamples = 256;
 
-// Threads per stream-mode block: the per-thread slots of 16 / 32 / 64 minibatches fill 48 KB of LDS.
-int stream_threads(int64_t num_mb) { return num_mb <= 16 ? 256 : (num_mb <= 32 ? 128 : 64); }
+// Threads per stream-mode block: the per-thread slots of 16 / 32 / 64 minibatches fill 72 / 48 / 48 KB of LDS.
+int stream_threads(int64_t num_mb) { return num_mb <= 16 ? 384 : (num_mb <= 32 ? 128 : 64); }
 
-// Stream-mode grid: blocks of `chunk` samples, kStreamBlocks of them (one resident round) unless a chunk
-// would give a thread more than kSlotSamples samples.
+// Stream-mode grid: blocks of `chunk` samples. Up to 16 minibatches, whole rounds of kStreamBlocks16
+// blocks of at most kBinCap samples (so that a chunk is a bin of the perm conversion, and a thread takes at
+// most 43 samples); else kStreamBlocks blocks (one resident round) unless a chunk would give a thread more
+// than kSlotSamples samples.
 int stream_blocks(int64_t B, int64_t num_mb, int64_t* chunk)
 {
-    const int64_t c = std::min<int64_t>(std::max<int64_t>(256, (B + kStreamBlocks - 1) / kStreamBlocks),
-                                        stream_threads(num_mb) * kSlotSamples);
+    int64_t c;
+    if (num_mb <= 16) {
+        const int64_t per_round = (int64_t)kStreamBlocks16 * kBinCap;
+        const int64_t rounds = (B + per_round - 1) / per_round;
+        c = std::max<int64_t>(256, (B + kStreamBlocks16 * rounds - 1) / (kStreamBlocks16 * rounds));
+    } else {
+        c = std::min<int64_t>(std::max<int64_t>(256, (B + kStreamBlocks - 1) / kStreamBlocks),
+                              stream_threads(num_mb) * kSlotSamples);
+    }
     *chunk = c;
     return (int)((B + c - 1) / c);
+}
+
+// How a perm becomes minibatch numbers (at most 64 minibatches): the sort with the stream pass placing its
+// own chunk's numbers (up to 16 minibatches; bins are the stream chunks), the sort and k_perm_place_runs
+// (bins of kBinCap), or past 2^24 samples the direct scatter.
+enum PermKind { kPermDirect, kPermPlaced, kPermInStream };
+
+struct PermPlan {
+    PermKind kind;
+    int64_t rows, bins, S;
+};
+
+PermPlan perm_plan(int64_t B, int64_t num_mb)
+{
+    PermPlan q{kPermDirect, (B + kSortPositions - 1) / kSortPositions, 0, 0};
+    if (B > ((int64_t)1 << 24)) return q;
+    if (num_mb <= 16) {
+        q.kind = kPermInStream;
+        q.bins = stream_blocks(B, num_mb, &q.S);
+    } else {
+        q.kind = kPermPlaced;
+        q.S = kBinCap;
+        q.bins = (B + kBinCap - 1) / kBinCap;
+    }
+    return q;
+}
+
+// Bytes behind the partials for a perm's conversion: the 2-byte minibatch numbers (unless the stream pass
+// places them itself), then for the sort its starts rows and staging rows.
+size_t perm_bytes(int64_t B, int64_t num_mb)
+{
+    const PermPlan q = perm_plan(B, num_mb);
+    size_t bytes = q.kind == kPermInStream ? 0 : rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
+    if (q.kind != kPermDirect)
+        bytes += rl::round_up(sizeof(int32_t) * (size_t)(q.rows * (q.bins + 1)), 256) +
+                 sizeof(uint32_t) * (size_t)(q.rows * kStagingStride);
+    return bytes;
 }
 
 }  // namespace
@@ -742,7 +799,7 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
     const size_t blocks = (size_t)std::max(blocks_per_mb(mb), num_mb <= kStreamMaxMinibatches ? stream_blocks(B, num_mb, &chunk) : 0);
     *bytes = partial_bytes(num_mb, blocks);
     // with at most 64 minibatches, room for turning a perm into minibatch numbers
-    if (num_mb <= kStreamMaxMinibatches) *bytes += perm_bytes(B);
+    if (num_mb <= kStreamMaxMinibatches) *bytes += perm_bytes(B, num_mb);
     return RL_OK;
 }
 
@@ -750,28 +807,39 @@ int rl_ppo_loss_workspace_bytes(int64_t B, int32_t mb, size_t* bytes)
 
 namespace {
 
+template <int AC, int NB, int THREADS, int U, bool GRAD, bool MAP = false>
+int launch_stream(const LossArgs& p, int64_t chunk, int nblk, hipStream_t st)
+{
+    auto* k = &k_ppo_loss_stream<AC, NB, THREADS, U, GRAD, MAP>;
+    constexpr size_t bytes = stream_lds_bytes(NB, THREADS, MAP);
+    if (int rc = rl::allow_launch_lds(k, bytes, "ppo_loss")) return rc;
+    hipLaunchKernelGGL(k, dim3(nblk), dim3(THREADS), bytes, st, p, chunk);
+    return RL_OK;
+}
+
 template <bool GRAD>
-void launch_loss(const LossArgs& p, int64_t num_mb, int A, bool stream_mode, int64_t chunk, int nblk, hipStream_t st)
+int launch_loss(const LossArgs& p, int64_t num_mb, int A, bool stream_mode, bool map, int64_t chunk, int nblk,
+                hipStream_t st)
 {
     if (stream_mode) {
         // With 64 minibatches a CU holds 3 one-wave blocks, so each thread loads 4 samples ahead; with
-        // 8 or 12 waves per CU the loads of one sample per thread already keep HBM busy.
-        const dim3 grid(nblk);
+        // 12 waves per CU (16 or 32 minibatches) the loads of one sample per thread already keep HBM busy.
         if (num_mb <= 16) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 16, 256, 1, GRAD>), grid, dim3(256), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 16, 256, 1, GRAD>), grid, dim3(256), 0, st, p, chunk);
-        } else if (num_mb <= 32) {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 32, 128, 1, GRAD>), grid, dim3(128), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 32, 128, 1, GRAD>), grid, dim3(128), 0, st, p, chunk);
-        } else {
-            if (A == 12) hipLaunchKernelGGL((k_ppo_loss_stream<12, 64, 64, 4, GRAD>), grid, dim3(64), 0, st, p, chunk);
-            else hipLaunchKernelGGL((k_ppo_loss_stream<0, 64, 64, 1, GRAD>), grid, dim3(64), 0, st, p, chunk);
+            if (map) return A == 12 ? launch_stream<12, 16, 384, 1, GRAD, true>(p, chunk, nblk, st)
+                                    : launch_stream<0, 16, 384, 1, GRAD, true>(p, chunk, nblk, st);
+            return A == 12 ? launch_stream<12, 16, 384, 1, GRAD>(p, chunk, nblk, st)
+                           : launch_stream<0, 16, 384, 1, GRAD>(p, chunk, nblk, st);
         }
-    } else {
-        const dim3 grid(nblk, (unsigned)num_mb);
-        if (A == 12) hipLaunchKernelGGL((k_ppo_loss<12, GRAD>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_ppo_loss<0, GRAD>), grid, dim3(256), 0, st, p);
+        if (num_mb <= 32)
+            return A == 12 ? launch_stream<12, 32, 128, 1, GRAD>(p, chunk, nblk, st)
+                           : launch_stream<0, 32, 128, 1, GRAD>(p, chunk, nblk, st);
+        return A == 12 ? launch_stream<12, 64, 64, 4, GRAD>(p, chunk, nblk, st)
+                       : launch_stream<0, 64, 64, 1, GRAD>(p, chunk, nblk, st);
     }
+    const dim3 grid(nblk, (unsigned)num_mb);
+    if (A == 12) hipLaunchKernelGGL((k_ppo_loss<12, GRAD>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_ppo_loss<0, GRAD>), grid, dim3(256), 0, st, p);
+    return RL_OK;
 }
 
 // Workspace bytes one call needs: the partials, and the perm's conversion only when a perm is given
@@ -780,7 +848,7 @@ int call_workspace_bytes(int64_t B, int32_t mb, bool with_perm, size_t* bytes)
 {
     if (int rc = rl_ppo_loss_workspace_bytes(B, mb, bytes)) return rc;
     const int64_t num_mb = B / mb;
-    if (!with_perm && num_mb <= kStreamMaxMinibatches) *bytes -= perm_bytes(B);
+    if (!with_perm && num_mb <= kStreamMaxMinibatches) *bytes -= perm_bytes(B, num_mb);
     return RL_OK;
 }
 
@@ -842,44 +910,45 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
     p.inv_mb = (float)(1.0 / (double)mb);
     p.dv_coef = (float)(2.0 * (double)vf_coef / (double)mb);
     hipStream_t st = rl::as_stream(stream);
+    p.runs = PermRuns{nullptr, nullptr, 0, 0};
+    bool map = false;
     if (perm && num_mb <= kStreamMaxMinibatches) {
-        // the perm's sets as minibatch numbers behind the partials, then the stream pass
+        // the perm's sets as minibatch numbers (behind the partials), then the stream pass
         int64_t c = 0;
         const size_t blocks = (size_t)std::max(blocks_per_mb(mb), stream_blocks(B, num_mb, &c));
-        uint8_t* tail = static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks);
-        uint16_t* ids = reinterpret_cast<uint16_t*>(tail);
-        const int64_t nbins = perm_bins(B);
-        if (nbins <= kMaxBins) {
-            const int64_t nblk = perm_blocks(B);
-            const int64_t groups = (nblk + kScanRows - 1) / kScanRows;
-            const size_t mat = rl::round_up(sizeof(int32_t) * (size_t)(nbins * nblk), 256);
-            uint8_t* w = tail + rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
-            int32_t* counts = reinterpret_cast<int32_t*>(w);
-            int32_t* offs = reinterpret_cast<int32_t*>(w + mat);
-            int32_t* gsum = reinterpret_cast<int32_t*>(w + 2 * mat);
-            w += 2 * mat + rl::round_up(sizeof(int32_t) * (size_t)(nbins * groups), 256);
-            int32_t* fill = reinterpret_cast<int32_t*>(w);
-            uint32_t* staging = reinterpret_cast<uint32_t*>(w + rl::round_up(sizeof(int32_t) * (size_t)nbins, 256));
-            const dim3 sgrid((unsigned)((nbins + 63) / 64), (unsigned)groups);
-            hipLaunchKernelGGL(k_perm_count, dim3((unsigned)nblk), dim3(256), 0, st, perm, (int32_t)B, (int)nbins, counts);
-            hipLaunchKernelGGL(k_perm_group_sums, sgrid, dim3(64), 0, st, counts, (int)nbins, (int)nblk, gsum);
-            hipLaunchKernelGGL(k_perm_offsets, sgrid, dim3(64), 0, st, counts, gsum, (int)nbins, (int)nblk, offs, fill);
-            hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)nblk), dim3(256), 0, st, perm, (int32_t)B, (int32_t)mb,
-                               (float)(1.0 / (double)mb), (int)nbins, counts, offs, staging);
-            hipLaunchKernelGGL(k_perm_place, dim3((unsigned)nbins), dim3(512), 0, st, fill, staging, B, ids);
-        } else {
+        uint8_t* w = static_cast<uint8_t*>(ws) + partial_bytes(num_mb, blocks);
+        const PermPlan q = perm_plan(B, num_mb);
+        uint16_t* ids = nullptr;
+        if (q.kind != kPermInStream) {
+            ids = reinterpret_cast<uint16_t*>(w);
+            w += rl::round_up(sizeof(uint16_t) * (size_t)B, 256);
+        }
+        if (q.kind == kPermDirect) {
             hipLaunchKernelGGL(k_perm_to_index, dim3((unsigned)blocks_per_mb(mb), (unsigned)num_mb), dim3(256), 0, st,
                                perm, B, (int64_t)mb, ids);
+        } else {
+            int32_t* starts = reinterpret_cast<int32_t*>(w);
+            uint32_t* staging = reinterpret_cast<uint32_t*>(w + rl::round_up(sizeof(int32_t) * (size_t)(q.rows * (q.bins + 1)), 256));
+            if (int rc = rl::allow_launch_lds(&k_perm_sort, kSortLdsBytes, "ppo_loss perm sort")) return rc;
+            hipLaunchKernelGGL(k_perm_sort, dim3((unsigned)q.rows), dim3(kSortThreads), kSortLdsBytes, st, perm, (int32_t)B,
+                               (int32_t)mb, (float)(1.0 / (double)mb), (int32_t)q.S, (float)(1.0 / (double)q.S),
+                               (int)q.bins, starts, staging);
+            p.runs = PermRuns{starts, staging, (int)q.rows, (int)q.bins};
+            if (q.kind == kPermPlaced)
+                hipLaunchKernelGGL(k_perm_place_runs, dim3((unsigned)q.bins), dim3(512), 0, st, p.runs, B, ids);
         }
         if (int rc = rl::check_launch("ppo_loss perm")) return rc;
+        map = q.kind == kPermInStream;
         mb_index = ids;
         p.mb_index = ids;
         p.perm = nullptr;
     }
+    const bool stream_mode = mb_index != nullptr || map;
     int64_t chunk = 0;
-    const int nblk = mb_index ? stream_blocks(B, num_mb, &chunk) : blocks_per_mb(mb);
-    if (dlogits) launch_loss<true>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
-    else launch_loss<false>(p, num_mb, A, mb_index != nullptr, chunk, nblk, st);
+    const int nblk = stream_mode ? stream_blocks(B, num_mb, &chunk) : blocks_per_mb(mb);
+    if (int rc = dlogits ? launch_loss<true>(p, num_mb, A, stream_mode, map, chunk, nblk, st)
+                         : launch_loss<false>(p, num_mb, A, stream_mode, map, chunk, nblk, st))
+        return rc;
     if (int rc = rl::check_launch("ppo_loss")) return rc;
     hipLaunchKernelGGL(k_ppo_finalize, dim3((unsigned)num_mb), dim3(256), 0, st, static_cast<const double*>(ws), nblk,
                        (int64_t)mb, vf_coef, ent_coef, out);

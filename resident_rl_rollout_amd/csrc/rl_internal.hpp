@@ -43,6 +43,26 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The block's LDS allocated at launch (the launch's shared-memory bytes). Kernels with a large LDS
+// footprint take it this way: on gfx950, measured, a kernel whose LDS is a static array and that carries
+// __launch_bounds__ gets one resident block per CU fewer than its size allows (48 KB: 2 instead of 3;
+// 64 to 80 KB: 1 instead of 2), while the same bytes given at launch keep the full count.
+__device__ __forceinline__ uint8_t* launch_lds()
+{
+    extern __shared__ __align__(16) uint8_t rl_launch_lds[];
+    return rl_launch_lds;
+}
+
+// Lets `kernel` take `bytes` of launch-time LDS (past 64 KB the runtime is asked first); call before each
+// launch: the runtime is asked once per kernel for the largest size so far.
+int allow_launch_lds_impl(const void* kernel, size_t bytes, const char* what);
+
+template <typename K>
+inline int allow_launch_lds(K* kernel, size_t bytes, const char* what)
+{
+    return bytes <= 65536 ? 0 : allow_launch_lds_impl(reinterpret_cast<const void*>(kernel), bytes, what);
+}
+
 constexpr int kWave = 64;
 
 // Whole-batch advantage statistics from per-block partial sums (sum A, sum A^2 of each scan block, in

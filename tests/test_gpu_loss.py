@@ -142,9 +142,10 @@ def test_minibatch_numbers_past_the_last_count_as_the_last(b, mb, gpu_lib):
 
 @pytest.mark.parametrize("b,mb", [(49616, 3101), (1 << 20, 1 << 16), (262144, 4096), (5, 5), (16384 * 5 + 16, 10242)])
 def test_perm_conversion_equals_minibatch_numbers(b, mb, gpu_lib):
-    # the perm is turned into minibatch numbers on the device (binned by destination, 16384 per bin; these
-    # sizes give one bin, several, and ragged last bins); the scalars must equal, bit for bit, those of the
-    # same split given as minibatch numbers, and the oracle's within tolerance
+    # the perm is turned into minibatch numbers on the device (sorted into bins by destination; up to 16
+    # minibatches the stream pass places its own chunk, else 2-byte numbers are written for it; these sizes
+    # give one bin, several, ragged last bins, and both routes); the scalars must equal, bit for bit, those
+    # of the same split given as minibatch numbers, and the oracle's within tolerance
     pi, adv, ret = _case(b + 7, b)
     args = (_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret), _dev(pi.new_values))
     out_perm = binding.ppo_loss(*args, _dev(pi.perm), mb).cpu().numpy()
@@ -157,6 +158,42 @@ def test_perm_conversion_equals_minibatch_numbers(b, mb, gpu_lib):
     torch.testing.assert_close(dl_p, dl_i, rtol=0, atol=0)
     torch.testing.assert_close(dv_p, dv_i, rtol=0, atol=0)
 
+
+
+def _perm_vs_index(b, mb, perm, seed):
+    pi, adv, ret = _case(seed, b, a=4)
+    args = (_dev(pi.new_logits), _dev(pi.actions), _dev(pi.old_logp), _dev(adv), _dev(ret), _dev(pi.new_values))
+    out_perm = binding.ppo_loss(*args, _dev(perm), mb).cpu().numpy()
+    out_idx = binding.ppo_loss(*args, None, mb, mb_index=_dev(inputs.minibatch_index(perm, mb))).cpu().numpy()
+    return pi, adv, ret, out_perm, out_idx
+
+
+@pytest.mark.parametrize("b,mb,kind", [(1 << 20, 1 << 16, "identity"), (1 << 20, 1 << 16, "reversed"),
+                                       (300000, 20000, "rotated"), (262144, 4096, "identity"),
+                                       (100480, 100480 // 40, "reversed")])
+def test_perm_conversion_with_long_runs(b, mb, kind, gpu_lib):
+    # perms that are not shuffles send a position block's entries to few bins, so the runs the conversion
+    # reads are thousands of entries long, far past the 64 a wave reads at once; the scalars must still
+    # equal those of the same split given as minibatch numbers, and the oracle's within tolerance
+    base = np.arange(b, dtype=np.int32)
+    perm = {"identity": base, "reversed": base[::-1].copy(), "rotated": np.roll(base, b // 3)}[kind]
+    pi, adv, ret, out_perm, out_idx = _perm_vs_index(b, mb, perm, b % 1000 + 3)
+    np.testing.assert_array_equal(out_perm, out_idx)
+    ref, scale = oracle.ppo_loss(pi.new_logits, pi.actions, pi.old_logp, adv, ret, pi.new_values, perm, mb)
+    assert_loss_close(out_perm, ref, scale, f"B={b} mb={mb} {kind} perm")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("b,nmb", [((1 << 23) + 16, 16), ((1 << 23) + 16, 48)])
+def test_perm_conversion_two_rounds_of_bins(b, nmb, gpu_lib):
+    # just past 2^23 samples the stream pass takes two rounds of 512 blocks (1024 bins) at 16 minibatches,
+    # and 513 sort rows; at 48 minibatches the placed numbers: bit for bit the minibatch-number results
+    # (those are checked against the oracle at other sizes)
+    rng = np.random.default_rng(b)
+    perm = rng.permutation(b).astype(np.int32)
+    _, _, _, out_perm, out_idx = _perm_vs_index(b, b // nmb, perm, 17)
+    np.testing.assert_array_equal(out_perm, out_idx)
+    assert np.isfinite(out_perm).all()
 
 
 @pytest.mark.timeout(300)
