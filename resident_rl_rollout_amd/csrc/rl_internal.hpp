@@ -43,10 +43,10 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// The block's LDS allocated at launch (the launch's shared-memory bytes). Kernels with a large LDS
-// footprint take it this way: on gfx950, measured, a kernel whose LDS is a static array and that carries
-// __launch_bounds__ gets one resident block per CU fewer than its size allows (48 KB: 2 instead of 3;
-// 64 to 80 KB: 1 instead of 2), while the same bytes given at launch keep the full count.
+// The block's LDS allocated at launch (the launch's shared-memory bytes). On gfx950, measured, a
+// 384-thread kernel whose LDS is a static array and that carries __launch_bounds__ gets one resident
+// block per CU fewer than its size allows (48 KB: 2 instead of 3; 64 to 80 KB: 1 instead of 2), while the
+// same bytes given at launch keep the full count (256- and 512-thread blocks get it either way).
 __device__ __forceinline__ uint8_t* launch_lds()
 {
     extern __shared__ __align__(16) uint8_t rl_launch_lds[];
