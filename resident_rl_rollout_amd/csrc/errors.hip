@@ -14,19 +14,27 @@ std::string& last_error()
 
 int allow_launch_lds_impl(const void* kernel, size_t bytes, const char* what)
 {
+    struct Allowed {
+        const void* kernel;
+        int device;
+        size_t bytes;   // the largest size allowed so far
+    };
     static std::mutex mu;
-    static std::vector<std::pair<const void*, size_t>> allowed;   // kernel, largest size allowed so far
+    static std::vector<Allowed> allowed;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RL_EHIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(mu);
     for (auto& a : allowed)
-        if (a.first == kernel && a.second >= bytes) return 0;
-    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (a.kernel == kernel && a.device == dev && a.bytes >= bytes) return 0;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return fail(RL_EHIP, "%s: %zu bytes of LDS: %s", what, bytes, hipGetErrorString(e));
     for (auto& a : allowed)
-        if (a.first == kernel) {
-            a.second = bytes;
+        if (a.kernel == kernel && a.device == dev) {
+            a.bytes = bytes;
             return 0;
         }
-    allowed.emplace_back(kernel, bytes);
+    allowed.push_back(Allowed{kernel, dev, bytes});
     return 0;
 }
 }  // namespace rl

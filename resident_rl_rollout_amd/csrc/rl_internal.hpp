@@ -54,7 +54,7 @@ __device__ __forceinline__ uint8_t* launch_lds()
 }
 
 // Lets `kernel` take `bytes` of launch-time LDS (past 64 KB the runtime is asked first); call before each
-// launch: the runtime is asked once per kernel for the largest size so far.
+// launch: the runtime is asked once per kernel and device for the largest size so far.
 int allow_launch_lds_impl(const void* kernel, size_t bytes, const char* what);
 
 template <typename K>
