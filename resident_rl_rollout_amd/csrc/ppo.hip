@@ -812,7 +812,6 @@ int launch_stream(const LossArgs& p, int64_t chunk, int nblk, hipStream_t st)
 {
     auto* k = &k_ppo_loss_stream<AC, NB, THREADS, U, GRAD, MAP>;
     constexpr size_t bytes = stream_lds_bytes(NB, THREADS, MAP);
-    if (int rc = rl::allow_launch_lds(k, bytes, "ppo_loss")) return rc;
     hipLaunchKernelGGL(k, dim3(nblk), dim3(THREADS), bytes, st, p, chunk);
     return RL_OK;
 }
@@ -929,7 +928,6 @@ int ppo_loss_impl(const float* logits, const int32_t* actions, const float* old_
         } else {
             int32_t* starts = reinterpret_cast<int32_t*>(w);
             uint32_t* staging = reinterpret_cast<uint32_t*>(w + rl::round_up(sizeof(int32_t) * (size_t)(q.rows * (q.bins + 1)), 256));
-            if (int rc = rl::allow_launch_lds(&k_perm_sort, kSortLdsBytes, "ppo_loss perm sort")) return rc;
             hipLaunchKernelGGL(k_perm_sort, dim3((unsigned)q.rows), dim3(kSortThreads), kSortLdsBytes, st, perm, (int32_t)B,
                                (int32_t)mb, (float)(1.0 / (double)mb), (int32_t)q.S, (float)(1.0 / (double)q.S),
                                (int)q.bins, starts, staging);

@@ -46,22 +46,14 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // The block's LDS allocated at launch (the launch's shared-memory bytes). On gfx950, measured, a
 // 384-thread kernel whose LDS is a static array and that carries __launch_bounds__ gets one resident
 // block per CU fewer than its size allows (48 KB: 2 instead of 3; 64 to 80 KB: 1 instead of 2), while the
-// same bytes given at launch keep the full count (256- and 512-thread blocks get it either way).
+// same bytes given at launch keep the full count (256- and 512-thread blocks get it either way). HIP on
+// gfx950 takes any launch-time size up to the CU's 160 KB without a per-kernel attribute (measured).
 __device__ __forceinline__ uint8_t* launch_lds()
 {
     extern __shared__ __align__(16) uint8_t rl_launch_lds[];
     return rl_launch_lds;
 }
 
-// Lets `kernel` take `bytes` of launch-time LDS (past 64 KB the runtime is asked first); call before each
-// launch: the runtime is asked once per kernel and device for the largest size so far.
-int allow_launch_lds_impl(const void* kernel, size_t bytes, const char* what);
-
-template <typename K>
-inline int allow_launch_lds(K* kernel, size_t bytes, const char* what)
-{
-    return bytes <= 65536 ? 0 : allow_launch_lds_impl(reinterpret_cast<const void*>(kernel), bytes, what);
-}
 
 constexpr int kWave = 64;
 
