@@ -26,9 +26,9 @@
  * The pages never fix the environment's mechanics; every constant and step of the tick below is a
  * reading, stated where it is used.
  *
- * Parity pins: GAE, normalisation and the loss are pinned by closed forms and hand-worked cases; the
- * environment is pinned by hand-worked episodes and invariants only, since no page gives its outputs
- * (its exhaustive-enumeration checks are "parity unpinned" beyond those invariants).
+ * Parity pins: GAE, normalisation and the loss are pinned by closed forms and hand-worked cases. No page
+ * gives the environment's outputs, so it is pinned to its stated reading: hand-worked episodes of every
+ * rule and invariants over an exhaustive enumeration of decision sequences.
  */
 #include <math.h>
 #include <stddef.h>
