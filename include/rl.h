@@ -344,7 +344,8 @@ int rl_ppo_loss(const float* logits, const int32_t* actions, const float* old_lo
  * on a device looks up that device's copy of the array (the device current at the call; `stream`, if not
  * NULL, must belong to it, else RL_EINVAL). A call whose workspace (rl_ppo_loss_workspace_bytes, less the
  * perm conversion's part when perm is NULL) exceeds 64 MiB returns RL_ESIZE and launches nothing: at
- * 16 minibatches that admits a perm up to 2^23 samples; mb_index any size (its partials take at most
+ * 16 minibatches that admits a perm up to 15,630,336 samples (1.86 x 2^23), at 32 or 64 up to about 10.7
+ * million; mb_index any size (its partials take at most
  * 1.2 MB); contiguous minibatches while their partials (24 bytes per minibatch and block) fit. Every call on one device shares that device's array and keeps
  * no state in it between calls (nothing in it must start at zero): calls that overlap on one device, on
  * different streams or from different host threads without ordering, race on it. */
