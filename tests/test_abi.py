@@ -216,5 +216,13 @@ def test_noalloc_loss_refuses_before_any_device_call():
     args = lambda b, mb, perm: (p, p, p, p, p, p, perm, None, None, b, 12, mb, 0.2, 0.5, 0.01, p, None)
     assert lib.rl_ppo_loss_noalloc(*args(1000, 300, None)) == -1                  # B not a multiple of mb
     assert "multiple" in lib.rl_last_error().decode()
-    assert lib.rl_ppo_loss_noalloc(*args(1 << 24, 1 << 20, p)) == -3              # 112 MiB with a perm
+    assert lib.rl_ppo_loss_noalloc(*args(1 << 24, 1 << 20, p)) == -3              # 68 MiB with a perm
     assert "fixed device array" in lib.rl_last_error().decode()
+    # at 16 minibatches the array admits a perm of up to 15,630,336 samples (the workspace size, a host-only
+    # call, says so); one minibatch row more is refused for its size
+    big = 15630336
+    need = ctypes.c_size_t()
+    assert lib.rl_ppo_loss_workspace_bytes(big, big // 16, ctypes.byref(need)) == 0 and need.value <= 64 << 20
+    assert lib.rl_ppo_loss_workspace_bytes(big + 16, (big + 16) // 16, ctypes.byref(need)) == 0
+    assert need.value > 64 << 20
+    assert lib.rl_ppo_loss_noalloc(*args(big + 16, (big + 16) // 16, p)) == -3
