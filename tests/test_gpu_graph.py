@@ -137,7 +137,8 @@ def test_counter_set_before_capture_is_refused_inside_it(gpu_lib):
 
 
 def test_captured_learn_phase_replays_bit_for_bit(gpu_lib):
-    # GAE with the deferred statistics, the loss from a permutation (its binned conversion) and the loss
+    # GAE with the deferred statistics, the loss from a permutation (its sort, then the stream pass placing
+    # its own bins, with launch-time LDS) and the loss
     # gradient from minibatch numbers, recorded into one graph: no call may allocate, synchronise or leave
     # a memset in the graph, so every replay must give the eager call's bits. Outputs are poisoned before
     # each replay; eager work and a synchronisation run between the replays.
