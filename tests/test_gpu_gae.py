@@ -122,7 +122,7 @@ def test_deterministic_stats(gpu_lib):
     np.testing.assert_array_equal(s1, s2)
 
 
-@pytest.mark.parametrize("t,n", [(128, 65536), (128, 2048), (37, 1000), (1500, 33), (1, 1)])
+@pytest.mark.parametrize("t,n", [(128, 65536), (129, 65536), (128, 2048), (37, 1000), (1500, 33), (1, 1)])
 def test_deferred_statistics_equal_the_finished_ones(t, n, gpu_lib):
     # normalize = 3 leaves the scan blocks' partial sums in adv_stats; finishing them (here, and inside the
     # loss) must give the very bits normalize = 2 gives, and the scan's outputs must not change
