@@ -1094,7 +1094,10 @@ def main():
                  "traffic": load_traffic("ppo_loss") if args.loss_mode == "stream" else None},
         "loss_perm": {"us": perm_s * 1e6, "min_us": float(np.min(iso["perm"])) * 1e3, "GB/s": perm_bytes / perm_s / 1e9,
                       "frac": perm_bytes / perm_s / 1e9 / HBM_PEAK_GBS, "bytes": perm_bytes,
-                      "vs_minibatch_numbers": None if stream_s is None else perm_s / stream_s},
+                      "vs_minibatch_numbers": None if stream_s is None else perm_s / stream_s,
+                      # the sort and the stream pass that places its own bins, from the counter runs
+                      "traffic": (lambda a, c: None if a is None or c is None else a + c)(
+                          load_traffic("ppo_loss_perm_sort"), load_traffic("ppo_loss_perm_stream"))},
         "loss_grad": {"us": grad_s * 1e6, "GB/s": grad_gbs, "frac": grad_gbs / HBM_PEAK_GBS, "bytes": grad_bytes,
                       "traffic": load_traffic("ppo_loss_grad")},
         "vtrace": {"us": vt_s * 1e6, "GB/s": vt_gbs, "frac": vt_gbs / HBM_PEAK_GBS, "bytes": vt_bytes,
