@@ -184,11 +184,12 @@ def test_perm_conversion_with_long_runs(b, mb, kind, gpu_lib):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("b,nmb", [((1 << 23) + 16, 16), ((1 << 23) + 16, 48)])
+@pytest.mark.parametrize("b,nmb", [((1 << 23) + 16, 16), ((1 << 23) + 16, 48), (1 << 24, 16)])
 def test_perm_conversion_two_rounds_of_bins(b, nmb, gpu_lib):
     # just past 2^23 samples the stream pass takes two rounds of 512 blocks (1024 bins) at 16 minibatches,
-    # and 513 sort rows; at 48 minibatches the placed numbers: bit for bit the minibatch-number results
-    # (those are checked against the oracle at other sizes)
+    # and 513 sort rows; at 48 minibatches the placed numbers; at 2^24, the largest sorted batch, 1024 bins
+    # (the most the sort holds) and 1024 sort rows: bit for bit the minibatch-number results (those are
+    # checked against the oracle at other sizes)
     rng = np.random.default_rng(b)
     perm = rng.permutation(b).astype(np.int32)
     _, _, _, out_perm, out_idx = _perm_vs_index(b, b // nmb, perm, 17)
